@@ -1,0 +1,492 @@
+/*
+ * moe_oracle.c -- plain, slow, fp64 CPU oracle of the fused MoE layer.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may call, link or
+ * load this file or the library built from it: only the test suite, the
+ * smoke check and the benchmark's CPU-baseline leg use it.  It shares no
+ * code, header, table or constant with the HIP path.
+ *
+ * Sources (web pages; cited by title and section):
+ *   [P3] "Mixture-of-Experts kernel engineering on Amazon SageMaker AI"
+ *        (summary text): a fused MoE merges token routing, data shuffling
+ *        and the expert network computations into one batched GPU op in
+ *        place of sequential per-expert loops; the expert GEMM is
+ *        C = A.B with A the tokens [M,K] and B the expert weights [K,N];
+ *        the Swap-AB passage (Figure 1) states C^T[N,M] = B^T[N,K].A^T[K,M],
+ *        so weights are held output-major as B^T[N,K]; the FP8 passage
+ *        names FP8 tensor scaling, matrix multiplication and expert
+ *        aggregation as the steps a one-pass backend fuses, for FP8
+ *        tensor-quantized (per-tensor scale) models.
+ *   [P2] "«До 10% пропускной способности и 9% к TTFT»: AWS раскрыла
+ *        оптимизации ядер MoE на SageMaker AI", sections "Зачем
+ *        оптимизировать ядра MoE" (same definition of fused MoE) and
+ *        "Triton вместо CUTLASS для FP8-квантования".
+ *   [P4] "AI混合专家模型性能优化全链路解析", chapter 1, dynamic expert load
+ *        balancing: experts are picked by top-k over router logits.
+ *
+ * What the oracle computes is the per-token expert loop that the fusion
+ * only reorders ([P3] summary, fused-MoE definition):
+ *
+ *   out[t] = sum_{j<k} w[t,j] * W2[e_tj] . ( silu(W1[e_tj][0:N] . x_t)
+ *                                            * (W1[e_tj][N:2N] . x_t) )
+ *
+ * The pages leave open the expert MLP's form, the gating details and the
+ * FP8 quantisation points.  The readings taken here (each one also listed
+ * in the design notes) are:
+ *   R1 logits are the fp32 rounding of the fp64 dot product x_t . W_r[e]
+ *      (+ bias[e] when a bias is given); every bf16*bf16 product is exact
+ *      in fp64.
+ *   R2 top-k selects the k largest fp32 logits, ties to the lower expert id,
+ *      slots in descending-logit order; selecting on logits equals selecting
+ *      on softmax probabilities since softmax is strictly increasing.
+ *   R3 routing weights are the softmax over all E renormalised over the k
+ *      selected, i.e. w_j = exp(l_j - l_0) / sum_j' exp(l_j' - l_0).
+ *   R4 W1[e] rows [0,N) are the gate, rows [N,2N) the up projection;
+ *      silu(z) = z / (1 + exp(-z)).
+ *   R5 the permutation is a stable counting sort of p = t*k + j by expert,
+ *      each expert's segment padded to a multiple of the block size with
+ *      the sentinel M*k.
+ *   R6 FP8 is OCP E4M3FN (bias 7, max 448, no infinities, NaN 0x7F/0xFF),
+ *      encoded round-to-nearest-even after clamping to +-448.
+ *   R7 FP8 activations are quantised per token (x) and per token-slot (the
+ *      SiLU*up activation), each with scale s = fp32(amax)/448 (1 if
+ *      amax = 0), code = E4M3(fp32(v) / s) with one correctly-rounded fp32
+ *      division; weight scales are per expert tensor.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+#define ORC_OK 0
+#define ORC_ERR_ARG 1
+#define ORC_ERR_MISSING_EXPERT 2
+#define ORC_ERR_NOMEM 3
+
+/* ---------------------------------------------------------------------- */
+/* Number formats                                                          */
+/* ---------------------------------------------------------------------- */
+
+/* bf16 is the top half of an IEEE binary32. */
+double orc_bf16_to_f64(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static float bf16_to_f32(uint16_t h)
+{
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return f;
+}
+
+/* OCP E4M3FN decode (R6): sign, 4 exponent bits (bias 7), 3 mantissa bits.
+ * Exponent field 0 is subnormal: m/8 * 2^-6.  S.1111.111 is NaN. */
+double orc_e4m3_to_f64(uint8_t c)
+{
+    int s = c >> 7;
+    int e = (c >> 3) & 15;
+    int m = c & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m, -9);
+    else
+        v = ldexp(1.0 + m / 8.0, e - 7);
+    return s ? -v : v;
+}
+
+/* OCP E4M3FN encode of an fp32 value (R6): nearest representable value,
+ * ties to the even mantissa, magnitudes clamped to 448 first.  All the
+ * arithmetic below is exact in double (power-of-two scalings of a float,
+ * then rint in the default round-half-even mode). */
+uint8_t orc_f32_to_e4m3(float f)
+{
+    double a;
+    int sign, ex;
+    double q;
+    if (isnan(f))
+        return 0x7F;
+    sign = signbit(f) ? 0x80 : 0;
+    a = fabs((double)f);
+    if (a > 448.0)
+        a = 448.0;
+    if (a < ldexp(1.0, -6)) {
+        /* subnormal range: grid step 2^-9; q == 8 is the smallest normal,
+         * whose code is also 8. */
+        q = rint(a * 512.0);
+        return (uint8_t)(sign | (int)q);
+    }
+    frexp(a, &ex);          /* a = f * 2^ex, f in [0.5, 1) */
+    ex -= 1;                /* a in [2^ex, 2^(ex+1)), ex in [-6, 8] */
+    q = rint(ldexp(a, 3 - ex)); /* mantissa incl. hidden bit, in [8, 16] */
+    if (q == 16.0) {
+        q = 8.0;
+        ex += 1;
+    }
+    return (uint8_t)(sign | ((ex + 7) << 3) | ((int)q - 8));
+}
+
+/* Per-row dynamic quantisation (R7) of n fp32 values. */
+static void quant_row_f32(const float *v, int64_t n, uint8_t *q, float *scale)
+{
+    float amax = 0.0f, s;
+    int64_t i;
+    for (i = 0; i < n; ++i) {
+        float a = fabsf(v[i]);
+        if (a > amax)
+            amax = a;
+    }
+    s = (amax == 0.0f) ? 1.0f : amax / 448.0f;
+    for (i = 0; i < n; ++i) {
+        float r = v[i] / s;
+        q[i] = orc_f32_to_e4m3(r);
+    }
+    *scale = s;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Gating                                                                  */
+/* ---------------------------------------------------------------------- */
+
+/* R1: logits[t,e] = fp32( sum_k x[t,k]*wr[e,k] + bias[e] ), k ascending. */
+int orc_logits(const uint16_t *x, const uint16_t *wr, const float *bias,
+               int64_t M, int64_t K, int64_t E, float *logits)
+{
+    int64_t t;
+    if (M < 0 || K <= 0 || E <= 0 || (M > 0 && (!x || !wr || !logits)))
+        return ORC_ERR_ARG;
+#pragma omp parallel for schedule(static)
+    for (t = 0; t < M; ++t) {
+        int64_t e, k;
+        for (e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (k = 0; k < K; ++k)
+                acc += orc_bf16_to_f64(x[t * K + k]) * orc_bf16_to_f64(wr[e * K + k]);
+            if (bias)
+                acc += (double)bias[e];
+            logits[t * E + e] = (float)acc;
+        }
+    }
+    return ORC_OK;
+}
+
+/* R2 + R3 on given fp32 logits: ids[t,j] int32 and weights[t,j] fp64. */
+int orc_topk(const float *logits, int64_t M, int64_t E, int64_t k,
+             int32_t *ids, double *weights)
+{
+    int64_t t;
+    if (M < 0 || E <= 0 || k < 1 || k > E || (M > 0 && (!logits || !ids)))
+        return ORC_ERR_ARG;
+    for (t = 0; t < M; ++t) {
+        const float *l = logits + t * E;
+        unsigned char *taken = (unsigned char *)calloc((size_t)E, 1);
+        double den = 0.0, l0;
+        int64_t j, e;
+        if (!taken)
+            return ORC_ERR_NOMEM;
+        for (j = 0; j < k; ++j) {
+            int64_t best = -1;
+            for (e = 0; e < E; ++e) {
+                if (taken[e])
+                    continue;
+                /* strict '>' keeps the lower id on equal logits */
+                if (best < 0 || l[e] > l[best])
+                    best = e;
+            }
+            taken[best] = 1;
+            ids[t * k + j] = (int32_t)best;
+        }
+        free(taken);
+        if (weights) {
+            l0 = (double)l[ids[t * k]];
+            for (j = 0; j < k; ++j)
+                den += exp((double)l[ids[t * k + j]] - l0);
+            for (j = 0; j < k; ++j)
+                weights[t * k + j] = exp((double)l[ids[t * k + j]] - l0) / den;
+        }
+    }
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Expert-sorted permutation (R5)                                           */
+/* ---------------------------------------------------------------------- */
+
+/* Capacity of sorted_ids: M*k + E*(B-1); of block_expert: capacity / B.
+ * Positions past num_padded hold the sentinel M*k and blocks past the last
+ * used one hold -1. */
+int orc_align(const int32_t *ids, int64_t M, int64_t k, int64_t E, int64_t B,
+              int32_t *sorted_ids, int32_t *block_expert,
+              int32_t *expert_offsets, int32_t *num_padded)
+{
+    int64_t n = M * k, cap, nblk, e, p, i;
+    int64_t *count, *fill;
+    if (M < 0 || k < 1 || E <= 0 || B < 1)
+        return ORC_ERR_ARG;
+    cap = n + E * (B - 1);
+    nblk = cap / B;
+    count = (int64_t *)calloc((size_t)E, sizeof *count);
+    fill = (int64_t *)calloc((size_t)E, sizeof *fill);
+    if (!count || !fill) {
+        free(count);
+        free(fill);
+        return ORC_ERR_NOMEM;
+    }
+    for (p = 0; p < n; ++p) {
+        if (ids[p] < 0 || ids[p] >= E) {
+            free(count);
+            free(fill);
+            return ORC_ERR_ARG;
+        }
+        count[ids[p]]++;
+    }
+    expert_offsets[0] = 0;
+    for (e = 0; e < E; ++e) {
+        int64_t padded = (count[e] + B - 1) / B * B;
+        expert_offsets[e + 1] = (int32_t)(expert_offsets[e] + padded);
+    }
+    *num_padded = expert_offsets[E];
+    for (i = 0; i < cap; ++i)
+        sorted_ids[i] = (int32_t)n;
+    for (p = 0; p < n; ++p) {     /* ascending p: stable within an expert */
+        e = ids[p];
+        sorted_ids[expert_offsets[e] + fill[e]] = (int32_t)p;
+        fill[e]++;
+    }
+    for (i = 0; i < nblk; ++i)
+        block_expert[i] = -1;
+    for (e = 0; e < E; ++e)
+        for (i = expert_offsets[e] / B; i < expert_offsets[e + 1] / B; ++i)
+            block_expert[i] = (int32_t)e;
+    free(count);
+    free(fill);
+    return ORC_OK;
+}
+
+/* ---------------------------------------------------------------------- */
+/* Expert MLP and combine                                                   */
+/* ---------------------------------------------------------------------- */
+
+static double silu(double z) { return z / (1.0 + exp(-z)); }
+
+/* One token-slot, bf16 weights: y[0:K] = W2 . (silu(W1g.x) * (W1u.x)). */
+static void expert_bf16(const uint16_t *xt, const uint16_t *w1, const uint16_t *w2,
+                        int64_t K, int64_t N, double *act, double *y)
+{
+    int64_t n, c, kk;
+    for (n = 0; n < N; ++n) {
+        const uint16_t *g = w1 + n * K;
+        const uint16_t *u = w1 + (N + n) * K;
+        double hg = 0.0, hu = 0.0;
+        for (kk = 0; kk < K; ++kk) {
+            double xv = orc_bf16_to_f64(xt[kk]);
+            hg += orc_bf16_to_f64(g[kk]) * xv;
+            hu += orc_bf16_to_f64(u[kk]) * xv;
+        }
+        act[n] = silu(hg) * hu;
+    }
+    for (c = 0; c < K; ++c) {
+        const uint16_t *r = w2 + c * N;
+        double acc = 0.0;
+        for (n = 0; n < N; ++n)
+            acc += orc_bf16_to_f64(r[n]) * act[n];
+        y[c] = acc;
+    }
+}
+
+/* One token-slot, e4m3 weights with per-tensor scales (R7). */
+static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, float w1s,
+                       const uint8_t *w2, float w2s, int64_t K, int64_t N,
+                       double *act, float *act32, uint8_t *aq, double *y)
+{
+    int64_t n, c, kk;
+    float sa;
+    for (n = 0; n < N; ++n) {
+        const uint8_t *g = w1 + n * K;
+        const uint8_t *u = w1 + (N + n) * K;
+        double hg = 0.0, hu = 0.0;
+        for (kk = 0; kk < K; ++kk) {
+            double xv = orc_e4m3_to_f64(xq[kk]);
+            hg += orc_e4m3_to_f64(g[kk]) * xv;
+            hu += orc_e4m3_to_f64(u[kk]) * xv;
+        }
+        hg *= (double)sx * (double)w1s;
+        hu *= (double)sx * (double)w1s;
+        act[n] = silu(hg) * hu;
+        act32[n] = (float)act[n];
+    }
+    quant_row_f32(act32, N, aq, &sa);
+    for (c = 0; c < K; ++c) {
+        const uint8_t *r = w2 + c * N;
+        double acc = 0.0;
+        for (n = 0; n < N; ++n)
+            acc += orc_e4m3_to_f64(r[n]) * orc_e4m3_to_f64(aq[n]);
+        y[c] = acc * (double)sa * (double)w2s;
+    }
+}
+
+/* Per-token dynamic quantisation of bf16 rows (R7): xq [M,K], sx [M]. */
+int orc_quant_rows_bf16(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sx)
+{
+    int64_t t;
+    float *row;
+    if (M < 0 || K <= 0)
+        return ORC_ERR_ARG;
+    row = (float *)malloc((size_t)K * sizeof *row);
+    if (!row)
+        return ORC_ERR_NOMEM;
+    for (t = 0; t < M; ++t) {
+        int64_t k;
+        for (k = 0; k < K; ++k)
+            row[k] = bf16_to_f32(x[t * K + k]);
+        quant_row_f32(row, K, xq + t * K, sx + t);
+    }
+    free(row);
+    return ORC_OK;
+}
+
+/* Per-row dynamic quantisation of fp32 rows (R7), exported for the pins. */
+int orc_quant_rows_f32(const float *v, int64_t M, int64_t K, uint8_t *q, float *s)
+{
+    int64_t t;
+    if (M < 0 || K <= 0)
+        return ORC_ERR_ARG;
+    for (t = 0; t < M; ++t)
+        quant_row_f32(v + t * K, K, q + t * K, s + t);
+    return ORC_OK;
+}
+
+/*
+ * The whole layer for a list of tokens.
+ *
+ *   dtype     0 = bf16 weights, 1 = e4m3 weights (w1s/w2s per expert)
+ *   x         bf16 [M,K] (all tokens: routing of token t reads row t only)
+ *   wr        bf16 [E,K]; bias fp32 [E] or NULL
+ *   w1[e]     expert e's W1 [2N,K] (bf16 or e4m3), NULL if not provided
+ *   w2[e]     expert e's W2 [K,N]
+ *   tokens    the n_tok token indices to evaluate (each in [0,M))
+ *   out       fp64 [n_tok, K]
+ *   ids_out   int32 [n_tok, k] or NULL; wts_out fp64 [n_tok, k] or NULL
+ *
+ * Returns ORC_ERR_MISSING_EXPERT if a selected expert's weights are NULL.
+ * Token-slots run in parallel; each writes its own y row, and the combine
+ * then sums the k slots of a token in ascending j, so results do not depend
+ * on the thread count.
+ */
+int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const float *bias,
+                    const void *const *w1, const void *const *w2,
+                    const float *w1s, const float *w2s,
+                    int64_t M, int64_t K, int64_t N, int64_t E, int64_t k,
+                    const int64_t *tokens, int64_t n_tok,
+                    double *out, int32_t *ids_out, double *wts_out)
+{
+    int64_t i, nslot = n_tok * k;
+    int32_t *ids;
+    double *wts, *y;
+    float *lg;
+    int rc = ORC_OK;
+    if ((dtype != 0 && dtype != 1) || M < 0 || K <= 0 || N <= 0 || E <= 0 ||
+        k < 1 || k > E || n_tok < 0 || !x || !wr || !w1 || !w2 || !out ||
+        (n_tok > 0 && !tokens) || (dtype == 1 && (!w1s || !w2s)))
+        return ORC_ERR_ARG;
+    for (i = 0; i < n_tok; ++i)
+        if (tokens[i] < 0 || tokens[i] >= M)
+            return ORC_ERR_ARG;
+    ids = (int32_t *)malloc((size_t)(nslot > 0 ? nslot : 1) * sizeof *ids);
+    wts = (double *)malloc((size_t)(nslot > 0 ? nslot : 1) * sizeof *wts);
+    lg = (float *)malloc((size_t)(n_tok > 0 ? n_tok : 1) * (size_t)E * sizeof *lg);
+    y = (double *)malloc((size_t)(nslot > 0 ? nslot : 1) * (size_t)K * sizeof *y);
+    if (!ids || !wts || !lg || !y) {
+        rc = ORC_ERR_NOMEM;
+        goto done;
+    }
+    /* gating for the chosen tokens (R1-R3) */
+    for (i = 0; i < n_tok; ++i) {
+        rc = orc_logits(x + tokens[i] * K, wr, bias, 1, K, E, lg + i * E);
+        if (rc)
+            goto done;
+    }
+    rc = orc_topk(lg, n_tok, E, k, ids, wts);
+    if (rc)
+        goto done;
+    for (i = 0; i < nslot; ++i)
+        if (!w1[ids[i]] || !w2[ids[i]]) {
+            rc = ORC_ERR_MISSING_EXPERT;
+            goto done;
+        }
+
+#pragma omp parallel
+    {
+        double *act = (double *)malloc((size_t)N * sizeof *act);
+        float *act32 = (float *)malloc((size_t)N * sizeof *act32);
+        uint8_t *aq = (uint8_t *)malloc((size_t)N);
+        uint8_t *xq = (uint8_t *)malloc((size_t)K);
+        float *xrow = (float *)malloc((size_t)K * sizeof *xrow);
+        int64_t s;
+#pragma omp for schedule(dynamic, 1)
+        for (s = 0; s < nslot; ++s) {
+            int64_t t = tokens[s / k];
+            int e = ids[s];
+            const uint16_t *xt = x + t * K;
+            if (dtype == 0) {
+                expert_bf16(xt, (const uint16_t *)w1[e], (const uint16_t *)w2[e],
+                            K, N, act, y + s * K);
+            } else {
+                float sx;
+                int64_t kk;
+                for (kk = 0; kk < K; ++kk)
+                    xrow[kk] = bf16_to_f32(xt[kk]);
+                quant_row_f32(xrow, K, xq, &sx);
+                expert_fp8(xq, sx, (const uint8_t *)w1[e], w1s[e],
+                           (const uint8_t *)w2[e], w2s[e], K, N, act, act32, aq,
+                           y + s * K);
+            }
+        }
+        free(act);
+        free(act32);
+        free(aq);
+        free(xq);
+        free(xrow);
+    }
+
+    /* weighted combine, slots in ascending j */
+    for (i = 0; i < n_tok; ++i) {
+        int64_t c, j;
+        for (c = 0; c < K; ++c) {
+            double acc = 0.0;
+            for (j = 0; j < k; ++j)
+                acc += wts[i * k + j] * y[(i * k + j) * K + c];
+            out[i * K + c] = acc;
+        }
+    }
+    if (ids_out)
+        memcpy(ids_out, ids, (size_t)nslot * sizeof *ids);
+    if (wts_out)
+        memcpy(wts_out, wts, (size_t)nslot * sizeof *wts);
+done:
+    free(ids);
+    free(wts);
+    free(lg);
+    free(y);
+    return rc;
+}
+
+/* Number of threads an OpenMP parallel region will use. */
+int orc_num_threads(void)
+{
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
