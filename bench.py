@@ -1,0 +1,269 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused MoE layer on one MI355X (gfx950).
+
+One step = one call of moe_fused_forward (router, permutation, GEMM1 +
+SiLU*up, GEMM2, combine) over one batch of synthetic tokens already resident
+in HBM.  The default workload is the Mixtral-shaped decode batch (M=8 tokens,
+K=4096, N=14336, E=8, top-2, bf16).  W untimed warm-up steps, then exactly K
+steps bracketed by torch.cuda.synchronize(); value = tokens per second.
+
+A second pass of K steps through moe_fused_forward_timed records HIP events
+between the kernels on the stream they run on; the dominant kernel's mean
+duration gives the roofline fraction (algorithmic bytes or FLOPs per launch
+/ duration vs the MI355X peak).  The CPU oracle is timed on this host's
+cores on a bounded sample of the same workload as a reference point.
+
+Prints ONE JSON line.  Only one GPU is used: --gpus N with N > 1 exits.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # dense
+STAGES = ["router_logits", "router_topk", "align", "gemm1", "act_quant", "gemm2", "combine"]
+METRIC = "fused-MoE layer tokens/s; decode HBM TB/s and prefill MFMA TFLOPS vs peak"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def hip_runtime():
+    import torch
+    path = os.path.join(os.path.dirname(torch.__file__), "lib", "libamdhip64.so")
+    hip = ctypes.CDLL(path if os.path.exists(path) else "libamdhip64.so")
+    hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+    hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                        ctypes.c_void_p]
+    hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+    return hip
+
+
+def source_digest(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        with open(p, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mixtral_decode")
+    ap.add_argument("--layers", type=int, default=0,
+                    help="distinct weight copies stepped round-robin (0 = enough to exceed "
+                         "the 256 MB last-level cache several times)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=0,
+                    help="tokens in the oracle's sample (0 = whole batch up to 8)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1",
+                          "n_gpus": args.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import moe_layer_04_amd as moe
+    from moe_layer_04_amd import workloads as wlm
+
+    if args.workload not in wlm.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; one of {list(wlm.WORKLOADS)}")
+    wl = wlm.WORKLOADS[args.workload]
+    if not torch.cuda.is_available():
+        sys.exit("no GPU visible")
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    moe.load_library(build_if_missing=True)
+
+    log(f"generating {wl}")
+    g = wlm.generate(wl, dev)
+    wbytes = 1 if wl.fp8 else 2
+    dtype_name = "fp8" if wl.fp8 else "bf16"
+    dtype = moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16
+
+    # routing of this batch (for the realised active-expert count)
+    ids, _, _ = moe.moe_topk(g["x"], g["w_router"], g["bias"], wl.topk)
+    torch.cuda.synchronize()
+    active = int(torch.unique(ids).numel())
+    w1_e = 2 * wl.N * wl.K * wbytes
+    w2_e = wl.K * wl.N * wbytes
+    touched = active * (w1_e + w2_e)
+    layers = args.layers or max(1, min(8, math.ceil(2 * 2**30 / touched)))
+    w1s = [g["w1"]] + [g["w1"].clone() for _ in range(layers - 1)]
+    w2s = [g["w2"]] + [g["w2"].clone() for _ in range(layers - 1)]
+    log(f"active experts {active}, {touched / 1e9:.3f} GB of weights per step, {layers} layer(s)")
+
+    need = moe.workspace_size(dtype, wl.M, wl.K, wl.N, wl.E, wl.topk)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    out = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device=dev)
+
+    def step(i):
+        moe.moe_fused_forward(g["x"], g["w_router"], g["bias"], w1s[i % layers], w2s[i % layers],
+                              wl.topk, w1_scale=g["w1_scale"], w2_scale=g["w2_scale"], out=out,
+                              workspace=ws)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    tokens_per_s = wl.M * args.steps / elapsed
+
+    # ---- per-kernel durations from HIP events on the layer's stream --------
+    hip = hip_runtime()
+    lib = moe.load_library()
+    stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+    nev = len(STAGES) + 1
+    evs = []
+    for _ in range(args.steps):
+        arr = (ctypes.c_void_p * nev)()
+        for j in range(nev):
+            h = ctypes.c_void_p()
+            assert hip.hipEventCreate(ctypes.byref(h)) == 0
+            arr[j] = h
+        evs.append(arr)
+    nbytes = ctypes.c_size_t(ws.numel())
+
+    def P(t):
+        return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+    torch.cuda.synchronize()
+    for i in range(args.steps):
+        L = i % layers
+        rc = lib.moe_fused_forward_timed(P(g["x"]), P(g["w_router"]), P(g["bias"]), P(w1s[L]),
+                                         P(w2s[L]), P(g["w1_scale"]), P(g["w2_scale"]), dtype,
+                                         wl.M, wl.K, wl.N, wl.E, wl.topk, 0, P(out), P(ws),
+                                         ctypes.byref(nbytes), stream, evs[i])
+        assert rc == 0, moe.status_string(rc)
+    torch.cuda.synchronize()
+    stage_ms = {s: [] for s in STAGES}
+    total_ms = []
+    for arr in evs:
+        f = ctypes.c_float()
+        for j, s in enumerate(STAGES):
+            assert hip.hipEventElapsedTime(ctypes.byref(f), arr[j], arr[j + 1]) == 0
+            stage_ms[s].append(f.value)
+        assert hip.hipEventElapsedTime(ctypes.byref(f), arr[0], arr[nev - 1]) == 0
+        total_ms.append(f.value)
+        for j in range(nev):
+            hip.hipEventDestroy(arr[j])
+    kern_us = {s: float(np.mean(v)) * 1e3 for s, v in stage_ms.items()}
+
+    # ---- algorithmic work and roofline --------------------------------------
+    slots = wl.M * wl.topk
+    alg_bytes = (touched + wl.M * wl.K * 2 * 2 + wl.E * wl.K * 2
+                 + (wl.E * 4 if wl.bias_var else 0) + (2 * wl.E * 4 if wl.fp8 else 0))
+    alg_flops = 6.0 * slots * wl.N * wl.K
+    step_s = ms_per_step / 1e3
+    decode = (slots <= 16 * wl.E) or wl.fp8
+    g1_s = kern_us["gemm1"] / 1e6
+    if decode:
+        # GEMM1 reads W1 of every active expert once plus the token rows
+        g1_bytes = active * w1_e + wl.M * wl.K * (1 if wl.fp8 else 2)
+        achieved = g1_bytes / g1_s / 1e9
+        roofline = {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                    "units_per_launch": active, "bytes_per_unit": w1_e}
+    else:
+        g1_flops = 4.0 * slots * wl.N * wl.K
+        achieved = g1_flops / g1_s / 1e12
+        peak = MFMA_PEAK_TFLOPS[dtype_name]
+        roofline = {"bound": "mfma", "kernel": "gemm1", "achieved": round(achieved, 1),
+                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "traffic": None, "units_per_launch": slots,
+                    "flops_per_unit": 4.0 * wl.N * wl.K}
+    # HBM traffic from committed counter runs, only while the kernels are unchanged
+    digest = source_digest(sorted(
+        os.path.join(ROOT, "moe_layer_04_amd", "csrc", f)
+        for f in os.listdir(os.path.join(ROOT, "moe_layer_04_amd", "csrc"))))
+    pmc = os.path.join(ROOT, "profiles", f"gemm1_{wl.name}_pmc.json")
+    if os.path.exists(pmc):
+        rec = json.load(open(pmc))
+        if rec.get("source_digest") == digest:
+            roofline["traffic"] = rec.get("bytes_per_launch")
+
+    result = {
+        "metric": METRIC,
+        "value": round(tokens_per_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype_name,
+        "data": "synthetic (seeded N(0,1/fan_in) weights, random init; no dataset)",
+        "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "E": wl.E,
+                   "topk": wl.topk, "weights": "e4m3 per-tensor" if wl.fp8 else "bf16",
+                   "router_bias_var": wl.bias_var, "seed": wl.seed, "layers": layers,
+                   "active_experts": active},
+        "step_hbm_GBps": round(alg_bytes / step_s / 1e9, 1),
+        "step_hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
+        "step_tflops": round(alg_flops / step_s / 1e12, 2),
+        "algorithmic_bytes": alg_bytes,
+        "algorithmic_flops": alg_flops,
+        "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
+        "timed_pass_ms_per_step": round(float(np.mean(total_ms)), 4),
+        "roofline": roofline,
+        "source_digest": digest,
+    }
+
+    # ---- CPU oracle on a bounded sample -------------------------------------
+    if not args.no_cpu_baseline:
+        import oracle
+        n_tok = args.cpu_tokens or min(wl.M, 8)
+        toks = list(range(n_tok))
+        x_h = wlm.to_numpy_bits(g["x"])
+        wr_h = wlm.to_numpy_bits(g["w_router"])
+        bias_h = None if g["bias"] is None else g["bias"].cpu().numpy()
+        rids, _ = oracle.topk(oracle.logits(x_h[toks], wr_h, bias_h), wl.topk)
+        need_e = sorted(set(rids.reshape(-1).tolist()))
+        w1h = [wlm.to_numpy_bits(g["w1"][e]) if e in need_e else None for e in range(wl.E)]
+        w2h = [wlm.to_numpy_bits(g["w2"][e]) if e in need_e else None for e in range(wl.E)]
+        s1 = None if g["w1_scale"] is None else g["w1_scale"].cpu().numpy()
+        s2 = None if g["w2_scale"] is None else g["w2_scale"].cpu().numpy()
+        log(f"oracle on {n_tok} token(s), {len(need_e)} expert(s)")
+        t0 = time.perf_counter()
+        ref, _, _ = oracle.moe_forward(x_h, wr_h, bias_h, w1h, w2h, wl.topk, w1_scale=s1,
+                                       w2_scale=s2, tokens=toks, fp8=wl.fp8)
+        cpu_s = time.perf_counter() - t0
+        got = out.float().cpu().numpy()[toks].astype(np.float64)
+        den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
+        err = float((np.abs(got - ref).max(axis=1) / den).max())
+        result["cpu_baseline"] = {
+            "value": round(n_tok / cpu_s, 3), "unit": "tokens/s",
+            "cores": min(oracle.num_threads(), n_tok * wl.topk), "kind": "oracle",
+            "sample": f"first {n_tok} of the {wl.M} tokens of the same batch "
+                      f"({n_tok * wl.topk} token-slots, fp64)",
+            "seconds": round(cpu_s, 3)}
+        result["parity_vs_oracle"] = {"max_row_rel_err": err, "tokens": n_tok,
+                                      "tol": 6e-2 if wl.fp8 else 2e-2}
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,227 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) fused Mixture-of-Experts layer.
+ *
+ * What the layer computes.  "Mixture-of-Experts kernel engineering on Amazon
+ * SageMaker AI" (summary text, fused-MoE definition) describes a fused MoE
+ * as one batched GPU operation that merges token routing, data shuffling
+ * and the expert networks, in place of sequential per-expert loops.  The
+ * expert GEMM there is C = A.B with A the tokens [M,K] and B the expert
+ * weights [K,N]; its Swap-AB passage (Figure 1) computes the transpose
+ * C^T[N,M] = B^T[N,K].A^T[K,M], so expert weights are held output-major
+ * with the reduction dimension contiguous.  This library keeps that layout:
+ *
+ *   x        bf16 [M,K]      tokens, row-major
+ *   w_router bf16 [E,K]      router weights
+ *   w1       [E,2N,K]        per expert: rows [0,N) gate, rows [N,2N) up
+ *   w2       [E,K,N]         per expert: down projection
+ *   out      bf16 [M,K]
+ *
+ *   out[t] = sum_{j<topk} w[t,j] * W2[e_tj] . (silu(W1g[e_tj].x_t) * (W1u[e_tj].x_t))
+ *
+ * with (e_t, w_t) the top-k experts of softmax(x_t.W_r^T + bias) and their
+ * probabilities renormalised over the k picked (ties to the lower expert id,
+ * slots in descending order).  FP8 follows the same page's FP8 passage
+ * ("tensor-quantized" models: one fp32 scale per expert weight tensor);
+ * activations are quantised per token at run time.
+ *
+ * Conventions shared by every entry point:
+ *   - Every pointer argument is a DEVICE pointer owned by the caller, except
+ *     the size_t* of moe_fused_forward, which is a host pointer.  The library
+ *     never allocates, frees or keeps device memory, keeps no mutable global
+ *     state and is re-entrant; calls on different streams may overlap as long
+ *     as their buffers do not.
+ *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
+ *     the default stream).  The library never synchronises the host.
+ *   - Arguments are validated before any HIP call, so every error path is
+ *     testable on a host without a GPU: a call that returns an error has
+ *     enqueued nothing.  MOE_ERR_HIP reports a launch failure
+ *     (hipGetLastError after the launches).
+ *   - Device pointers must be 16-byte aligned; tensors are dense row-major
+ *     with no strides.
+ *   - M == 0 is a valid no-op returning MOE_OK.
+ */
+#ifndef MOE_LAYER_MOE_H
+#define MOE_LAYER_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = 1, /* null required pointer, negative size, topk out of [1,E], misalignment */
+    MOE_ERR_UNSUPPORTED = 2, /* a size outside the supported envelope (see each call) */
+    MOE_ERR_WORKSPACE = 3,   /* workspace smaller than the size the query returned */
+    MOE_ERR_HIP = 4          /* a HIP launch failed */
+} moe_status;
+
+typedef enum {
+    MOE_BF16 = 0,     /* w1/w2 bf16; w1_scale/w2_scale must be NULL */
+    MOE_FP8_E4M3 = 1  /* w1/w2 OCP E4M3FN codes (uint8) with fp32 per-expert scales */
+} moe_dtype;
+
+/* Kernel family used by the expert GEMMs; results agree up to fp32
+ * summation order whichever is picked. */
+typedef enum {
+    MOE_REGIME_AUTO = 0,    /* pick from the mean rows per expert, M*topk/E */
+    MOE_REGIME_DECODE = 1,  /* Swap-AB: weight rows on the MFMA row dimension */
+    MOE_REGIME_PREFILL = 2  /* full MFMA tiles of token rows x weight rows */
+} moe_regime;
+
+/* Supported envelope: 1 <= E <= 256, 1 <= topk <= min(E,16), K >= 1 and
+ * N >= 1; moe_fused_forward additionally needs K and N multiples of 128,
+ * M*topk < 2^31 and (E*(block)+M*topk) * max(K,N) < 2^31. */
+#define MOE_MAX_EXPERTS 256
+#define MOE_MAX_TOPK 16
+
+/*
+ * moe_topk -- router: logits, top-k selection and routing weights.
+ *
+ * Source: "Mixture-of-Experts kernel engineering on Amazon SageMaker AI"
+ * (summary text, fused-MoE definition: token routing is part of the fused
+ * op); "AI混合专家模型性能优化全链路解析", chapter 1 (experts are chosen by
+ * top-k over the router logits).
+ *
+ *   x            bf16 [M,K]
+ *   w_router     bf16 [E,K]
+ *   router_bias  fp32 [E] added to every token's logits, or NULL
+ *   topk_ids     out int32 [M,topk]: the topk largest logits, descending,
+ *                equal logits ordered by ascending expert id
+ *   topk_weights out fp32 [M,topk]: exp(l_j - l_0) / sum_j' exp(l_j' - l_0)
+ *   logits       out fp32 [M,E] (required): each logit is the fp32 rounding
+ *                of an fp64-accumulated dot product plus bias
+ *
+ * Errors: INVALID_ARG for null pointers (x, w_router, topk_ids,
+ * topk_weights, logits), M < 0, K < 1, topk < 1 or topk > E;
+ * UNSUPPORTED for E > 256 or topk > 16.
+ */
+moe_status moe_topk(const void *x, const void *w_router, const float *router_bias,
+                    int M, int K, int E, int topk,
+                    int32_t *topk_ids, float *topk_weights, float *logits,
+                    void *stream);
+
+/*
+ * moe_align -- expert-sorted, block-padded permutation of the token slots.
+ *
+ * Source: "Mixture-of-Experts kernel engineering on Amazon SageMaker AI"
+ * (summary text: data shuffling is part of the fused op; the FP8 passage's
+ * scheduling around variable token bucketing); "Amazon SageMaker AI上的混合
+ * 专家模型内核工程优化", section on H200 bottlenecks (per-expert batch sizes
+ * change dynamically).
+ *
+ * Slot p = t*topk + j (token t, slot j) is sorted stably by expert id, so
+ * each expert's slots are contiguous and ascending in p; each expert's
+ * segment is padded to a multiple of block_m with the sentinel M*topk.
+ *
+ *   topk_ids       int32 [M,topk], each in [0,E)
+ *   sorted_ids     out int32 [cap], cap = M*topk + E*(block_m-1); entries at
+ *                  and past num_padded hold the sentinel
+ *   block_expert   out int32 [cap / block_m]: expert owning each block of
+ *                  block_m sorted rows, -1 past the last used block
+ *   expert_offsets out int32 [E+1]: padded segment starts, [E] = num_padded
+ *   num_padded     out int32 [1]
+ *
+ * Errors: INVALID_ARG for null pointers, M < 0, topk < 1, E < 1 or
+ * block_m < 1; UNSUPPORTED for E > 256, block_m > 1024 or M*topk >= 2^30.
+ * Ids outside [0,E) are a caller error; they are clamped into range on the
+ * device so no access goes out of bounds, and the result is unspecified.
+ */
+moe_status moe_align(const int32_t *topk_ids, int M, int topk, int E, int block_m,
+                     int32_t *sorted_ids, int32_t *block_expert,
+                     int32_t *expert_offsets, int32_t *num_padded, void *stream);
+
+/*
+ * moe_quant_rows_e4m3 -- per-row dynamic FP8 quantisation of bf16 rows, the
+ * step the fused forward applies to the tokens before GEMM1 in the e4m3 path.
+ *
+ * Source: "Mixture-of-Experts kernel engineering on Amazon SageMaker AI"
+ * (summary text, FP8 passage: FP8 tensor scaling is one of the steps fused
+ * into the single pass); "Amazon SageMaker AI上的混合专家模型内核工程优化",
+ * section 2 (scale factors recomputed dynamically at inference time).
+ *
+ *   x      bf16 [M,K]
+ *   q      out uint8 [M,K]: OCP E4M3FN code of x/s, round to nearest even,
+ *          magnitudes clamped to 448
+ *   scale  out fp32 [M]: s = amax_k |x[t,k]| / 448 (one correctly rounded
+ *          fp32 division), 1 when the row is all zero
+ *
+ * Errors: INVALID_ARG for null pointers, M < 0 or K < 1; UNSUPPORTED for
+ * M*K >= 2^31.
+ */
+moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *scale,
+                               void *stream);
+
+/*
+ * moe_fused_forward -- the whole layer: router, permutation, GEMM1 with the
+ * SiLU*up epilogue, GEMM2 with the routing-weighted un-permute, combine.
+ *
+ * Source: "Mixture-of-Experts kernel engineering on Amazon SageMaker AI"
+ * (summary text: fused-MoE definition; decode-phase passage and Figure 1,
+ * Swap-AB; FP8 passage: FP8 tensor scaling, matrix multiplication and
+ * expert aggregation fused, for per-tensor FP8 models).
+ *
+ *   x, w_router, router_bias   as moe_topk
+ *   w1        [E,2N,K] bf16 or e4m3 (dtype)
+ *   w2        [E,K,N]  bf16 or e4m3
+ *   w1_scale  fp32 [E] (MOE_FP8_E4M3) / NULL (MOE_BF16); likewise w2_scale
+ *   out       out bf16 [M,K]
+ *   workspace device buffer of at least *workspace_bytes bytes (256-byte
+ *             aligned), or NULL to query: with workspace == NULL the call
+ *             stores the required size in *workspace_bytes, enqueues
+ *             nothing and returns MOE_OK.  The size depends only on
+ *             (dtype, M, K, N, E, topk).
+ *   workspace_bytes  host pointer: in = size of `workspace`, out = required
+ *
+ * FP8: x is quantised per token to e4m3 with scale amax/448; the SiLU*up
+ * activation per token-slot likewise; GEMM accumulation is fp32.
+ *
+ * Errors: as moe_topk, plus INVALID_ARG for null w1/w2/out/workspace_bytes,
+ * N < 1, a bad dtype, scales given for bf16 or missing for fp8;
+ * UNSUPPORTED for K or N not a multiple of 128 or the size limits above;
+ * WORKSPACE if *workspace_bytes is below the required size.
+ */
+moe_status moe_fused_forward(const void *x, const void *w_router, const float *router_bias,
+                             const void *w1, const void *w2,
+                             const float *w1_scale, const float *w2_scale,
+                             int dtype, int M, int K, int N, int E, int topk,
+                             void *out, void *workspace, size_t *workspace_bytes,
+                             void *stream);
+
+/* moe_fused_forward with the GEMM kernel family chosen by the caller
+ * (moe_regime).  Used to cross-check the Swap-AB decode kernels against the
+ * full-tile kernels on identical inputs (C^T = B^T.A^T, Figure 1 of the
+ * page above). */
+moe_status moe_fused_forward_ex(const void *x, const void *w_router, const float *router_bias,
+                                const void *w1, const void *w2,
+                                const float *w1_scale, const float *w2_scale,
+                                int dtype, int M, int K, int N, int E, int topk,
+                                int regime, void *out, void *workspace,
+                                size_t *workspace_bytes, void *stream);
+
+/* moe_fused_forward_ex instrumented with timing events: `events` is a host
+ * array of 8 hipEvent_t handles created by the caller.  events[0] is
+ * recorded on `stream` before the first launch and events[i] after stage i:
+ * 1 router logits, 2 top-k (+ token quantisation), 3 align, 4 GEMM1 +
+ * SiLU*up, 5 activation quantisation (recorded with nothing before it on
+ * the bf16 path), 6 GEMM2, 7 combine.  Used by the benchmark to time each
+ * kernel on the stream it runs on.  Errors as moe_fused_forward_ex, plus
+ * INVALID_ARG for a NULL `events` when workspace is non-NULL. */
+moe_status moe_fused_forward_timed(const void *x, const void *w_router, const float *router_bias,
+                                   const void *w1, const void *w2,
+                                   const float *w1_scale, const float *w2_scale,
+                                   int dtype, int M, int K, int N, int E, int topk,
+                                   int regime, void *out, void *workspace,
+                                   size_t *workspace_bytes, void *stream,
+                                   void *const *events);
+
+/* Static, NUL-terminated name of a status code. */
+const char *moe_status_string(int status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_LAYER_MOE_H */

@@ -1,0 +1,216 @@
+"""Thin ctypes binding of libmoe.so (the C ABI in include/moe.h).
+
+Argument marshalling only: tensors are checked for device, dtype, shape and
+contiguity, outputs and the workspace are allocated with torch (plumbing),
+and every step of the layer runs in the library's HIP kernels on the
+current torch stream.  There is no fallback: if the library is missing or a
+call fails, an exception is raised.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+from typing import Optional
+
+import torch
+
+from . import build as _build
+
+LIB_PATH = _build.LIB
+
+MOE_OK = 0
+MOE_ERR_INVALID_ARG = 1
+MOE_ERR_UNSUPPORTED = 2
+MOE_ERR_WORKSPACE = 3
+MOE_ERR_HIP = 4
+
+MOE_BF16 = 0
+MOE_FP8_E4M3 = 1
+
+MOE_REGIME_AUTO = 0
+MOE_REGIME_DECODE = 1
+MOE_REGIME_PREFILL = 2
+
+EXPORTS = ("moe_topk", "moe_align", "moe_quant_rows_e4m3", "moe_fused_forward",
+           "moe_fused_forward_ex", "moe_fused_forward_timed", "moe_status_string")
+
+_lock = threading.Lock()
+_lib = None
+
+
+class MoEError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what} failed: {status_string(status)} ({status})")
+
+
+def load_library(build_if_missing: bool = False):
+    """Load libmoe.so (torch first, so the process has one HIP runtime)."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            if not build_if_missing:
+                raise RuntimeError(
+                    f"{LIB_PATH} is missing: build it with `python -m moe_layer_04_amd.build`")
+            _build.build()
+        lib = ctypes.CDLL(LIB_PATH)
+        P, I, SZP = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
+        lib.moe_topk.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
+        lib.moe_align.argtypes = [P, I, I, I, I, P, P, P, P, P]
+        lib.moe_quant_rows_e4m3.argtypes = [P, I, I, P, P, P]
+        lib.moe_fused_forward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, SZP, P]
+        lib.moe_fused_forward_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
+                                             SZP, P]
+        lib.moe_fused_forward_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
+                                                SZP, P, P]
+        for name in ("moe_topk", "moe_align", "moe_quant_rows_e4m3", "moe_fused_forward",
+                     "moe_fused_forward_ex", "moe_fused_forward_timed"):
+            getattr(lib, name).restype = ctypes.c_int
+        lib.moe_status_string.argtypes = [I]
+        lib.moe_status_string.restype = ctypes.c_char_p
+        _lib = lib
+        return lib
+
+
+def status_string(status: int) -> str:
+    return load_library().moe_status_string(int(status)).decode()
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _check(rc: int, what: str):
+    if rc != MOE_OK:
+        raise MoEError(rc, what)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    return t
+
+
+# --------------------------------------------------------------------------
+# entry points (same names as the C ABI)
+# --------------------------------------------------------------------------
+
+def moe_topk(x: torch.Tensor, w_router: torch.Tensor, router_bias: Optional[torch.Tensor],
+             topk: int):
+    """Router: (topk_ids int32 [M,k], topk_weights fp32 [M,k], logits fp32 [M,E])."""
+    lib = load_library()
+    M, K = x.shape
+    E = w_router.shape[0]
+    _dev(x, "x", torch.bfloat16)
+    _dev(w_router, "w_router", torch.bfloat16, (E, K))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    dev = x.device
+    ids = torch.empty((M, topk), dtype=torch.int32, device=dev)
+    w = torch.empty((M, topk), dtype=torch.float32, device=dev)
+    logits = torch.empty((M, E), dtype=torch.float32, device=dev)
+    _check(lib.moe_topk(_ptr(x), _ptr(w_router), _ptr(router_bias), M, K, E, topk, _ptr(ids),
+                        _ptr(w), _ptr(logits), _stream(dev)), "moe_topk")
+    return ids, w, logits
+
+
+def moe_align(topk_ids: torch.Tensor, num_experts: int, block_m: int):
+    """(sorted_ids [M*k + E*(B-1)], block_expert [that // B], expert_offsets [E+1],
+    num_padded [1]), all int32 on the device."""
+    lib = load_library()
+    _dev(topk_ids, "topk_ids", torch.int32)
+    M, k = topk_ids.shape
+    cap = M * k + num_experts * (block_m - 1)
+    dev = topk_ids.device
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.moe_align(_ptr(topk_ids), M, k, num_experts, block_m, _ptr(sorted_ids),
+                         _ptr(block_expert), _ptr(offsets), _ptr(npad), _stream(dev)),
+           "moe_align")
+    return sorted_ids, block_expert[: cap // block_m], offsets, npad
+
+
+def moe_quant_rows_e4m3(x: torch.Tensor):
+    """Per-row dynamic e4m3: (codes uint8 [M,K], scales fp32 [M])."""
+    lib = load_library()
+    _dev(x, "x", torch.bfloat16)
+    M, K = x.shape
+    q = torch.empty((M, K), dtype=torch.uint8, device=x.device)
+    s = torch.empty(M, dtype=torch.float32, device=x.device)
+    _check(lib.moe_quant_rows_e4m3(_ptr(x), M, K, _ptr(q), _ptr(s), _stream(x.device)),
+           "moe_quant_rows_e4m3")
+    return q, s
+
+
+def workspace_size(dtype: int, M: int, K: int, N: int, E: int, topk: int,
+                   regime: int = MOE_REGIME_AUTO) -> int:
+    """Bytes of workspace moe_fused_forward needs (no GPU call is made)."""
+    lib = load_library()
+    nbytes = ctypes.c_size_t(0)
+    dummy = ctypes.c_void_p(0x100)
+    s1 = dummy if dtype == MOE_FP8_E4M3 else None
+    _check(lib.moe_fused_forward_ex(dummy, dummy, None, dummy, dummy, s1, s1, dtype, M, K, N, E,
+                                    topk, regime, dummy, None, ctypes.byref(nbytes), None),
+           "workspace query")
+    return int(nbytes.value)
+
+
+def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
+                      router_bias: Optional[torch.Tensor], w1: torch.Tensor, w2: torch.Tensor,
+                      topk: int, *, w1_scale: Optional[torch.Tensor] = None,
+                      w2_scale: Optional[torch.Tensor] = None, regime: int = MOE_REGIME_AUTO,
+                      out: Optional[torch.Tensor] = None,
+                      workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The whole layer; returns out bf16 [M,K].
+
+    w1 [E,2N,K] / w2 [E,K,N] are bf16, or uint8 e4m3 codes with fp32 per-expert
+    w1_scale / w2_scale.  ``workspace`` (uint8, at least workspace_size bytes)
+    may be passed to avoid an allocation per call."""
+    lib = load_library()
+    fp8 = w1.dtype == torch.uint8
+    dtype = MOE_FP8_E4M3 if fp8 else MOE_BF16
+    M, K = x.shape
+    E, twoN, K1 = w1.shape
+    N = twoN // 2
+    _dev(x, "x", torch.bfloat16)
+    _dev(w_router, "w_router", torch.bfloat16, (E, K))
+    if router_bias is not None:
+        _dev(router_bias, "router_bias", torch.float32, (E,))
+    wdt = torch.uint8 if fp8 else torch.bfloat16
+    _dev(w1, "w1", wdt, (E, 2 * N, K))
+    _dev(w2, "w2", wdt, (E, K, N))
+    if fp8:
+        _dev(w1_scale, "w1_scale", torch.float32, (E,))
+        _dev(w2_scale, "w2_scale", torch.float32, (E,))
+    elif w1_scale is not None or w2_scale is not None:
+        raise ValueError("scales are only for e4m3 weights")
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    _dev(out, "out", torch.bfloat16, (M, K))
+    need = workspace_size(dtype, M, K, N, E, topk, regime)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    nbytes = ctypes.c_size_t(workspace.numel())
+    _check(lib.moe_fused_forward_ex(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1),
+                                    _ptr(w2), _ptr(w1_scale), _ptr(w2_scale), dtype, M, K, N, E,
+                                    topk, regime, _ptr(out), _ptr(workspace),
+                                    ctypes.byref(nbytes), _stream(dev)),
+           "moe_fused_forward")
+    return out

@@ -1,0 +1,287 @@
+// api.cpp -- the C ABI of include/moe.h: argument validation (before any HIP
+// call), the workspace layout, the choice of kernel family and the launch
+// sequence of the fused MoE layer.
+//
+// Launch sequence of moe_fused_forward (all on the caller's stream, no host
+// synchronisation, grids sized from host-known upper bounds so no device
+// value is read back):
+//   1 router logits (fp64 dot products)      2 top-k + weights (+ x -> e4m3)
+//   3 align (sorted rows, block owners)       4 GEMM1 + SiLU*up
+//   5 (e4m3) per-row activation quantisation  6 GEMM2 * routing weight, scattered
+//   7 combine into bf16 out
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "launch.hpp"
+
+#define MOE_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+constexpr int kDecodeBlock = 16;
+constexpr int kPrefillBlock = 128;
+constexpr size_t kAlign = 256;
+
+bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+struct Plan {
+    int regime = MOE_REGIME_DECODE;
+    int block = kDecodeBlock;
+    int cap = 0;         // rows of the sorted list: M*topk + E*(block-1)
+    int max_blocks = 0;  // cap / block
+    int nsplit = 1;      // GEMM2 reduction split (decode)
+    size_t logits = 0, ids = 0, wts = 0, sorted = 0, bexp = 0, offs = 0, npad = 0;
+    size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
+};
+
+Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
+    Plan p;
+    const long slots = (long)M * topk;
+    if (regime == MOE_REGIME_AUTO)
+        regime = (dtype == MOE_FP8_E4M3 || slots <= 16L * E) ? MOE_REGIME_DECODE
+                                                              : MOE_REGIME_PREFILL;
+    p.regime = regime;
+    p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
+    p.cap = (int)(slots + (long)E * (p.block - 1));
+    p.max_blocks = p.cap / p.block;
+    if (regime == MOE_REGIME_DECODE) {
+        // split GEMM2's reduction when few (block, row-tile) pairs exist, so
+        // the weight stream spreads over all CUs
+        const long est_blocks = slots < E ? slots : E;
+        const long tiles = est_blocks * (K / 128);
+        while (tiles * p.nsplit < 1024 && p.nsplit < 16 && (N / (p.nsplit * 2)) % 128 == 0)
+            p.nsplit *= 2;
+    }
+    size_t o = 0;
+    auto take = [&](size_t bytes) {
+        const size_t at = o;
+        o += round_up(bytes);
+        return at;
+    };
+    p.logits = take((size_t)M * E * 4);
+    p.ids = take((size_t)slots * 4);
+    p.wts = take((size_t)slots * 4);
+    p.sorted = take((size_t)p.cap * 4);
+    p.bexp = take((size_t)p.max_blocks * 4);
+    p.offs = take((size_t)(E + 1) * 4);
+    p.npad = take(4);
+    if (dtype == MOE_FP8_E4M3) {
+        p.xq = take((size_t)M * K);
+        p.xs = take((size_t)M * 4);
+        p.amax = take((size_t)p.cap * 4);
+        p.act = take((size_t)p.cap * N * 4);
+        p.actq = take((size_t)p.cap * N);
+        p.as = take((size_t)p.cap * 4);
+    } else {
+        p.act = take((size_t)p.cap * N * 2);
+    }
+    p.ypart = take((size_t)p.nsplit * slots * K * 4);
+    p.total = o;
+    return p;
+}
+
+}  // namespace
+
+MOE_API const char* moe_status_string(int status) {
+    switch (status) {
+        case MOE_OK: return "MOE_OK";
+        case MOE_ERR_INVALID_ARG: return "MOE_ERR_INVALID_ARG";
+        case MOE_ERR_UNSUPPORTED: return "MOE_ERR_UNSUPPORTED";
+        case MOE_ERR_WORKSPACE: return "MOE_ERR_WORKSPACE";
+        case MOE_ERR_HIP: return "MOE_ERR_HIP";
+        default: return "MOE_ERR_UNKNOWN";
+    }
+}
+
+static moe_status finish_launches() {
+    return hipGetLastError() == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_topk(const void* x, const void* w_router, const float* router_bias, int M,
+                            int K, int E, int topk, int32_t* topk_ids, float* topk_weights,
+                            float* logits, void* stream) {
+    if (M < 0 || K < 1 || E < 1 || topk < 1 || topk > E) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if ((long)M * K >= (1L << 31) || (long)E * K >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!x || !w_router || !topk_ids || !topk_weights || !logits) return MOE_ERR_INVALID_ARG;
+    if (misaligned(x) || misaligned(w_router) || misaligned(router_bias) ||
+        misaligned(topk_ids) || misaligned(topk_weights) || misaligned(logits))
+        return MOE_ERR_INVALID_ARG;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, s);
+    moe::launch_router_topk(logits, M, E, topk, topk_ids, topk_weights, nullptr, K, nullptr,
+                            nullptr, s);
+    return finish_launches();
+}
+
+MOE_API moe_status moe_quant_rows_e4m3(const void* x, int M, int K, uint8_t* q, float* scale,
+                                       void* stream) {
+    if (M < 0 || K < 1) return MOE_ERR_INVALID_ARG;
+    if ((long)M * K >= (1L << 31)) return MOE_ERR_UNSUPPORTED;
+    if (M == 0) return MOE_OK;
+    if (!x || !q || !scale || misaligned(x) || misaligned(q) || misaligned(scale))
+        return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    moe::launch_quant_rows(x, M, K, q, scale, (hipStream_t)stream);
+    return finish_launches();
+}
+
+MOE_API moe_status moe_align(const int32_t* topk_ids, int M, int topk, int E, int block_m,
+                             int32_t* sorted_ids, int32_t* block_expert,
+                             int32_t* expert_offsets, int32_t* num_padded, void* stream) {
+    if (M < 0 || topk < 1 || E < 1 || block_m < 1) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || block_m > 1024 || (long)M * topk >= (1L << 30))
+        return MOE_ERR_UNSUPPORTED;
+    if (!sorted_ids || !block_expert || !expert_offsets || !num_padded ||
+        (M > 0 && !topk_ids))
+        return MOE_ERR_INVALID_ARG;
+    if (misaligned(topk_ids) || misaligned(sorted_ids) || misaligned(block_expert) ||
+        misaligned(expert_offsets) || misaligned(num_padded))
+        return MOE_ERR_INVALID_ARG;
+    const int n = M * topk;
+    const int cap = n + E * (block_m - 1);
+    (void)hipGetLastError();
+    moe::launch_align(topk_ids, n, E, block_m, cap, sorted_ids, block_expert, expert_offsets,
+                      num_padded, nullptr, 0, (hipStream_t)stream);
+    return finish_launches();
+}
+
+static moe_status fused_impl(const void* x, const void* w_router, const float* router_bias,
+                             const void* w1, const void* w2, const float* w1_scale,
+                             const float* w2_scale, int dtype, int M, int K, int N, int E,
+                             int topk, int regime, void* out, void* workspace,
+                             size_t* workspace_bytes, void* stream, void* const* events,
+                             bool timed) {
+    if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+    if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_PREFILL) return MOE_ERR_INVALID_ARG;
+    if (M < 0 || K < 1 || N < 1 || E < 1 || topk < 1 || topk > E) return MOE_ERR_INVALID_ARG;
+    if (dtype == MOE_BF16 && (w1_scale || w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (dtype == MOE_FP8_E4M3 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
+    if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
+    if (dtype == MOE_FP8_E4M3 && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
+    const long slots = (long)M * topk;
+    const long kn = K > N ? K : N;
+    if (slots >= (1L << 30) || (slots + (long)E * kPrefillBlock) * kn >= (1L << 31) ||
+        (long)M * K >= (1L << 31) || (long)E * 2 * N >= (1L << 31))
+        return MOE_ERR_UNSUPPORTED;
+    const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
+    if (p.max_blocks > 65535) return MOE_ERR_UNSUPPORTED;
+    if (!workspace) {
+        *workspace_bytes = p.total;
+        return MOE_OK;
+    }
+    if (M == 0) return MOE_OK;
+    if (!x || !w_router || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
+    if (misaligned(x) || misaligned(w_router) || misaligned(router_bias) || misaligned(w1) ||
+        misaligned(w2) || misaligned(w1_scale) || misaligned(w2_scale) || misaligned(out) ||
+        ((uintptr_t)workspace & (kAlign - 1)))
+        return MOE_ERR_INVALID_ARG;
+    if (*workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
+    if (timed && !events) return MOE_ERR_INVALID_ARG;
+
+    char* ws = (char*)workspace;
+    float* logits = (float*)(ws + p.logits);
+    int32_t* ids = (int32_t*)(ws + p.ids);
+    float* wts = (float*)(ws + p.wts);
+    int32_t* sorted = (int32_t*)(ws + p.sorted);
+    int32_t* bexp = (int32_t*)(ws + p.bexp);
+    int32_t* offs = (int32_t*)(ws + p.offs);
+    int32_t* npad = (int32_t*)(ws + p.npad);
+    float* ypart = (float*)(ws + p.ypart);
+    const int nslots = (int)slots;
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    auto mark = [&](int i) {
+        if (timed) (void)hipEventRecord((hipEvent_t)events[i], s);
+    };
+
+    mark(0);
+    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, s);
+    mark(1);
+    if (dtype == MOE_FP8_E4M3) {
+        uint8_t* xq = (uint8_t*)(ws + p.xq);
+        float* xs = (float*)(ws + p.xs);
+        uint32_t* amax = (uint32_t*)(ws + p.amax);
+        float* act = (float*)(ws + p.act);
+        uint8_t* actq = (uint8_t*)(ws + p.actq);
+        float* as = (float*)(ws + p.as);
+        moe::launch_router_topk(logits, M, E, topk, ids, wts, x, K, xq, xs, s);
+        mark(2);
+        moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax, p.cap,
+                          s);
+        mark(3);
+        moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, sorted, bexp, npad, topk, nslots, K,
+                                     N, p.max_blocks, act, amax, s);
+        mark(4);
+        moe::launch_act_quant(act, amax, sorted, npad, nslots, N, p.cap, actq, as, s);
+        mark(5);
+        moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, wts, sorted, bexp, npad, nslots, K,
+                                     N, p.nsplit, p.max_blocks, ypart, s);
+        mark(6);
+    } else {
+        void* act = ws + p.act;
+        moe::launch_router_topk(logits, M, E, topk, ids, wts, nullptr, K, nullptr, nullptr, s);
+        mark(2);
+        moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, nullptr, 0,
+                          s);
+        mark(3);
+        if (p.regime == MOE_REGIME_DECODE)
+            moe::launch_gemm1_decode_bf16(x, w1, sorted, bexp, npad, topk, nslots, K, N,
+                                          p.max_blocks, act, s);
+        else
+            moe::launch_gemm1_prefill_bf16(x, w1, sorted, bexp, npad, topk, nslots, K, N,
+                                           p.max_blocks, act, s);
+        mark(4);
+        mark(5);
+        if (p.regime == MOE_REGIME_DECODE)
+            moe::launch_gemm2_decode_bf16(act, w2, wts, sorted, bexp, npad, nslots, K, N,
+                                          p.nsplit, p.max_blocks, ypart, s);
+        else
+            moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, nslots, K, N,
+                                           p.max_blocks, ypart, s);
+        mark(6);
+    }
+    moe::launch_combine(ypart, M, K, topk, p.nsplit, out, s);
+    mark(7);
+    return finish_launches();
+}
+
+MOE_API moe_status moe_fused_forward_ex(const void* x, const void* w_router,
+                                        const float* router_bias, const void* w1,
+                                        const void* w2, const float* w1_scale,
+                                        const float* w2_scale, int dtype, int M, int K, int N,
+                                        int E, int topk, int regime, void* out,
+                                        void* workspace, size_t* workspace_bytes,
+                                        void* stream) {
+    return fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K, N, E,
+                      topk, regime, out, workspace, workspace_bytes, stream, nullptr, false);
+}
+
+MOE_API moe_status moe_fused_forward_timed(const void* x, const void* w_router,
+                                           const float* router_bias, const void* w1,
+                                           const void* w2, const float* w1_scale,
+                                           const float* w2_scale, int dtype, int M, int K,
+                                           int N, int E, int topk, int regime, void* out,
+                                           void* workspace, size_t* workspace_bytes,
+                                           void* stream, void* const* events) {
+    return fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K, N, E,
+                      topk, regime, out, workspace, workspace_bytes, stream, events, true);
+}
+
+MOE_API moe_status moe_fused_forward(const void* x, const void* w_router,
+                                     const float* router_bias, const void* w1, const void* w2,
+                                     const float* w1_scale, const float* w2_scale, int dtype,
+                                     int M, int K, int N, int E, int topk, void* out,
+                                     void* workspace, size_t* workspace_bytes, void* stream) {
+    return moe_fused_forward_ex(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K,
+                                N, E, topk, MOE_REGIME_AUTO, out, workspace, workspace_bytes,
+                                stream);
+}

@@ -1,0 +1,58 @@
+// launch.hpp -- host-side launchers of the layer's kernels (internal to the
+// library; the public interface is include/moe.h).  Every launcher only
+// enqueues on the given stream; shapes are validated by the caller.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#define MOE_KERNEL_MAX_EXPERTS 256
+#define MOE_KERNEL_MAX_TOPK 16
+
+namespace moe {
+
+void launch_router_logits(const void* x, const void* wr, const float* bias, int M, int K, int E,
+                          float* logits, hipStream_t s);
+void launch_router_topk(const float* logits, int M, int E, int topk, int32_t* ids, float* w,
+                        const void* x, int K, uint8_t* xq, float* xscale, hipStream_t s);
+void launch_quant_rows(const void* x, int M, int K, uint8_t* q, float* scale, hipStream_t s);
+
+void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,
+                  int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
+                  uint32_t* zero_buf, int zero_words, hipStream_t s);
+
+void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded, int topk,
+                              int nslots, int K, int N, int max_blocks, void* act,
+                              hipStream_t s);
+void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk_w,
+                              const int32_t* sorted_ids, const int32_t* block_expert,
+                              const int32_t* num_padded, int nslots, int K, int N, int nsplit,
+                              int max_blocks, float* ypart, hipStream_t s);
+void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
+                             const float* w1_scale, const int32_t* sorted_ids,
+                             const int32_t* block_expert, const int32_t* num_padded, int topk,
+                             int nslots, int K, int N, int max_blocks, float* act,
+                             uint32_t* amax, hipStream_t s);
+void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sorted_ids,
+                      const int32_t* num_padded, int nslots, int N, int cap, uint8_t* act_q,
+                      float* ascale, hipStream_t s);
+void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
+                             const float* w2_scale, const float* topk_w,
+                             const int32_t* sorted_ids, const int32_t* block_expert,
+                             const int32_t* num_padded, int nslots, int K, int N, int nsplit,
+                             int max_blocks, float* ypart, hipStream_t s);
+
+void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
+                               const int32_t* block_expert, const int32_t* num_padded, int topk,
+                               int nslots, int K, int N, int max_blocks, void* act,
+                               hipStream_t s);
+void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
+                               const int32_t* sorted_ids, const int32_t* block_expert,
+                               const int32_t* num_padded, int nslots, int K, int N,
+                               int max_blocks, float* ypart, hipStream_t s);
+
+void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
+                    hipStream_t s);
+
+}  // namespace moe

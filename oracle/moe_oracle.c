@@ -136,6 +136,21 @@ uint8_t orc_f32_to_e4m3(float f)
     return (uint8_t)(sign | ((ex + 7) << 3) | ((int)q - 8));
 }
 
+/* Decode table of the 256 codes, filled once from orc_e4m3_to_f64 so the
+ * expert loops do not re-derive every code. */
+static double e4m3_table[256];
+static int e4m3_table_ready = 0;
+
+static void init_e4m3_table(void)
+{
+    int c;
+    if (e4m3_table_ready)
+        return;
+    for (c = 0; c < 256; ++c)
+        e4m3_table[c] = orc_e4m3_to_f64((uint8_t)c);
+    e4m3_table_ready = 1;
+}
+
 /* Per-row dynamic quantisation (R7) of n fp32 values. */
 static void quant_row_f32(const float *v, int64_t n, uint8_t *q, float *scale)
 {
@@ -316,9 +331,9 @@ static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, float w1s
         const uint8_t *u = w1 + (N + n) * K;
         double hg = 0.0, hu = 0.0;
         for (kk = 0; kk < K; ++kk) {
-            double xv = orc_e4m3_to_f64(xq[kk]);
-            hg += orc_e4m3_to_f64(g[kk]) * xv;
-            hu += orc_e4m3_to_f64(u[kk]) * xv;
+            double xv = e4m3_table[xq[kk]];
+            hg += e4m3_table[g[kk]] * xv;
+            hu += e4m3_table[u[kk]] * xv;
         }
         hg *= (double)sx * (double)w1s;
         hu *= (double)sx * (double)w1s;
@@ -330,7 +345,7 @@ static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, float w1s
         const uint8_t *r = w2 + c * N;
         double acc = 0.0;
         for (n = 0; n < N; ++n)
-            acc += orc_e4m3_to_f64(r[n]) * orc_e4m3_to_f64(aq[n]);
+            acc += e4m3_table[r[n]] * e4m3_table[aq[n]];
         y[c] = acc * (double)sa * (double)w2s;
     }
 }
@@ -402,6 +417,7 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
     for (i = 0; i < n_tok; ++i)
         if (tokens[i] < 0 || tokens[i] >= M)
             return ORC_ERR_ARG;
+    init_e4m3_table();
     ids = (int32_t *)malloc((size_t)(nslot > 0 ? nslot : 1) * sizeof *ids);
     wts = (double *)malloc((size_t)(nslot > 0 ? nslot : 1) * sizeof *wts);
     lg = (float *)malloc((size_t)(n_tok > 0 ? n_tok : 1) * (size_t)E * sizeof *lg);

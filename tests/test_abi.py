@@ -1,0 +1,121 @@
+"""The C ABI on a host without a GPU: the library loads, exports every entry
+point include/moe.h declares, and rejects bad arguments with the documented
+status before making any HIP call (so no device is touched here)."""
+import ctypes
+import os
+import re
+
+import pytest
+import torch  # noqa: F401  (loads the HIP runtime the library links against)
+
+import moe_layer_04_amd as moe
+from moe_layer_04_amd import _binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+FAKE = ctypes.c_void_p(0x10000)      # aligned, never dereferenced on error paths
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:moe_status|const char \*)\s*(moe_\w+)\s*\(", text,
+                                 re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return moe.load_library(build_if_missing=True)
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) >= {"moe_topk", "moe_align", "moe_fused_forward"}
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTS)
+
+
+def test_status_strings(lib):
+    assert moe.status_string(0) == "MOE_OK"
+    assert moe.status_string(3) == "MOE_ERR_WORKSPACE"
+    assert moe.status_string(99) == "MOE_ERR_UNKNOWN"
+
+
+def topk_call(lib, x=FAKE, wr=FAKE, bias=None, M=4, K=64, E=8, k=2, ids=FAKE, w=FAKE, lg=FAKE):
+    return lib.moe_topk(x, wr, bias, M, K, E, k, ids, w, lg, None)
+
+
+def test_topk_validation(lib):
+    assert topk_call(lib, M=-1) == B.MOE_ERR_INVALID_ARG
+    assert topk_call(lib, K=0) == B.MOE_ERR_INVALID_ARG
+    assert topk_call(lib, k=0) == B.MOE_ERR_INVALID_ARG
+    assert topk_call(lib, k=9) == B.MOE_ERR_INVALID_ARG          # topk > E
+    assert topk_call(lib, E=300, k=2) == B.MOE_ERR_UNSUPPORTED
+    assert topk_call(lib, E=32, k=17) == B.MOE_ERR_UNSUPPORTED
+    assert topk_call(lib, x=None) == B.MOE_ERR_INVALID_ARG
+    assert topk_call(lib, lg=None) == B.MOE_ERR_INVALID_ARG
+    assert topk_call(lib, wr=MISALIGNED) == B.MOE_ERR_INVALID_ARG
+    assert topk_call(lib, M=0, x=None, ids=None, w=None, lg=None) == B.MOE_OK   # no-op
+
+
+def test_align_validation(lib):
+    f = lib.moe_align
+    assert f(FAKE, -1, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 0, 8, 16, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 8, 0, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 257, 16, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, 4, 2, 8, 2048, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_UNSUPPORTED
+    assert f(None, 4, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 8, 16, None, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+    assert f(FAKE, 4, 2, 8, 16, MISALIGNED, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG
+
+
+def fused(lib, *, x=FAKE, wr=FAKE, bias=None, w1=FAKE, w2=FAKE, s1=None, s2=None, dtype=0,
+          M=8, K=256, N=512, E=8, k=2, regime=0, out=FAKE, ws=FAKE, nbytes=None):
+    n = ctypes.c_size_t(1 << 40 if nbytes is None else nbytes)
+    rc = lib.moe_fused_forward_ex(x, wr, bias, w1, w2, s1, s2, dtype, M, K, N, E, k, regime, out,
+                                  ws, ctypes.byref(n), None)
+    return rc, n.value
+
+
+def test_fused_validation(lib):
+    INV, UNS, WSP = B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE
+    assert fused(lib, dtype=2)[0] == INV
+    assert fused(lib, regime=3)[0] == INV
+    assert fused(lib, M=-1)[0] == INV
+    assert fused(lib, N=0)[0] == INV
+    assert fused(lib, k=9)[0] == INV
+    assert fused(lib, s1=FAKE, s2=FAKE)[0] == INV                     # scales with bf16
+    assert fused(lib, dtype=1)[0] == INV                              # fp8 without scales
+    assert fused(lib, dtype=1, s1=FAKE, s2=None)[0] == INV
+    assert fused(lib, E=257, k=2)[0] == UNS
+    assert fused(lib, E=64, k=17)[0] == UNS
+    assert fused(lib, K=200)[0] == UNS                               # not a multiple of 128
+    assert fused(lib, N=192)[0] == UNS
+    assert fused(lib, dtype=1, s1=FAKE, s2=FAKE, regime=2)[0] == UNS  # no fp8 full-tile kernels
+    assert fused(lib, x=None)[0] == INV
+    assert fused(lib, out=None)[0] == INV
+    assert fused(lib, w2=MISALIGNED)[0] == INV
+    assert fused(lib, ws=ctypes.c_void_p(0x10010))[0] == INV          # workspace not 256-aligned
+    rc, need = fused(lib, ws=None)
+    assert rc == B.MOE_OK and need > 0
+    assert fused(lib, nbytes=need - 1)[0] == WSP
+    assert lib.moe_fused_forward_ex(FAKE, FAKE, None, FAKE, FAKE, None, None, 0, 8, 256, 512, 8,
+                                    2, 0, FAKE, FAKE, None, None) == INV  # null size pointer
+    rc, _ = fused(lib, M=0, x=None, out=None)
+    assert rc == B.MOE_OK                                             # M == 0: no-op
+
+
+def test_workspace_query_sizes(lib):
+    # the query makes no HIP call; sizes grow with M and follow the dtype
+    s_dec = moe.workspace_size(moe.MOE_BF16, 8, 4096, 14336, 8, 2)
+    s_pre = moe.workspace_size(moe.MOE_BF16, 4096, 4096, 14336, 8, 2)
+    s_fp8 = moe.workspace_size(moe.MOE_FP8_E4M3, 128, 7168, 2048, 256, 8)
+    assert 0 < s_dec < s_pre
+    # prefill: the bf16 SiLU*up activation [M*k + E*127, N] dominates
+    assert s_pre >= (4096 * 2 + 8 * 127) * 14336 * 2
+    # fp8: fp32 + e4m3 activations of [M*k + E*15, N]
+    assert s_fp8 >= (128 * 8 + 256 * 15) * 2048 * 5
+    assert moe.workspace_size(moe.MOE_BF16, 8, 4096, 14336, 8, 2, moe.MOE_REGIME_PREFILL) > s_dec

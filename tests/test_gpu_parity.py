@@ -1,0 +1,318 @@
+"""Parity of the HIP path (through the C ABI) with the CPU oracle.
+
+Integer work -- top-k ids, the sorted permutation, block owners, offsets,
+e4m3 codes of the token quantiser -- must match bit for bit.  Floating
+outputs must match within the layer's stated tolerances, measured as the
+max over tokens of max|gpu - ref| / max|ref| (row max of the fp64 oracle):
+2e-2 for bf16 weights, 6e-2 for e4m3 weights.  Routing weights: 1e-6
+absolute (fp32 softmax vs the oracle's fp64 on the same logits).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from moe_layer_04_amd import workloads as wlm
+from tests._brute import row_rel_err
+
+pytestmark = pytest.mark.gpu
+
+TOL_BF16 = 2e-2
+TOL_FP8 = 6e-2
+TOL_WEIGHTS = 1e-6
+
+
+def note(msg):
+    print(f"[gpu-test] {msg}", flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def moe():
+    import moe_layer_04_amd as m
+    m.load_library()
+    return m
+
+
+def bits(t):
+    return wlm.to_numpy_bits(t)
+
+
+def gen_small(wl, seed=None):
+    """Small workloads are drawn on the CPU and copied to the GPU."""
+    if seed is not None:
+        wl = wl.resized(seed=seed)
+    d = wlm.generate(wl, "cpu")
+    g = {k: (v.cuda() if isinstance(v, torch.Tensor) else v) for k, v in d.items()}
+    return d, g
+
+
+def run_layer(moe, g, wl, regime=0, poison=True):
+    dtype = moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16
+    need = moe.workspace_size(dtype, wl.M, wl.K, wl.N, wl.E, wl.topk, regime)
+    ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
+    if poison:
+        ws.fill_(0xFF)   # any read of a never-written workspace byte turns into NaN
+    out = torch.full((wl.M, wl.K), float("nan"), dtype=torch.bfloat16, device="cuda")
+    moe.moe_fused_forward(g["x"], g["w_router"], g["bias"], g["w1"], g["w2"], wl.topk,
+                          w1_scale=g["w1_scale"], w2_scale=g["w2_scale"], regime=regime,
+                          out=out, workspace=ws)
+    torch.cuda.synchronize()
+    return out
+
+
+def oracle_layer(d, wl, tokens=None):
+    s1 = None if d["w1_scale"] is None else d["w1_scale"].numpy()
+    s2 = None if d["w2_scale"] is None else d["w2_scale"].numpy()
+    return oracle.moe_forward(bits(d["x"]), bits(d["w_router"]),
+                              None if d["bias"] is None else d["bias"].numpy(),
+                              bits(d["w1"]), bits(d["w2"]), wl.topk, w1_scale=s1, w2_scale=s2,
+                              tokens=tokens, fp8=wl.fp8)
+
+
+def out_f64(out):
+    return out.float().cpu().numpy().astype(np.float64)
+
+
+# --------------------------------------------------------------------------
+# token quantiser: bit-exact codes and scales
+# --------------------------------------------------------------------------
+
+def test_quant_rows_bit_exact_all_bf16_values(moe):
+    note("quant_rows: every finite bf16 value")
+    pat = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    finite = ((pat & 0x7F80) != 0x7F80)
+    vals = pat[finite]
+    K = 640
+    M = (vals.size + K - 1) // K
+    xb = np.zeros(M * K, np.uint16)
+    xb[: vals.size] = vals
+    xb = xb.reshape(M, K)
+    rng = np.random.default_rng(0)
+    rng.shuffle(xb, axis=1)
+    xb = np.concatenate([xb, np.zeros((1, K), np.uint16)])   # an all-zero row -> scale 1
+    # rows with very different ranges: scale one row's magnitudes down
+    x = torch.from_numpy(xb.view(np.int16)).view(torch.bfloat16).cuda()
+    q, s = moe.moe_quant_rows_e4m3(x)
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_rows_bf16(xb)
+    assert np.array_equal(s.cpu().numpy(), rs)
+    assert np.array_equal(q.cpu().numpy(), rq)
+
+
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (5, 4096), (2, 7168 + 3)])
+def test_quant_rows_ragged(moe, M, K):
+    note(f"quant_rows M={M} K={K}")
+    g = torch.Generator().manual_seed(M * 31 + K)
+    x = (torch.randn((M, K), generator=g) * 3).to(torch.bfloat16)
+    q, s = moe.moe_quant_rows_e4m3(x.cuda())
+    torch.cuda.synchronize()
+    rq, rs = oracle.quant_rows_bf16(bits(x))
+    assert np.array_equal(s.cpu().numpy(), rs) and np.array_equal(q.cpu().numpy(), rq)
+
+
+# --------------------------------------------------------------------------
+# router: bit-exact logits, ids; weights within 1e-6
+# --------------------------------------------------------------------------
+
+def check_router(moe, x, wr, bias, k):
+    ids, w, lg = moe.moe_topk(x.cuda(), wr.cuda(), None if bias is None else bias.cuda(), k)
+    torch.cuda.synchronize()
+    ids, w, lg = ids.cpu().numpy(), w.cpu().numpy(), lg.cpu().numpy()
+    rlg = oracle.logits(bits(x), bits(wr), None if bias is None else bias.numpy())
+    # selection on the GPU's own logits must be the oracle's selection
+    sids, sw = oracle.topk(lg, k)
+    assert np.array_equal(ids, sids)
+    assert np.abs(w - sw).max() <= TOL_WEIGHTS
+    # and the logits themselves are the oracle's (fp64 dot product, one rounding)
+    assert np.array_equal(lg, rlg)
+    rids, _ = oracle.topk(rlg, k)
+    assert np.array_equal(ids, rids)
+    return ids
+
+
+@pytest.mark.parametrize("name", list(wlm.WORKLOADS))
+def test_router_full_size(moe, name):
+    wl = wlm.WORKLOADS[name]
+    note(f"router {name} M={wl.M} K={wl.K} E={wl.E} k={wl.topk}")
+    g = torch.Generator().manual_seed(0)
+    x = torch.randn((wl.M, wl.K), generator=g).to(torch.bfloat16)
+    wr = (torch.randn((wl.E, wl.K), generator=g) / math.sqrt(wl.K)).to(torch.bfloat16)
+    bias = (torch.randn(wl.E, generator=g) * math.sqrt(wl.bias_var)) if wl.bias_var else None
+    check_router(moe, x, wr, bias, wl.topk)
+
+
+@pytest.mark.parametrize("M,K,E,k", [(1, 1, 1, 1), (7, 100, 3, 2), (33, 264, 256, 16),
+                                     (64, 96, 64, 8), (5, 8, 200, 200 // 13)])
+def test_router_ragged(moe, M, K, E, k):
+    note(f"router ragged M={M} K={K} E={E} k={k}")
+    g = torch.Generator().manual_seed(M + K + E)
+    x = torch.randn((M, K), generator=g).to(torch.bfloat16)
+    wr = (torch.randn((E, K), generator=g)).to(torch.bfloat16)
+    check_router(moe, x, wr, None, k)
+
+
+def test_router_ties_lower_id(moe):
+    note("router ties")
+    g = torch.Generator().manual_seed(5)
+    M, K, E = 40, 128, 12
+    x = torch.randn((M, K), generator=g).to(torch.bfloat16)
+    wr = torch.randn((E, K), generator=g).to(torch.bfloat16)
+    wr[7] = wr[2]
+    wr[9] = wr[2]
+    wr[11] = wr[4]
+    ids = check_router(moe, x, wr, None, 4)
+    x0 = torch.zeros((3, K), dtype=torch.bfloat16)   # all logits equal -> experts 0..3
+    ids0 = check_router(moe, x0, wr, None, 4)
+    assert ids0.tolist() == [[0, 1, 2, 3]] * 3
+
+
+# --------------------------------------------------------------------------
+# align: bit-exact
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("M,k,E,B", [(64, 2, 8, 16), (8, 2, 8, 16), (1, 2, 16, 16),
+                                     (4096, 2, 8, 128), (128, 8, 256, 16), (0, 2, 8, 16),
+                                     (37, 3, 17, 64), (20000, 4, 64, 128), (300, 1, 256, 1),
+                                     (9, 5, 5, 1024)])
+def test_align_bit_exact(moe, M, k, E, B):
+    note(f"align M={M} k={k} E={E} B={B}")
+    rng = np.random.default_rng(M * 7 + E)
+    if M:
+        # skewed expert popularity, distinct experts per token
+        pop = rng.dirichlet(np.full(E, 0.3))
+        ids = np.stack([rng.choice(E, size=k, replace=False, p=pop) for _ in range(M)])
+    else:
+        ids = np.zeros((0, k))
+    ids = ids.astype(np.int32)
+    s, b, o, npad = moe.moe_align(torch.from_numpy(ids).cuda(), E, B)
+    torch.cuda.synchronize()
+    rs, rb, ro, rn = oracle.align(ids, E, B)
+    assert int(npad.item()) == rn
+    assert np.array_equal(o.cpu().numpy(), ro)
+    assert np.array_equal(b.cpu().numpy(), rb)
+    assert np.array_equal(s.cpu().numpy(), rs)
+
+
+# --------------------------------------------------------------------------
+# the fused layer at small sizes (the oracle evaluates every token)
+# --------------------------------------------------------------------------
+
+SMALL = [
+    # name, M, K, N, E, k, fp8, bias_var, regime
+    ("tiny", 64, 256, 512, 8, 2, False, None, 0),
+    ("tiny_prefill_tiles", 64, 256, 512, 8, 2, False, None, 2),
+    ("decode_ragged", 5, 384, 640, 6, 2, False, None, 0),
+    ("k1", 9, 256, 256, 4, 1, False, None, 0),
+    ("k_eq_e", 6, 256, 384, 4, 4, False, None, 0),
+    ("e1_dense", 3, 128, 256, 1, 1, False, None, 0),
+    ("many_empty_experts", 3, 256, 256, 256, 8, False, None, 0),
+    ("prefill_skewed", 700, 256, 384, 8, 2, False, 0.5, 0),
+    ("prefill_ragged", 333, 384, 640, 5, 3, False, None, 2),
+    ("fp8_tiny", 16, 512, 256, 16, 4, True, None, 0),
+    ("fp8_ragged", 7, 384, 640, 32, 8, True, None, 0),
+    ("fp8_many_rows", 300, 256, 384, 8, 2, True, None, 0),
+    ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=[c[0] for c in SMALL])
+def test_fused_small(moe, case):
+    name, M, K, N, E, k, fp8, bias_var, regime = case
+    note(f"fused small {case}")
+    wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, bias_var=bias_var, seed=3)
+    d, g = gen_small(wl)
+    out = run_layer(moe, g, wl, regime)
+    ref, _, _ = oracle_layer(d, wl)
+    got = out_f64(out)
+    assert np.isfinite(got).all()
+    err = row_rel_err(got, ref)
+    note(f"  err={err:.3e}")
+    assert err <= (TOL_FP8 if fp8 else TOL_BF16)
+
+
+def test_fused_m0_is_noop(moe):
+    note("fused M=0")
+    wl = wlm.Workload("m0", M=0, K=256, N=256, E=4, topk=2)
+    d, g = gen_small(wl)
+    out = torch.empty((0, 256), dtype=torch.bfloat16, device="cuda")
+    moe.moe_fused_forward(g["x"], g["w_router"], None, g["w1"], g["w2"], 2, out=out)
+    torch.cuda.synchronize()
+
+
+def test_swap_ab_identity_decode_vs_prefill(moe):
+    """C^T = B^T.A^T: the Swap-AB decode kernels and the full-tile kernels give
+    the same layer output on identical inputs (up to fp32 summation order and
+    the bf16 rounding of the intermediate)."""
+    note("swap-ab cross-check")
+    wl = wlm.Workload("xcheck", M=96, K=512, N=768, E=6, topk=2, seed=11)
+    d, g = gen_small(wl)
+    a = out_f64(run_layer(moe, g, wl, 1))
+    b = out_f64(run_layer(moe, g, wl, 2))
+    ref, _, _ = oracle_layer(d, wl)
+    assert row_rel_err(a, ref) <= TOL_BF16 and row_rel_err(b, ref) <= TOL_BF16
+    assert row_rel_err(a, b) <= 1e-2
+
+
+def test_fused_deterministic(moe):
+    note("determinism")
+    wl = wlm.Workload("det", M=40, K=512, N=512, E=8, topk=2, seed=4)
+    d, g = gen_small(wl)
+    outs = [run_layer(moe, g, wl).clone() for _ in range(5)]
+    for o in outs[1:]:
+        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
+    wl8 = wl.resized(fp8=True)
+    d8, g8 = gen_small(wl8)
+    o8 = [run_layer(moe, g8, wl8).clone() for _ in range(3)]
+    for o in o8[1:]:
+        assert torch.equal(o.view(torch.int16), o8[0].view(torch.int16))
+
+
+# --------------------------------------------------------------------------
+# the five workloads at full size, in the launch configuration the benchmark
+# times; the oracle evaluates sampled tokens one by one
+# --------------------------------------------------------------------------
+
+def sample_tokens(M, n=6):
+    if M <= n:
+        return list(range(M))
+    rng = np.random.default_rng(M)
+    mid = sorted(rng.choice(np.arange(1, M - 1), size=n - 2, replace=False).tolist())
+    return [0] + mid + [M - 1]
+
+
+@pytest.mark.parametrize("name", list(wlm.WORKLOADS))
+def test_fused_full_size_sampled(moe, name):
+    wl = wlm.WORKLOADS[name]
+    note(f"full size {name}: generate on GPU")
+    g = wlm.generate(wl, "cuda")
+    out = run_layer(moe, g, wl, poison=False)
+    got = out_f64(out)
+    assert np.isfinite(got).all()
+    # routing of every token is bit-exact with the oracle
+    ids, _, lg = moe.moe_topk(g["x"], g["w_router"], g["bias"], wl.topk)
+    torch.cuda.synchronize()
+    x_h, wr_h = bits(g["x"]), bits(g["w_router"])
+    bias_h = None if g["bias"] is None else g["bias"].cpu().numpy()
+    rlg = oracle.logits(x_h, wr_h, bias_h)
+    assert np.array_equal(lg.cpu().numpy(), rlg)
+    rids, _ = oracle.topk(rlg, wl.topk)
+    assert np.array_equal(ids.cpu().numpy(), rids)
+    # sampled tokens through the oracle, with only their experts copied to the host
+    toks = sample_tokens(wl.M)
+    need = sorted(set(rids[toks].reshape(-1).tolist()))
+    note(f"  oracle on tokens {toks}, {len(need)} experts")
+    w1 = [bits(g["w1"][e]) if e in need else None for e in range(wl.E)]
+    w2 = [bits(g["w2"][e]) if e in need else None for e in range(wl.E)]
+    s1 = None if g["w1_scale"] is None else g["w1_scale"].cpu().numpy()
+    s2 = None if g["w2_scale"] is None else g["w2_scale"].cpu().numpy()
+    ref, _, _ = oracle.moe_forward(x_h, wr_h, bias_h, w1, w2, wl.topk, w1_scale=s1,
+                                   w2_scale=s2, tokens=toks, fp8=wl.fp8)
+    err = row_rel_err(got[toks], ref)
+    note(f"  err={err:.3e}")
+    assert err <= (TOL_FP8 if wl.fp8 else TOL_BF16)
+    del g
+    torch.cuda.empty_cache()
