@@ -169,8 +169,11 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     if (dtype == MOE_FP8_E4M3 && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
     const long kn = K > N ? K : N;
-    if (slots >= (1L << 30) || (slots + (long)E * kPrefillBlock) * kn >= (1L << 31) ||
-        (long)M * K >= (1L << 31) || (long)E * 2 * N >= (1L << 31))
+    // 32-bit buffer offsets: the sorted activation rows in fp32, the tokens
+    // and one expert's W1 must each stay below 2 GiB
+    if (slots >= (1L << 30) || (slots + (long)E * kPrefillBlock) * kn * 4 >= (1L << 31) ||
+        (long)M * K * 2 >= (1L << 31) || (long)2 * N * K * 2 >= (1L << 31) ||
+        (long)E * 2 * N >= (1L << 31))
         return MOE_ERR_UNSUPPORTED;
     const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
     if (p.max_blocks > 65535) return MOE_ERR_UNSUPPORTED;
@@ -218,13 +221,13 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax, p.cap,
                           s);
         mark(3);
-        moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, sorted, bexp, npad, topk, nslots, K,
-                                     N, p.max_blocks, act, amax, s);
+        moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, sorted, bexp, npad, M, topk, nslots,
+                                     K, N, p.max_blocks, act, amax, s);
         mark(4);
         moe::launch_act_quant(act, amax, sorted, npad, nslots, N, p.cap, actq, as, s);
         mark(5);
-        moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, wts, sorted, bexp, npad, nslots, K,
-                                     N, p.nsplit, p.max_blocks, ypart, s);
+        moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, wts, sorted, bexp, npad, p.cap,
+                                     nslots, K, N, p.nsplit, p.max_blocks, ypart, s);
         mark(6);
     } else {
         void* act = ws + p.act;
@@ -234,18 +237,18 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                           s);
         mark(3);
         if (p.regime == MOE_REGIME_DECODE)
-            moe::launch_gemm1_decode_bf16(x, w1, sorted, bexp, npad, topk, nslots, K, N,
+            moe::launch_gemm1_decode_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
                                           p.max_blocks, act, s);
         else
-            moe::launch_gemm1_prefill_bf16(x, w1, sorted, bexp, npad, topk, nslots, K, N,
+            moe::launch_gemm1_prefill_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
                                            p.max_blocks, act, s);
         mark(4);
         mark(5);
         if (p.regime == MOE_REGIME_DECODE)
-            moe::launch_gemm2_decode_bf16(act, w2, wts, sorted, bexp, npad, nslots, K, N,
+            moe::launch_gemm2_decode_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
                                           p.nsplit, p.max_blocks, ypart, s);
         else
-            moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, nslots, K, N,
+            moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
                                            p.max_blocks, ypart, s);
         mark(6);
     }

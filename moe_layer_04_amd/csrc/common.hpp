@@ -157,6 +157,16 @@ __device__ __forceinline__ uint32_t col_max_bits(uint32_t v) {
 // misc
 // ---------------------------------------------------------------------------
 
+// Pin an accumulator at this point of the program.  Without it the compiler
+// may sink the last MFMAs of a loop into a lane-divergent epilogue branch,
+// where operands it materialises under the partial EXEC mask (such as the
+// block-scale constant of the scaled FP8 MFMA) are left unset in inactive
+// lanes -- while the MFMA itself still reads every lane.
+template <typename T>
+__device__ __forceinline__ void pin(T& v) {
+    asm volatile("" : "+v"(v));
+}
+
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
 __device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }

@@ -10,16 +10,22 @@
 // B^T (output-major, reduction dimension contiguous), then stream as large
 // contiguous blocks.  On gfx950 the MFMA row dimension is 16 (not Hopper's
 // 64), so the swap wastes at most 15 of 16 token columns while every byte of
-// weights read from HBM feeds a full MFMA row.  The weights are loaded from
-// HBM straight into registers, 16 contiguous bytes per lane, two K-steps in
-// flight per wave; decode is bound by that HBM stream.
+// weights read from HBM feeds a full MFMA row.  Decode is bound by that HBM
+// stream; the kernels load weights straight into registers.
 //
-// Work split: one workgroup (4 waves) per (16-row block of one expert,
-// tile of weight rows).  GEMM1 waves own 16 gate rows and the matching 16
-// up rows, so SiLU(gate)*up is formed in registers (the fused epilogue);
-// GEMM2 waves own 32 output rows and may split the reduction (N) across
-// workgroups, writing fp32 partial rows scattered back to slot order and
-// already multiplied by the routing weight.
+// Work split: one workgroup (4 waves) per (16-row block of one expert, tile
+// of weight rows).  GEMM1 waves own 16 gate rows and the matching 16 up rows,
+// so SiLU(gate)*up is formed in registers (the fused epilogue); GEMM2 waves
+// own 32 output rows and may split the reduction (N) across workgroups,
+// writing fp32 partial rows scattered back to slot order and already
+// multiplied by the routing weight.
+//
+// Memory access: all operands go through buffer loads.  A buffer resource is
+// bounds-checked by the hardware, so padding lanes of a block (sentinel rows)
+// get zeros by passing an offset past the end -- no branch, no traffic.
+// Each wave starts its reduction at a different, rotated K-step: waves that
+// all began at k = 0 would hit the same column slab of rows that are K*2
+// bytes apart, concentrating the stream on few HBM channels.
 //
 // MFMA operand layout used (16x16 family): lane l supplies row (l % 16) of
 // the A tile and column (l % 16) of the B tile, each with a K-slice chosen
@@ -31,72 +37,97 @@
 
 namespace moe {
 
-constexpr int kDecRows = 16;  // token rows per block (the align block size)
+constexpr int kDecRows = 16;            // token rows per block (the align block size)
+constexpr uint32_t kOob = 0x80000000u;  // offset past every resource: loads return 0
+constexpr int kRot = 7;                 // K-step rotation per wave
 
-__device__ __forceinline__ bf16x8_t ld16(const uint16_t* p) {
-    return *reinterpret_cast<const bf16x8_t*>(p);
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* base, uint32_t bytes) {
+    // dword3 = 0x00020000: raw (untyped) 32-bit buffer access on CDNA
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ i32x8_t ld32(const uint8_t* p) {
-    return *reinterpret_cast<const i32x8_t*>(p);
+__device__ __forceinline__ i32x4_t bload(rsrc_t r, uint32_t off) {
+    return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+}
+__device__ __forceinline__ i32x8_t bload32(rsrc_t r, uint32_t off) {
+    const i32x4_t a = bload(r, off), b = bload(r, off + 16);
+    return i32x8_t{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
 }
 
-__device__ __forceinline__ f32x4_t mfma_bf16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+__device__ __forceinline__ f32x4_t mfma_bf16(i32x4_t a, i32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16((bf16x8_t)a, (bf16x8_t)b, c, 0, 0, 0);
 }
 // e4m3 x e4m3, block scales fixed at 2^0 (E8M0 code 127).
 __device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
 
+// K-step j of a wave whose sequence is rotated by `rot` (steps in [0, n)).
+__device__ __forceinline__ int rotated(int j, int rot, int n) {
+    const int q = j + rot;
+    return q >= n ? q - n : q;
+}
+
 // ---------------------------------------------------------------------------
 // GEMM1 + SiLU*up, bf16.  grid = (N/64, blocks); wave w of workgroup x owns
 // gate rows n0..n0+15 with n0 = (4x + w)*16 and up rows N+n0..N+n0+15.
+// A K-step is 128 elements: 4 MFMAs per row tile.
 // ---------------------------------------------------------------------------
-struct FragBf16G1 {
-    bf16x8_t g[4], u[4], b[4];
-};
-
 __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
-    const int32_t* __restrict__ num_padded, int topk, int nslots, int K, int N,
+    const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     uint16_t* __restrict__ act) {
     const int blk = (int)blockIdx.y;
     if (blk * kDecRows >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
-    const int wave = (int)threadIdx.x / kWave;
-    const int n0 = ((int)blockIdx.x * 4 + wave) * 16;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
+    const int gw = (int)blockIdx.x * 4 + wave;
+    const int n0 = gw * 16;
     const int i = lane & 15, kq = lane >> 4;
     const int p = sorted_ids[blk * kDecRows + i];
     const bool valid = p < nslots;
-    const uint16_t* xr = x + (size_t)(valid ? p / topk : 0) * K + kq * 8;
-    const uint16_t* gr = w1 + ((size_t)e * 2 * N + n0 + i) * K + kq * 8;
-    const uint16_t* ur = gr + (size_t)N * K;
 
-    auto load = [&](FragBf16G1& f, int k) {
+    const size_t row_bytes = (size_t)K * 2;
+    const rsrc_t rg = make_rsrc(w1 + ((size_t)e * 2 * N + n0) * K, (uint32_t)(16 * row_bytes));
+    const rsrc_t ru = make_rsrc(w1 + ((size_t)e * 2 * N + N + n0) * K, (uint32_t)(16 * row_bytes));
+    const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)M * row_bytes));
+    const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 16;
+    const uint32_t xo = valid ? (uint32_t)((size_t)(p / topk) * row_bytes) + kq * 16 : kOob;
+
+    struct Frag { i32x4_t g[4], u[4], b[4]; };
+    auto load = [&](Frag& f, int k) {
+        const uint32_t kb = (uint32_t)k * 2;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            f.g[s] = ld16(gr + k + s * 32);
-            f.u[s] = ld16(ur + k + s * 32);
+            f.g[s] = bload(rg, wo + kb + s * 64);
+            f.u[s] = bload(ru, wo + kb + s * 64);
+            f.b[s] = bload(rx, xo + kb + s * 64);
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) f.b[s] = valid ? ld16(xr + k + s * 32) : bf16x8_t{};
     };
-
     f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    FragBf16G1 cur, nxt;
-    load(cur, 0);
-    for (int k = 0; k < K; k += 128) {
-        const bool more = k + 128 < K;
-        if (more) load(nxt, k + 128);
+    auto compute = [&](const Frag& f) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            accg = mfma_bf16(cur.g[s], cur.b[s], accg);
-            accu = mfma_bf16(cur.u[s], cur.b[s], accu);
+            accg = mfma_bf16(f.g[s], f.b[s], accg);
+            accu = mfma_bf16(f.u[s], f.b[s], accu);
         }
-        if (more) cur = nxt;
+    };
+    const int nst = K / 128;
+    const int rot = (gw * kRot + blk * 5) % nst;
+    Frag cur;
+    load(cur, rotated(0, rot, nst) * 128);
+    for (int j = 1; j < nst; ++j) {
+        Frag nxt;
+        load(nxt, rotated(j, rot, nst) * 128);
+        compute(cur);
+        cur = nxt;
     }
+    compute(cur);
+    pin(accg);
+    pin(accu);
 
     if (valid) {
         u16x4_t o;
@@ -111,54 +142,64 @@ __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
 // workgroup x owns output rows c0..c0+31, c0 = (4x + w)*32, over the
 // reduction range [z*N/nsplit, (z+1)*N/nsplit).
 // ---------------------------------------------------------------------------
-struct FragBf16G2 {
-    bf16x8_t a0[4], a1[4], b[4];
-};
-
 __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
     const int blk = (int)blockIdx.y;
     if (blk * kDecRows >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
-    const int wave = (int)threadIdx.x / kWave;
-    const int c0 = ((int)blockIdx.x * 4 + wave) * 32;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
+    const int gw = (int)blockIdx.x * 4 + wave;
+    const int c0 = gw * 32;
     const int i = lane & 15, kq = lane >> 4;
     const int z = (int)blockIdx.z;
     const int nlen = N / nsplit;
     const int nbeg = z * nlen;
-    const int p = sorted_ids[blk * kDecRows + i];
+    const int r = blk * kDecRows + i;
+    const int p = sorted_ids[r];
     const bool valid = p < nslots;
-    const uint16_t* ar = act + (size_t)(blk * kDecRows + i) * N + nbeg + kq * 8;
-    const uint16_t* w0 = w2 + ((size_t)e * K + c0 + i) * N + nbeg + kq * 8;
-    const uint16_t* w1r = w0 + (size_t)16 * N;
 
-    auto load = [&](FragBf16G2& f, int n) {
+    const size_t row_bytes = (size_t)N * 2;
+    const rsrc_t rw = make_rsrc(w2 + ((size_t)e * K + c0) * N, (uint32_t)(32 * row_bytes));
+    const rsrc_t ra = make_rsrc(act, (uint32_t)((size_t)cap * row_bytes));
+    const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg * 2 + kq * 16;
+    const uint32_t wo1 = wo + (uint32_t)(16 * row_bytes);
+    const uint32_t ao = valid ? (uint32_t)((size_t)r * row_bytes) + nbeg * 2 + kq * 16 : kOob;
+
+    struct Frag { i32x4_t a0[4], a1[4], b[4]; };
+    auto load = [&](Frag& f, int n) {
+        const uint32_t nb = (uint32_t)n * 2;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            f.a0[s] = ld16(w0 + n + s * 32);
-            f.a1[s] = ld16(w1r + n + s * 32);
+            f.a0[s] = bload(rw, wo + nb + s * 64);
+            f.a1[s] = bload(rw, wo1 + nb + s * 64);
+            f.b[s] = bload(ra, ao + nb + s * 64);
         }
-#pragma unroll
-        for (int s = 0; s < 4; ++s) f.b[s] = valid ? ld16(ar + n + s * 32) : bf16x8_t{};
     };
-
     f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    FragBf16G2 cur, nxt;
-    load(cur, 0);
-    for (int n = 0; n < nlen; n += 128) {
-        const bool more = n + 128 < nlen;
-        if (more) load(nxt, n + 128);
+    auto compute = [&](const Frag& f) {
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-            acc0 = mfma_bf16(cur.a0[s], cur.b[s], acc0);
-            acc1 = mfma_bf16(cur.a1[s], cur.b[s], acc1);
+            acc0 = mfma_bf16(f.a0[s], f.b[s], acc0);
+            acc1 = mfma_bf16(f.a1[s], f.b[s], acc1);
         }
-        if (more) cur = nxt;
+    };
+    const int nst = nlen / 128;
+    const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
+    Frag cur;
+    load(cur, rotated(0, rot, nst) * 128);
+    for (int j = 1; j < nst; ++j) {
+        Frag nxt;
+        load(nxt, rotated(j, rot, nst) * 128);
+        compute(cur);
+        cur = nxt;
     }
+    compute(cur);
+    pin(acc0);
+    pin(acc1);
 
     if (valid) {
         const float w = topk_w[p];
@@ -169,68 +210,66 @@ __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
-// FP8 (OCP e4m3) versions.  One 16x16x128 MFMA consumes 32 codes per lane.
-// GEMM1 applies s_x[t] * w1_scale[e] to the fp32 accumulators, forms
-// SiLU*up in fp32, stores it and folds each row's |act| max into amax[r]
-// (float bits, atomicMax: exact and order-free for non-negative floats).
+// FP8 (OCP e4m3) versions.  One 16x16x128 MFMA consumes 32 codes per lane; a
+// K-step is one 128-code chunk.  GEMM1 applies s_x[t] * w1_scale[e] to the
+// fp32 accumulators, forms SiLU*up in fp32, stores it and folds each row's
+// |act| max into amax[r] (float bits, atomicMax: exact and order-free for
+// non-negative floats).
 // ---------------------------------------------------------------------------
-struct FragFp8G1 {
-    i32x8_t g[2], u[2], b[2];
-};
-
 __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
     const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
-    const int32_t* __restrict__ num_padded, int topk, int nslots, int K, int N,
+    const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     float* __restrict__ act, uint32_t* __restrict__ amax) {
     const int blk = (int)blockIdx.y;
     if (blk * kDecRows >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
-    const int wave = (int)threadIdx.x / kWave;
-    const int n0 = ((int)blockIdx.x * 4 + wave) * 16;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
+    const int gw = (int)blockIdx.x * 4 + wave;
+    const int n0 = gw * 16;
     const int i = lane & 15, kq = lane >> 4;
     const int p = sorted_ids[blk * kDecRows + i];
     const bool valid = p < nslots;
     const int t = valid ? p / topk : 0;
-    const uint8_t* xr = xq + (size_t)t * K + kq * 32;
-    const uint8_t* gr = w1 + ((size_t)e * 2 * N + n0 + i) * K + kq * 32;
-    const uint8_t* ur = gr + (size_t)N * K;
 
-    // K is a multiple of 128; a step covers two 128-code chunks, and the
-    // second chunk is neither loaded nor used past the end of the row.
-    const int ksteps = K / 128;
-    auto load = [&](FragFp8G1& f, int c) {
-        const int k = c * 128;
-        const bool two = c + 1 < ksteps;
-        f.g[0] = ld32(gr + k);
-        f.u[0] = ld32(ur + k);
-        f.g[1] = two ? ld32(gr + k + 128) : i32x8_t{};
-        f.u[1] = two ? ld32(ur + k + 128) : i32x8_t{};
-        f.b[0] = valid ? ld32(xr + k) : i32x8_t{};
-        f.b[1] = (valid && two) ? ld32(xr + k + 128) : i32x8_t{};
+    const size_t row_bytes = (size_t)K;
+    const rsrc_t rg = make_rsrc(w1 + ((size_t)e * 2 * N + n0) * K, (uint32_t)(16 * row_bytes));
+    const rsrc_t ru = make_rsrc(w1 + ((size_t)e * 2 * N + N + n0) * K, (uint32_t)(16 * row_bytes));
+    const rsrc_t rx = make_rsrc(xq, (uint32_t)((size_t)M * row_bytes));
+    const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 32;
+    const uint32_t xo = valid ? (uint32_t)((size_t)t * row_bytes) + kq * 32 : kOob;
+
+    struct Frag { i32x8_t g, u, b; };
+    auto load = [&](Frag& f, int k) {
+        f.g = bload32(rg, wo + k);
+        f.u = bload32(ru, wo + k);
+        f.b = bload32(rx, xo + k);
     };
-
     f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    FragFp8G1 cur, nxt;
-    load(cur, 0);
-    for (int c = 0; c < ksteps; c += 2) {
-        const bool more = c + 2 < ksteps;
-        if (more) load(nxt, c + 2);
-        accg = mfma_fp8(cur.g[0], cur.b[0], accg);
-        accu = mfma_fp8(cur.u[0], cur.b[0], accu);
-        if (c + 1 < ksteps) {
-            accg = mfma_fp8(cur.g[1], cur.b[1], accg);
-            accu = mfma_fp8(cur.u[1], cur.b[1], accu);
-        }
-        if (more) cur = nxt;
+    auto compute = [&](const Frag& f) {
+        accg = mfma_fp8(f.g, f.b, accg);
+        accu = mfma_fp8(f.u, f.b, accu);
+    };
+    const int nst = K / 128;
+    const int rot = (gw * kRot + blk * 5) % nst;
+    Frag cur;
+    load(cur, rotated(0, rot, nst) * 128);
+    for (int j = 1; j < nst; ++j) {
+        Frag nxt;
+        load(nxt, rotated(j, rot, nst) * 128);
+        compute(cur);
+        cur = nxt;
     }
+    compute(cur);
+    pin(accg);
+    pin(accu);
 
     float m = 0.0f;
-    f32x4_t o;
     if (valid) {
         const float sc = xscale[t] * w1_scale[e];
+        f32x4_t o;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
             o[v] = silu(accg[v] * sc) * (accu[v] * sc);
@@ -264,22 +303,19 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     if (lane == 0) ascale[r] = s;
 }
 
-struct FragFp8G2 {
-    i32x8_t a0[2], a1[2], b[2];
-};
-
 __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
     const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
-    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
     const int blk = (int)blockIdx.y;
     if (blk * kDecRows >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
-    const int wave = (int)threadIdx.x / kWave;
-    const int c0 = ((int)blockIdx.x * 4 + wave) * 32;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
+    const int gw = (int)blockIdx.x * 4 + wave;
+    const int c0 = gw * 32;
     const int i = lane & 15, kq = lane >> 4;
     const int z = (int)blockIdx.z;
     const int nlen = N / nsplit;
@@ -287,36 +323,38 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     const int r = blk * kDecRows + i;
     const int p = sorted_ids[r];
     const bool valid = p < nslots;
-    const uint8_t* ar = act_q + (size_t)r * N + nbeg + kq * 32;
-    const uint8_t* w0 = w2 + ((size_t)e * K + c0 + i) * N + nbeg + kq * 32;
-    const uint8_t* w1r = w0 + (size_t)16 * N;
 
-    const int nsteps = nlen / 128;
-    auto load = [&](FragFp8G2& f, int c) {
-        const int n = c * 128;
-        const bool two = c + 1 < nsteps;
-        f.a0[0] = ld32(w0 + n);
-        f.a1[0] = ld32(w1r + n);
-        f.a0[1] = two ? ld32(w0 + n + 128) : i32x8_t{};
-        f.a1[1] = two ? ld32(w1r + n + 128) : i32x8_t{};
-        f.b[0] = valid ? ld32(ar + n) : i32x8_t{};
-        f.b[1] = (valid && two) ? ld32(ar + n + 128) : i32x8_t{};
+    const size_t row_bytes = (size_t)N;
+    const rsrc_t rw = make_rsrc(w2 + ((size_t)e * K + c0) * N, (uint32_t)(32 * row_bytes));
+    const rsrc_t ra = make_rsrc(act_q, (uint32_t)((size_t)cap * row_bytes));
+    const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg + kq * 32;
+    const uint32_t wo1 = wo + (uint32_t)(16 * row_bytes);
+    const uint32_t ao = valid ? (uint32_t)((size_t)r * row_bytes) + nbeg + kq * 32 : kOob;
+
+    struct Frag { i32x8_t a0, a1, b; };
+    auto load = [&](Frag& f, int n) {
+        f.a0 = bload32(rw, wo + n);
+        f.a1 = bload32(rw, wo1 + n);
+        f.b = bload32(ra, ao + n);
     };
-
     f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    FragFp8G2 cur, nxt;
-    load(cur, 0);
-    for (int c = 0; c < nsteps; c += 2) {
-        const bool more = c + 2 < nsteps;
-        if (more) load(nxt, c + 2);
-        acc0 = mfma_fp8(cur.a0[0], cur.b[0], acc0);
-        acc1 = mfma_fp8(cur.a1[0], cur.b[0], acc1);
-        if (c + 1 < nsteps) {
-            acc0 = mfma_fp8(cur.a0[1], cur.b[1], acc0);
-            acc1 = mfma_fp8(cur.a1[1], cur.b[1], acc1);
-        }
-        if (more) cur = nxt;
+    auto compute = [&](const Frag& f) {
+        acc0 = mfma_fp8(f.a0, f.b, acc0);
+        acc1 = mfma_fp8(f.a1, f.b, acc1);
+    };
+    const int nst = nlen / 128;
+    const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
+    Frag cur;
+    load(cur, rotated(0, rot, nst) * 128);
+    for (int j = 1; j < nst; ++j) {
+        Frag nxt;
+        load(nxt, rotated(j, rot, nst) * 128);
+        compute(cur);
+        cur = nxt;
     }
+    compute(cur);
+    pin(acc0);
+    pin(acc1);
 
     if (valid) {
         const float w = topk_w[p] * ascale[r] * w2_scale[e];
@@ -330,33 +368,33 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
 // host launchers
 // ---------------------------------------------------------------------------
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
-                              const int32_t* block_expert, const int32_t* num_padded, int topk,
-                              int nslots, int K, int N, int max_blocks, void* act,
+                              const int32_t* block_expert, const int32_t* num_padded, int M,
+                              int topk, int nslots, int K, int N, int max_blocks, void* act,
                               hipStream_t s) {
     dim3 grid(N / 64, max_blocks);
     gemm1_decode_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)w1,
-                                                  sorted_ids, block_expert, num_padded, topk,
+                                                  sorted_ids, block_expert, num_padded, M, topk,
                                                   nslots, K, N, (uint16_t*)act);
 }
 
 void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk_w,
                               const int32_t* sorted_ids, const int32_t* block_expert,
-                              const int32_t* num_padded, int nslots, int K, int N, int nsplit,
-                              int max_blocks, float* ypart, hipStream_t s) {
+                              const int32_t* num_padded, int cap, int nslots, int K, int N,
+                              int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     dim3 grid(K / 128, max_blocks, nsplit);
     gemm2_decode_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)act, (const uint16_t*)w2,
                                                   topk_w, sorted_ids, block_expert, num_padded,
-                                                  nslots, K, N, nsplit, ypart);
+                                                  cap, nslots, K, N, nsplit, ypart);
 }
 
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
                              const float* w1_scale, const int32_t* sorted_ids,
-                             const int32_t* block_expert, const int32_t* num_padded, int topk,
-                             int nslots, int K, int N, int max_blocks, float* act,
+                             const int32_t* block_expert, const int32_t* num_padded, int M,
+                             int topk, int nslots, int K, int N, int max_blocks, float* act,
                              uint32_t* amax, hipStream_t s) {
     dim3 grid(N / 64, max_blocks);
     gemm1_decode_fp8_kernel<<<grid, 256, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale,
-                                                 sorted_ids, block_expert, num_padded, topk,
+                                                 sorted_ids, block_expert, num_padded, M, topk,
                                                  nslots, K, N, act, amax);
 }
 
@@ -370,12 +408,12 @@ void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sor
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
                              const float* w2_scale, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,
-                             const int32_t* num_padded, int nslots, int K, int N, int nsplit,
-                             int max_blocks, float* ypart, hipStream_t s) {
+                             const int32_t* num_padded, int cap, int nslots, int K, int N,
+                             int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     dim3 grid(K / 128, max_blocks, nsplit);
     gemm2_decode_fp8_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale,
                                                  topk_w, sorted_ids, block_expert, num_padded,
-                                                 nslots, K, N, nsplit, ypart);
+                                                 cap, nslots, K, N, nsplit, ypart);
 }
 
 }  // namespace moe

@@ -22,17 +22,17 @@ void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sor
                   uint32_t* zero_buf, int zero_words, hipStream_t s);
 
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
-                              const int32_t* block_expert, const int32_t* num_padded, int topk,
-                              int nslots, int K, int N, int max_blocks, void* act,
+                              const int32_t* block_expert, const int32_t* num_padded, int M,
+                              int topk, int nslots, int K, int N, int max_blocks, void* act,
                               hipStream_t s);
 void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk_w,
                               const int32_t* sorted_ids, const int32_t* block_expert,
-                              const int32_t* num_padded, int nslots, int K, int N, int nsplit,
-                              int max_blocks, float* ypart, hipStream_t s);
+                              const int32_t* num_padded, int cap, int nslots, int K, int N,
+                              int nsplit, int max_blocks, float* ypart, hipStream_t s);
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
                              const float* w1_scale, const int32_t* sorted_ids,
-                             const int32_t* block_expert, const int32_t* num_padded, int topk,
-                             int nslots, int K, int N, int max_blocks, float* act,
+                             const int32_t* block_expert, const int32_t* num_padded, int M,
+                             int topk, int nslots, int K, int N, int max_blocks, float* act,
                              uint32_t* amax, hipStream_t s);
 void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sorted_ids,
                       const int32_t* num_padded, int nslots, int N, int cap, uint8_t* act_q,
@@ -40,16 +40,16 @@ void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sor
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
                              const float* w2_scale, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,
-                             const int32_t* num_padded, int nslots, int K, int N, int nsplit,
-                             int max_blocks, float* ypart, hipStream_t s);
+                             const int32_t* num_padded, int cap, int nslots, int K, int N,
+                             int nsplit, int max_blocks, float* ypart, hipStream_t s);
 
 void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
-                               const int32_t* block_expert, const int32_t* num_padded, int topk,
-                               int nslots, int K, int N, int max_blocks, void* act,
+                               const int32_t* block_expert, const int32_t* num_padded, int M,
+                               int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s);
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
-                               const int32_t* num_padded, int nslots, int K, int N,
+                               const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int max_blocks, float* ypart, hipStream_t s);
 
 void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
