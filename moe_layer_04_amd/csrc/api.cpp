@@ -55,6 +55,8 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         const long tiles = est_blocks * (K / 128);
         while (tiles * p.nsplit < 1024 && p.nsplit < 16 && (N / (p.nsplit * 2)) % 128 == 0)
             p.nsplit *= 2;
+    } else {
+        p.nsplit = moe::prefill_gemm2_splits(K, N);
     }
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -249,7 +251,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                           p.nsplit, p.max_blocks, ypart, s);
         else
             moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
-                                           p.max_blocks, ypart, s);
+                                           p.nsplit, p.max_blocks, ypart, s);
         mark(6);
     }
     moe::launch_combine(ypart, M, K, topk, p.nsplit, out, s);

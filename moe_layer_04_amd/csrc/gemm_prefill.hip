@@ -10,20 +10,23 @@
 // as in the decode kernels; tokens are the columns, gathered through the
 // expert-sorted row list for GEMM1 and contiguous for GEMM2.
 //
-// Per workgroup (4 waves, 2x2): each wave owns TW/2 weight rows x 64 token
-// columns, i.e. (TW/64) x 2 MFMA tiles of 32x32.  In GEMM1 the workgroup's
-// weight rows are TW/2 gate rows followed by the matching TW/2 up rows and
-// each wave takes the same n-range from both halves, so SiLU(gate)*up is
-// formed from its own accumulators.
+// Waves: 4 per workgroup, WW along the weight rows and 4/WW along the token
+// columns.  In GEMM1 the workgroup's weight rows are TW/2 gate rows followed
+// by the matching TW/2 up rows and each wave takes the same n-range from
+// both halves, so SiLU(gate)*up is formed from its own accumulators.
 //
-// Staging: K advances BK at a time through two LDS buffers.  Each step
-// issues the next step's global loads (buffer loads into registers), runs
-// the MFMAs of the current buffer, writes the registers into the other
-// buffer and meets the workgroup at one barrier.  LDS rows are padded by
-// 16 bytes so the 32 rows one MFMA operand read touches fall in distinct
-// banks.  Padding token rows (sentinels) load token row 0 for GEMM1 / their
+// Staging: both operand tiles are copied global -> LDS by the gfx950 buffer
+// loads with an LDS destination (no register round trip) into a ring of
+// STAGES slots.  Each K-step waits (vmcnt) for its own slot, meets the
+// workgroup at one raw s_barrier (the __syncthreads fence would wait for
+// every in-flight copy), issues the copy STAGES-1 steps ahead and runs its
+// MFMAs.  Padding token rows (sentinels) copy token row 0 for GEMM1 / their
 // own in-bounds act row for GEMM2: an MFMA output column depends only on its
 // own B column, and those columns are never stored.
+//
+// GEMM2 may split its reduction (N) across workgroups into fp32 partial
+// rows (combined later in a fixed order), because K/TW weight tiles per
+// token block are too few to fill the chip in whole waves of workgroups.
 //
 // Tile order: the linear workgroup id is dealt to the 8 XCDs round-robin by
 // the hardware; each XCD is given a contiguous range of tiles, and tiles are
@@ -47,9 +50,6 @@ typedef __amdgpu_buffer_rsrc_t prsrc_t;
 __device__ __forceinline__ prsrc_t pmake_rsrc(const void* base, uint32_t bytes) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
-__device__ __forceinline__ bf16x8_t pload(prsrc_t r, uint32_t off) {
-    return (bf16x8_t)__builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
-}
 __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
@@ -69,104 +69,144 @@ __device__ __forceinline__ bool tile_of(int g, int n_wtiles, int n_blocks, int& 
     return true;
 }
 
-// The shared main loop.  wrow_off(q) / xrow_off(q): byte offsets (at k = 0)
-// of the rows this thread stages; FW = A tiles per wave (TW/64).
-template <int TW, int BK>
+// LDS layout of one ring slot: TW weight rows then 128 token rows, each row
+// BK bf16 (BK*2 bytes) without padding, its 16-byte chunks permuted by an
+// XOR of the row index (swz) so that the 16 consecutive rows an MFMA operand
+// read touches in one LDS cycle land in distinct banks.  The DMA writes 1 KB
+// per wave instruction in lane order, so lane l of an instruction covering
+// rows r0.. stores physical chunk (l % CPR) of row r0 + l / CPR and therefore
+// fetches logical chunk (l % CPR) ^ swz(row) from global memory.
+template <int BK>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (BK == 32) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+    else return (r & 7) ^ ((r >> 3) & 1);
+}
+
+// s_waitcnt vmcnt(N) leaving the LDS/export counters unconstrained.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// The shared main loop: DMA ring of STAGES slots, one raw barrier per step.
+// Every thread issues kWInstr + kXInstr DMA instructions per step; the wait
+// at the top of step s leaves only the younger, already-issued steps in
+// flight.  The barrier then publishes step s to the workgroup and proves
+// that every wave has finished reading the slot the next DMA overwrites.
+template <int TW, int BK, int STAGES, int WW>
 struct PrefillCore {
-    static constexpr int kStride = BK + 8;                 // bf16 per LDS row
-    static constexpr int kWChunks = TW * BK / 8 / 256;     // 16-B chunks per thread (weights)
-    static constexpr int kXChunks = kPreRows * BK / 8 / 256;
-    static constexpr int kCPR = BK / 8;                    // chunks per row
-    static constexpr int FW = TW / 64;
-    static constexpr int kLdsW = TW * kStride;
-    static constexpr int kLdsX = kPreRows * kStride;
-    static constexpr int kLdsBytes = 2 * (kLdsW + kLdsX) * 2;
+    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kCPR = BK / 8;                    // 16-B chunks per row
+    static constexpr int kRowsPerInstr = 64 / kCPR;        // rows one wave instruction covers
+    static constexpr int kWInstr = TW / kRowsPerInstr / 4; // per wave per step
+    static constexpr int kXInstr = kPreRows / kRowsPerInstr / 4;
+    static constexpr int kSlotBytes = (TW + kPreRows) * kRowBytes;
+    static constexpr int kLdsBytes = STAGES * kSlotBytes;
+    static constexpr int kPerStep = kWInstr + kXInstr;
+    static constexpr int WT = 4 / WW;                      // waves along the token dimension
+    static constexpr int FW = TW / WW / 32;                // 32-row A tiles per wave
+    static constexpr int FT = kPreRows / WT / 32;          // 32-column B tiles per wave
 
-    f32x16_t acc[FW][2];
+    f32x16_t acc[FW][FT];
 
-    __device__ __forceinline__ void run(uint16_t* lds, prsrc_t rw, const uint32_t* woff,
-                                        prsrc_t rx, const uint32_t* xoff, int K, int wa, int wb,
+    // Row (within the slot's weight / token region) that lane `lane` of DMA
+    // instruction q of wave `wave` fills, and the logical chunk it fetches.
+    __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
+        return (q * 4 + wave) * kRowsPerInstr + lane / kCPR;
+    }
+    __device__ static __forceinline__ int dma_chunk(int row, int lane) {
+        return (lane % kCPR) ^ swz<BK>(row);
+    }
+
+    // woff[q] / xoff[q]: byte offset at k = kbeg of this lane's source chunk;
+    // the loop covers klen reduction elements.
+    __device__ __forceinline__ void run(char* lds, prsrc_t rw, const uint32_t* woff, prsrc_t rx,
+                                        const uint32_t* xoff, int klen, int wave, int wb,
                                         const int* arow) {
-        const int tid = (int)threadIdx.x;
         const int lane = lane_id();
 #pragma unroll
         for (int a = 0; a < FW; ++a)
 #pragma unroll
-            for (int b = 0; b < 2; ++b)
+            for (int b = 0; b < FT; ++b)
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-        int wl[kWChunks], xl[kXChunks];
+        auto dma = [&](int step, int slot) {
+            const uint32_t kb = (uint32_t)step * kRowBytes;
+            char* base = lds + slot * kSlotBytes;
 #pragma unroll
-        for (int q = 0; q < kWChunks; ++q) {
-            const int c = tid + 256 * q;
-            wl[q] = (c / kCPR) * kStride + (c % kCPR) * 8;
-        }
+            for (int q = 0; q < kWInstr; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (__attribute__((address_space(3))) void*)(base + (q * 4 + wave) * 1024),
+                    16, woff[q] + kb, 0, 0, 0);
 #pragma unroll
-        for (int q = 0; q < kXChunks; ++q) {
-            const int c = tid + 256 * q;
-            xl[q] = (c / kCPR) * kStride + (c % kCPR) * 8;
-        }
-        bf16x8_t rw_[kWChunks], rx_[kXChunks];
-        auto gload = [&](int k) {
-            const uint32_t kb = (uint32_t)k * 2;
-#pragma unroll
-            for (int q = 0; q < kWChunks; ++q) rw_[q] = pload(rw, woff[q] + kb);
-#pragma unroll
-            for (int q = 0; q < kXChunks; ++q) rx_[q] = pload(rx, xoff[q] + kb);
+            for (int q = 0; q < kXInstr; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx,
+                    (__attribute__((address_space(3))) void*)(base + TW * kRowBytes +
+                                                              (q * 4 + wave) * 1024),
+                    16, xoff[q] + kb, 0, 0, 0);
         };
-        auto lstore = [&](int buf) {
-            uint16_t* sw = lds + buf * (kLdsW + kLdsX);
-            uint16_t* sx = sw + kLdsW;
+
+        // per-lane LDS read offsets (bytes within a slot) for each k16 step
+        const int li = lane & 31, half = lane >> 5;
+        int aoff[BK / 16][FW], boff[BK / 16][FT];
 #pragma unroll
-            for (int q = 0; q < kWChunks; ++q) *reinterpret_cast<bf16x8_t*>(sw + wl[q]) = rw_[q];
+        for (int ks = 0; ks < BK / 16; ++ks) {
+            const int c = 2 * ks + half;
 #pragma unroll
-            for (int q = 0; q < kXChunks; ++q) *reinterpret_cast<bf16x8_t*>(sx + xl[q]) = rx_[q];
-        };
-        const int li = lane & 31, lk = (lane >> 5) * 8;
-        int ar[FW];
+            for (int a = 0; a < FW; ++a) {
+                const int r = arow[a] + li;
+                aoff[ks][a] = r * kRowBytes + ((c ^ swz<BK>(r)) << 4);
+            }
 #pragma unroll
-        for (int a = 0; a < FW; ++a) ar[a] = (arow[a] + li) * kStride + lk;
-        const int xb0 = (wb * 64 + li) * kStride + lk;
-        const int xb1 = xb0 + 32 * kStride;
-        auto compute = [&](int buf) {
-            const uint16_t* sw = lds + buf * (kLdsW + kLdsX);
-            const uint16_t* sx = sw + kLdsW;
+            for (int b = 0; b < FT; ++b) {
+                const int r = wb * (kPreRows / WT) + b * 32 + li;
+                boff[ks][b] = (TW + r) * kRowBytes + ((c ^ swz<BK>(r)) << 4);
+            }
+        }
+        auto compute = [&](int slot) {
+            const char* base = lds + slot * kSlotBytes;
 #pragma unroll
-            for (int ks = 0; ks < BK; ks += 16) {
-                bf16x8_t av[FW];
+            for (int ks = 0; ks < BK / 16; ++ks) {
+                bf16x8_t av[FW], bv[FT];
 #pragma unroll
                 for (int a = 0; a < FW; ++a)
-                    av[a] = *reinterpret_cast<const bf16x8_t*>(sw + ar[a] + ks);
-                const bf16x8_t b0 = *reinterpret_cast<const bf16x8_t*>(sx + xb0 + ks);
-                const bf16x8_t b1 = *reinterpret_cast<const bf16x8_t*>(sx + xb1 + ks);
+                    av[a] = *reinterpret_cast<const bf16x8_t*>(base + aoff[ks][a]);
 #pragma unroll
-                for (int a = 0; a < FW; ++a) {
-                    acc[a][0] = mfma32_bf16(av[a], b0, acc[a][0]);
-                    acc[a][1] = mfma32_bf16(av[a], b1, acc[a][1]);
-                }
+                for (int b = 0; b < FT; ++b)
+                    bv[b] = *reinterpret_cast<const bf16x8_t*>(base + boff[ks][b]);
+#pragma unroll
+                for (int a = 0; a < FW; ++a)
+#pragma unroll
+                    for (int b = 0; b < FT; ++b) acc[a][b] = mfma32_bf16(av[a], bv[b], acc[a][b]);
             }
         };
 
-        const int steps = K / BK;
-        gload(0);
-        lstore(0);
-        __syncthreads();
-        for (int s = 0; s + 1 < steps; ++s) {
-            gload((s + 1) * BK);
-            // keep the next step's loads ahead of this step's MFMAs (the
-            // scheduler would otherwise sink them to just before their use)
-            __builtin_amdgcn_sched_barrier(0);
-            compute(s & 1);
-            lstore((s + 1) & 1);
-            __syncthreads();
-        }
-        compute((steps - 1) & 1);
+        const int steps = klen / BK;
 #pragma unroll
-        for (int a = 0; a < FW; ++a) {
-            pin(acc[a][0]);
-            pin(acc[a][1]);
+        for (int s = 0; s < STAGES - 1; ++s)
+            if (s < steps) dma(s, s);
+        int slot = 0;
+        for (int s = 0; s < steps; ++s) {
+            // step s has landed once at most the (STAGES-2) younger steps are
+            // outstanding; near the end fewer were issued
+            if (s + STAGES - 2 < steps) wait_vmcnt<(STAGES - 2) * kPerStep>();
+            else wait_vmcnt<0>();
+            __builtin_amdgcn_s_barrier();
+            if (s + STAGES - 1 < steps) {
+                int nslot = slot + STAGES - 1;
+                if (nslot >= STAGES) nslot -= STAGES;
+                dma(s + STAGES - 1, nslot);
+            }
+            compute(slot);
+            if (++slot == STAGES) slot = 0;
         }
+#pragma unroll
+        for (int a = 0; a < FW; ++a)
+#pragma unroll
+            for (int b = 0; b < FT; ++b) pin(acc[a][b]);
     }
 };
 
@@ -174,62 +214,60 @@ struct PrefillCore {
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
-template <int TW, int BK>
-__global__ __launch_bounds__(256, 2) void gemm1_prefill_bf16_kernel(
+template <int TW, int BK, int STAGES, int WW, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     int max_blocks, uint16_t* __restrict__ act) {
-    using Core = PrefillCore<TW, BK>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[Core::kLdsBytes / 2];
+    using Core = PrefillCore<TW, BK, STAGES, WW>;
+    __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int HW = TW / 2;  // n-values per tile
+    constexpr int WN = HW / WW; // n-values per wave
 
     int wt, blk;
     if (!tile_of((int)blockIdx.x, N / HW, max_blocks, wt, blk)) return;
     if (blk * kPreRows >= *num_padded) return;
     const int e = block_expert[blk];
-    const int tid = (int)threadIdx.x;
     const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wa = wave & 1, wb = wave >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wa = wave % WW, wb = wave / WW;
 
     const size_t row_bytes = (size_t)K * 2;
     const prsrc_t rw = pmake_rsrc(w1 + (size_t)e * 2 * N * K, (uint32_t)(2 * (size_t)N * row_bytes));
     const prsrc_t rx = pmake_rsrc(x, (uint32_t)((size_t)M * row_bytes));
-    uint32_t woff[Core::kWChunks], xoff[Core::kXChunks];
+    uint32_t woff[Core::kWInstr], xoff[Core::kXInstr];
 #pragma unroll
-    for (int q = 0; q < Core::kWChunks; ++q) {
-        const int c = tid + 256 * q;
-        const int row = c / Core::kCPR, col = (c % Core::kCPR) * 8;
+    for (int q = 0; q < Core::kWInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
         const int wrow = (row < HW) ? (wt * HW + row) : (N + wt * HW + row - HW);
-        woff[q] = (uint32_t)(wrow * row_bytes) + col * 2;
+        woff[q] = (uint32_t)(wrow * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
 #pragma unroll
-    for (int q = 0; q < Core::kXChunks; ++q) {
-        const int c = tid + 256 * q;
-        const int row = c / Core::kCPR, col = (c % Core::kCPR) * 8;
+    for (int q = 0; q < Core::kXInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
         const int p = sorted_ids[blk * kPreRows + row];
         const int t = p < nslots ? p / topk : 0;
-        xoff[q] = (uint32_t)(t * row_bytes) + col * 2;
+        xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
-    // A tiles of this wave: gate frags then the matching up frags
+    // A tiles of this wave: its gate frags, then the matching up frags
     int arow[Core::FW];
 #pragma unroll
     for (int a = 0; a < Core::FW / 2; ++a) {
-        arow[a] = wa * (HW / 2) + a * 32;
-        arow[a + Core::FW / 2] = HW + wa * (HW / 2) + a * 32;
+        arow[a] = wa * WN + a * 32;
+        arow[a + Core::FW / 2] = HW + wa * WN + a * 32;
     }
     Core core;
-    core.run(lds, rw, woff, rx, xoff, K, wa, wb, arow);
+    core.run(lds, rw, woff, rx, xoff, K, wave, wb, arow);
 
     const int li = lane & 31;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int r = blk * kPreRows + wb * 64 + b * 32 + li;
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * kPreRows + wb * (kPreRows / Core::WT) + b * 32 + li;
         if (sorted_ids[r] >= nslots) continue;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
-            uint16_t* dst = act + (size_t)r * N + wt * HW + wa * (HW / 2) + a * 32 + 4 * (lane >> 5);
+            uint16_t* dst = act + (size_t)r * N + wt * HW + wa * WN + a * 32 + 4 * (lane >> 5);
 #pragma unroll
             for (int vg = 0; vg < 4; ++vg) {
                 u16x4_t o;
@@ -247,56 +285,61 @@ __global__ __launch_bounds__(256, 2) void gemm1_prefill_bf16_kernel(
 // GEMM2 (bf16): weight tile wt covers output rows wt*TW..+TW; the epilogue
 // multiplies by the routing weight and scatters token row r to slot p.
 // ---------------------------------------------------------------------------
-template <int TW, int BK>
-__global__ __launch_bounds__(256, 2) void gemm2_prefill_bf16_kernel(
+template <int TW, int BK, int STAGES, int WW, int OCC>
+__global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
-    int nslots, int K, int N, int max_blocks, float* __restrict__ ypart) {
-    using Core = PrefillCore<TW, BK>;
-    __shared__ __attribute__((aligned(16))) uint16_t lds[Core::kLdsBytes / 2];
+    int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
+    using Core = PrefillCore<TW, BK, STAGES, WW>;
+    __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
+    constexpr int WR = TW / WW;  // output rows per wave
 
-    int wt, blk;
-    if (!tile_of((int)blockIdx.x, K / TW, max_blocks, wt, blk)) return;
+    // the split index is the slowest-varying part of the weight-tile index
+    int wtz, blk;
+    const int n_wt = K / TW;
+    if (!tile_of((int)blockIdx.x, n_wt * nsplit, max_blocks, wtz, blk)) return;
     if (blk * kPreRows >= *num_padded) return;
+    const int wt = wtz % n_wt, z = wtz / n_wt;
+    const int nlen = N / nsplit, nbeg = z * nlen;
     const int e = block_expert[blk];
-    const int tid = (int)threadIdx.x;
     const int lane = lane_id();
-    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-    const int wa = wave & 1, wb = wave >> 1;
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wa = wave % WW, wb = wave / WW;
 
     const size_t row_bytes = (size_t)N * 2;
     const prsrc_t rw = pmake_rsrc(w2 + ((size_t)e * K + (size_t)wt * TW) * N,
                                   (uint32_t)(TW * row_bytes));
     const prsrc_t ra = pmake_rsrc(act, (uint32_t)((size_t)cap * row_bytes));
-    uint32_t woff[Core::kWChunks], aoff[Core::kXChunks];
+    uint32_t woff[Core::kWInstr], aoff[Core::kXInstr];
 #pragma unroll
-    for (int q = 0; q < Core::kWChunks; ++q) {
-        const int c = tid + 256 * q;
-        woff[q] = (uint32_t)((c / Core::kCPR) * row_bytes) + (c % Core::kCPR) * 16;
+    for (int q = 0; q < Core::kWInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
+        woff[q] = (uint32_t)(row * row_bytes) + nbeg * 2 + Core::dma_chunk(row, lane) * 16;
     }
 #pragma unroll
-    for (int q = 0; q < Core::kXChunks; ++q) {
-        const int c = tid + 256 * q;
-        const int r = blk * kPreRows + c / Core::kCPR;
-        aoff[q] = (uint32_t)(r * row_bytes) + (c % Core::kCPR) * 16;
+    for (int q = 0; q < Core::kXInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
+        aoff[q] = (uint32_t)((blk * kPreRows + row) * row_bytes) + nbeg * 2 +
+                  Core::dma_chunk(row, lane) * 16;
     }
     int arow[Core::FW];
 #pragma unroll
-    for (int a = 0; a < Core::FW; ++a) arow[a] = wa * (TW / 2) + a * 32;
+    for (int a = 0; a < Core::FW; ++a) arow[a] = wa * WR + a * 32;
     Core core;
-    core.run(lds, rw, woff, ra, aoff, N, wa, wb, arow);
+    core.run(lds, rw, woff, ra, aoff, nlen, wave, wb, arow);
 
     const int li = lane & 31;
 #pragma unroll
-    for (int b = 0; b < 2; ++b) {
-        const int r = blk * kPreRows + wb * 64 + b * 32 + li;
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * kPreRows + wb * (kPreRows / Core::WT) + b * 32 + li;
         const int p = sorted_ids[r];
         if (p >= nslots) continue;
         const float w = topk_w[p];
 #pragma unroll
         for (int a = 0; a < Core::FW; ++a) {
-            float* dst = ypart + (size_t)p * K + wt * TW + wa * (TW / 2) + a * 32 + 4 * (lane >> 5);
+            float* dst = ypart + ((size_t)z * nslots + p) * K + wt * TW + wa * WR + a * 32 +
+                         4 * (lane >> 5);
 #pragma unroll
             for (int vg = 0; vg < 4; ++vg) {
                 f32x4_t o;
@@ -313,33 +356,37 @@ __global__ __launch_bounds__(256, 2) void gemm2_prefill_bf16_kernel(
 // ---------------------------------------------------------------------------
 static int grid_for(int tiles) { return (tiles + 7) / 8 * 8; }
 
-constexpr int kG1TW = 256, kG1BK = 32;
-constexpr int kG2BK = 32;
-
 void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
-    const int grid = grid_for((N / (kG1TW / 2)) * max_blocks);
-    gemm1_prefill_bf16_kernel<kG1TW, kG1BK><<<grid, 256, 0, s>>>(
+    const int grid = grid_for((N / 128) * max_blocks);
+    gemm1_prefill_bf16_kernel<256, 32, 3, 4, 2><<<grid, 256, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
+}
+
+// GEMM2 has K/256 weight tiles per token block -- too few to fill the chip
+// in whole waves of workgroups -- so its reduction is split in four.
+int prefill_gemm2_splits(int K, int N) {
+    (void)K;
+    return (N % (4 * 32) == 0) ? 4 : 1;
 }
 
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
-                               int max_blocks, float* ypart, hipStream_t s) {
+                               int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     if (K % 256 == 0) {
-        const int grid = grid_for((K / 256) * max_blocks);
-        gemm2_prefill_bf16_kernel<256, kG2BK><<<grid, 256, 0, s>>>(
+        const int grid = grid_for((K / 256) * nsplit * max_blocks);
+        gemm2_prefill_bf16_kernel<256, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
-            num_padded, cap, nslots, K, N, max_blocks, ypart);
+            num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else {
-        const int grid = grid_for((K / 128) * max_blocks);
-        gemm2_prefill_bf16_kernel<128, kG2BK><<<grid, 256, 0, s>>>(
+        const int grid = grid_for((K / 128) * nsplit * max_blocks);
+        gemm2_prefill_bf16_kernel<128, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
-            num_padded, cap, nslots, K, N, max_blocks, ypart);
+            num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     }
 }
 
