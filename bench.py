@@ -51,6 +51,50 @@ def hip_runtime():
     return hip
 
 
+COPY_BYTES = 1 << 30
+
+
+def kernel_digest():
+    csrc = os.path.join(ROOT, "moe_layer_04_amd", "csrc")
+    return source_digest(sorted(os.path.join(csrc, f) for f in os.listdir(csrc)))
+
+
+def _pmc_rows(path, counter):
+    import csv
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        out.setdefault(r["Kernel_Name"].split("(")[0], []).append(float(r["Counter_Value"]))
+    return out
+
+
+def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
+    """Per-dispatch HBM traffic of the GEMM1 kernel from counter CSVs, each
+    counter scaled by what it reads for the plain copy of COPY_BYTES."""
+    import statistics
+    cf = _pmc_rows(copy_fetch_csv, "FETCH_SIZE")
+    cw = _pmc_rows(copy_write_csv, "WRITE_SIZE")
+    # the copy dispatches are the large ones of the calibration run
+    copy_f = max(statistics.median(v) for v in cf.values())
+    copy_w = max(statistics.median(v) for v in cw.values())
+    f_scale = COPY_BYTES / (copy_f * 1024)
+    w_scale = COPY_BYTES / (copy_w * 1024)
+    kf = _pmc_rows(fetch_csv, "FETCH_SIZE")
+    kw = _pmc_rows(write_csv, "WRITE_SIZE")
+    name = next(k for k in kf if "gemm1" in k)
+    fetch = statistics.median(kf[name]) * 1024 * f_scale
+    write = statistics.median(kw[name]) * 1024 * w_scale
+    rec = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fetch,
+           "write_bytes_per_launch": write, "bytes_per_launch": fetch + write,
+           "fetch_scale": f_scale, "write_scale": w_scale,
+           "dispatches": len(kf[name]), "source_digest": kernel_digest()}
+    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_pmc.json")
+    with open(path, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -71,7 +115,17 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's sample (0 = whole batch up to 8)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy 3 times (for scaling the "
+                         "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
+                                                        "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
+                    help="turn rocprofv3 --pmc counter CSVs of this workload and of the "
+                         "copy calibration into profiles/gemm1_<workload>_pmc.json and exit")
     args = ap.parse_args()
+    if args.pmc_summary:
+        pmc_summary(args.workload, *args.pmc_summary)
+        return
     if args.gpus != 1:
         print(json.dumps({"error": "this build measures one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
@@ -90,6 +144,14 @@ def main():
         sys.exit("no GPU visible")
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": COPY_BYTES, "reps": 3}))
+        return
     moe.load_library(build_if_missing=True)
 
     log(f"generating {wl}")
@@ -195,9 +257,7 @@ def main():
                     "traffic": None, "units_per_launch": slots,
                     "flops_per_unit": 4.0 * wl.N * wl.K}
     # HBM traffic from committed counter runs, only while the kernels are unchanged
-    digest = source_digest(sorted(
-        os.path.join(ROOT, "moe_layer_04_amd", "csrc", f)
-        for f in os.listdir(os.path.join(ROOT, "moe_layer_04_amd", "csrc"))))
+    digest = kernel_digest()
     pmc = os.path.join(ROOT, "profiles", f"gemm1_{wl.name}_pmc.json")
     if os.path.exists(pmc):
         rec = json.load(open(pmc))
