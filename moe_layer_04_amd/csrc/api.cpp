@@ -116,9 +116,8 @@ MOE_API moe_status moe_topk(const void* x, const void* w_router, const float* ro
         return MOE_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, s);
-    moe::launch_router_topk(logits, M, E, topk, topk_ids, topk_weights, nullptr, K, nullptr,
-                            nullptr, s);
+    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, nullptr, nullptr, s);
+    moe::launch_router_topk(logits, M, E, topk, topk_ids, topk_weights, s);
     return finish_launches();
 }
 
@@ -208,17 +207,17 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         if (timed) (void)hipEventRecord((hipEvent_t)events[i], s);
     };
 
+    uint8_t* xq = dtype == MOE_FP8_E4M3 ? (uint8_t*)(ws + p.xq) : nullptr;
+    float* xs = dtype == MOE_FP8_E4M3 ? (float*)(ws + p.xs) : nullptr;
     mark(0);
-    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, s);
+    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, xq, xs, s);
     mark(1);
     if (dtype == MOE_FP8_E4M3) {
-        uint8_t* xq = (uint8_t*)(ws + p.xq);
-        float* xs = (float*)(ws + p.xs);
         uint32_t* amax = (uint32_t*)(ws + p.amax);
         float* act = (float*)(ws + p.act);
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
-        moe::launch_router_topk(logits, M, E, topk, ids, wts, x, K, xq, xs, s);
+        moe::launch_router_topk(logits, M, E, topk, ids, wts, s);
         mark(2);
         moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax, p.cap,
                           s);
@@ -233,7 +232,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         mark(6);
     } else {
         void* act = ws + p.act;
-        moe::launch_router_topk(logits, M, E, topk, ids, wts, nullptr, K, nullptr, nullptr, s);
+        moe::launch_router_topk(logits, M, E, topk, ids, wts, s);
         mark(2);
         moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, nullptr, 0,
                           s);

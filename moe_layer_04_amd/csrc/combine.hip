@@ -10,31 +10,55 @@
 
 namespace moe {
 
+// One thread per 4 columns when there are many tokens; per column when few
+// (then the partial rows of one token are read by more threads at once).
+template <int V>
 __global__ __launch_bounds__(256) void combine_kernel(const float* __restrict__ ypart, int M,
                                                       int K, int topk, int nsplit,
                                                       uint16_t* __restrict__ out) {
-    const long idx = (long)blockIdx.x * 256 + threadIdx.x;  // one thread per 4 columns
-    const int kq = K / 4;
+    typedef float fv_t __attribute__((ext_vector_type(V)));
+    typedef unsigned short uv_t __attribute__((ext_vector_type(V)));
+    const long idx = (long)blockIdx.x * 256 + threadIdx.x;
+    const int kq = K / V;
     if (idx >= (long)M * kq) return;
     const int t = (int)(idx / kq);
-    const int c = (int)(idx % kq) * 4;
+    const int c = (int)(idx % kq) * V;
     const size_t nslots = (size_t)M * topk;
-    f32x4_t acc = {0, 0, 0, 0};
-    for (int j = 0; j < topk; ++j)
-        for (int z = 0; z < nsplit; ++z)
-            acc += *reinterpret_cast<const f32x4_t*>(
-                ypart + ((size_t)z * nslots + (size_t)t * topk + j) * K + c);
-    u16x4_t o;
+    // partial i = j*nsplit + z lives at ypart[z][t*topk + j]; loads are issued
+    // eight at a time and added in ascending i (a fixed order)
+    const int n = topk * nsplit;
+    auto at = [&](int i) {
+        const int j = i / nsplit, z = i - j * nsplit;
+        return *reinterpret_cast<const fv_t*>(ypart +
+                                              ((size_t)z * nslots + (size_t)t * topk + j) * K + c);
+    };
+    fv_t acc = {};
+    int i = 0;
+    for (; i + 8 <= n; i += 8) {
+        fv_t v[8];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_bits(acc[v]);
-    *reinterpret_cast<u16x4_t*>(out + (size_t)t * K + c) = o;
+        for (int u = 0; u < 8; ++u) v[u] = at(i + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc += v[u];
+    }
+    for (; i < n; ++i) acc += at(i);
+    uv_t o;
+#pragma unroll
+    for (int v = 0; v < V; ++v) o[v] = f32_to_bf16_bits(acc[v]);
+    *reinterpret_cast<uv_t*>(out + (size_t)t * K + c) = o;
 }
 
 void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
                     hipStream_t s) {
-    const long n = (long)M * (K / 4);
-    const int grid = (int)((n + 255) / 256);
-    combine_kernel<<<grid, 256, 0, s>>>(ypart, M, K, topk, nsplit, (uint16_t*)out);
+    if ((long)M * K >= 256L * 256) {
+        const long n = (long)M * (K / 4);
+        combine_kernel<4><<<(int)((n + 255) / 256), 256, 0, s>>>(ypart, M, K, topk, nsplit,
+                                                                 (uint16_t*)out);
+    } else {
+        const long n = (long)M * K;
+        combine_kernel<1><<<(int)((n + 255) / 256), 256, 0, s>>>(ypart, M, K, topk, nsplit,
+                                                                 (uint16_t*)out);
+    }
 }
 
 }  // namespace moe

@@ -54,20 +54,43 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Map the linear workgroup id to (weight tile, token block); false if idle.
-__device__ __forceinline__ bool tile_of(int g, int n_wtiles, int n_blocks, int& wt, int& blk) {
-    const int total = n_wtiles * n_blocks;
-    const int per_xcd = (total + 7) / 8;
-    const int t = (g % 8) * per_xcd + g / 8;
-    if (t >= total) return false;
-    const int span = kGroup * n_blocks;
-    const int grp = t / span;
-    const int in = t % span;
-    const int gsize = min(kGroup, n_wtiles - grp * kGroup);
-    wt = grp * kGroup + in % gsize;
-    blk = in / gsize;
-    return true;
-}
+// Tile schedule.  The hardware deals workgroup g to XCD g % 8; each XCD is
+// given a contiguous range of tiles, numbered with kGroup weight tiles
+// varying fastest, then token blocks, so the workgroups resident on one XCD
+// at a time cover a kGroup x (resident/kGroup) block of tiles whose weight
+// and token panels they share in that XCD's L2.  The walk below also
+// supports a persistent grid (fewer workgroups than tiles, each taking
+// every nslot-th tile of its XCD's range); the launchers size the grid to
+// one tile per workgroup, which measured less memory traffic.
+struct TileWalk {
+    int xcd, slot, nslot, per_xcd, total, n_wtiles, n_blocks, r;
+    __device__ TileWalk(int n_wt, int n_blk) {
+        const int g = (int)blockIdx.x;
+        xcd = g % 8;
+        slot = g / 8;
+        nslot = (int)gridDim.x / 8;
+        n_wtiles = n_wt;
+        n_blocks = n_blk;
+        total = n_wt * n_blk;
+        per_xcd = (total + 7) / 8;
+        r = 0;
+    }
+    // next tile of this workgroup; false when its share is done
+    __device__ bool next(int& wt, int& blk) {
+        const int local = r * nslot + slot;
+        ++r;
+        if (local >= per_xcd) return false;
+        const int t = xcd * per_xcd + local;
+        if (t >= total) return false;
+        const int span = kGroup * n_blocks;
+        const int grp = t / span;
+        const int in = t % span;
+        const int gsize = min(kGroup, n_wtiles - grp * kGroup);
+        wt = grp * kGroup + in % gsize;
+        blk = in / gsize;
+        return true;
+    }
+};
 
 // LDS layout of one ring slot: TW weight rows then 128 token rows, each row
 // BK bf16 (BK*2 bytes) without padding, its 16-byte chunks permuted by an
@@ -185,6 +208,8 @@ struct PrefillCore {
         };
 
         const int steps = klen / BK;
+        // the previous tile's last reads of the ring are done before refilling it
+        __builtin_amdgcn_s_barrier();
 #pragma unroll
         for (int s = 0; s < STAGES - 1; ++s)
             if (s < steps) dma(s, s);
@@ -225,13 +250,15 @@ __global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
     constexpr int HW = TW / 2;  // n-values per tile
     constexpr int WN = HW / WW; // n-values per wave
 
-    int wt, blk;
-    if (!tile_of((int)blockIdx.x, N / HW, max_blocks, wt, blk)) return;
-    if (blk * kPreRows >= *num_padded) return;
-    const int e = block_expert[blk];
+    const int npad = *num_padded;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int wa = wave % WW, wb = wave / WW;
+    TileWalk walk(N / HW, max_blocks);
+    int wt, blk;
+    while (walk.next(wt, blk)) {
+    if (blk * kPreRows >= npad) continue;
+    const int e = block_expert[blk];
 
     const size_t row_bytes = (size_t)K * 2;
     const prsrc_t rw = pmake_rsrc(w1 + (size_t)e * 2 * N * K, (uint32_t)(2 * (size_t)N * row_bytes));
@@ -279,6 +306,7 @@ __global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
             }
         }
     }
+    }  // tiles
 }
 
 // ---------------------------------------------------------------------------
@@ -296,16 +324,18 @@ __global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
     constexpr int WR = TW / WW;  // output rows per wave
 
     // the split index is the slowest-varying part of the weight-tile index
-    int wtz, blk;
     const int n_wt = K / TW;
-    if (!tile_of((int)blockIdx.x, n_wt * nsplit, max_blocks, wtz, blk)) return;
-    if (blk * kPreRows >= *num_padded) return;
-    const int wt = wtz % n_wt, z = wtz / n_wt;
-    const int nlen = N / nsplit, nbeg = z * nlen;
-    const int e = block_expert[blk];
+    const int npad = *num_padded;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int wa = wave % WW, wb = wave / WW;
+    TileWalk walk(n_wt * nsplit, max_blocks);
+    int wtz, blk;
+    while (walk.next(wtz, blk)) {
+    if (blk * kPreRows >= npad) continue;
+    const int wt = wtz % n_wt, z = wtz / n_wt;
+    const int nlen = N / nsplit, nbeg = z * nlen;
+    const int e = block_expert[blk];
 
     const size_t row_bytes = (size_t)N * 2;
     const prsrc_t rw = pmake_rsrc(w2 + ((size_t)e * K + (size_t)wt * TW) * N,
@@ -349,25 +379,25 @@ __global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
             }
         }
     }
+    }  // tiles
 }
 
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
-static int grid_for(int tiles) { return (tiles + 7) / 8 * 8; }
+// One workgroup per tile, rounded up to whole XCD groups of 8.
+static int tile_grid(int tiles) { return (tiles + 7) / 8 * 8; }
 
 void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
-    const int grid = grid_for((N / 128) * max_blocks);
-    gemm1_prefill_bf16_kernel<256, 32, 3, 4, 2><<<grid, 256, 0, s>>>(
+    const int grid = tile_grid((N / 128) * max_blocks);
+    gemm1_prefill_bf16_kernel<256, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
 
-// GEMM2 has K/256 weight tiles per token block -- too few to fill the chip
-// in whole waves of workgroups -- so its reduction is split in four.
 int prefill_gemm2_splits(int K, int N) {
     (void)K;
     return (N % (4 * 32) == 0) ? 4 : 1;
@@ -378,12 +408,12 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     if (K % 256 == 0) {
-        const int grid = grid_for((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
+        const int grid = tile_grid((K / 256) * nsplit * max_blocks);
+        gemm2_prefill_bf16_kernel<256, 32, 3, 4, 2><<<grid, 256, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else {
-        const int grid = grid_for((K / 128) * nsplit * max_blocks);
+        const int grid = tile_grid((K / 128) * nsplit * max_blocks);
         gemm2_prefill_bf16_kernel<128, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);

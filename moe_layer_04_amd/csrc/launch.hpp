@@ -11,10 +11,12 @@
 
 namespace moe {
 
+// logits [M,E]; with xq/xscale non-null also the per-token e4m3 codes and
+// scales (a second kernel; K % 8 == 0)
 void launch_router_logits(const void* x, const void* wr, const float* bias, int M, int K, int E,
-                          float* logits, hipStream_t s);
+                          float* logits, uint8_t* xq, float* xscale, hipStream_t s);
 void launch_router_topk(const float* logits, int M, int E, int topk, int32_t* ids, float* w,
-                        const void* x, int K, uint8_t* xq, float* xscale, hipStream_t s);
+                        hipStream_t s);
 void launch_quant_rows(const void* x, int M, int K, uint8_t* q, float* scale, hipStream_t s);
 
 void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,

@@ -15,45 +15,47 @@
 namespace moe {
 
 // ---------------------------------------------------------------------------
-// Logits.  One wave computes a TT-token x TE-expert tile: its 64 lanes split
-// K into 8-element slices, each lane accumulates bf16*bf16 products (exact in
-// fp64) in fp64, and the tile is summed across lanes with DPP/ds_swizzle.
+// Logits.  A workgroup (4 waves) computes a TT-token x TE-expert tile; its
+// waves split K into four contiguous quarters, each lane accumulates
+// bf16*bf16 products (exact in fp64) in fp64 over 8-element slices, the
+// wave sums its lanes with DPP/ds_swizzle, and the four wave partials are
+// added in wave order through LDS (a fixed order: deterministic).  Small
+// problems use 1x1 tiles so every (token, expert) pair gets a workgroup.
 // ---------------------------------------------------------------------------
-constexpr int kTT = 4;
-constexpr int kTE = 4;
-
-template <bool VEC>
+template <int TT, int TE, bool VEC>
 __global__ __launch_bounds__(256) void router_logits_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
     const float* __restrict__ bias, int M, int K, int E, float* __restrict__ logits) {
+    __shared__ double part[4][TT * TE];
     const int lane = lane_id();
-    const int wave = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
-    const int tiles_e = (E + kTE - 1) / kTE;
-    const int t0 = (wave / tiles_e) * kTT;
-    const int e0 = (wave % tiles_e) * kTE;
-    if (t0 >= M) return;  // wave-uniform
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int tiles_e = (E + TE - 1) / TE;
+    const int t0 = ((int)blockIdx.x / tiles_e) * TT;
+    const int e0 = ((int)blockIdx.x % tiles_e) * TE;
 
-    double acc[kTT][kTE];
+    double acc[TT][TE];
 #pragma unroll
-    for (int a = 0; a < kTT; ++a)
+    for (int a = 0; a < TT; ++a)
 #pragma unroll
-        for (int b = 0; b < kTE; ++b) acc[a][b] = 0.0;
+        for (int b = 0; b < TE; ++b) acc[a][b] = 0.0;
 
     // Rows past M / E are clamped to a valid row; their sums are discarded.
-    const uint16_t* xr[kTT];
-    const uint16_t* wrr[kTE];
+    const uint16_t* xr[TT];
+    const uint16_t* wrr[TE];
 #pragma unroll
-    for (int a = 0; a < kTT; ++a) xr[a] = x + (size_t)min(t0 + a, M - 1) * K;
+    for (int a = 0; a < TT; ++a) xr[a] = x + (size_t)min(t0 + a, M - 1) * K;
 #pragma unroll
-    for (int b = 0; b < kTE; ++b) wrr[b] = wr + (size_t)min(e0 + b, E - 1) * K;
+    for (int b = 0; b < TE; ++b) wrr[b] = wr + (size_t)min(e0 + b, E - 1) * K;
 
     if constexpr (VEC) {
-        // K % 8 == 0: 16-byte loads, lane owns elements [k, k+8) of each row.
-        for (int k = lane * 8; k < K; k += kWave * 8) {
-            double xv[kTT][8], wv[kTE][8];
+        // K % 8 == 0: wave w covers [kb, ke) in 16-byte slices, lane-strided
+        const int kq = ((K / 8 + 3) / 4) * 8;
+        const int kb = wave * kq, ke = min(K, kb + kq);
+        for (int k = kb + lane * 8; k < ke; k += kWave * 8) {
+            double xv[TT][8], wv[TE][8];
 #pragma unroll
-            for (int a = 0; a < kTT; ++a) {
-                i32x4_t v = *reinterpret_cast<const i32x4_t*>(xr[a] + k);
+            for (int a = 0; a < TT; ++a) {
+                const i32x4_t v = *reinterpret_cast<const i32x4_t*>(xr[a] + k);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     xv[a][2 * q] = (double)bf16_bits_to_f32((uint32_t)v[q] & 0xffffu);
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
                 }
             }
 #pragma unroll
-            for (int b = 0; b < kTE; ++b) {
-                i32x4_t v = *reinterpret_cast<const i32x4_t*>(wrr[b] + k);
+            for (int b = 0; b < TE; ++b) {
+                const i32x4_t v = *reinterpret_cast<const i32x4_t*>(wrr[b] + k);
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     wv[b][2 * q] = (double)bf16_bits_to_f32((uint32_t)v[q] & 0xffffu);
@@ -70,42 +72,91 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
                 }
             }
 #pragma unroll
-            for (int a = 0; a < kTT; ++a)
+            for (int a = 0; a < TT; ++a)
 #pragma unroll
-                for (int b = 0; b < kTE; ++b)
+                for (int b = 0; b < TE; ++b)
 #pragma unroll
                     for (int q = 0; q < 8; ++q) acc[a][b] = __fma_rn(xv[a][q], wv[b][q], acc[a][b]);
         }
     } else {
-        for (int k = lane; k < K; k += kWave) {
-            double xv[kTT], wv[kTE];
+        const int kq = (K + 3) / 4;
+        const int kb = wave * kq, ke = min(K, kb + kq);
+        for (int k = kb + lane; k < ke; k += kWave) {
+            double xv[TT], wv[TE];
 #pragma unroll
-            for (int a = 0; a < kTT; ++a) xv[a] = (double)bf16_bits_to_f32(xr[a][k]);
+            for (int a = 0; a < TT; ++a) xv[a] = (double)bf16_bits_to_f32(xr[a][k]);
 #pragma unroll
-            for (int b = 0; b < kTE; ++b) wv[b] = (double)bf16_bits_to_f32(wrr[b][k]);
+            for (int b = 0; b < TE; ++b) wv[b] = (double)bf16_bits_to_f32(wrr[b][k]);
 #pragma unroll
-            for (int a = 0; a < kTT; ++a)
+            for (int a = 0; a < TT; ++a)
 #pragma unroll
-                for (int b = 0; b < kTE; ++b) acc[a][b] = __fma_rn(xv[a], wv[b], acc[a][b]);
+                for (int b = 0; b < TE; ++b) acc[a][b] = __fma_rn(xv[a], wv[b], acc[a][b]);
         }
     }
 
 #pragma unroll
-    for (int a = 0; a < kTT; ++a)
+    for (int a = 0; a < TT; ++a)
 #pragma unroll
-        for (int b = 0; b < kTE; ++b) {
-            double s = wave_sum_f64(acc[a][b]);
-            const int t = t0 + a, e = e0 + b;
-            if (lane == 0 && t < M && e < E) {
-                if (bias) s += (double)bias[e];
-                logits[(size_t)t * E + e] = (float)s;
-            }
+        for (int b = 0; b < TE; ++b) {
+            const double s = wave_sum_f64(acc[a][b]);
+            if (lane == 0) part[wave][a * TE + b] = s;
         }
+    __syncthreads();
+    const int tid = (int)threadIdx.x;
+    if (tid < TT * TE) {
+        const int t = t0 + tid / TE, e = e0 + tid % TE;
+        if (t < M && e < E) {
+            double s = ((part[0][tid] + part[1][tid]) + part[2][tid]) + part[3][tid];
+            if (bias) s += (double)bias[e];
+            logits[(size_t)t * E + e] = (float)s;
+        }
+    }
+
+}
+
+// Per-token dynamic e4m3 quantisation for the fused FP8 path: one workgroup
+// per token row, 16-byte loads (K % 8 == 0), s = amax/448 (1 if amax == 0),
+// code = E4M3(x/s) with one correctly rounded fp32 division.
+__global__ __launch_bounds__(256) void quant_rows_vec_kernel(const uint16_t* __restrict__ x,
+                                                             int M, int K,
+                                                             uint8_t* __restrict__ q,
+                                                             float* __restrict__ scale) {
+    __shared__ uint32_t wmax[4];
+    const int t = (int)blockIdx.x;
+    const int tid = (int)threadIdx.x, lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const uint16_t* row = x + (size_t)t * K;
+    uint32_t amax = 0;
+    for (int k = tid * 8; k < K; k += 256 * 8) {
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(row + k);
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            amax = max(amax, max((uint32_t)v[u] & 0x7fffu, ((uint32_t)v[u] >> 16) & 0x7fffu));
+    }
+    amax = wave_max_bits(amax << 16);
+    if (lane == 0) wmax[wave] = amax;
+    __syncthreads();
+    amax = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    const float am = __uint_as_float(amax);
+    const float sc = (am == 0.0f) ? 1.0f : am / 448.0f;
+    uint8_t* dst = q + (size_t)t * K;
+    for (int k = tid * 8; k < K; k += 256 * 8) {
+        const i32x4_t v = *reinterpret_cast<const i32x4_t*>(row + k);
+        uint32_t lo = 0, hi = 0;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            lo |= f32_to_e4m3(bf16_bits_to_f32((uint32_t)v[u] & 0xffffu) / sc) << (16 * u);
+            lo |= f32_to_e4m3(bf16_bits_to_f32((uint32_t)v[u] >> 16) / sc) << (16 * u + 8);
+            hi |= f32_to_e4m3(bf16_bits_to_f32((uint32_t)v[u + 2] & 0xffffu) / sc) << (16 * u);
+            hi |= f32_to_e4m3(bf16_bits_to_f32((uint32_t)v[u + 2] >> 16) / sc) << (16 * u + 8);
+        }
+        *reinterpret_cast<uint2*>(dst + k) = make_uint2(lo, hi);
+    }
+    if (tid == 0) scale[t] = sc;
 }
 
 // ---------------------------------------------------------------------------
-// Top-k + weights (+ optional per-token e4m3 quantisation of x).  One wave per
-// token.  Lane l holds logits of experts l, l+64, l+128, l+192.  A 64-bit key
+// Top-k + weights.  One wave per token.  Lane l holds logits of experts l, l+64, l+128, l+192.  A 64-bit key
 // orders (logit, -expert): the high word maps the float to an unsigned with
 // the same order, the low word is ~expert, so the wave max (DPP/ds_swizzle)
 // is the largest logit with ties to the lower id.
@@ -117,9 +168,7 @@ __device__ __forceinline__ uint32_t ordered_bits(float f) {
 
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ logits, int M, int E, int topk,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
-    const uint16_t* __restrict__ x, int K, uint8_t* __restrict__ xq,
-    float* __restrict__ xscale) {
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
     const int lane = lane_id();
     const int t = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
     if (t >= M) return;  // wave-uniform
@@ -170,18 +219,6 @@ __global__ __launch_bounds__(256) void router_topk_kernel(
         topk_weights[(size_t)t * topk + lane] = mine / den;
     }
 
-    if (xq) {
-        // per-token dynamic e4m3: s = amax/448 (1 if amax == 0), code = E4M3(x/s)
-        const uint16_t* xr = x + (size_t)t * K;
-        uint32_t amax = 0;
-        for (int k = lane; k < K; k += kWave) amax = max(amax, (uint32_t)xr[k] & 0x7fffu);
-        amax = wave_max_bits(amax << 16);
-        const float a = __uint_as_float(amax);
-        const float s = (a == 0.0f) ? 1.0f : a / 448.0f;
-        for (int k = lane; k < K; k += kWave)
-            xq[(size_t)t * K + k] = (uint8_t)f32_to_e4m3(bf16_bits_to_f32(xr[k]) / s);
-        if (lane == 0) xscale[t] = s;
-    }
 }
 
 // ---------------------------------------------------------------------------
@@ -208,27 +245,38 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 // host launchers
 // ---------------------------------------------------------------------------
 void launch_router_logits(const void* x, const void* wr, const float* bias, int M, int K, int E,
-                          float* logits, hipStream_t s) {
-    const long tiles = (long)((M + kTT - 1) / kTT) * ((E + kTE - 1) / kTE);
-    const int grid = (int)((tiles + 3) / 4);
-    if (K % 8 == 0)
-        router_logits_kernel<true><<<grid, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)wr,
-                                                         bias, M, K, E, logits);
-    else
-        router_logits_kernel<false><<<grid, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)wr,
-                                                          bias, M, K, E, logits);
+                          float* logits, uint8_t* xq, float* xscale, hipStream_t s) {
+    const uint16_t* xp = (const uint16_t*)x;
+    const uint16_t* wp = (const uint16_t*)wr;
+    if ((long)M * E <= 8192) {
+        const int grid = M * E;
+        if (K % 8 == 0)
+            router_logits_kernel<1, 1, true><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
+        else
+            router_logits_kernel<1, 1, false><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
+    } else {
+        const int grid = ((M + 3) / 4) * ((E + 3) / 4);
+        if (K % 8 == 0)
+            router_logits_kernel<4, 4, true><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
+        else
+            router_logits_kernel<4, 4, false><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
+    }
+    if (xq) quant_rows_vec_kernel<<<M, 256, 0, s>>>(xp, M, K, xq, xscale);
 }
 
 void launch_router_topk(const float* logits, int M, int E, int topk, int32_t* ids, float* w,
-                        const void* x, int K, uint8_t* xq, float* xscale, hipStream_t s) {
+                        hipStream_t s) {
     const int grid = (M + 3) / 4;
-    router_topk_kernel<<<grid, 256, 0, s>>>(logits, M, E, topk, ids, w, (const uint16_t*)x, K,
-                                            xq, xscale);
+    router_topk_kernel<<<grid, 256, 0, s>>>(logits, M, E, topk, ids, w);
 }
 
 void launch_quant_rows(const void* x, int M, int K, uint8_t* q, float* scale, hipStream_t s) {
-    const int grid = (M + 3) / 4;
-    quant_rows_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, M, K, q, scale);
+    if (K % 8 == 0) {
+        quant_rows_vec_kernel<<<M, 256, 0, s>>>((const uint16_t*)x, M, K, q, scale);
+    } else {
+        const int grid = (M + 3) / 4;
+        quant_rows_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, M, K, q, scale);
+    }
 }
 
 }  // namespace moe
