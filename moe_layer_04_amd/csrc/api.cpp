@@ -20,8 +20,8 @@
 
 namespace {
 
-constexpr int kDecodeBlock = 16;
-constexpr int kPrefillBlock = 128;
+constexpr int kDecodeBlock = moe::kDecodeRows;
+constexpr int kPrefillBlock = moe::kPrefillRows;
 constexpr size_t kAlign = 256;
 
 bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }

@@ -37,7 +37,7 @@
 
 namespace moe {
 
-constexpr int kDecRows = 16;            // token rows per block (the align block size)
+constexpr int kDecRows = kDecodeRows;   // token rows per block (the align block size)
 constexpr uint32_t kOob = 0x80000000u;  // offset past every resource: loads return 0
 constexpr int kRot = 7;                 // K-step rotation per wave
 

@@ -4,14 +4,16 @@
 // The fused MoE of "Mixture-of-Experts kernel engineering on Amazon
 // SageMaker AI" (summary text) groups all active experts into one launch;
 // with hundreds of token rows per expert the GEMMs are MFMA-bound, so each
-// workgroup computes a full TW (weight rows) x 128 (token rows) tile from
-// LDS with 32x32x16 bf16 MFMAs.  Weights stay in the pages' B^T layout
+// workgroup computes a full TW (weight rows) x TT (token rows) tile from
+// LDS with 32x32x16 bf16 MFMAs; the launchers use 256 x 256 tiles (each
+// token block re-reads its expert's weights, so the token tile sets the
+// weight traffic).  Weights stay in the pages' B^T layout
 // (output-major, reduction dimension contiguous) on the MFMA row dimension,
 // as in the decode kernels; tokens are the columns, gathered through the
 // expert-sorted row list for GEMM1 and contiguous for GEMM2.
 //
-// Waves: 4 per workgroup, WW along the weight rows and 4/WW along the token
-// columns.  In GEMM1 the workgroup's weight rows are TW/2 gate rows followed
+// Waves: NW per workgroup, WW along the weight rows and NW/WW along the
+// token columns.  In GEMM1 the workgroup's weight rows are TW/2 gate rows followed
 // by the matching TW/2 up rows and each wave takes the same n-range from
 // both halves, so SiLU(gate)*up is formed from its own accumulators.
 //
@@ -42,7 +44,6 @@
 
 namespace moe {
 
-constexpr int kPreRows = 128;  // token rows per block (the align block size)
 constexpr int kGroup = 8;
 
 typedef __amdgpu_buffer_rsrc_t prsrc_t;
@@ -117,26 +118,28 @@ __device__ __forceinline__ void wait_vmcnt() {
 // at the top of step s leaves only the younger, already-issued steps in
 // flight.  The barrier then publishes step s to the workgroup and proves
 // that every wave has finished reading the slot the next DMA overwrites.
-template <int TW, int BK, int STAGES, int WW>
+template <int TW, int TT, int BK, int STAGES, int WW, int NW>
 struct PrefillCore {
     static constexpr int kRowBytes = BK * 2;
-    static constexpr int kCPR = BK / 8;                    // 16-B chunks per row
-    static constexpr int kRowsPerInstr = 64 / kCPR;        // rows one wave instruction covers
-    static constexpr int kWInstr = TW / kRowsPerInstr / 4; // per wave per step
-    static constexpr int kXInstr = kPreRows / kRowsPerInstr / 4;
-    static constexpr int kSlotBytes = (TW + kPreRows) * kRowBytes;
+    static constexpr int kCPR = BK / 8;                     // 16-B chunks per row
+    static constexpr int kRowsPerInstr = 64 / kCPR;         // rows one wave instruction covers
+    static constexpr int kWInstr = TW / kRowsPerInstr / NW; // per wave per step
+    static constexpr int kXInstr = TT / kRowsPerInstr / NW;
+    static constexpr int kSlotBytes = (TW + TT) * kRowBytes;
     static constexpr int kLdsBytes = STAGES * kSlotBytes;
     static constexpr int kPerStep = kWInstr + kXInstr;
-    static constexpr int WT = 4 / WW;                      // waves along the token dimension
-    static constexpr int FW = TW / WW / 32;                // 32-row A tiles per wave
-    static constexpr int FT = kPreRows / WT / 32;          // 32-column B tiles per wave
+    static constexpr int WT = NW / WW;                      // waves along the token dimension
+    static constexpr int FW = TW / WW / 32;                 // 32-row A tiles per wave
+    static constexpr int FT = TT / WT / 32;                 // 32-column B tiles per wave
+    static_assert(kWInstr * kRowsPerInstr * NW == TW && kXInstr * kRowsPerInstr * NW == TT,
+                  "tile rows must split evenly over the waves' DMA instructions");
 
     f32x16_t acc[FW][FT];
 
     // Row (within the slot's weight / token region) that lane `lane` of DMA
     // instruction q of wave `wave` fills, and the logical chunk it fetches.
     __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
-        return (q * 4 + wave) * kRowsPerInstr + lane / kCPR;
+        return (q * NW + wave) * kRowsPerInstr + lane / kCPR;
     }
     __device__ static __forceinline__ int dma_chunk(int row, int lane) {
         return (lane % kCPR) ^ swz<BK>(row);
@@ -161,14 +164,14 @@ struct PrefillCore {
 #pragma unroll
             for (int q = 0; q < kWInstr; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rw, (__attribute__((address_space(3))) void*)(base + (q * 4 + wave) * 1024),
+                    rw, (__attribute__((address_space(3))) void*)(base + (q * NW + wave) * 1024),
                     16, woff[q] + kb, 0, 0, 0);
 #pragma unroll
             for (int q = 0; q < kXInstr; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rx,
                     (__attribute__((address_space(3))) void*)(base + TW * kRowBytes +
-                                                              (q * 4 + wave) * 1024),
+                                                              (q * NW + wave) * 1024),
                     16, xoff[q] + kb, 0, 0, 0);
         };
 
@@ -185,7 +188,7 @@ struct PrefillCore {
             }
 #pragma unroll
             for (int b = 0; b < FT; ++b) {
-                const int r = wb * (kPreRows / WT) + b * 32 + li;
+                const int r = wb * (TT / WT) + b * 32 + li;
                 boff[ks][b] = (TW + r) * kRowBytes + ((c ^ swz<BK>(r)) << 4);
             }
         }
@@ -239,13 +242,13 @@ struct PrefillCore {
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
-template <int TW, int BK, int STAGES, int WW, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
+template <int TW, int TT, int BK, int STAGES, int WW, int NW, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     int max_blocks, uint16_t* __restrict__ act) {
-    using Core = PrefillCore<TW, BK, STAGES, WW>;
+    using Core = PrefillCore<TW, TT, BK, STAGES, WW, NW>;
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int HW = TW / 2;  // n-values per tile
     constexpr int WN = HW / WW; // n-values per wave
@@ -257,7 +260,7 @@ __global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
     TileWalk walk(N / HW, max_blocks);
     int wt, blk;
     while (walk.next(wt, blk)) {
-    if (blk * kPreRows >= npad) continue;
+    if (blk * TT >= npad) continue;
     const int e = block_expert[blk];
 
     const size_t row_bytes = (size_t)K * 2;
@@ -273,7 +276,7 @@ __global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
-        const int p = sorted_ids[blk * kPreRows + row];
+        const int p = sorted_ids[blk * TT + row];
         const int t = p < nslots ? p / topk : 0;
         xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
@@ -290,7 +293,7 @@ __global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
     const int li = lane & 31;
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
-        const int r = blk * kPreRows + wb * (kPreRows / Core::WT) + b * 32 + li;
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
         if (sorted_ids[r] >= nslots) continue;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
@@ -313,13 +316,13 @@ __global__ __launch_bounds__(256, OCC) void gemm1_prefill_bf16_kernel(
 // GEMM2 (bf16): weight tile wt covers output rows wt*TW..+TW; the epilogue
 // multiplies by the routing weight and scatters token row r to slot p.
 // ---------------------------------------------------------------------------
-template <int TW, int BK, int STAGES, int WW, int OCC>
-__global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
+template <int TW, int TT, int BK, int STAGES, int WW, int NW, int OCC>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
-    using Core = PrefillCore<TW, BK, STAGES, WW>;
+    using Core = PrefillCore<TW, TT, BK, STAGES, WW, NW>;
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int WR = TW / WW;  // output rows per wave
 
@@ -332,7 +335,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
     TileWalk walk(n_wt * nsplit, max_blocks);
     int wtz, blk;
     while (walk.next(wtz, blk)) {
-    if (blk * kPreRows >= npad) continue;
+    if (blk * TT >= npad) continue;
     const int wt = wtz % n_wt, z = wtz / n_wt;
     const int nlen = N / nsplit, nbeg = z * nlen;
     const int e = block_expert[blk];
@@ -350,7 +353,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
-        aoff[q] = (uint32_t)((blk * kPreRows + row) * row_bytes) + nbeg * 2 +
+        aoff[q] = (uint32_t)((blk * TT + row) * row_bytes) + nbeg * 2 +
                   Core::dma_chunk(row, lane) * 16;
     }
     int arow[Core::FW];
@@ -362,7 +365,7 @@ __global__ __launch_bounds__(256, OCC) void gemm2_prefill_bf16_kernel(
     const int li = lane & 31;
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
-        const int r = blk * kPreRows + wb * (kPreRows / Core::WT) + b * 32 + li;
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
         const int p = sorted_ids[r];
         if (p >= nslots) continue;
         const float w = topk_w[p];
@@ -393,7 +396,7 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_bf16_kernel<256, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
+    gemm1_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
@@ -409,12 +412,12 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
                                int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     if (K % 256 == 0) {
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, 32, 3, 4, 2><<<grid, 256, 0, s>>>(
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else {
         const int grid = tile_grid((K / 128) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<128, 32, 3, 2, 2><<<grid, 256, 0, s>>>(
+        gemm2_prefill_bf16_kernel<128, kPrefillRows, 32, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     }

@@ -10,6 +10,13 @@
 #define MOE_KERNEL_MAX_TOPK 16
 
 namespace moe {
+// token rows per block of the sorted list (the align block size) for the
+// Swap-AB decode kernels and for the full-tile kernels
+constexpr int kDecodeRows = 16;
+constexpr int kPrefillRows = 256;
+}
+
+namespace moe {
 
 // logits [M,E]; with xq/xscale non-null also the per-token e4m3 codes and
 // scales (a second kernel; K % 8 == 0)
