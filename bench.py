@@ -51,6 +51,7 @@ def hip_runtime():
     return hip
 
 
+CPU_SECONDS = 10.0  # oracle work timed for the CPU baseline
 COPY_BYTES = 1 << 30
 
 
@@ -69,9 +70,32 @@ def _pmc_rows(path, counter):
     return out
 
 
-def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
-    """Per-dispatch HBM traffic of the GEMM1 kernel from counter CSVs, each
-    counter scaled by what it reads for the plain copy of COPY_BYTES."""
+def _request_bytes(path):
+    """Bytes the L2 read from memory per dispatch, per kernel, resolved by
+    request size: TCC_EA0_RDREQ counts every read request, the _32B / _64B /
+    _128B counters the requests of each size (the rest are 64-byte)."""
+    import statistics
+    c = {n: _pmc_rows(path, n) for n in ("TCC_EA0_RDREQ_sum", "TCC_EA0_RDREQ_32B_sum",
+                                         "TCC_EA0_RDREQ_64B_sum", "TCC_EA0_RDREQ_128B_sum")}
+    out = {}
+    for k in c["TCC_EA0_RDREQ_sum"]:
+        n = {name: statistics.median(v[k]) for name, v in c.items()}
+        n32, n64 = n["TCC_EA0_RDREQ_32B_sum"], n["TCC_EA0_RDREQ_64B_sum"]
+        n128 = n["TCC_EA0_RDREQ_128B_sum"]
+        rest = n["TCC_EA0_RDREQ_sum"] - n32 - n64 - n128
+        out[k] = 32 * n32 + 64 * (n64 + rest) + 128 * n128
+    return out
+
+
+def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
+                req_csv=None, copy_req_csv=None):
+    """Per-dispatch HBM traffic of the GEMM1 kernel from counter CSVs.
+
+    Each counter is scaled by what it reads for the plain copy of COPY_BYTES.
+    FETCH_SIZE counts a 128-byte read request as 64 bytes on this GPU, so its
+    copy factor only holds for kernels whose request mix matches the copy's;
+    with the request-size runs (REQ_CSV, COPY_REQ_CSV) the kernel's fetch is
+    the request-resolved byte count, checked on the copy against COPY_BYTES."""
     import statistics
     cf = _pmc_rows(copy_fetch_csv, "FETCH_SIZE")
     cw = _pmc_rows(copy_write_csv, "WRITE_SIZE")
@@ -83,12 +107,19 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv):
     kf = _pmc_rows(fetch_csv, "FETCH_SIZE")
     kw = _pmc_rows(write_csv, "WRITE_SIZE")
     name = next(k for k in kf if "gemm1" in k)
-    fetch = statistics.median(kf[name]) * 1024 * f_scale
+    fetch_counter = statistics.median(kf[name]) * 1024
+    fetch = fetch_counter * f_scale
     write = statistics.median(kw[name]) * 1024 * w_scale
-    rec = {"kernel": name, "workload": workload, "fetch_bytes_per_launch": fetch,
-           "write_bytes_per_launch": write, "bytes_per_launch": fetch + write,
-           "fetch_scale": f_scale, "write_scale": w_scale,
-           "dispatches": len(kf[name]), "source_digest": kernel_digest()}
+    rec = {"kernel": name, "workload": workload, "fetch_size_bytes": fetch_counter,
+           "fetch_scale_copy": f_scale, "write_scale": w_scale,
+           "dispatches": len(kf[name])}
+    if req_csv and copy_req_csv:
+        copy_req = max(_request_bytes(copy_req_csv).values())
+        rec["copy_request_bytes_over_known"] = copy_req / COPY_BYTES
+        fetch = _request_bytes(req_csv)[name]
+        rec["fetch_scale_kernel"] = fetch / fetch_counter
+    rec.update({"fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
+                "bytes_per_launch": fetch + write, "source_digest": kernel_digest()})
     path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_pmc.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
@@ -118,16 +149,19 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
-    ap.add_argument("--pmc-summary", nargs=4, metavar=("FETCH_CSV", "WRITE_CSV",
-                                                        "COPY_FETCH_CSV", "COPY_WRITE_CSV"),
-                    help="turn rocprofv3 --pmc counter CSVs of this workload and of the "
-                         "copy calibration into profiles/gemm1_<workload>_pmc.json and exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                    help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [REQ_CSV COPY_REQ_CSV]: "
+                         "turn rocprofv3 --pmc counter CSVs of this workload and of the copy "
+                         "calibration (FETCH_SIZE, WRITE_SIZE, and optionally the TCC_EA0_RDREQ "
+                         "request-size counters) into profiles/gemm1_<workload>_pmc.json and exit")
     args = ap.parse_args()
     if args.pmc_summary:
+        if len(args.pmc_summary) not in (4, 6):
+            ap.error("--pmc-summary takes 4 or 6 CSV paths")
         pmc_summary(args.workload, *args.pmc_summary)
         return
     if args.gpus != 1:
-        print(json.dumps({"error": "this build measures one GPU; --gpus must be 1",
+        print(json.dumps({"error": "the benchmark runs on one GPU; --gpus must be 1",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
@@ -307,18 +341,24 @@ def main():
         s1 = None if g["w1_scale"] is None else g["w1_scale"].cpu().numpy()
         s2 = None if g["w2_scale"] is None else g["w2_scale"].cpu().numpy()
         log(f"oracle on {n_tok} token(s), {len(need_e)} expert(s)")
+        # the sample is evaluated repeatedly until about CPU_SECONDS of work
+        reps = 0
         t0 = time.perf_counter()
-        ref, _, _ = oracle.moe_forward(x_h, wr_h, bias_h, w1h, w2h, wl.topk, w1_scale=s1,
-                                       w2_scale=s2, tokens=toks, fp8=wl.fp8)
+        while True:
+            ref, _, _ = oracle.moe_forward(x_h, wr_h, bias_h, w1h, w2h, wl.topk, w1_scale=s1,
+                                           w2_scale=s2, tokens=toks, fp8=wl.fp8)
+            reps += 1
+            if time.perf_counter() - t0 >= CPU_SECONDS:
+                break
         cpu_s = time.perf_counter() - t0
         got = out.float().cpu().numpy()[toks].astype(np.float64)
         den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
         err = float((np.abs(got - ref).max(axis=1) / den).max())
         result["cpu_baseline"] = {
-            "value": round(n_tok / cpu_s, 3), "unit": "tokens/s",
+            "value": round(n_tok * reps / cpu_s, 3), "unit": "tokens/s",
             "cores": min(oracle.num_threads(), n_tok * wl.topk), "kind": "oracle",
             "sample": f"first {n_tok} of the {wl.M} tokens of the same batch "
-                      f"({n_tok * wl.topk} token-slots, fp64)",
+                      f"({n_tok * wl.topk} token-slots, fp64), evaluated {reps} times",
             "seconds": round(cpu_s, 3)}
         result["parity_vs_oracle"] = {"max_row_rel_err": err, "tokens": n_tok,
                                       "tol": 6e-2 if wl.fp8 else 2e-2}

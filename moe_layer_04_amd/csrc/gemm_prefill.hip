@@ -42,6 +42,8 @@
 #include "common.hpp"
 #include "launch.hpp"
 
+#include <type_traits>
+
 namespace moe {
 
 constexpr int kGroup = 8;
@@ -93,13 +95,13 @@ struct TileWalk {
     }
 };
 
-// LDS layout of one ring slot: TW weight rows then 128 token rows, each row
-// BK bf16 (BK*2 bytes) without padding, its 16-byte chunks permuted by an
-// XOR of the row index (swz) so that the 16 consecutive rows an MFMA operand
-// read touches in one LDS cycle land in distinct banks.  The DMA writes 1 KB
-// per wave instruction in lane order, so lane l of an instruction covering
-// rows r0.. stores physical chunk (l % CPR) of row r0 + l / CPR and therefore
-// fetches logical chunk (l % CPR) ^ swz(row) from global memory.
+// LDS rows: each operand row of a K-step is BK bf16 (BK*2 bytes) without
+// padding, its 16-byte chunks permuted by an XOR of the row index (swz) so
+// that the 16 consecutive rows an MFMA operand read touches in one LDS cycle
+// land in distinct banks.  The DMA writes 1 KB per wave instruction in lane
+// order, so lane l of an instruction covering rows r0.. stores physical
+// chunk (l % CPR) of row r0 + l / CPR and therefore fetches logical chunk
+// (l % CPR) ^ swz(row) from global memory.
 template <int BK>
 __device__ __forceinline__ int swz(int r) {
     if constexpr (BK == 32) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
@@ -113,30 +115,46 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// The shared main loop: DMA ring of STAGES slots, one raw barrier per step.
-// Every thread issues kWInstr + kXInstr DMA instructions per step; the wait
-// at the top of step s leaves only the younger, already-issued steps in
-// flight.  The barrier then publishes step s to the workgroup and proves
-// that every wave has finished reading the slot the next DMA overwrites.
-template <int TW, int TT, int BK, int STAGES, int WW, int NW>
+// The shared main loop.  The weight rows and the token rows of each K-step
+// stream through two LDS rings, of WST and XST slots: the weight copy of a
+// step is issued WST-1 steps ahead, the token copy XST-1 steps ahead (the
+// token panel is shared by more co-resident workgroups and mostly hits in
+// L2, so it gets the shorter lead when LDS runs out).  At step s every wave
+// issues the token copy of step s+XST-1 and the weight copy of step s+WST-1
+// into the slots step s-1 used; before the last MFMAs of step s it waits
+// (vmcnt) for its own copies of step s+1, meets the workgroup at one raw
+// s_barrier (the __syncthreads fence would wait for every copy in flight),
+// and reads the first fragments of step s+1, so those MFMAs cover the
+// barrier and the LDS latency.  The barrier also proves that every wave is
+// done reading step s, whose slots the copies issued at step s+1 overwrite.
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW>
 struct PrefillCore {
     static constexpr int kRowBytes = BK * 2;
     static constexpr int kCPR = BK / 8;                     // 16-B chunks per row
     static constexpr int kRowsPerInstr = 64 / kCPR;         // rows one wave instruction covers
     static constexpr int kWInstr = TW / kRowsPerInstr / NW; // per wave per step
     static constexpr int kXInstr = TT / kRowsPerInstr / NW;
-    static constexpr int kSlotBytes = (TW + TT) * kRowBytes;
-    static constexpr int kLdsBytes = STAGES * kSlotBytes;
-    static constexpr int kPerStep = kWInstr + kXInstr;
+    static constexpr int kWSlot = TW * kRowBytes;
+    static constexpr int kXSlot = TT * kRowBytes;
+    static constexpr int kXBase = WST * kWSlot;
+    static constexpr int kLdsBytes = WST * kWSlot + XST * kXSlot;
     static constexpr int WT = NW / WW;                      // waves along the token dimension
     static constexpr int FW = TW / WW / 32;                 // 32-row A tiles per wave
     static constexpr int FT = TT / WT / 32;                 // 32-column B tiles per wave
+    static constexpr int KS = BK / 16;                      // MFMA k-slices per step
     static_assert(kWInstr * kRowsPerInstr * NW == TW && kXInstr * kRowsPerInstr * NW == TT,
                   "tile rows must split evenly over the waves' DMA instructions");
+    static_assert(XST >= 2 && (WST == XST || WST == XST + 1),
+                  "weights lead the tokens by at most one step");
+    static_assert(KS % 2 == 0, "fragment double buffer alternates per k-slice");
+    // Copies a wave may leave in flight when step s must have landed, given
+    // that every younger copy was issued (issue order per step: tokens, then
+    // weights).
+    static constexpr int kYounger = (XST - 2) * (kWInstr + kXInstr) + (WST - XST) * kWInstr;
 
     f32x16_t acc[FW][FT];
 
-    // Row (within the slot's weight / token region) that lane `lane` of DMA
+    // Row (within the weight / token rows of a step) that lane `lane` of DMA
     // instruction q of wave `wave` fills, and the logical chunk it fetches.
     __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
         return (q * NW + wave) * kRowsPerInstr + lane / kCPR;
@@ -158,28 +176,29 @@ struct PrefillCore {
 #pragma unroll
                 for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
 
-        auto dma = [&](int step, int slot) {
+        typedef __attribute__((address_space(3))) void* lds_ptr_t;
+        auto dma_w = [&](int step, int slot) {
             const uint32_t kb = (uint32_t)step * kRowBytes;
-            char* base = lds + slot * kSlotBytes;
+            char* base = lds + slot * kWSlot;
 #pragma unroll
             for (int q = 0; q < kWInstr; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rw, (__attribute__((address_space(3))) void*)(base + (q * NW + wave) * 1024),
-                    16, woff[q] + kb, 0, 0, 0);
+                    rw, (lds_ptr_t)(base + (q * NW + wave) * 1024), 16, woff[q] + kb, 0, 0, 0);
+        };
+        auto dma_x = [&](int step, int slot) {
+            const uint32_t kb = (uint32_t)step * kRowBytes;
+            char* base = lds + kXBase + slot * kXSlot;
 #pragma unroll
             for (int q = 0; q < kXInstr; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rx,
-                    (__attribute__((address_space(3))) void*)(base + TW * kRowBytes +
-                                                              (q * NW + wave) * 1024),
-                    16, xoff[q] + kb, 0, 0, 0);
+                    rx, (lds_ptr_t)(base + (q * NW + wave) * 1024), 16, xoff[q] + kb, 0, 0, 0);
         };
 
-        // per-lane LDS read offsets (bytes within a slot) for each k16 step
+        // per-lane LDS read offsets (bytes within a slot) for each k16 slice
         const int li = lane & 31, half = lane >> 5;
-        int aoff[BK / 16][FW], boff[BK / 16][FT];
+        int aoff[KS][FW], boff[KS][FT];
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
+        for (int ks = 0; ks < KS; ++ks) {
             const int c = 2 * ks + half;
 #pragma unroll
             for (int a = 0; a < FW; ++a) {
@@ -189,48 +208,81 @@ struct PrefillCore {
 #pragma unroll
             for (int b = 0; b < FT; ++b) {
                 const int r = wb * (TT / WT) + b * 32 + li;
-                boff[ks][b] = (TW + r) * kRowBytes + ((c ^ swz<BK>(r)) << 4);
+                boff[ks][b] = r * kRowBytes + ((c ^ swz<BK>(r)) << 4);
             }
         }
-        auto compute = [&](int slot) {
-            const char* base = lds + slot * kSlotBytes;
+        struct Frags { bf16x8_t a[FW], b[FT]; };
+        auto read = [&](Frags& f, int wslot, int xslot, int ks) {
+            const char* wbase = lds + wslot * kWSlot;
+            const char* xbase = lds + kXBase + xslot * kXSlot;
 #pragma unroll
-            for (int ks = 0; ks < BK / 16; ++ks) {
-                bf16x8_t av[FW], bv[FT];
+            for (int a = 0; a < FW; ++a)
+                f.a[a] = *reinterpret_cast<const bf16x8_t*>(wbase + aoff[ks][a]);
 #pragma unroll
-                for (int a = 0; a < FW; ++a)
-                    av[a] = *reinterpret_cast<const bf16x8_t*>(base + aoff[ks][a]);
+            for (int b = 0; b < FT; ++b)
+                f.b[b] = *reinterpret_cast<const bf16x8_t*>(xbase + boff[ks][b]);
+        };
+        auto mfmas = [&](const Frags& f) {
 #pragma unroll
-                for (int b = 0; b < FT; ++b)
-                    bv[b] = *reinterpret_cast<const bf16x8_t*>(base + boff[ks][b]);
+            for (int a = 0; a < FW; ++a)
 #pragma unroll
-                for (int a = 0; a < FW; ++a)
-#pragma unroll
-                    for (int b = 0; b < FT; ++b) acc[a][b] = mfma32_bf16(av[a], bv[b], acc[a][b]);
-            }
+                for (int b = 0; b < FT; ++b) acc[a][b] = mfma32_bf16(f.a[a], f.b[b], acc[a][b]);
         };
 
         const int steps = klen / BK;
-        // the previous tile's last reads of the ring are done before refilling it
+        // the previous tile's last reads of the rings are done before refilling them
         __builtin_amdgcn_s_barrier();
+        // prologue: the copies steps -WST+1 .. -1 would have issued
 #pragma unroll
-        for (int s = 0; s < STAGES - 1; ++s)
-            if (s < steps) dma(s, s);
-        int slot = 0;
-        for (int s = 0; s < steps; ++s) {
-            // step s has landed once at most the (STAGES-2) younger steps are
-            // outstanding; near the end fewer were issued
-            if (s + STAGES - 2 < steps) wait_vmcnt<(STAGES - 2) * kPerStep>();
-            else wait_vmcnt<0>();
-            __builtin_amdgcn_s_barrier();
-            if (s + STAGES - 1 < steps) {
-                int nslot = slot + STAGES - 1;
-                if (nslot >= STAGES) nslot -= STAGES;
-                dma(s + STAGES - 1, nslot);
-            }
-            compute(slot);
-            if (++slot == STAGES) slot = 0;
+        for (int v = 1 - WST; v < 0; ++v) {
+            const int xs = v + XST - 1, ws = v + WST - 1;
+            if (xs >= 0 && xs < steps) dma_x(xs, xs);
+            if (ws >= 0 && ws < steps) dma_w(ws, ws);
         }
+        // wait for step s (issued through step s-1): vmcnt takes an
+        // immediate, so the two counts that occur are branches
+        auto arrive = [&](int s) {
+            if (s + WST - 2 < steps) wait_vmcnt<kYounger>();
+            else wait_vmcnt<0>();
+            // this wave's LDS reads of older steps are complete: after the
+            // barrier another wave may refill their slots
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            __builtin_amdgcn_s_barrier();
+        };
+        Frags f[2];
+        // one K-step from slots (wsl, xsl); with MORE, step s+1 is published
+        // and its first fragments read from (nwsl, nxsl) before the last MFMAs
+        auto step = [&](auto more, int s, int wsl, int xsl, int nwsl, int nxsl) {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                if (ks + 1 < KS) {
+                    read(f[(ks + 1) & 1], wsl, xsl, ks + 1);
+                } else if constexpr (decltype(more)::value) {
+                    arrive(s + 1);
+                    read(f[0], nwsl, nxsl, 0);
+                }
+                // keep the reads ahead of the MFMAs that hide their latency
+                __builtin_amdgcn_sched_barrier(0);
+                mfmas(f[ks & 1]);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        };
+        arrive(0);
+        read(f[0], 0, 0, 0);
+        int wsl = 0, xsl = 0;  // slots of step s
+        int s = 0;
+        for (; s + 1 < steps; ++s) {
+            const int pw = wsl == 0 ? WST - 1 : wsl - 1;  // slots of step s-1
+            const int px = xsl == 0 ? XST - 1 : xsl - 1;
+            if (s + XST - 1 < steps) dma_x(s + XST - 1, px);
+            if (s + WST - 1 < steps) dma_w(s + WST - 1, pw);
+            const int nw = wsl + 1 == WST ? 0 : wsl + 1;
+            const int nx = xsl + 1 == XST ? 0 : xsl + 1;
+            step(std::true_type{}, s, wsl, xsl, nw, nx);
+            wsl = nw;
+            xsl = nx;
+        }
+        if (steps > 0) step(std::false_type{}, s, wsl, xsl, wsl, xsl);
 #pragma unroll
         for (int a = 0; a < FW; ++a)
 #pragma unroll
@@ -242,13 +294,13 @@ struct PrefillCore {
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int STAGES, int WW, int NW, int OCC>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     int max_blocks, uint16_t* __restrict__ act) {
-    using Core = PrefillCore<TW, TT, BK, STAGES, WW, NW>;
+    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW>;
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int HW = TW / 2;  // n-values per tile
     constexpr int WN = HW / WW; // n-values per wave
@@ -316,13 +368,13 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
 // GEMM2 (bf16): weight tile wt covers output rows wt*TW..+TW; the epilogue
 // multiplies by the routing weight and scatters token row r to slot p.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int STAGES, int WW, int NW, int OCC>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
-    using Core = PrefillCore<TW, TT, BK, STAGES, WW, NW>;
+    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW>;
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int WR = TW / WW;  // output rows per wave
 
@@ -396,7 +448,7 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
+    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1><<<grid, 512, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
@@ -410,14 +462,20 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int nsplit, int max_blocks, float* ypart, hipStream_t s) {
-    if (K % 256 == 0) {
+    if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
+        // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1><<<grid, 512, 0, s>>>(
+            (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
+            num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
+    } else if (K % 256 == 0) {
+        const int grid = tile_grid((K / 256) * nsplit * max_blocks);
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else {
         const int grid = tile_grid((K / 128) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<128, kPrefillRows, 32, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<128, kPrefillRows, 32, 3, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     }
