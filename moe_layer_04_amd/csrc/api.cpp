@@ -5,8 +5,10 @@
 // Launch sequence of moe_fused_forward (all on the caller's stream, no host
 // synchronisation, grids sized from host-known upper bounds so no device
 // value is read back):
-//   1 router logits (fp64 dot products)      2 top-k + weights (+ x -> e4m3)
-//   3 align (sorted rows, block owners)       4 GEMM1 + SiLU*up
+//   1 router logits (fp64 dot products) (+ x -> e4m3)
+//   2 top-k + weights                         3 align (sorted rows, block owners)
+//     (2-3 are one single-workgroup launch for up to 1024 token-slots)
+//   4 GEMM1 + SiLU*up
 //   5 (e4m3) per-row activation quantisation  6 GEMM2 * routing weight, scattered
 //   7 combine into bf16 out
 #include <hip/hip_runtime.h>
@@ -23,6 +25,9 @@ namespace {
 constexpr int kDecodeBlock = moe::kDecodeRows;
 constexpr int kPrefillBlock = moe::kPrefillRows;
 constexpr size_t kAlign = 256;
+// up to this many tokens the FP8 token quantisation runs inside the
+// single-workgroup top-k + align launch (a wave per token)
+constexpr int kLateQuantRows = 16;
 
 bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
 
@@ -207,21 +212,36 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         if (timed) (void)hipEventRecord((hipEvent_t)events[i], s);
     };
 
-    uint8_t* xq = dtype == MOE_FP8_E4M3 ? (uint8_t*)(ws + p.xq) : nullptr;
-    float* xs = dtype == MOE_FP8_E4M3 ? (float*)(ws + p.xs) : nullptr;
+    const bool fp8 = dtype == MOE_FP8_E4M3;
+    uint8_t* xq = fp8 ? (uint8_t*)(ws + p.xq) : nullptr;
+    float* xs = fp8 ? (float*)(ws + p.xs) : nullptr;
+    // FP8: GEMM1's epilogue folds each row's |act| max into amax, which the
+    // routing clears on the way
+    uint32_t* amax = fp8 ? (uint32_t*)(ws + p.amax) : nullptr;
+    const int amax_words = fp8 ? p.cap : 0;
     mark(0);
-    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, xq, xs, s);
-    mark(1);
-    if (dtype == MOE_FP8_E4M3) {
-        uint32_t* amax = (uint32_t*)(ws + p.amax);
+    if (moe::topk_align_fits(M, topk)) {
+        // the FP8 token codes go with top-k + align when the tokens are few
+        const bool q_late = fp8 && M <= kLateQuantRows;
+        moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits,
+                                  q_late ? nullptr : xq, xs, s);
+        mark(1);
+        moe::launch_topk_align(logits, x, M, K, E, topk, ids, wts, q_late ? xq : nullptr, xs,
+                               p.block, p.cap, sorted, bexp, offs, npad, amax, amax_words, s);
+        mark(2);
+    } else {
+        moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, xq, xs, s);
+        mark(1);
+        moe::launch_router_topk(logits, M, E, topk, ids, wts, s);
+        mark(2);
+        moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax,
+                          amax_words, s);
+    }
+    mark(3);
+    if (fp8) {
         float* act = (float*)(ws + p.act);
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
-        moe::launch_router_topk(logits, M, E, topk, ids, wts, s);
-        mark(2);
-        moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax, p.cap,
-                          s);
-        mark(3);
         moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, sorted, bexp, npad, M, topk, nslots,
                                      K, N, p.max_blocks, act, amax, s);
         mark(4);
@@ -232,11 +252,6 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         mark(6);
     } else {
         void* act = ws + p.act;
-        moe::launch_router_topk(logits, M, E, topk, ids, wts, s);
-        mark(2);
-        moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, nullptr, 0,
-                          s);
-        mark(3);
         if (p.regime == MOE_REGIME_DECODE)
             moe::launch_gemm1_decode_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
                                           p.max_blocks, act, s);

@@ -30,6 +30,17 @@ void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sor
                   int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
                   uint32_t* zero_buf, int zero_words, hipStream_t s);
 
+// Top-k + align (and, with xq not null, the FP8 token codes; meant for a
+// few tokens) in one single-workgroup launch, for at most kRouteSmallMaxTokens
+// tokens and kRouteSmallMaxSlots token-slots.
+constexpr int kRouteSmallMaxTokens = 64;
+constexpr int kRouteSmallMaxSlots = 1024;
+bool topk_align_fits(int M, int topk);
+void launch_topk_align(const float* logits, const void* x, int M, int K, int E, int topk,
+                       int32_t* ids, float* w, uint8_t* xq, float* xscale, int B, int cap,
+                       int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
+                       int32_t* num_padded, uint32_t* zero_buf, int zero_words, hipStream_t s);
+
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded, int M,
                               int topk, int nslots, int K, int N, int max_blocks, void* act,

@@ -9,8 +9,7 @@
 // logits are taken in descending order with ties to the lower expert id;
 // the weights are the softmax over the picked logits (equal to the full
 // softmax renormalised over them).
-#include "common.hpp"
-#include "launch.hpp"
+#include "routing.hpp"
 
 namespace moe {
 
@@ -156,69 +155,15 @@ __global__ __launch_bounds__(256) void quant_rows_vec_kernel(const uint16_t* __r
 }
 
 // ---------------------------------------------------------------------------
-// Top-k + weights.  One wave per token.  Lane l holds logits of experts l, l+64, l+128, l+192.  A 64-bit key
-// orders (logit, -expert): the high word maps the float to an unsigned with
-// the same order, the low word is ~expert, so the wave max (DPP/ds_swizzle)
-// is the largest logit with ties to the lower id.
+// Top-k + weights: one wave per token (topk_wave in routing.hpp).
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ uint32_t ordered_bits(float f) {
-    uint32_t u = __float_as_uint(f + 0.0f);  // -0 -> +0
-    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
-
 __global__ __launch_bounds__(256) void router_topk_kernel(
     const float* __restrict__ logits, int M, int E, int topk,
     int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
-    const int lane = lane_id();
     const int t = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
     if (t >= M) return;  // wave-uniform
-
-    uint64_t key[4];
-    float lv[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        if (e < E) {
-            lv[i] = logits[(size_t)t * E + e];
-            key[i] = ((uint64_t)ordered_bits(lv[i]) << 32) | (uint32_t)(~(uint32_t)e);
-        } else {
-            lv[i] = 0.0f;
-            key[i] = 0;
-        }
-    }
-
-    float sel_l[MOE_KERNEL_MAX_TOPK];
-    int sel_e[MOE_KERNEL_MAX_TOPK];
-#pragma unroll
-    for (int j = 0; j < MOE_KERNEL_MAX_TOPK; ++j) {
-        if (j >= topk) break;
-        uint64_t best = max_u64(max_u64(key[0], key[1]), max_u64(key[2], key[3]));
-        best = wave_max_u64(best);
-        const int e = (int)(~(uint32_t)best);
-        sel_e[j] = e;
-        // the owning lane removes it and broadcasts its logit
-        float l = 0.0f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-            if (lane + 64 * i == e) { key[i] = 0; l = lv[i]; }
-        sel_l[j] = __shfl(l, e & 63);
-    }
-    if (lane < topk) {
-        // every lane holds the same sel_l[]; lane j writes slot j
-        const float l0 = sel_l[0];
-        float den = 0.0f, mine = 0.0f;
-        int mye = 0;
-#pragma unroll
-        for (int j = 0; j < MOE_KERNEL_MAX_TOPK; ++j) {
-            if (j >= topk) break;
-            const float w = expf(sel_l[j] - l0);
-            den += w;
-            if (j == lane) { mine = w; mye = sel_e[j]; }
-        }
-        topk_ids[(size_t)t * topk + lane] = mye;
-        topk_weights[(size_t)t * topk + lane] = mine / den;
-    }
-
+    topk_wave(logits + (size_t)t * E, E, topk, topk_ids + (size_t)t * topk,
+              topk_weights + (size_t)t * topk, nullptr);
 }
 
 // ---------------------------------------------------------------------------
