@@ -164,7 +164,10 @@ struct PrefillCore {
     }
 
     // woff[q] / xoff[q]: byte offset at k = kbeg of this lane's source chunk;
-    // the loop covers klen reduction elements.
+    // the loop covers klen reduction elements.  With COMPUTE false the wave
+    // only takes its share of the copies and barriers (its token columns are
+    // all padding): no LDS reads, no MFMAs, accumulators stay zero.
+    template <bool COMPUTE>
     __device__ __forceinline__ void run(char* lds, prsrc_t rw, const uint32_t* woff, prsrc_t rx,
                                         const uint32_t* xoff, int klen, int wave, int wb,
                                         const int* arow) {
@@ -213,6 +216,7 @@ struct PrefillCore {
         }
         struct Frags { bf16x8_t a[FW], b[FT]; };
         auto read = [&](Frags& f, int wslot, int xslot, int ks) {
+            if constexpr (!COMPUTE) return;
             const char* wbase = lds + wslot * kWSlot;
             const char* xbase = lds + kXBase + xslot * kXSlot;
 #pragma unroll
@@ -223,6 +227,7 @@ struct PrefillCore {
                 f.b[b] = *reinterpret_cast<const bf16x8_t*>(xbase + boff[ks][b]);
         };
         auto mfmas = [&](const Frags& f) {
+            if constexpr (!COMPUTE) return;
 #pragma unroll
             for (int a = 0; a < FW; ++a)
 #pragma unroll
@@ -340,7 +345,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
         arow[a + Core::FW / 2] = HW + wa * WN + a * 32;
     }
     Core core;
-    core.run(lds, rw, woff, rx, xoff, K, wave, wb, arow);
+    // a wave whose token rows are all padding (the tail of an expert's last
+    // block) skips its MFMAs
+    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+        core.template run<true>(lds, rw, woff, rx, xoff, K, wave, wb, arow);
+    else
+        core.template run<false>(lds, rw, woff, rx, xoff, K, wave, wb, arow);
 
     const int li = lane & 31;
 #pragma unroll
@@ -412,7 +422,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
 #pragma unroll
     for (int a = 0; a < Core::FW; ++a) arow[a] = wa * WR + a * 32;
     Core core;
-    core.run(lds, rw, woff, ra, aoff, nlen, wave, wb, arow);
+    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+        core.template run<true>(lds, rw, woff, ra, aoff, nlen, wave, wb, arow);
+    else
+        core.template run<false>(lds, rw, woff, ra, aoff, nlen, wave, wb, arow);
 
     const int li = lane & 31;
 #pragma unroll
