@@ -117,9 +117,8 @@ __device__ __forceinline__ void wait_vmcnt() {
 
 // The shared main loop.  The weight rows and the token rows of each K-step
 // stream through two LDS rings, of WST and XST slots: the weight copy of a
-// step is issued WST-1 steps ahead, the token copy XST-1 steps ahead (the
-// token panel is shared by more co-resident workgroups and mostly hits in
-// L2, so it gets the shorter lead when LDS runs out).  At step s every wave
+// step is issued WST-1 steps ahead, the token copy XST-1 steps ahead (when
+// LDS runs out one operand gets the shorter lead).  At step s every wave
 // issues the token copy of step s+XST-1 and the weight copy of step s+WST-1
 // into the slots step s-1 used; before the last MFMAs of step s it waits
 // (vmcnt) for its own copies of step s+1, meets the workgroup at one raw
@@ -144,13 +143,17 @@ struct PrefillCore {
     static constexpr int KS = BK / 16;                      // MFMA k-slices per step
     static_assert(kWInstr * kRowsPerInstr * NW == TW && kXInstr * kRowsPerInstr * NW == TT,
                   "tile rows must split evenly over the waves' DMA instructions");
-    static_assert(XST >= 2 && (WST == XST || WST == XST + 1),
-                  "weights lead the tokens by at most one step");
+    static_assert(WST >= 2 && XST >= 2 && WST - XST <= 1 && XST - WST <= 1,
+                  "the two rings' leads differ by at most one step");
     static_assert(KS % 2 == 0, "fragment double buffer alternates per k-slice");
-    // Copies a wave may leave in flight when step s must have landed, given
-    // that every younger copy was issued (issue order per step: tokens, then
-    // weights).
-    static constexpr int kYounger = (XST - 2) * (kWInstr + kXInstr) + (WST - XST) * kWInstr;
+    // Per step the operand with the shorter lead is issued first.  Copies a
+    // wave may leave in flight when step s must have landed, given that every
+    // younger copy was issued:
+    static constexpr bool kWFirst = XST > WST;
+    static constexpr int kMinSt = WST < XST ? WST : XST;
+    static constexpr int kMaxSt = WST < XST ? XST : WST;
+    static constexpr int kLongInstr = WST > XST ? kWInstr : (XST > WST ? kXInstr : 0);
+    static constexpr int kYounger = (kMinSt - 2) * (kWInstr + kXInstr) + kLongInstr;
 
     f32x16_t acc[FW][FT];
 
@@ -237,17 +240,22 @@ struct PrefillCore {
         const int steps = klen / BK;
         // the previous tile's last reads of the rings are done before refilling them
         __builtin_amdgcn_s_barrier();
-        // prologue: the copies steps -WST+1 .. -1 would have issued
+        // prologue: the copies steps 1-kMaxSt .. -1 would have issued
 #pragma unroll
-        for (int v = 1 - WST; v < 0; ++v) {
+        for (int v = 1 - kMaxSt; v < 0; ++v) {
             const int xs = v + XST - 1, ws = v + WST - 1;
-            if (xs >= 0 && xs < steps) dma_x(xs, xs);
-            if (ws >= 0 && ws < steps) dma_w(ws, ws);
+            if constexpr (kWFirst) {
+                if (ws >= 0 && ws < steps) dma_w(ws, ws);
+                if (xs >= 0 && xs < steps) dma_x(xs, xs);
+            } else {
+                if (xs >= 0 && xs < steps) dma_x(xs, xs);
+                if (ws >= 0 && ws < steps) dma_w(ws, ws);
+            }
         }
         // wait for step s (issued through step s-1): vmcnt takes an
         // immediate, so the two counts that occur are branches
         auto arrive = [&](int s) {
-            if (s + WST - 2 < steps) wait_vmcnt<kYounger>();
+            if (s + kMaxSt - 2 < steps) wait_vmcnt<kYounger>();
             else wait_vmcnt<0>();
             // this wave's LDS reads of older steps are complete: after the
             // barrier another wave may refill their slots
@@ -279,8 +287,13 @@ struct PrefillCore {
         for (; s + 1 < steps; ++s) {
             const int pw = wsl == 0 ? WST - 1 : wsl - 1;  // slots of step s-1
             const int px = xsl == 0 ? XST - 1 : xsl - 1;
-            if (s + XST - 1 < steps) dma_x(s + XST - 1, px);
-            if (s + WST - 1 < steps) dma_w(s + WST - 1, pw);
+            if constexpr (kWFirst) {
+                if (s + WST - 1 < steps) dma_w(s + WST - 1, pw);
+                if (s + XST - 1 < steps) dma_x(s + XST - 1, px);
+            } else {
+                if (s + XST - 1 < steps) dma_x(s + XST - 1, px);
+                if (s + WST - 1 < steps) dma_w(s + WST - 1, pw);
+            }
             const int nw = wsl + 1 == WST ? 0 : wsl + 1;
             const int nx = xsl + 1 == XST ? 0 : xsl + 1;
             step(std::true_type{}, s, wsl, xsl, nw, nx);

@@ -113,6 +113,83 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 
 }
 
+// ---------------------------------------------------------------------------
+// Logits of large batches on the fp64 matrix cores: a workgroup computes a
+// 16-token x 16-expert tile with v_mfma_f64_16x16x4_f64; its 16 waves split
+// K into contiguous ranges (K % 512 == 0) and the per-wave fp64 sums are
+// added in wave order through LDS (deterministic), then the bias and one
+// fp32 rounding.  Operand layout: lane l supplies token / expert row l % 16
+// at k-slot l / 16, and each 16-byte load of a row gives the elements of 8
+// successive MFMAs (MFMA m takes element m of every lane's 8-element run,
+// the same k for both operands).  Accumulator element q of lane l is tile
+// entry (token 4q + l/16, expert l % 16).
+// ---------------------------------------------------------------------------
+typedef double f64x4_t __attribute__((ext_vector_type(4)));
+constexpr int kLogitWaves = 16;
+
+__global__ __launch_bounds__(kLogitWaves * 64) void router_logits_f64mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
+    const float* __restrict__ bias, int M, int K, int E, float* __restrict__ logits) {
+    __shared__ double part[kLogitWaves][256];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int tiles_e = (E + 15) / 16;
+    const int t0 = ((int)blockIdx.x / tiles_e) * 16;
+    const int e0 = ((int)blockIdx.x % tiles_e) * 16;
+    const int r = lane & 15, kq = lane >> 4;
+    // rows past M / E are clamped to a valid row; their sums are discarded
+    const uint16_t* xr = x + (size_t)min(t0 + r, M - 1) * K + kq * 8;
+    const uint16_t* wrr = wr + (size_t)min(e0 + r, E - 1) * K + kq * 8;
+    const int kw = K / kLogitWaves;
+    const int kb = wave * kw;
+    const int nblk = kw / 32;
+
+    f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
+    auto mma8 = [&](i32x4_t va, i32x4_t vb) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                (double)bf16_bits_to_f32((uint32_t)va[q] & 0xffffu),
+                (double)bf16_bits_to_f32((uint32_t)vb[q] & 0xffffu), acc, 0, 0, 0);
+            acc = __builtin_amdgcn_mfma_f64_16x16x4f64(
+                (double)bf16_bits_to_f32((uint32_t)va[q] >> 16),
+                (double)bf16_bits_to_f32((uint32_t)vb[q] >> 16), acc, 0, 0, 0);
+        }
+    };
+    // two 32-deep blocks in flight ahead of the one being multiplied
+    i32x4_t a0 = *reinterpret_cast<const i32x4_t*>(xr + kb);
+    i32x4_t b0 = *reinterpret_cast<const i32x4_t*>(wrr + kb);
+    i32x4_t a1 = a0, b1 = b0;
+    if (nblk > 1) {
+        a1 = *reinterpret_cast<const i32x4_t*>(xr + kb + 32);
+        b1 = *reinterpret_cast<const i32x4_t*>(wrr + kb + 32);
+    }
+    for (int i = 0; i < nblk; ++i) {
+        i32x4_t a2 = a1, b2 = b1;
+        if (i + 2 < nblk) {
+            a2 = *reinterpret_cast<const i32x4_t*>(xr + kb + (i + 2) * 32);
+            b2 = *reinterpret_cast<const i32x4_t*>(wrr + kb + (i + 2) * 32);
+        }
+        mma8(a0, b0);
+        a0 = a1; b0 = b1;
+        a1 = a2; b1 = b2;
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) part[wave][(4 * q + kq) * 16 + r] = acc[q];
+    __syncthreads();
+    const int tid = (int)threadIdx.x;
+    if (tid < 256) {
+        const int t = t0 + tid / 16, e = e0 + tid % 16;
+        if (t < M && e < E) {
+            double s = part[0][tid];
+#pragma unroll
+            for (int w = 1; w < kLogitWaves; ++w) s += part[w][tid];
+            if (bias) s += (double)bias[e];
+            logits[(size_t)t * E + e] = (float)s;
+        }
+    }
+}
+
 // Per-token dynamic e4m3 quantisation for the fused FP8 path: one workgroup
 // per token row, 16-byte loads (K % 8 == 0), s = amax/448 (1 if amax == 0),
 // code = E4M3(x/s) with one correctly rounded fp32 division.
@@ -199,6 +276,10 @@ void launch_router_logits(const void* x, const void* wr, const float* bias, int 
             router_logits_kernel<1, 1, true><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
         else
             router_logits_kernel<1, 1, false><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
+    } else if (K % (kLogitWaves * 32) == 0) {
+        const int grid = ((M + 15) / 16) * ((E + 15) / 16);
+        router_logits_f64mfma_kernel<<<grid, kLogitWaves * 64, 0, s>>>(xp, wp, bias, M, K, E,
+                                                                      logits);
     } else {
         const int grid = ((M + 3) / 4) * ((E + 3) / 4);
         if (K % 8 == 0)

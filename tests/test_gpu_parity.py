@@ -145,14 +145,21 @@ def test_router_full_size(moe, name):
     check_router(moe, x, wr, bias, wl.topk)
 
 
-@pytest.mark.parametrize("M,K,E,k", [(1, 1, 1, 1), (7, 100, 3, 2), (33, 264, 256, 16),
-                                     (64, 96, 64, 8), (5, 8, 200, 200 // 13)])
-def test_router_ragged(moe, M, K, E, k):
-    note(f"router ragged M={M} K={K} E={E} k={k}")
+# the last three take the fp64 matrix-core logits (M*E > 8192, K % 512 == 0)
+# with token and expert counts that are not multiples of its 16 x 16 tile
+@pytest.mark.parametrize("M,K,E,k,with_bias", [(1, 1, 1, 1, False), (7, 100, 3, 2, False),
+                                               (33, 264, 256, 16, False), (64, 96, 64, 8, False),
+                                               (5, 8, 200, 200 // 13, False),
+                                               (37, 1024, 250, 8, False),
+                                               (45, 512, 200, 4, True),
+                                               (1000, 1536, 9, 2, True)])
+def test_router_ragged(moe, M, K, E, k, with_bias):
+    note(f"router ragged M={M} K={K} E={E} k={k} bias={with_bias}")
     g = torch.Generator().manual_seed(M + K + E)
     x = torch.randn((M, K), generator=g).to(torch.bfloat16)
     wr = (torch.randn((E, K), generator=g)).to(torch.bfloat16)
-    check_router(moe, x, wr, None, k)
+    bias = torch.randn(E, generator=g) if with_bias else None
+    check_router(moe, x, wr, bias, k)
 
 
 def test_router_ties_lower_id(moe):
