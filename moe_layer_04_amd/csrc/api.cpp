@@ -37,7 +37,11 @@ struct Plan {
     int regime = MOE_REGIME_DECODE;
     int block = kDecodeBlock;
     int cap = 0;         // rows of the sorted list: M*topk + E*(block-1)
-    int max_blocks = 0;  // cap / block
+    int max_blocks = 0;  // cap / block: entries of block_expert
+    // Launch grids cover at most this many blocks: summed over the experts
+    // that received rows, ceil(c_e / block) <= floor(slots / block) +
+    // (number of such experts), and that number is <= min(E, slots).
+    int grid_blocks = 0;
     int nsplit = 1;      // GEMM2 reduction split (decode)
     size_t logits = 0, ids = 0, wts = 0, sorted = 0, bexp = 0, offs = 0, npad = 0;
     size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
@@ -53,6 +57,10 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
     p.cap = (int)(slots + (long)E * (p.block - 1));
     p.max_blocks = p.cap / p.block;
+    {
+        const long bound = slots / p.block + (slots < E ? slots : E);
+        p.grid_blocks = (int)(bound < p.max_blocks ? bound : p.max_blocks);
+    }
     if (regime == MOE_REGIME_DECODE) {
         // split GEMM2's reduction when few (block, row-tile) pairs exist, so
         // the weight stream spreads over all CUs
@@ -243,29 +251,29 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
         moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, sorted, bexp, npad, M, topk, nslots,
-                                     K, N, p.max_blocks, act, amax, s);
+                                     K, N, p.grid_blocks, act, amax, s);
         mark(4);
         moe::launch_act_quant(act, amax, sorted, npad, nslots, N, p.cap, actq, as, s);
         mark(5);
         moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, wts, sorted, bexp, npad, p.cap,
-                                     nslots, K, N, p.nsplit, p.max_blocks, ypart, s);
+                                     nslots, K, N, p.nsplit, p.grid_blocks, ypart, s);
         mark(6);
     } else {
         void* act = ws + p.act;
         if (p.regime == MOE_REGIME_DECODE)
             moe::launch_gemm1_decode_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
-                                          p.max_blocks, act, s);
+                                          p.grid_blocks, act, s);
         else
             moe::launch_gemm1_prefill_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
-                                           p.max_blocks, act, s);
+                                           p.grid_blocks, act, s);
         mark(4);
         mark(5);
         if (p.regime == MOE_REGIME_DECODE)
             moe::launch_gemm2_decode_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
-                                          p.nsplit, p.max_blocks, ypart, s);
+                                          p.nsplit, p.grid_blocks, ypart, s);
         else
             moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
-                                           p.nsplit, p.max_blocks, ypart, s);
+                                           p.nsplit, p.grid_blocks, ypart, s);
         mark(6);
     }
     moe::launch_combine(ypart, M, K, topk, p.nsplit, out, s);

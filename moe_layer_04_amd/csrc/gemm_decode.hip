@@ -294,11 +294,25 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     const float s = (a == 0.0f) ? 1.0f : a / 448.0f;
     const float* src = act + (size_t)r * N;
     uint8_t* dst = act_q + (size_t)r * N;
-    for (int n = lane * 4; n < N; n += kWave * 4) {
-        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(src + n);
-        const uint32_t q = f32_to_e4m3(v[0] / s) | (f32_to_e4m3(v[1] / s) << 8) |
-                           (f32_to_e4m3(v[2] / s) << 16) | (f32_to_e4m3(v[3] / s) << 24);
-        *reinterpret_cast<uint32_t*>(dst + n) = q;
+    // the row's loads are issued in groups of 8 per lane before any is used
+    constexpr int G = 8;
+    for (int n0 = lane * 4; n0 < N; n0 += G * kWave * 4) {
+        f32x4_t v[G];
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int n = n0 + g * kWave * 4;
+            if (n < N) v[g] = *reinterpret_cast<const f32x4_t*>(src + n);
+        }
+#pragma unroll
+        for (int g = 0; g < G; ++g) {
+            const int n = n0 + g * kWave * 4;
+            if (n < N) {
+                const uint32_t q = f32_to_e4m3(v[g][0] / s) | (f32_to_e4m3(v[g][1] / s) << 8) |
+                                   (f32_to_e4m3(v[g][2] / s) << 16) |
+                                   (f32_to_e4m3(v[g][3] / s) << 24);
+                *reinterpret_cast<uint32_t*>(dst + n) = q;
+            }
+        }
     }
     if (lane == 0) ascale[r] = s;
 }
