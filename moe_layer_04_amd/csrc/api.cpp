@@ -66,7 +66,7 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         // the weight stream spreads over all CUs
         const long est_blocks = slots < E ? slots : E;
         const long tiles = est_blocks * (K / 128);
-        while (tiles * p.nsplit < 1024 && p.nsplit < 16 && (N / (p.nsplit * 2)) % 128 == 0)
+        while (tiles * p.nsplit < 2048 && p.nsplit < 16 && (N / (p.nsplit * 2)) % 128 == 0)
             p.nsplit *= 2;
     } else {
         p.nsplit = moe::prefill_gemm2_splits(K, N);
