@@ -32,9 +32,10 @@
 //
 // Tile order: the linear workgroup id is dealt to the 8 XCDs round-robin by
 // the hardware; each XCD is given a contiguous range of tiles, and tiles are
-// numbered so that a run of consecutive ids covers kGroup weight tiles for
+// numbered so that a run of consecutive ids covers G weight tiles for
 // successive token blocks, so workgroups resident on one XCD share both
-// operands in its L2.
+// operands in its L2 (G = 4 for GEMM1, 8 for GEMM2: the measured minima of
+// time and HBM fetch).
 //
 // 32x32x16 layouts (gfx950): lane l supplies row/column (l % 32) with the
 // K-slice 8*(l/32)..+8 for both operands; the accumulator lane l holds
@@ -46,8 +47,6 @@
 
 namespace moe {
 
-constexpr int kGroup = 8;
-
 typedef __amdgpu_buffer_rsrc_t prsrc_t;
 
 __device__ __forceinline__ prsrc_t pmake_rsrc(const void* base, uint32_t bytes) {
@@ -58,13 +57,14 @@ __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t
 }
 
 // Tile schedule.  The hardware deals workgroup g to XCD g % 8; each XCD is
-// given a contiguous range of tiles, numbered with kGroup weight tiles
-// varying fastest, then token blocks, so the workgroups resident on one XCD
-// at a time cover a kGroup x (resident/kGroup) block of tiles whose weight
+// given a contiguous range of tiles, numbered with G weight tiles varying
+// fastest, then token blocks, so the workgroups resident on one XCD at a
+// time cover a G x (resident/G) block of tiles whose weight
 // and token panels they share in that XCD's L2.  The walk below also
 // supports a persistent grid (fewer workgroups than tiles, each taking
 // every nslot-th tile of its XCD's range); the launchers size the grid to
 // one tile per workgroup, which measured less memory traffic.
+template <int G>
 struct TileWalk {
     int xcd, slot, nslot, per_xcd, total, n_wtiles, n_blocks, r;
     __device__ TileWalk(int n_wt, int n_blk) {
@@ -85,11 +85,11 @@ struct TileWalk {
         if (local >= per_xcd) return false;
         const int t = xcd * per_xcd + local;
         if (t >= total) return false;
-        const int span = kGroup * n_blocks;
+        const int span = G * n_blocks;
         const int grp = t / span;
         const int in = t % span;
-        const int gsize = min(kGroup, n_wtiles - grp * kGroup);
-        wt = grp * kGroup + in % gsize;
+        const int gsize = min(G, n_wtiles - grp * G);
+        wt = grp * G + in % gsize;
         blk = in / gsize;
         return true;
     }
@@ -312,7 +312,7 @@ struct PrefillCore {
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
@@ -327,7 +327,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int wa = wave % WW, wb = wave / WW;
-    TileWalk walk(N / HW, max_blocks);
+    TileWalk<GROUP> walk(N / HW, max_blocks);
     int wt, blk;
     while (walk.next(wt, blk)) {
     if (blk * TT >= npad) continue;
@@ -391,7 +391,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
 // GEMM2 (bf16): weight tile wt covers output rows wt*TW..+TW; the epilogue
 // multiplies by the routing weight and scatters token row r to slot p.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int wa = wave % WW, wb = wave / WW;
-    TileWalk walk(n_wt * nsplit, max_blocks);
+    TileWalk<GROUP> walk(n_wt * nsplit, max_blocks);
     int wtz, blk;
     while (walk.next(wtz, blk)) {
     if (blk * TT >= npad) continue;
@@ -474,7 +474,7 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1><<<grid, 512, 0, s>>>(
+    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 4><<<grid, 512, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
@@ -491,17 +491,17 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
     if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
         // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1><<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 8><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else if (K % 256 == 0) {
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 3, 4, 8, 1, 8><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else {
         const int grid = tile_grid((K / 128) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<128, kPrefillRows, 32, 3, 3, 4, 8, 1><<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<128, kPrefillRows, 32, 3, 3, 4, 8, 1, 8><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     }
