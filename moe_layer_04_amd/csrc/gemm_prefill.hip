@@ -22,8 +22,8 @@
 // STAGES slots.  Each K-step waits (vmcnt) for its own slot, meets the
 // workgroup at one raw s_barrier (the __syncthreads fence would wait for
 // every in-flight copy), issues the copy STAGES-1 steps ahead and runs its
-// MFMAs.  Padding token rows (sentinels) copy token row 0 for GEMM1 / their
-// own in-bounds act row for GEMM2: an MFMA output column depends only on its
+// MFMAs.  Padding token rows (sentinels) copy token row 0 for GEMM1 / the
+// block's first act row for GEMM2: an MFMA output column depends only on its
 // own B column, and those columns are never stored.
 //
 // GEMM2 may split its reduction (N) across workgroups into fp32 partial
@@ -428,8 +428,10 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
-        aoff[q] = (uint32_t)((blk * TT + row) * row_bytes) + nbeg * 2 +
-                  Core::dma_chunk(row, lane) * 16;
+        // padding rows (never written by GEMM1) copy the block's first row
+        // instead, an L2 hit; their columns are never stored
+        const int src = sorted_ids[blk * TT + row] < nslots ? blk * TT + row : blk * TT;
+        aoff[q] = (uint32_t)(src * row_bytes) + nbeg * 2 + Core::dma_chunk(row, lane) * 16;
     }
     int arow[Core::FW];
 #pragma unroll
