@@ -7,7 +7,9 @@ in HBM.  The default workload is the Mixtral-shaped decode batch (M=8 tokens,
 K=4096, N=14336, E=8, top-2, bf16).  W untimed warm-up steps, then exactly K
 steps bracketed by torch.cuda.synchronize(); value = tokens per second.
 
-A second pass of K steps through moe_fused_forward_timed records HIP events
+The same K steps are then replayed from HIP graphs captured from the layer
+(graph_ms_per_step, graph_tokens_per_s), the launch mode of a serving loop.
+A third pass of K steps through moe_fused_forward_timed records HIP events
 between the kernels on the stream they run on; the dominant kernel's mean
 duration gives the roofline fraction (algorithmic bytes or FLOPs per launch
 / duration vs the MI355X peak).  The CPU oracle is timed on this host's
@@ -226,6 +228,20 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = wl.M * args.steps / elapsed
 
+    # ---- the same steps replayed from captured HIP graphs (one per weight copy)
+    graphs = [moe.FusedForwardGraph(g["x"], g["w_router"], g["bias"], w1s[L], w2s[L], wl.topk,
+                                    w1_scale=g["w1_scale"], w2_scale=g["w2_scale"])
+              for L in range(layers)]
+    for i in range(args.warmup):
+        graphs[i % layers].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        graphs[i % layers].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+    del graphs
+
     # ---- per-kernel durations from HIP events on the layer's stream --------
     hip = hip_runtime()
     lib = moe.load_library()
@@ -322,6 +338,8 @@ def main():
         "algorithmic_flops": alg_flops,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "timed_pass_ms_per_step": round(float(np.mean(total_ms)), 4),
+        "graph_ms_per_step": round(graph_ms, 4),
+        "graph_tokens_per_s": round(wl.M / (graph_ms / 1e3), 1),
         "roofline": roofline,
         "source_digest": digest,
     }

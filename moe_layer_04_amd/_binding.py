@@ -214,3 +214,45 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
                                     ctypes.byref(nbytes), _stream(dev)),
            "moe_fused_forward")
     return out
+
+
+class FusedForwardGraph:
+    """One moe_fused_forward captured in a HIP graph (torch.cuda.CUDAGraph),
+    for serving loops that re-run the layer on fixed buffers.
+
+    The layer's launches only enqueue kernels on the current stream (no
+    allocation, host synchronisation or memset), so the whole launch
+    sequence is captured as it is.  The graph is bound to the tensors given
+    here: ``replay()`` recomputes ``out`` from whatever ``x`` (and the
+    weights) hold at that moment.  ``out`` and the workspace are owned by
+    this object."""
+
+    def __init__(self, x: torch.Tensor, w_router: torch.Tensor,
+                 router_bias: Optional[torch.Tensor], w1: torch.Tensor, w2: torch.Tensor,
+                 topk: int, *, w1_scale: Optional[torch.Tensor] = None,
+                 w2_scale: Optional[torch.Tensor] = None, regime: int = MOE_REGIME_AUTO):
+        dev = x.device
+        fp8 = w1.dtype == torch.uint8
+        M, K = x.shape
+        E, twoN, _ = w1.shape
+        need = workspace_size(MOE_FP8_E4M3 if fp8 else MOE_BF16, M, K, twoN // 2, E, topk,
+                              regime)
+        self.out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+        args = (x, w_router, router_bias, w1, w2, topk)
+        kw = dict(w1_scale=w1_scale, w2_scale=w2_scale, regime=regime, out=self.out,
+                  workspace=self.workspace)
+        # one eager call on a side stream before capture (library and kernel
+        # loading happen outside the graph)
+        side = torch.cuda.Stream(device=dev)
+        side.wait_stream(torch.cuda.current_stream(dev))
+        with torch.cuda.stream(side):
+            moe_fused_forward(*args, **kw)
+        torch.cuda.current_stream(dev).wait_stream(side)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            moe_fused_forward(*args, **kw)
+
+    def replay(self) -> torch.Tensor:
+        self.graph.replay()
+        return self.out
