@@ -54,6 +54,9 @@ def hip_runtime():
 
 
 CPU_SECONDS = 10.0  # oracle work timed for the CPU baseline
+# the library's automatic kernel-family choice (api.cpp): Swap-AB decode
+# kernels up to this many token-slots per expert, full tiles above
+DECODE_MAX_ROWS_PER_EXPERT = 8
 COPY_BYTES = 1 << 30
 
 
@@ -128,6 +131,41 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     print(json.dumps(rec))
 
 
+def regime_sweep(moe, wlm, wl, dev):
+    """Both kernel families (bf16 weights) on batches of M = 8 .. 1024 tokens
+    of this workload's shape: mean ms per layer call over 10 calls after 3."""
+    import torch
+    ms_list = [8, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024]
+    big = wlm.Workload(wl.name + "_sweep", M=max(ms_list), K=wl.K, N=wl.N, E=wl.E,
+                       topk=wl.topk, seed=wl.seed)
+    g = wlm.generate(big, dev)
+    for M in ms_list:
+        x = g["x"][:M].contiguous()
+        rows = M * wl.topk / wl.E
+        row = {"workload": wl.name, "M": M, "rows_per_expert": rows}
+        for regime, key in ((moe.MOE_REGIME_DECODE, "decode_ms"),
+                            (moe.MOE_REGIME_PREFILL, "tiles_ms")):
+            if regime == moe.MOE_REGIME_DECODE and rows > 256:
+                continue  # the decode kernels re-stream the weights per 16-row block
+            need = moe.workspace_size(moe.MOE_BF16, M, wl.K, wl.N, wl.E, wl.topk, regime)
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+            out = torch.empty((M, wl.K), dtype=torch.bfloat16, device=dev)
+
+            def call():
+                moe.moe_fused_forward(x, g["w_router"], None, g["w1"], g["w2"], wl.topk,
+                                      regime=regime, out=out, workspace=ws)
+
+            for _ in range(3):
+                call()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(10):
+                call()
+            torch.cuda.synchronize()
+            row[key] = round((time.perf_counter() - t0) * 1e3 / 10, 4)
+        print(json.dumps(row), flush=True)
+
+
 def source_digest(paths):
     h = hashlib.sha256()
     for p in paths:
@@ -151,6 +189,10 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--regime-sweep", action="store_true",
+                    help="time the decode and full-tile kernel families (bf16) over batch "
+                         "sizes M = 8 .. 1024 at this workload's K, N, E, top-k; one JSON "
+                         "line per M, then exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [REQ_CSV COPY_REQ_CSV]: "
                          "turn rocprofv3 --pmc counter CSVs of this workload and of the copy "
@@ -189,6 +231,9 @@ def main():
         print(json.dumps({"copy_bytes": COPY_BYTES, "reps": 3}))
         return
     moe.load_library(build_if_missing=True)
+    if args.regime_sweep:
+        regime_sweep(moe, wlm, wl, dev)
+        return
 
     log(f"generating {wl}")
     g = wlm.generate(wl, dev)
@@ -288,7 +333,7 @@ def main():
                  + (wl.E * 4 if wl.bias_var else 0) + (2 * wl.E * 4 if wl.fp8 else 0))
     alg_flops = 6.0 * slots * wl.N * wl.K
     step_s = ms_per_step / 1e3
-    decode = (slots <= 16 * wl.E) or wl.fp8
+    decode = (slots <= DECODE_MAX_ROWS_PER_EXPERT * wl.E) or wl.fp8
     g1_s = kern_us["gemm1"] / 1e6
     if decode:
         # GEMM1 reads W1 of every active expert once plus the token rows

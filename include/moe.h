@@ -66,7 +66,9 @@ typedef enum {
 /* Kernel family used by the expert GEMMs; results agree up to fp32
  * summation order whichever is picked. */
 typedef enum {
-    MOE_REGIME_AUTO = 0,    /* pick from the mean rows per expert, M*topk/E */
+    MOE_REGIME_AUTO = 0,    /* DECODE while M*topk <= 8*E (at most 8 token-slots
+                               per expert on average) or for e4m3 weights,
+                               else PREFILL: the measured crossover */
     MOE_REGIME_DECODE = 1,  /* Swap-AB: weight rows on the MFMA row dimension */
     MOE_REGIME_PREFILL = 2  /* full MFMA tiles of token rows x weight rows */
 } moe_regime;

@@ -25,6 +25,14 @@ namespace {
 constexpr int kDecodeBlock = moe::kDecodeRows;
 constexpr int kPrefillBlock = moe::kPrefillRows;
 constexpr size_t kAlign = 256;
+// Kernel family chosen per token bucket, from a sweep of both families over
+// batch sizes on one MI355X (bf16; K, N, E, k = 4096, 14336, 8, 2 /
+// 4096, 8192, 16, 2 / 7168, 2048, 256, 8; M = 8 .. 1024): the Swap-AB decode
+// kernels are faster up to 8 token-slots per expert on all three shapes, the
+// full-tile kernels from 12 on (8-12 is the crossover).  Past 16 rows an
+// expert takes a second 16-row decode block and its weights are streamed
+// again.  The e4m3 weights have only the decode kernels.
+constexpr long kDecodeMaxRowsPerExpert = 8;
 // up to this many tokens the FP8 token quantisation runs inside the
 // single-workgroup top-k + align launch (a wave per token)
 constexpr int kLateQuantRows = 16;
@@ -51,8 +59,9 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     Plan p;
     const long slots = (long)M * topk;
     if (regime == MOE_REGIME_AUTO)
-        regime = (dtype == MOE_FP8_E4M3 || slots <= 16L * E) ? MOE_REGIME_DECODE
-                                                              : MOE_REGIME_PREFILL;
+        regime = (dtype == MOE_FP8_E4M3 || slots <= (long)kDecodeMaxRowsPerExpert * E)
+                     ? MOE_REGIME_DECODE
+                     : MOE_REGIME_PREFILL;
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
     p.cap = (int)(slots + (long)E * (p.block - 1));
