@@ -31,7 +31,8 @@ ORC_ERR_MISSING_EXPERT = 2
 ORC_ERR_NOMEM = 3
 
 BF16 = 0
-FP8_E4M3 = 1
+FP8_E4M3 = 1            # per-tensor weight scales [E]
+FP8_E4M3_ROWWISE = 2    # per-channel weight scales [E,2N] / [E,K]
 
 
 def build() -> str:
@@ -204,8 +205,10 @@ def moe_forward(x, w_router, bias, w1, w2, k, *, w1_scale=None, w2_scale=None,
 
     ``w1`` / ``w2`` are either full arrays [E,2N,K] / [E,K,N] or sequences of
     per-expert arrays (None where an expert's weights are not provided; the
-    oracle fails if a routed expert is missing).  Returns
-    (out float64 [n_tok,K], ids int32 [n_tok,k], weights float64 [n_tok,k]).
+    oracle fails if a routed expert is missing).  With ``fp8`` the scales are
+    per expert tensor ([E]) or per output channel ([E,2N] and [E,K]).
+    Returns (out float64 [n_tok,K], ids int32 [n_tok,k], weights float64
+    [n_tok,k]).
     """
     lib = _load()
     x = _c(x, np.uint16)
@@ -233,7 +236,15 @@ def moe_forward(x, w_router, bias, w1, w2, k, *, w1_scale=None, w2_scale=None,
     out = np.empty((n_tok, K), np.float64)
     ids = np.empty((n_tok, k), np.int32)
     wts = np.empty((n_tok, k), np.float64)
-    rc = lib.orc_moe_forward(FP8_E4M3 if fp8 else BF16, _ptr(x), _ptr(wr), _ptr(b),
+    dtype = BF16
+    if fp8:
+        dtype = FP8_E4M3
+        if s1 is not None and s1.ndim == 2:
+            assert s1.shape == (E, 2 * N) and s2 is not None and s2.shape == (E, K)
+            dtype = FP8_E4M3_ROWWISE
+        else:
+            assert s1 is not None and s1.shape == (E,) and s2 is not None and s2.shape == (E,)
+    rc = lib.orc_moe_forward(dtype, _ptr(x), _ptr(wr), _ptr(b),
                              ctypes.cast(arr1, ctypes.c_void_p),
                              ctypes.cast(arr2, ctypes.c_void_p), _ptr(s1), _ptr(s2),
                              M, K, N, E, k, _ptr(toks), n_tok, _ptr(out), _ptr(ids),

@@ -52,6 +52,10 @@
  *      SiLU*up activation), each with scale s = fp32(amax)/448 (1 if
  *      amax = 0), code = E4M3(fp32(v) / s) with one correctly-rounded fp32
  *      division; weight scales are per expert tensor.
+ *   R8 (a scheme the pages do not describe; the per-tensor one generalised)
+ *      per-channel weight scales: one fp32 scale per output row of each
+ *      expert's W1 (2N rows, gate then up) and W2 (K rows), multiplying that
+ *      row's dot products where R7 multiplies by the tensor's scale.
  */
 #include <math.h>
 #include <stdint.h>
@@ -319,10 +323,12 @@ static void expert_bf16(const uint16_t *xt, const uint16_t *w1, const uint16_t *
     }
 }
 
-/* One token-slot, e4m3 weights with per-tensor scales (R7). */
-static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, float w1s,
-                       const uint8_t *w2, float w2s, int64_t K, int64_t N,
-                       double *act, float *act32, uint8_t *aq, double *y)
+/* One token-slot, e4m3 weights: per-tensor scales (R7, rs = 0: every row
+ * reads w1s[0] / w2s[0]) or per-channel scales (R8, rs = 1: row r reads
+ * w1s[r] / w2s[r]). */
+static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, const float *w1s,
+                       const uint8_t *w2, const float *w2s, int64_t rs, int64_t K,
+                       int64_t N, double *act, float *act32, uint8_t *aq, double *y)
 {
     int64_t n, c, kk;
     float sa;
@@ -335,8 +341,8 @@ static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, float w1s
             hg += e4m3_table[g[kk]] * xv;
             hu += e4m3_table[u[kk]] * xv;
         }
-        hg *= (double)sx * (double)w1s;
-        hu *= (double)sx * (double)w1s;
+        hg *= (double)sx * (double)w1s[n * rs];
+        hu *= (double)sx * (double)w1s[(N + n) * rs];
         act[n] = silu(hg) * hu;
         act32[n] = (float)act[n];
     }
@@ -346,7 +352,7 @@ static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, float w1s
         double acc = 0.0;
         for (n = 0; n < N; ++n)
             acc += e4m3_table[r[n]] * e4m3_table[aq[n]];
-        y[c] = acc * (double)sa * (double)w2s;
+        y[c] = acc * (double)sa * (double)w2s[c * rs];
     }
 }
 
@@ -384,7 +390,9 @@ int orc_quant_rows_f32(const float *v, int64_t M, int64_t K, uint8_t *q, float *
 /*
  * The whole layer for a list of tokens.
  *
- *   dtype     0 = bf16 weights, 1 = e4m3 weights (w1s/w2s per expert)
+ *   dtype     0 = bf16 weights, 1 = e4m3 weights with w1s/w2s [E] (one
+ *             scale per expert tensor), 2 = e4m3 weights with per-channel
+ *             scales w1s [E,2N], w2s [E,K] (R8)
  *   x         bf16 [M,K] (all tokens: routing of token t reads row t only)
  *   wr        bf16 [E,K]; bias fp32 [E] or NULL
  *   w1[e]     expert e's W1 [2N,K] (bf16 or e4m3), NULL if not provided
@@ -410,9 +418,9 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
     double *wts, *y;
     float *lg;
     int rc = ORC_OK;
-    if ((dtype != 0 && dtype != 1) || M < 0 || K <= 0 || N <= 0 || E <= 0 ||
+    if (dtype < 0 || dtype > 2 || M < 0 || K <= 0 || N <= 0 || E <= 0 ||
         k < 1 || k > E || n_tok < 0 || !x || !wr || !w1 || !w2 || !out ||
-        (n_tok > 0 && !tokens) || (dtype == 1 && (!w1s || !w2s)))
+        (n_tok > 0 && !tokens) || (dtype != 0 && (!w1s || !w2s)))
         return ORC_ERR_ARG;
     for (i = 0; i < n_tok; ++i)
         if (tokens[i] < 0 || tokens[i] >= M)
@@ -463,9 +471,14 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
                 for (kk = 0; kk < K; ++kk)
                     xrow[kk] = bf16_to_f32(xt[kk]);
                 quant_row_f32(xrow, K, xq, &sx);
-                expert_fp8(xq, sx, (const uint8_t *)w1[e], w1s[e],
-                           (const uint8_t *)w2[e], w2s[e], K, N, act, act32, aq,
-                           y + s * K);
+                if (dtype == 1)
+                    expert_fp8(xq, sx, (const uint8_t *)w1[e], w1s + e,
+                               (const uint8_t *)w2[e], w2s + e, 0, K, N, act, act32, aq,
+                               y + s * K);
+                else
+                    expert_fp8(xq, sx, (const uint8_t *)w1[e], w1s + e * 2 * N,
+                               (const uint8_t *)w2[e], w2s + e * K, 1, K, N, act, act32,
+                               aq, y + s * K);
             }
         }
         free(act);

@@ -67,7 +67,8 @@ def dense_layer(x_bits, wr_bits, bias, w1, w2, k, *, fp8=False, w1_scale=None,
         if fp8:
             W1 = e4m3_codes_to_f64(w1[e])
             W2 = e4m3_codes_to_f64(w2[e])
-            h = (xd @ W1.T) * (sx.astype(np.float64)[:, None] * float(w1_scale[e]))
+            s1 = np.asarray(w1_scale[e], dtype=np.float64).reshape(-1)  # [1] or [2N]
+            h = (xd @ W1.T) * sx.astype(np.float64)[:, None] * s1[None, :]
         else:
             W1 = bf16_bits_to_f64(w1[e])
             W2 = bf16_bits_to_f64(w2[e])
@@ -76,8 +77,8 @@ def dense_layer(x_bits, wr_bits, bias, w1, w2, k, *, fp8=False, w1_scale=None,
         act = silu(h[:, :N]) * h[:, N:]
         if fp8:
             aq, sa = quant_rows(act.astype(np.float32))
-            y = (e4m3_codes_to_f64(aq) @ W2.T) * (sa.astype(np.float64)[:, None]
-                                                  * float(w2_scale[e]))
+            s2 = np.asarray(w2_scale[e], dtype=np.float64).reshape(-1)  # [1] or [K]
+            y = (e4m3_codes_to_f64(aq) @ W2.T) * sa.astype(np.float64)[:, None] * s2[None, :]
         else:
             y = act @ W2.T
         out += wfull[:, e:e + 1] * y

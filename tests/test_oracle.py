@@ -277,6 +277,54 @@ def test_layer_fp8_vs_dense_bruteforce(M, K, N, E, k):
     assert row_rel_err(out, ref) <= 1e-12
 
 
+def rowwise_scales(rng, E, N, K):
+    s1 = (rng.uniform(0.25, 4, (E, 2 * N)) / 448 / math.sqrt(K)).astype(np.float32)
+    s2 = (rng.uniform(0.25, 4, (E, K)) / 448 / math.sqrt(N)).astype(np.float32)
+    return s1, s2
+
+
+@pytest.mark.parametrize("M,K,N,E,k", [(6, 64, 32, 8, 2), (4, 128, 16, 5, 3), (3, 32, 64, 2, 2)])
+def test_layer_fp8_rowwise_vs_dense_bruteforce(M, K, N, E, k):
+    """Per-channel weight scales (one per output row of W1 and of W2)."""
+    rng = np.random.default_rng(17 + M + K + N)
+    x, wr, b, w1, w2, _, _ = make_layer(rng, M, K, N, E, fp8=True)
+    s1, s2 = rowwise_scales(rng, E, N, K)
+    out, ids, _ = oracle.moe_forward(x, wr, b, w1, w2, k, w1_scale=s1, w2_scale=s2, fp8=True)
+    ref, rids, _ = dense_layer(x, wr, b, w1, w2, k, fp8=True, w1_scale=s1, w2_scale=s2)
+    assert np.array_equal(ids, rids)
+    assert row_rel_err(out, ref) <= 1e-12
+
+
+def test_layer_fp8_rowwise_equal_rows_is_per_tensor():
+    """Row scales all equal to the expert's tensor scale give the per-tensor
+    result bit for bit."""
+    rng = np.random.default_rng(23)
+    M, K, N, E, k = 7, 64, 48, 6, 2
+    x, wr, b, w1, w2, s1, s2 = make_layer(rng, M, K, N, E, fp8=True)
+    r1 = np.repeat(s1[:, None], 2 * N, axis=1)
+    r2 = np.repeat(s2[:, None], K, axis=1)
+    a, _, _ = oracle.moe_forward(x, wr, b, w1, w2, k, w1_scale=s1, w2_scale=s2, fp8=True)
+    c, _, _ = oracle.moe_forward(x, wr, b, w1, w2, k, w1_scale=r1, w2_scale=r2, fp8=True)
+    assert np.array_equal(a, c)
+
+
+def test_layer_fp8_rowwise_w2_row_scale_hits_its_column():
+    """Doubling the scale of W2 row c (of every expert) doubles output column
+    c exactly and leaves every other column unchanged."""
+    rng = np.random.default_rng(29)
+    M, K, N, E, k = 5, 32, 16, 4, 2
+    x, wr, b, w1, w2, _, _ = make_layer(rng, M, K, N, E, fp8=True)
+    s1, s2 = rowwise_scales(rng, E, N, K)
+    a, _, _ = oracle.moe_forward(x, wr, b, w1, w2, k, w1_scale=s1, w2_scale=s2, fp8=True)
+    c = 11
+    t2 = s2.copy()
+    t2[:, c] *= 2
+    d, _, _ = oracle.moe_forward(x, wr, b, w1, w2, k, w1_scale=s1, w2_scale=t2, fp8=True)
+    assert np.array_equal(d[:, c], 2 * a[:, c])
+    keep = np.arange(K) != c
+    assert np.array_equal(d[:, keep], a[:, keep])
+
+
 def test_dense_swiglu_special_case_page_decode_shape():
     """E=1, k=1: the layer is one dense SwiGLU MLP; shapes of the pages' decode
     example (A 1 x 4096, expert block 4096 x 8192)."""
