@@ -189,6 +189,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--fp8-rowwise", action="store_true",
+                    help="with an e4m3 workload: per-channel weight scales (one per output "
+                         "row) instead of one per expert tensor")
     ap.add_argument("--regime-sweep", action="store_true",
                     help="time the decode and full-tile kernel families (bf16) over batch "
                          "sizes M = 8 .. 1024 at this workload's K, N, E, top-k; one JSON "
@@ -218,6 +221,10 @@ def main():
     if args.workload not in wlm.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; one of {list(wlm.WORKLOADS)}")
     wl = wlm.WORKLOADS[args.workload]
+    if args.fp8_rowwise:
+        if not wl.fp8:
+            sys.exit("--fp8-rowwise needs an e4m3 workload")
+        wl = wl.resized(name=wl.name + "_rowwise", fp8_rowwise=True)
     if not torch.cuda.is_available():
         sys.exit("no GPU visible")
     dev = torch.device("cuda:0")
@@ -330,7 +337,9 @@ def main():
     # ---- algorithmic work and roofline --------------------------------------
     slots = wl.M * wl.topk
     alg_bytes = (touched + wl.M * wl.K * 2 * 2 + wl.E * wl.K * 2
-                 + (wl.E * 4 if wl.bias_var else 0) + (2 * wl.E * 4 if wl.fp8 else 0))
+                 + (wl.E * 4 if wl.bias_var else 0)
+                 + ((wl.E * (2 * wl.N + wl.K) * 4 if wl.fp8_rowwise else 2 * wl.E * 4)
+                    if wl.fp8 else 0))
     alg_flops = 6.0 * slots * wl.N * wl.K
     step_s = ms_per_step / 1e3
     decode = (slots <= DECODE_MAX_ROWS_PER_EXPERT * wl.E) or wl.fp8
@@ -373,7 +382,7 @@ def main():
         "dtype": dtype_name,
         "data": "synthetic (seeded N(0,1/fan_in) weights, random init; no dataset)",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "E": wl.E,
-                   "topk": wl.topk, "weights": "e4m3 per-tensor" if wl.fp8 else "bf16",
+                   "topk": wl.topk, "weights": ("e4m3 per-channel" if wl.fp8_rowwise else "e4m3 per-tensor") if wl.fp8 else "bf16",
                    "router_bias_var": wl.bias_var, "seed": wl.seed, "layers": layers,
                    "active_experts": active},
         "step_hbm_GBps": round(alg_bytes / step_s / 1e9, 1),

@@ -27,6 +27,7 @@ MOE_ERR_HIP = 4
 
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
+MOE_FP8_E4M3_ROWWISE = 2
 
 MOE_REGIME_AUTO = 0
 MOE_REGIME_DECODE = 1
@@ -157,13 +158,23 @@ def moe_quant_rows_e4m3(x: torch.Tensor):
     return q, s
 
 
+def _weight_dtype(w1: torch.Tensor, w1_scale: Optional[torch.Tensor]) -> int:
+    """bf16 weights, or e4m3 codes (uint8) with per-tensor scales [E] or
+    per-channel scales [E,2N] (MOE_FP8_E4M3_ROWWISE)."""
+    if w1.dtype != torch.uint8:
+        return MOE_BF16
+    if w1_scale is not None and w1_scale.dim() == 2:
+        return MOE_FP8_E4M3_ROWWISE
+    return MOE_FP8_E4M3
+
+
 def workspace_size(dtype: int, M: int, K: int, N: int, E: int, topk: int,
                    regime: int = MOE_REGIME_AUTO) -> int:
     """Bytes of workspace moe_fused_forward needs (no GPU call is made)."""
     lib = load_library()
     nbytes = ctypes.c_size_t(0)
     dummy = ctypes.c_void_p(0x100)
-    s1 = dummy if dtype == MOE_FP8_E4M3 else None
+    s1 = dummy if dtype in (MOE_FP8_E4M3, MOE_FP8_E4M3_ROWWISE) else None
     _check(lib.moe_fused_forward_ex(dummy, dummy, None, dummy, dummy, s1, s1, dtype, M, K, N, E,
                                     topk, regime, dummy, None, ctypes.byref(nbytes), None),
            "workspace query")
@@ -178,12 +189,13 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
                       workspace: Optional[torch.Tensor] = None) -> torch.Tensor:
     """The whole layer; returns out bf16 [M,K].
 
-    w1 [E,2N,K] / w2 [E,K,N] are bf16, or uint8 e4m3 codes with fp32 per-expert
-    w1_scale / w2_scale.  ``workspace`` (uint8, at least workspace_size bytes)
+    w1 [E,2N,K] / w2 [E,K,N] are bf16, or uint8 e4m3 codes with fp32 scales:
+    per expert (w1_scale, w2_scale [E]) or per output row (w1_scale [E,2N],
+    w2_scale [E,K]).  ``workspace`` (uint8, at least workspace_size bytes)
     may be passed to avoid an allocation per call."""
     lib = load_library()
     fp8 = w1.dtype == torch.uint8
-    dtype = MOE_FP8_E4M3 if fp8 else MOE_BF16
+    dtype = _weight_dtype(w1, w1_scale)
     M, K = x.shape
     E, twoN, K1 = w1.shape
     N = twoN // 2
@@ -194,7 +206,10 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
     wdt = torch.uint8 if fp8 else torch.bfloat16
     _dev(w1, "w1", wdt, (E, 2 * N, K))
     _dev(w2, "w2", wdt, (E, K, N))
-    if fp8:
+    if dtype == MOE_FP8_E4M3_ROWWISE:
+        _dev(w1_scale, "w1_scale", torch.float32, (E, 2 * N))
+        _dev(w2_scale, "w2_scale", torch.float32, (E, K))
+    elif fp8:
         _dev(w1_scale, "w1_scale", torch.float32, (E,))
         _dev(w2_scale, "w2_scale", torch.float32, (E,))
     elif w1_scale is not None or w2_scale is not None:
@@ -232,11 +247,9 @@ class FusedForwardGraph:
                  topk: int, *, w1_scale: Optional[torch.Tensor] = None,
                  w2_scale: Optional[torch.Tensor] = None, regime: int = MOE_REGIME_AUTO):
         dev = x.device
-        fp8 = w1.dtype == torch.uint8
         M, K = x.shape
         E, twoN, _ = w1.shape
-        need = workspace_size(MOE_FP8_E4M3 if fp8 else MOE_BF16, M, K, twoN // 2, E, topk,
-                              regime)
+        need = workspace_size(_weight_dtype(w1, w1_scale), M, K, twoN // 2, E, topk, regime)
         self.out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
         self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
         args = (x, w_router, router_bias, w1, w2, topk)

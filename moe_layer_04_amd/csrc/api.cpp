@@ -55,11 +55,13 @@ struct Plan {
     size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
 };
 
+bool is_fp8(int dtype) { return dtype == MOE_FP8_E4M3 || dtype == MOE_FP8_E4M3_ROWWISE; }
+
 Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     Plan p;
     const long slots = (long)M * topk;
     if (regime == MOE_REGIME_AUTO)
-        regime = (dtype == MOE_FP8_E4M3 || slots <= (long)kDecodeMaxRowsPerExpert * E)
+        regime = (is_fp8(dtype) || slots <= (long)kDecodeMaxRowsPerExpert * E)
                      ? MOE_REGIME_DECODE
                      : MOE_REGIME_PREFILL;
     p.regime = regime;
@@ -93,7 +95,7 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     p.bexp = take((size_t)p.max_blocks * 4);
     p.offs = take((size_t)(E + 1) * 4);
     p.npad = take(4);
-    if (dtype == MOE_FP8_E4M3) {
+    if (is_fp8(dtype)) {
         p.xq = take((size_t)M * K);
         p.xs = take((size_t)M * 4);
         p.amax = take((size_t)p.cap * 4);
@@ -182,14 +184,14 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                              size_t* workspace_bytes, void* stream, void* const* events,
                              bool timed) {
     if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
-    if (dtype != MOE_BF16 && dtype != MOE_FP8_E4M3) return MOE_ERR_INVALID_ARG;
+    if (dtype != MOE_BF16 && !is_fp8(dtype)) return MOE_ERR_INVALID_ARG;
     if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_PREFILL) return MOE_ERR_INVALID_ARG;
     if (M < 0 || K < 1 || N < 1 || E < 1 || topk < 1 || topk > E) return MOE_ERR_INVALID_ARG;
     if (dtype == MOE_BF16 && (w1_scale || w2_scale)) return MOE_ERR_INVALID_ARG;
-    if (dtype == MOE_FP8_E4M3 && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (is_fp8(dtype) && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
     if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
-    if (dtype == MOE_FP8_E4M3 && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
+    if (is_fp8(dtype) && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
     const long kn = K > N ? K : N;
     // 32-bit buffer offsets: the sorted activation rows in fp32, the tokens
@@ -229,7 +231,9 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         if (timed) (void)hipEventRecord((hipEvent_t)events[i], s);
     };
 
-    const bool fp8 = dtype == MOE_FP8_E4M3;
+    const bool fp8 = is_fp8(dtype);
+    // per-channel scales: row r of expert e's W1 / W2 reads its own scale
+    const int rowwise = dtype == MOE_FP8_E4M3_ROWWISE ? 1 : 0;
     uint8_t* xq = fp8 ? (uint8_t*)(ws + p.xq) : nullptr;
     float* xs = fp8 ? (float*)(ws + p.xs) : nullptr;
     // FP8: GEMM1's epilogue folds each row's |act| max into amax, which the
@@ -259,13 +263,13 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         float* act = (float*)(ws + p.act);
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
-        moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, sorted, bexp, npad, M, topk, nslots,
-                                     K, N, p.grid_blocks, act, amax, s);
+        moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M, topk,
+                                     nslots, K, N, p.grid_blocks, act, amax, s);
         mark(4);
         moe::launch_act_quant(act, amax, sorted, npad, nslots, N, p.cap, actq, as, s);
         mark(5);
-        moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, wts, sorted, bexp, npad, p.cap,
-                                     nslots, K, N, p.nsplit, p.grid_blocks, ypart, s);
+        moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp, npad,
+                                     p.cap, nslots, K, N, p.nsplit, p.grid_blocks, ypart, s);
         mark(6);
     } else {
         void* act = ws + p.act;

@@ -218,7 +218,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
-    const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale,
+    const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale, int rowwise,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     float* __restrict__ act, uint32_t* __restrict__ amax) {
@@ -268,11 +268,20 @@ __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
 
     float m = 0.0f;
     if (valid) {
-        const float sc = xscale[t] * w1_scale[e];
+        // accumulator element v is gate row n0 + 4*kq + v (and that up row)
+        const float sx = xscale[t];
         f32x4_t o;
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-            o[v] = silu(accg[v] * sc) * (accu[v] * sc);
+            float sg, su;
+            if (rowwise) {
+                const float* sr = w1_scale + (size_t)e * 2 * N + n0 + 4 * kq + v;
+                sg = sx * sr[0];
+                su = sx * sr[N];
+            } else {
+                sg = su = sx * w1_scale[e];
+            }
+            o[v] = silu(accg[v] * sg) * (accu[v] * su);
             m = fmaxf(m, fabsf(o[v]));
         }
         *reinterpret_cast<f32x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 4 * kq) = o;
@@ -319,7 +328,7 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
 
 __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
-    const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale,
+    const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale, int rowwise,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
@@ -371,10 +380,21 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     pin(acc1);
 
     if (valid) {
-        const float w = topk_w[p] * ascale[r] * w2_scale[e];
+        const float w = topk_w[p] * ascale[r];
         float* yr = ypart + ((size_t)z * nslots + p) * K + c0 + 4 * kq;
-        *reinterpret_cast<f32x4_t*>(yr) = acc0 * w;
-        *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * w;
+        if (rowwise) {
+            // accumulator element v of acc0 / acc1 is output column
+            // c0 + 4*kq + v / c0 + 16 + 4*kq + v
+            const float* sr = w2_scale + (size_t)e * K + c0 + 4 * kq;
+            const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sr);
+            const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sr + 16);
+            *reinterpret_cast<f32x4_t*>(yr) = acc0 * (s0 * w);
+            *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * (s1 * w);
+        } else {
+            const float ws = w * w2_scale[e];
+            *reinterpret_cast<f32x4_t*>(yr) = acc0 * ws;
+            *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * ws;
+        }
     }
 }
 
@@ -402,13 +422,13 @@ void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk
 }
 
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
-                             const float* w1_scale, const int32_t* sorted_ids,
+                             const float* w1_scale, int rowwise, const int32_t* sorted_ids,
                              const int32_t* block_expert, const int32_t* num_padded, int M,
                              int topk, int nslots, int K, int N, int max_blocks, float* act,
                              uint32_t* amax, hipStream_t s) {
     dim3 grid(N / 64, max_blocks);
     gemm1_decode_fp8_kernel<<<grid, 256, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale,
-                                                 sorted_ids, block_expert, num_padded, M, topk,
+                                                 rowwise, sorted_ids, block_expert, num_padded, M, topk,
                                                  nslots, K, N, act, amax);
 }
 
@@ -420,13 +440,13 @@ void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sor
 }
 
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
-                             const float* w2_scale, const float* topk_w,
+                             const float* w2_scale, int rowwise, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,
                              const int32_t* num_padded, int cap, int nslots, int K, int N,
                              int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     dim3 grid(K / 128, max_blocks, nsplit);
     gemm2_decode_fp8_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale,
-                                                 topk_w, sorted_ids, block_expert, num_padded,
+                                                 rowwise, topk_w, sorted_ids, block_expert, num_padded,
                                                  cap, nslots, K, N, nsplit, ypart);
 }
 

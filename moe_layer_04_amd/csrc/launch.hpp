@@ -49,8 +49,9 @@ void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
                               int nsplit, int max_blocks, float* ypart, hipStream_t s);
+// rowwise: w1_scale [E,2N] / w2_scale [E,K] (one per output row) instead of [E]
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
-                             const float* w1_scale, const int32_t* sorted_ids,
+                             const float* w1_scale, int rowwise, const int32_t* sorted_ids,
                              const int32_t* block_expert, const int32_t* num_padded, int M,
                              int topk, int nslots, int K, int N, int max_blocks, float* act,
                              uint32_t* amax, hipStream_t s);
@@ -58,7 +59,7 @@ void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sor
                       const int32_t* num_padded, int nslots, int N, int cap, uint8_t* act_q,
                       float* ascale, hipStream_t s);
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
-                             const float* w2_scale, const float* topk_w,
+                             const float* w2_scale, int rowwise, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,
                              const int32_t* num_padded, int cap, int nslots, int K, int N,
                              int nsplit, int max_blocks, float* ypart, hipStream_t s);

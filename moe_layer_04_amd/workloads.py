@@ -15,9 +15,9 @@ it produces.  Recipe (one ``torch.Generator`` per workload, seeded with
 
 The variances are fan-in variances (N(0, 1/fan_in) gives unit-variance
 logits and pre-activations).  For e4m3 workloads each expert tensor is
-stored per-tensor quantised, the way an FP8 "tensor-quantized" checkpoint
-arrives: scale = amax/448 in fp32, codes = torch's float8_e4m3fn cast of
-W/scale clamped to +-448.  That offline weight preparation is input
+stored per-tensor quantised, the way an FP8 per-tensor checkpoint arrives:
+scale = amax/448 in fp32, codes = torch's float8_e4m3fn cast of W/scale
+clamped to +-448 (with fp8_rowwise: the same per output row).  That offline weight preparation is input
 generation, not a step of the layer; the activations are quantised by the
 layer itself at run time.
 
@@ -43,6 +43,7 @@ class Workload:
     E: int
     topk: int
     fp8: bool = False
+    fp8_rowwise: bool = False   # e4m3 scales per output row instead of per tensor
     bias_var: Optional[float] = None
     seed: int = 0
 
@@ -68,11 +69,18 @@ WORKLOADS = {
 }
 
 
-def _quant_tensor(w32: torch.Tensor):
-    amax = w32.abs().max().to(torch.float32)
-    scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
-    q = (w32 / scale).clamp(-448.0, 448.0).to(torch.float8_e4m3fn).view(torch.uint8)
-    return q, scale
+def _quant_tensor(w32: torch.Tensor, rowwise: bool = False):
+    """e4m3 codes and fp32 scale(s) amax/448: one for the tensor, or one per
+    row (output channel) with ``rowwise``."""
+    if rowwise:
+        amax = w32.abs().amax(dim=1).to(torch.float32)
+        scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (w32 / scale[:, None]).clamp(-448.0, 448.0)
+    else:
+        amax = w32.abs().max().to(torch.float32)
+        scale = torch.where(amax > 0, amax / 448.0, torch.ones_like(amax))
+        q = (w32 / scale).clamp(-448.0, 448.0)
+    return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
 
 
 def generate(wl: Workload, device="cpu") -> dict:
@@ -80,7 +88,8 @@ def generate(wl: Workload, device="cpu") -> dict:
 
     Returns a dict with x [M,K] bf16, w_router [E,K] bf16, bias [E] fp32 or
     None, w1 [E,2N,K] and w2 [E,K,N] (bf16, or uint8 e4m3 codes), and
-    w1_scale / w2_scale [E] fp32 (None for bf16)."""
+    w1_scale / w2_scale fp32: [E] per tensor, or [E,2N] / [E,K] per output
+    row with ``fp8_rowwise`` (None for bf16)."""
     device = torch.device(device)
     g = torch.Generator(device=device)
     g.manual_seed(wl.seed)
@@ -96,19 +105,21 @@ def generate(wl: Workload, device="cpu") -> dict:
     wdt = torch.uint8 if wl.fp8 else torch.bfloat16
     w1 = torch.empty((E, 2 * N, K), dtype=wdt, device=device)
     w2 = torch.empty((E, K, N), dtype=wdt, device=device)
-    w1_scale = torch.empty(E, dtype=torch.float32, device=device) if wl.fp8 else None
-    w2_scale = torch.empty(E, dtype=torch.float32, device=device) if wl.fp8 else None
+    s1_shape = (E, 2 * N) if wl.fp8_rowwise else (E,)
+    s2_shape = (E, K) if wl.fp8_rowwise else (E,)
+    w1_scale = torch.empty(s1_shape, dtype=torch.float32, device=device) if wl.fp8 else None
+    w2_scale = torch.empty(s2_shape, dtype=torch.float32, device=device) if wl.fp8 else None
     for e in range(E):
         w = normal((2 * N, K), 1.0 / K)
         if wl.fp8:
-            w1[e], w1_scale[e] = _quant_tensor(w)
+            w1[e], w1_scale[e] = _quant_tensor(w, wl.fp8_rowwise)
         else:
             w1[e] = w.to(torch.bfloat16)
         del w
     for e in range(E):
         w = normal((K, N), 1.0 / N)
         if wl.fp8:
-            w2[e], w2_scale[e] = _quant_tensor(w)
+            w2[e], w2_scale[e] = _quant_tensor(w, wl.fp8_rowwise)
         else:
             w2[e] = w.to(torch.bfloat16)
         del w

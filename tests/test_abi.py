@@ -82,7 +82,10 @@ def fused(lib, *, x=FAKE, wr=FAKE, bias=None, w1=FAKE, w2=FAKE, s1=None, s2=None
 
 def test_fused_validation(lib):
     INV, UNS, WSP = B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE
-    assert fused(lib, dtype=2)[0] == INV
+    assert fused(lib, dtype=3)[0] == INV
+    assert fused(lib, dtype=2)[0] == INV                              # rowwise fp8 without scales
+    assert fused(lib, dtype=2, s1=FAKE, s2=None)[0] == INV
+    assert fused(lib, dtype=2, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
     assert fused(lib, regime=3)[0] == INV
     assert fused(lib, M=-1)[0] == INV
     assert fused(lib, N=0)[0] == INV
@@ -114,8 +117,10 @@ def test_workspace_query_sizes(lib):
     s_pre = moe.workspace_size(moe.MOE_BF16, 4096, 4096, 14336, 8, 2)
     s_fp8 = moe.workspace_size(moe.MOE_FP8_E4M3, 128, 7168, 2048, 256, 8)
     assert 0 < s_dec < s_pre
-    # prefill: the bf16 SiLU*up activation [M*k + E*127, N] dominates
-    assert s_pre >= (4096 * 2 + 8 * 127) * 14336 * 2
+    # prefill: the bf16 SiLU*up activation [M*k + E*255, N] dominates
+    assert s_pre >= (4096 * 2 + 8 * 255) * 14336 * 2
     # fp8: fp32 + e4m3 activations of [M*k + E*15, N]
     assert s_fp8 >= (128 * 8 + 256 * 15) * 2048 * 5
     assert moe.workspace_size(moe.MOE_BF16, 8, 4096, 14336, 8, 2, moe.MOE_REGIME_PREFILL) > s_dec
+    # per-channel scales change no workspace region
+    assert moe.workspace_size(moe.MOE_FP8_E4M3_ROWWISE, 128, 7168, 2048, 256, 8) == s_fp8

@@ -222,6 +222,10 @@ SMALL = [
     ("fp8_tiny", 16, 512, 256, 16, 4, True, None, 0),
     ("fp8_ragged", 7, 384, 640, 32, 8, True, None, 0),
     ("fp8_many_rows", 300, 256, 384, 8, 2, True, None, 0),
+    # e4m3 weights with per-channel scales (one per output row)
+    ("fp8_rowwise_tiny", 16, 512, 256, 16, 4, "rowwise", None, 0),
+    ("fp8_rowwise_ragged", 7, 384, 640, 32, 8, "rowwise", None, 0),
+    ("fp8_rowwise_many_rows", 300, 256, 384, 8, 2, "rowwise", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
 ]
 
@@ -230,7 +234,10 @@ SMALL = [
 def test_fused_small(moe, case):
     name, M, K, N, E, k, fp8, bias_var, regime = case
     note(f"fused small {case}")
-    wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, bias_var=bias_var, seed=3)
+    rowwise = fp8 == "rowwise"
+    fp8 = bool(fp8)
+    wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, fp8_rowwise=rowwise,
+                      bias_var=bias_var, seed=3)
     d, g = gen_small(wl)
     out = run_layer(moe, g, wl, regime)
     ref, _, _ = oracle_layer(d, wl)
@@ -291,9 +298,13 @@ def sample_tokens(M, n=6):
     return [0] + mid + [M - 1]
 
 
-@pytest.mark.parametrize("name", list(wlm.WORKLOADS))
+# the DeepSeek-shaped batch also with per-channel e4m3 weight scales
+@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise"])
 def test_fused_full_size_sampled(moe, name):
-    wl = wlm.WORKLOADS[name]
+    if name == "dsv3_fp8_rowwise":
+        wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, fp8_rowwise=True)
+    else:
+        wl = wlm.WORKLOADS[name]
     note(f"full size {name}: generate on GPU")
     g = wlm.generate(wl, "cuda")
     out = run_layer(moe, g, wl, poison=False)
