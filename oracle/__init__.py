@@ -33,6 +33,7 @@ ORC_ERR_NOMEM = 3
 BF16 = 0
 FP8_E4M3 = 1            # per-tensor weight scales [E]
 FP8_E4M3_ROWWISE = 2    # per-channel weight scales [E,2N] / [E,K]
+MXFP4 = 3               # e2m1 weights, E8M0 scale per 32 elements of a row
 
 
 def build() -> str:
@@ -59,6 +60,10 @@ def _load():
         lib.orc_bf16_to_f64.restype = ctypes.c_double
         lib.orc_e4m3_to_f64.argtypes = [ctypes.c_uint8]
         lib.orc_e4m3_to_f64.restype = ctypes.c_double
+        lib.orc_e2m1_to_f64.argtypes = [ctypes.c_uint8]
+        lib.orc_e2m1_to_f64.restype = ctypes.c_double
+        lib.orc_e8m0_to_f64.argtypes = [ctypes.c_uint8]
+        lib.orc_e8m0_to_f64.restype = ctypes.c_double
         lib.orc_f32_to_e4m3.argtypes = [ctypes.c_float]
         lib.orc_f32_to_e4m3.restype = ctypes.c_uint8
         lib.orc_logits.argtypes = [P, P, P, I64, I64, I64, P]
@@ -199,14 +204,30 @@ def quant_rows_f32(v):
     return q, s
 
 
+def e2m1_to_f64(codes) -> np.ndarray:
+    """The oracle's e2m1 decoding of 4-bit codes (R9)."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_e2m1_to_f64(int(v)) for v in c.reshape(-1)]).reshape(c.shape)
+
+
+def e8m0_to_f64(codes) -> np.ndarray:
+    """The oracle's E8M0 scale decoding (R9)."""
+    lib = _load()
+    c = np.asarray(codes, dtype=np.uint8)
+    return np.array([lib.orc_e8m0_to_f64(int(v)) for v in c.reshape(-1)]).reshape(c.shape)
+
+
 def moe_forward(x, w_router, bias, w1, w2, k, *, w1_scale=None, w2_scale=None,
-                tokens=None, fp8=False):
+                tokens=None, fp8=False, mxfp4=False):
     """The whole layer in fp64 for the given tokens (default: all).
 
     ``w1`` / ``w2`` are either full arrays [E,2N,K] / [E,K,N] or sequences of
     per-expert arrays (None where an expert's weights are not provided; the
     oracle fails if a routed expert is missing).  With ``fp8`` the scales are
-    per expert tensor ([E]) or per output channel ([E,2N] and [E,K]).
+    per expert tensor ([E]) or per output channel ([E,2N] and [E,K]).  With
+    ``mxfp4`` the weights are packed e2m1 (w1[e] [2N,K/2], w2[e] [K,N/2]) and
+    the scales E8M0 bytes (w1_scale [E,2N,K/32], w2_scale [E,K,N/32]).
     Returns (out float64 [n_tok,K], ids int32 [n_tok,k], weights float64
     [n_tok,k]).
     """
@@ -215,7 +236,7 @@ def moe_forward(x, w_router, bias, w1, w2, k, *, w1_scale=None, w2_scale=None,
     wr = _c(w_router, np.uint16)
     M, K = x.shape
     E = wr.shape[0]
-    wdt = np.uint8 if fp8 else np.uint16
+    wdt = np.uint8 if (fp8 or mxfp4) else np.uint16
     w1_list = [None if w is None else _c(w, wdt) for w in w1]
     w2_list = [None if w is None else _c(w, wdt) for w in w2]
     assert len(w1_list) == E and len(w2_list) == E
@@ -223,21 +244,29 @@ def moe_forward(x, w_router, bias, w1, w2, k, *, w1_scale=None, w2_scale=None,
     for a, b in zip(w1_list, w2_list):
         if a is not None:
             N = a.shape[0] // 2
-            assert a.shape == (2 * N, K) and b.shape == (K, N)
+            if mxfp4:
+                assert a.shape == (2 * N, K // 2) and b.shape == (K, N // 2)
+            else:
+                assert a.shape == (2 * N, K) and b.shape == (K, N)
     if N is None:
         raise ValueError("no expert weights given")
     arr1 = (ctypes.c_void_p * E)(*[None if a is None else a.ctypes.data for a in w1_list])
     arr2 = (ctypes.c_void_p * E)(*[None if a is None else a.ctypes.data for a in w2_list])
     b = None if bias is None else _c(bias, np.float32)
-    s1 = None if w1_scale is None else _c(w1_scale, np.float32)
-    s2 = None if w2_scale is None else _c(w2_scale, np.float32)
+    sdt = np.uint8 if mxfp4 else np.float32
+    s1 = None if w1_scale is None else _c(w1_scale, sdt)
+    s2 = None if w2_scale is None else _c(w2_scale, sdt)
     toks = np.arange(M, dtype=np.int64) if tokens is None else _c(tokens, np.int64)
     n_tok = toks.shape[0]
     out = np.empty((n_tok, K), np.float64)
     ids = np.empty((n_tok, k), np.int32)
     wts = np.empty((n_tok, k), np.float64)
     dtype = BF16
-    if fp8:
+    if mxfp4:
+        assert s1 is not None and s1.shape == (E, 2 * N, K // 32)
+        assert s2 is not None and s2.shape == (E, K, N // 32)
+        dtype = MXFP4
+    elif fp8:
         dtype = FP8_E4M3
         if s1 is not None and s1.ndim == 2:
             assert s1.shape == (E, 2 * N) and s2 is not None and s2.shape == (E, K)

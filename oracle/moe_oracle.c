@@ -56,6 +56,12 @@
  *      per-channel weight scales: one fp32 scale per output row of each
  *      expert's W1 (2N rows, gate then up) and W2 (K rows), multiplying that
  *      row's dot products where R7 multiplies by the tensor's scale.
+ *   R9 (also beyond the pages) MXFP4 weights, OCP microscaling: e2m1
+ *      elements (sign, 2 exponent bits with bias 1, 1 mantissa bit; exponent
+ *      0 is subnormal: 0 or 0.5) packed two per byte, the even element of a
+ *      row in the low nibble, and one E8M0 scale 2^(e-127) (e = 255: NaN) per
+ *      32 consecutive elements of a row along the reduction dimension; a
+ *      weight is its element times its block's scale.  Activations as R7.
  */
 #include <math.h>
 #include <stdint.h>
@@ -356,6 +362,57 @@ static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, const flo
     }
 }
 
+/* e2m1 code (low 4 bits) -> value, from the format's definition (R9). */
+double orc_e2m1_to_f64(uint8_t c)
+{
+    int sgn = (c >> 3) & 1, ex = (c >> 1) & 3, man = c & 1;
+    double v = ex == 0 ? 0.5 * man : ldexp(1.0 + 0.5 * man, ex - 1);
+    return sgn ? -v : v;
+}
+
+/* E8M0 scale byte -> 2^(e-127); 255 is NaN (R9). */
+double orc_e8m0_to_f64(uint8_t e)
+{
+    return e == 255 ? NAN : ldexp(1.0, (int)e - 127);
+}
+
+/* Weight r,k of an MXFP4 matrix with `cols` elements per row (R9). */
+static double mx_weight(const uint8_t *w, const uint8_t *sc, int64_t cols, int64_t r, int64_t k)
+{
+    uint8_t byte = w[r * (cols / 2) + k / 2];
+    uint8_t code = (k & 1) ? (uint8_t)(byte >> 4) : (uint8_t)(byte & 15);
+    return orc_e2m1_to_f64(code) * orc_e8m0_to_f64(sc[r * (cols / 32) + k / 32]);
+}
+
+/* One token-slot, MXFP4 weights (R9): w1 [2N, K/2] packed with scales
+ * s1 [2N, K/32], w2 [K, N/2] with s2 [K, N/32]. */
+static void expert_mxfp4(const uint8_t *xq, float sx, const uint8_t *w1, const uint8_t *s1,
+                         const uint8_t *w2, const uint8_t *s2, int64_t K, int64_t N,
+                         double *act, float *act32, uint8_t *aq, double *y)
+{
+    int64_t n, c, kk;
+    float sa;
+    for (n = 0; n < N; ++n) {
+        double hg = 0.0, hu = 0.0;
+        for (kk = 0; kk < K; ++kk) {
+            double xv = e4m3_table[xq[kk]];
+            hg += mx_weight(w1, s1, K, n, kk) * xv;
+            hu += mx_weight(w1, s1, K, N + n, kk) * xv;
+        }
+        hg *= (double)sx;
+        hu *= (double)sx;
+        act[n] = silu(hg) * hu;
+        act32[n] = (float)act[n];
+    }
+    quant_row_f32(act32, N, aq, &sa);
+    for (c = 0; c < K; ++c) {
+        double acc = 0.0;
+        for (n = 0; n < N; ++n)
+            acc += mx_weight(w2, s2, N, c, n) * e4m3_table[aq[n]];
+        y[c] = acc * (double)sa;
+    }
+}
+
 /* Per-token dynamic quantisation of bf16 rows (R7): xq [M,K], sx [M]. */
 int orc_quant_rows_bf16(const uint16_t *x, int64_t M, int64_t K, uint8_t *xq, float *sx)
 {
@@ -390,9 +447,11 @@ int orc_quant_rows_f32(const float *v, int64_t M, int64_t K, uint8_t *q, float *
 /*
  * The whole layer for a list of tokens.
  *
- *   dtype     0 = bf16 weights, 1 = e4m3 weights with w1s/w2s [E] (one
- *             scale per expert tensor), 2 = e4m3 weights with per-channel
- *             scales w1s [E,2N], w2s [E,K] (R8)
+ *   dtype     0 = bf16 weights, 1 = e4m3 weights with fp32 w1s/w2s [E] (one
+ *             scale per expert tensor), 2 = e4m3 weights with fp32
+ *             per-channel scales w1s [E,2N], w2s [E,K] (R8), 3 = MXFP4
+ *             weights (w1[e] [2N,K/2], w2[e] [K,N/2] packed) with E8M0 byte
+ *             scales w1s [E,2N,K/32], w2s [E,K,N/32] (R9)
  *   x         bf16 [M,K] (all tokens: routing of token t reads row t only)
  *   wr        bf16 [E,K]; bias fp32 [E] or NULL
  *   w1[e]     expert e's W1 [2N,K] (bf16 or e4m3), NULL if not provided
@@ -408,7 +467,7 @@ int orc_quant_rows_f32(const float *v, int64_t M, int64_t K, uint8_t *q, float *
  */
 int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const float *bias,
                     const void *const *w1, const void *const *w2,
-                    const float *w1s, const float *w2s,
+                    const void *w1s, const void *w2s,
                     int64_t M, int64_t K, int64_t N, int64_t E, int64_t k,
                     const int64_t *tokens, int64_t n_tok,
                     double *out, int32_t *ids_out, double *wts_out)
@@ -418,9 +477,10 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
     double *wts, *y;
     float *lg;
     int rc = ORC_OK;
-    if (dtype < 0 || dtype > 2 || M < 0 || K <= 0 || N <= 0 || E <= 0 ||
+    if (dtype < 0 || dtype > 3 || M < 0 || K <= 0 || N <= 0 || E <= 0 ||
         k < 1 || k > E || n_tok < 0 || !x || !wr || !w1 || !w2 || !out ||
-        (n_tok > 0 && !tokens) || (dtype != 0 && (!w1s || !w2s)))
+        (n_tok > 0 && !tokens) || (dtype != 0 && (!w1s || !w2s)) ||
+        (dtype == 3 && (K % 32 || N % 32)))
         return ORC_ERR_ARG;
     for (i = 0; i < n_tok; ++i)
         if (tokens[i] < 0 || tokens[i] >= M)
@@ -472,13 +532,20 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
                     xrow[kk] = bf16_to_f32(xt[kk]);
                 quant_row_f32(xrow, K, xq, &sx);
                 if (dtype == 1)
-                    expert_fp8(xq, sx, (const uint8_t *)w1[e], w1s + e,
-                               (const uint8_t *)w2[e], w2s + e, 0, K, N, act, act32, aq,
+                    expert_fp8(xq, sx, (const uint8_t *)w1[e], (const float *)w1s + e,
+                               (const uint8_t *)w2[e], (const float *)w2s + e, 0, K, N,
+                               act, act32, aq, y + s * K);
+                else if (dtype == 2)
+                    expert_fp8(xq, sx, (const uint8_t *)w1[e],
+                               (const float *)w1s + e * 2 * N, (const uint8_t *)w2[e],
+                               (const float *)w2s + e * K, 1, K, N, act, act32, aq,
                                y + s * K);
                 else
-                    expert_fp8(xq, sx, (const uint8_t *)w1[e], w1s + e * 2 * N,
-                               (const uint8_t *)w2[e], w2s + e * K, 1, K, N, act, act32,
-                               aq, y + s * K);
+                    expert_mxfp4(xq, sx, (const uint8_t *)w1[e],
+                                 (const uint8_t *)w1s + e * 2 * N * (K / 32),
+                                 (const uint8_t *)w2[e],
+                                 (const uint8_t *)w2s + e * K * (N / 32), K, N, act, act32,
+                                 aq, y + s * K);
             }
         }
         free(act);

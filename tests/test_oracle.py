@@ -15,7 +15,9 @@ import torch
 
 import oracle
 from tests._brute import (bf16_bits_to_f64, dense_layer, e4m3_codes_to_f64,
-                          f32_to_e4m3_codes, row_rel_err)
+                          f32_to_e4m3_codes, row_rel_err,
+                          e2m1_as_e4m3_code, mx_dequant)
+from tests._brute import e8m0_to_f64 as mx_e8m0_to_f64
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "pages_values.json")
 
@@ -320,6 +322,87 @@ def test_layer_fp8_rowwise_w2_row_scale_hits_its_column():
     t2 = s2.copy()
     t2[:, c] *= 2
     d, _, _ = oracle.moe_forward(x, wr, b, w1, w2, k, w1_scale=s1, w2_scale=t2, fp8=True)
+    assert np.array_equal(d[:, c], 2 * a[:, c])
+    keep = np.arange(K) != c
+    assert np.array_equal(d[:, keep], a[:, keep])
+
+
+# --------------------------------------------------------------------------
+# MXFP4 weights (e2m1 elements, E8M0 scale per 32 elements of a row)
+# --------------------------------------------------------------------------
+
+def test_e2m1_decode_matches_e4m3_codec():
+    """Each of the 16 e2m1 codes decodes to the value of the e4m3 code with
+    the same sign, exponent and mantissa (torch's e4m3 codec); the magnitudes
+    are 8 distinct values up to 6, negatives mirror them."""
+    c = np.arange(16, dtype=np.uint8)
+    got = oracle.e2m1_to_f64(c)
+    ref = e4m3_codes_to_f64(e2m1_as_e4m3_code(c))
+    assert np.array_equal(got, ref)
+    assert len(set(np.abs(got[:8]).tolist())) == 8 and np.abs(got).max() == 6.0
+    assert np.array_equal(got[8:], -got[:8])
+
+
+def test_e8m0_decode_matches_torch():
+    c = np.arange(255, dtype=np.uint8)
+    assert np.array_equal(oracle.e8m0_to_f64(c), mx_e8m0_to_f64(c))
+    assert np.isnan(oracle.e8m0_to_f64([255])[0])
+
+
+def make_mx_layer(rng, M, K, N, E, scale_lo=117, scale_hi=124):
+    x = rand_bf16(rng, (M, K))
+    wr = rand_bf16(rng, (E, K), 1 / math.sqrt(K))
+    w1 = rng.integers(0, 256, (E, 2 * N, K // 2)).astype(np.uint8)
+    w2 = rng.integers(0, 256, (E, K, N // 2)).astype(np.uint8)
+    s1 = rng.integers(scale_lo, scale_hi, (E, 2 * N, K // 32)).astype(np.uint8)
+    s2 = rng.integers(scale_lo, scale_hi, (E, K, N // 32)).astype(np.uint8)
+    return x, wr, w1, w2, s1, s2
+
+
+@pytest.mark.parametrize("M,K,N,E,k", [(6, 64, 32, 8, 2), (4, 128, 64, 5, 3), (3, 32, 96, 2, 2)])
+def test_layer_mxfp4_vs_dense_bruteforce(M, K, N, E, k):
+    rng = np.random.default_rng(31 + M + K + N)
+    x, wr, w1, w2, s1, s2 = make_mx_layer(rng, M, K, N, E)
+    out, ids, _ = oracle.moe_forward(x, wr, None, w1, w2, k, w1_scale=s1, w2_scale=s2,
+                                     mxfp4=True)
+    W1 = np.stack([mx_dequant(w1[e], s1[e]) for e in range(E)])
+    W2 = np.stack([mx_dequant(w2[e], s2[e]) for e in range(E)])
+    ref, rids, _ = dense_layer(x, wr, None, None, None, k, fp8=True, w_f64=(W1, W2))
+    assert np.array_equal(ids, rids)
+    assert row_rel_err(out, ref) <= 1e-12
+
+
+def test_layer_mxfp4_unit_scales_equals_fp8_per_tensor():
+    """With every block scale 1 (E8M0 127) the MXFP4 layer is the e4m3 layer
+    with per-tensor scale 1 on the same weight values, bit for bit."""
+    rng = np.random.default_rng(37)
+    M, K, N, E, k = 7, 64, 64, 6, 2
+    x, wr, w1, w2, s1, s2 = make_mx_layer(rng, M, K, N, E, 127, 128)
+    a, _, _ = oracle.moe_forward(x, wr, None, w1, w2, k, w1_scale=s1, w2_scale=s2, mxfp4=True)
+
+    def unpack_as_e4m3(p):
+        c = np.empty(p.shape[:-1] + (2 * p.shape[-1],), np.uint8)
+        c[..., 0::2] = p & 15
+        c[..., 1::2] = p >> 4
+        return e2m1_as_e4m3_code(c)
+
+    ones = np.ones(E, np.float32)
+    b, _, _ = oracle.moe_forward(x, wr, None, unpack_as_e4m3(w1), unpack_as_e4m3(w2), k,
+                                 w1_scale=ones, w2_scale=ones, fp8=True)
+    assert np.array_equal(a, b)
+
+
+def test_layer_mxfp4_w2_row_scales_hit_their_column():
+    """One more E8M0 step on every block of W2 row c doubles output column c
+    exactly and leaves every other column unchanged."""
+    rng = np.random.default_rng(41)
+    M, K, N, E, k = 5, 64, 64, 4, 2
+    x, wr, w1, w2, s1, s2 = make_mx_layer(rng, M, K, N, E)
+    a, _, _ = oracle.moe_forward(x, wr, None, w1, w2, k, w1_scale=s1, w2_scale=s2, mxfp4=True)
+    c = 13
+    t2 = s2.copy()
+    t2[:, c, :] += 1
+    d, _, _ = oracle.moe_forward(x, wr, None, w1, w2, k, w1_scale=s1, w2_scale=t2, mxfp4=True)
     assert np.array_equal(d[:, c], 2 * a[:, c])
     keep = np.arange(K) != c
     assert np.array_equal(d[:, keep], a[:, keep])
