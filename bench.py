@@ -192,6 +192,9 @@ def main():
     ap.add_argument("--fp8-rowwise", action="store_true",
                     help="with an e4m3 workload: per-channel weight scales (one per output "
                          "row) instead of one per expert tensor")
+    ap.add_argument("--mxfp4", action="store_true",
+                    help="the workload with MXFP4 weights (e2m1, E8M0 scale per 32 "
+                         "elements) and e4m3 activations")
     ap.add_argument("--regime-sweep", action="store_true",
                     help="time the decode and full-tile kernel families (bf16) over batch "
                          "sizes M = 8 .. 1024 at this workload's K, N, E, top-k; one JSON "
@@ -225,6 +228,8 @@ def main():
         if not wl.fp8:
             sys.exit("--fp8-rowwise needs an e4m3 workload")
         wl = wl.resized(name=wl.name + "_rowwise", fp8_rowwise=True)
+    if args.mxfp4:
+        wl = wl.resized(name=wl.name + "_mxfp4", fp8=False, fp8_rowwise=False, mxfp4=True)
     if not torch.cuda.is_available():
         sys.exit("no GPU visible")
     dev = torch.device("cuda:0")
@@ -244,16 +249,18 @@ def main():
 
     log(f"generating {wl}")
     g = wlm.generate(wl, dev)
-    wbytes = 1 if wl.fp8 else 2
-    dtype_name = "fp8" if wl.fp8 else "bf16"
-    dtype = moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16
+    wbytes = 0.5 + 1 / 32 if wl.mxfp4 else (1 if wl.fp8 else 2)   # weight + block-scale bytes
+    dtype_name = "mxfp4/e4m3" if wl.mxfp4 else ("fp8" if wl.fp8 else "bf16")
+    dtype = (moe.MOE_MXFP4_E2M1 if wl.mxfp4 else
+             moe.MOE_FP8_E4M3_ROWWISE if wl.fp8_rowwise else
+             moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
 
     # routing of this batch (for the realised active-expert count)
     ids, _, _ = moe.moe_topk(g["x"], g["w_router"], g["bias"], wl.topk)
     torch.cuda.synchronize()
     active = int(torch.unique(ids).numel())
-    w1_e = 2 * wl.N * wl.K * wbytes
-    w2_e = wl.K * wl.N * wbytes
+    w1_e = int(2 * wl.N * wl.K * wbytes)
+    w2_e = int(wl.K * wl.N * wbytes)
     touched = active * (w1_e + w2_e)
     layers = args.layers or max(1, min(8, math.ceil(2 * 2**30 / touched)))
     w1s = [g["w1"]] + [g["w1"].clone() for _ in range(layers - 1)]
@@ -342,11 +349,11 @@ def main():
                     if wl.fp8 else 0))
     alg_flops = 6.0 * slots * wl.N * wl.K
     step_s = ms_per_step / 1e3
-    decode = (slots <= DECODE_MAX_ROWS_PER_EXPERT * wl.E) or wl.fp8
+    decode = (slots <= DECODE_MAX_ROWS_PER_EXPERT * wl.E) or wl.fp8 or wl.mxfp4
     g1_s = kern_us["gemm1"] / 1e6
     if decode:
         # GEMM1 reads W1 of every active expert once plus the token rows
-        g1_bytes = active * w1_e + wl.M * wl.K * (1 if wl.fp8 else 2)
+        g1_bytes = active * w1_e + wl.M * wl.K * (1 if (wl.fp8 or wl.mxfp4) else 2)
         achieved = g1_bytes / g1_s / 1e9
         roofline = {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",

@@ -62,10 +62,18 @@ typedef enum {
     MOE_BF16 = 0,              /* w1/w2 bf16; w1_scale/w2_scale must be NULL */
     MOE_FP8_E4M3 = 1,          /* w1/w2 OCP E4M3FN codes (uint8) with fp32 per-expert
                                   scales w1_scale [E], w2_scale [E] */
-    MOE_FP8_E4M3_ROWWISE = 2   /* e4m3 codes with fp32 per-channel scales: one per
+    MOE_FP8_E4M3_ROWWISE = 2,  /* e4m3 codes with fp32 per-channel scales: one per
                                   output row, w1_scale [E,2N] (gate rows, then up
                                   rows), w2_scale [E,K] (a scheme the pages do not
                                   describe: the per-tensor one, per row) */
+    MOE_MXFP4_E2M1 = 3         /* OCP MXFP4 weights (also beyond the pages): e2m1
+                                  codes two per byte, the even element in the low
+                                  nibble, w1 [E,2N,K/2], w2 [E,K,N/2]; one E8M0 scale
+                                  byte (2^(e-127)) per 32 elements of a row,
+                                  w1_scale [E,2N,K/32], w2_scale [E,K,N/32], passed
+                                  through the float pointer parameters as uint8
+                                  arrays; activations are quantised per token to
+                                  e4m3 as for MOE_FP8_E4M3 */
 } moe_dtype;
 
 /* Kernel family used by the expert GEMMs; results agree up to fp32
@@ -174,8 +182,9 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  *   x, w_router, router_bias   as moe_topk
  *   w1        [E,2N,K] bf16 or e4m3 (dtype)
  *   w2        [E,K,N]  bf16 or e4m3
- *   w1_scale  fp32 [E] (MOE_FP8_E4M3), [E,2N] (MOE_FP8_E4M3_ROWWISE) or NULL
- *             (MOE_BF16); w2_scale likewise [E], [E,K] or NULL
+ *   w1_scale  fp32 [E] (MOE_FP8_E4M3), [E,2N] (MOE_FP8_E4M3_ROWWISE), uint8
+ *             E8M0 [E,2N,K/32] (MOE_MXFP4_E2M1) or NULL (MOE_BF16); w2_scale
+ *             likewise [E], [E,K], [E,K,N/32] or NULL
  *   out       out bf16 [M,K]
  *   workspace device buffer of at least *workspace_bytes bytes (256-byte
  *             aligned), or NULL to query: with workspace == NULL the call

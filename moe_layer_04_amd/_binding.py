@@ -28,6 +28,7 @@ MOE_ERR_HIP = 4
 MOE_BF16 = 0
 MOE_FP8_E4M3 = 1
 MOE_FP8_E4M3_ROWWISE = 2
+MOE_MXFP4_E2M1 = 3
 
 MOE_REGIME_AUTO = 0
 MOE_REGIME_DECODE = 1
@@ -163,6 +164,8 @@ def _weight_dtype(w1: torch.Tensor, w1_scale: Optional[torch.Tensor]) -> int:
     per-channel scales [E,2N] (MOE_FP8_E4M3_ROWWISE)."""
     if w1.dtype != torch.uint8:
         return MOE_BF16
+    if w1_scale is not None and w1_scale.dtype == torch.uint8:
+        return MOE_MXFP4_E2M1
     if w1_scale is not None and w1_scale.dim() == 2:
         return MOE_FP8_E4M3_ROWWISE
     return MOE_FP8_E4M3
@@ -174,7 +177,7 @@ def workspace_size(dtype: int, M: int, K: int, N: int, E: int, topk: int,
     lib = load_library()
     nbytes = ctypes.c_size_t(0)
     dummy = ctypes.c_void_p(0x100)
-    s1 = dummy if dtype in (MOE_FP8_E4M3, MOE_FP8_E4M3_ROWWISE) else None
+    s1 = dummy if dtype in (MOE_FP8_E4M3, MOE_FP8_E4M3_ROWWISE, MOE_MXFP4_E2M1) else None
     _check(lib.moe_fused_forward_ex(dummy, dummy, None, dummy, dummy, s1, s1, dtype, M, K, N, E,
                                     topk, regime, dummy, None, ctypes.byref(nbytes), None),
            "workspace query")
@@ -191,8 +194,10 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
 
     w1 [E,2N,K] / w2 [E,K,N] are bf16, or uint8 e4m3 codes with fp32 scales:
     per expert (w1_scale, w2_scale [E]) or per output row (w1_scale [E,2N],
-    w2_scale [E,K]).  ``workspace`` (uint8, at least workspace_size bytes)
-    may be passed to avoid an allocation per call."""
+    w2_scale [E,K]), or MXFP4: packed e2m1 w1 [E,2N,K/2] / w2 [E,K,N/2] with
+    uint8 E8M0 block scales w1_scale [E,2N,K/32] / w2_scale [E,K,N/32].
+    ``workspace`` (uint8, at least workspace_size bytes) may be passed to
+    avoid an allocation per call."""
     lib = load_library()
     fp8 = w1.dtype == torch.uint8
     dtype = _weight_dtype(w1, w1_scale)
@@ -204,16 +209,22 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
     if router_bias is not None:
         _dev(router_bias, "router_bias", torch.float32, (E,))
     wdt = torch.uint8 if fp8 else torch.bfloat16
-    _dev(w1, "w1", wdt, (E, 2 * N, K))
-    _dev(w2, "w2", wdt, (E, K, N))
-    if dtype == MOE_FP8_E4M3_ROWWISE:
-        _dev(w1_scale, "w1_scale", torch.float32, (E, 2 * N))
-        _dev(w2_scale, "w2_scale", torch.float32, (E, K))
-    elif fp8:
-        _dev(w1_scale, "w1_scale", torch.float32, (E,))
-        _dev(w2_scale, "w2_scale", torch.float32, (E,))
-    elif w1_scale is not None or w2_scale is not None:
-        raise ValueError("scales are only for e4m3 weights")
+    if dtype == MOE_MXFP4_E2M1:
+        _dev(w1, "w1", wdt, (E, 2 * N, K // 2))
+        _dev(w2, "w2", wdt, (E, K, N // 2))
+        _dev(w1_scale, "w1_scale", torch.uint8, (E, 2 * N, K // 32))
+        _dev(w2_scale, "w2_scale", torch.uint8, (E, K, N // 32))
+    else:
+        _dev(w1, "w1", wdt, (E, 2 * N, K))
+        _dev(w2, "w2", wdt, (E, K, N))
+        if dtype == MOE_FP8_E4M3_ROWWISE:
+            _dev(w1_scale, "w1_scale", torch.float32, (E, 2 * N))
+            _dev(w2_scale, "w2_scale", torch.float32, (E, K))
+        elif fp8:
+            _dev(w1_scale, "w1_scale", torch.float32, (E,))
+            _dev(w2_scale, "w2_scale", torch.float32, (E,))
+        elif w1_scale is not None or w2_scale is not None:
+            raise ValueError("scales are only for e4m3 / MXFP4 weights")
     dev = x.device
     if out is None:
         out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)

@@ -36,6 +36,7 @@ constexpr long kDecodeMaxRowsPerExpert = 8;
 // up to this many tokens the FP8 token quantisation runs inside the
 // single-workgroup top-k + align launch (a wave per token)
 constexpr int kLateQuantRows = 16;
+constexpr int kLateQuantCols = 1024;
 
 bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
 
@@ -55,7 +56,10 @@ struct Plan {
     size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
 };
 
-bool is_fp8(int dtype) { return dtype == MOE_FP8_E4M3 || dtype == MOE_FP8_E4M3_ROWWISE; }
+// every dtype with e4m3-quantised activations (the e4m3 and MXFP4 weights)
+bool is_fp8(int dtype) {
+    return dtype == MOE_FP8_E4M3 || dtype == MOE_FP8_E4M3_ROWWISE || dtype == MOE_MXFP4_E2M1;
+}
 
 Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     Plan p;
@@ -243,7 +247,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     mark(0);
     if (moe::topk_align_fits(M, topk)) {
         // the FP8 token codes go with top-k + align when the tokens are few
-        const bool q_late = fp8 && M <= kLateQuantRows;
+        // and short (a wave per token there; a workgroup per token otherwise)
+        const bool q_late = fp8 && M <= kLateQuantRows && K <= kLateQuantCols;
         moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits,
                                   q_late ? nullptr : xq, xs, s);
         mark(1);
@@ -263,13 +268,25 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         float* act = (float*)(ws + p.act);
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
-        moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M, topk,
-                                     nslots, K, N, p.grid_blocks, act, amax, s);
+        const bool mx = dtype == MOE_MXFP4_E2M1;
+        if (mx)
+            moe::launch_gemm1_decode_mxfp4(xq, xs, w1, (const uint8_t*)w1_scale, sorted, bexp,
+                                           npad, M, topk, nslots, K, N, p.grid_blocks, act, amax,
+                                           s);
+        else
+            moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
+                                         topk, nslots, K, N, p.grid_blocks, act, amax, s);
         mark(4);
         moe::launch_act_quant(act, amax, sorted, npad, nslots, N, p.cap, actq, as, s);
         mark(5);
-        moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp, npad,
-                                     p.cap, nslots, K, N, p.nsplit, p.grid_blocks, ypart, s);
+        if (mx)
+            moe::launch_gemm2_decode_mxfp4(actq, as, w2, (const uint8_t*)w2_scale, wts, sorted,
+                                           bexp, npad, p.cap, nslots, K, N, p.nsplit,
+                                           p.grid_blocks, ypart, s);
+        else
+            moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
+                                         npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
+                                         ypart, s);
         mark(6);
     } else {
         void* act = ws + p.act;

@@ -62,6 +62,15 @@ __device__ __forceinline__ f32x4_t mfma_bf16(i32x4_t a, i32x4_t b, f32x4_t c) {
 __device__ __forceinline__ f32x4_t mfma_fp8(i32x8_t a, i32x8_t b, f32x4_t c) {
     return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
 }
+// A = 32 e2m1 codes per lane (4 dwords; cbsz 4) with the lane's E8M0 block
+// scale, B = 32 e4m3 codes per lane with scale 1 (E8M0 127).
+__device__ __forceinline__ f32x4_t mfma_fp4_fp8(i32x4_t a, int scale_a, i32x8_t b, f32x4_t c) {
+    const i32x8_t a8 = {a[0], a[1], a[2], a[3], 0, 0, 0, 0};
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a8, b, c, 4, 0, 0, scale_a, 0, 127);
+}
+__device__ __forceinline__ uint32_t bload_u32(rsrc_t r, uint32_t off) {
+    return (uint32_t)__builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0);
+}
 
 // K-step j of a wave whose sequence is rotated by `rot` (steps in [0, n)).
 __device__ __forceinline__ int rotated(int j, int rot, int n) {
@@ -291,39 +300,43 @@ __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
 }
 
 // act32 [cap,N] + amax [cap] -> act_q [cap,N] e4m3 and s_a [cap]; one wave per row.
+// A wave per (row, chunk of kActChunk elements): the row's scale comes from
+// the amax GEMM1 folded, so the chunks of a row are independent.
+constexpr int kActChunk = 8 * kWave * 4;
+
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const float* __restrict__ act, const uint32_t* __restrict__ amax,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ num_padded, int nslots,
-    int N, uint8_t* __restrict__ act_q, float* __restrict__ ascale) {
-    const int r = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
-    if (r >= *num_padded) return;
+    int N, int nchunk, int cap, uint8_t* __restrict__ act_q, float* __restrict__ ascale) {
+    const int w = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
+    const int r = w / nchunk, ch = w % nchunk;
+    if (r >= cap || r >= *num_padded) return;
     if (sorted_ids[r] >= nslots) return;
     const int lane = lane_id();
     const float a = __uint_as_float(amax[r]);
     const float s = (a == 0.0f) ? 1.0f : a / 448.0f;
     const float* src = act + (size_t)r * N;
     uint8_t* dst = act_q + (size_t)r * N;
-    // the row's loads are issued in groups of 8 per lane before any is used
+    // the chunk's loads are issued (8 per lane) before any is used
     constexpr int G = 8;
-    for (int n0 = lane * 4; n0 < N; n0 += G * kWave * 4) {
-        f32x4_t v[G];
+    const int n0 = ch * kActChunk + lane * 4;
+    f32x4_t v[G];
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int n = n0 + g * kWave * 4;
-            if (n < N) v[g] = *reinterpret_cast<const f32x4_t*>(src + n);
-        }
+    for (int g = 0; g < G; ++g) {
+        const int n = n0 + g * kWave * 4;
+        if (n < N) v[g] = *reinterpret_cast<const f32x4_t*>(src + n);
+    }
 #pragma unroll
-        for (int g = 0; g < G; ++g) {
-            const int n = n0 + g * kWave * 4;
-            if (n < N) {
-                const uint32_t q = f32_to_e4m3(v[g][0] / s) | (f32_to_e4m3(v[g][1] / s) << 8) |
-                                   (f32_to_e4m3(v[g][2] / s) << 16) |
-                                   (f32_to_e4m3(v[g][3] / s) << 24);
-                *reinterpret_cast<uint32_t*>(dst + n) = q;
-            }
+    for (int g = 0; g < G; ++g) {
+        const int n = n0 + g * kWave * 4;
+        if (n < N) {
+            const uint32_t q = f32_to_e4m3(v[g][0] / s) | (f32_to_e4m3(v[g][1] / s) << 8) |
+                               (f32_to_e4m3(v[g][2] / s) << 16) |
+                               (f32_to_e4m3(v[g][3] / s) << 24);
+            *reinterpret_cast<uint32_t*>(dst + n) = q;
         }
     }
-    if (lane == 0) ascale[r] = s;
+    if (ch == 0 && lane == 0) ascale[r] = s;
 }
 
 __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
@@ -399,6 +412,186 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 weights (OCP microscaling: e2m1 codes two per byte, even element in
+// the low nibble, one E8M0 scale per 32 elements of a row) against the
+// layer's per-token e4m3 activations.  In the scaled 16x16x128 MFMA an FP4
+// lane holds 32 consecutive K (lane group q: K 32q .. 32q+31 of the step),
+// exactly one MX block, so the block scale is the lane's scale operand; the
+// e4m3 operand's lane group q holds K 16q .. 16q+15 and 64+16q .. 64+16q+15
+// (its two 16-byte halves).  Both layouts were measured on gfx950.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
+    const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1e8,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
+    float* __restrict__ act, uint32_t* __restrict__ amax) {
+    const int blk = (int)blockIdx.y;
+    if (blk * kDecRows >= *num_padded) return;
+    const int e = block_expert[blk];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
+    const int gw = (int)blockIdx.x * 4 + wave;
+    const int n0 = gw * 16;
+    const int i = lane & 15, kq = lane >> 4;
+    const int p = sorted_ids[blk * kDecRows + i];
+    const bool valid = p < nslots;
+    const int t = valid ? p / topk : 0;
+
+    const size_t row_bytes = (size_t)K / 2;   // packed e2m1
+    const size_t srow = (size_t)K / 32;       // E8M0 scales per row
+    const size_t g0 = (size_t)e * 2 * N + n0, u0 = g0 + N;
+    const rsrc_t rg = make_rsrc(w1 + g0 * row_bytes, (uint32_t)(16 * row_bytes));
+    const rsrc_t ru = make_rsrc(w1 + u0 * row_bytes, (uint32_t)(16 * row_bytes));
+    const rsrc_t rsg = make_rsrc(w1e8 + g0 * srow, (uint32_t)(16 * srow));
+    const rsrc_t rsu = make_rsrc(w1e8 + u0 * srow, (uint32_t)(16 * srow));
+    const rsrc_t rx = make_rsrc(xq, (uint32_t)((size_t)M * K));
+    const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 16;
+    const uint32_t so = (uint32_t)(i * srow);
+    const uint32_t xo = valid ? (uint32_t)((size_t)t * K) + kq * 16 : kOob;
+    const int sh = 8 * kq;
+
+    // A 128-deep chunk carries a quarter of the bf16 kernels' weight bytes,
+    // so a step is two chunks and the next step's loads are in flight while
+    // the current one is multiplied.
+    struct Chunk { i32x4_t g, u, b0, b1; uint32_t sg, su; };
+    struct Frag { Chunk c[2]; };
+    auto load1 = [&](Chunk& f, int k) {
+        f.g = bload(rg, wo + k / 2);
+        f.u = bload(ru, wo + k / 2);
+        f.b0 = bload(rx, xo + k);
+        f.b1 = bload(rx, xo + k + 64);
+        f.sg = bload_u32(rsg, so + k / 32);
+        f.su = bload_u32(rsu, so + k / 32);
+    };
+    f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    auto compute1 = [&](const Chunk& f) {
+        const i32x8_t b = {f.b0[0], f.b0[1], f.b0[2], f.b0[3], f.b1[0], f.b1[1], f.b1[2], f.b1[3]};
+        accg = mfma_fp4_fp8(f.g, (int)((f.sg >> sh) & 0xffu), b, accg);
+        accu = mfma_fp4_fp8(f.u, (int)((f.su >> sh) & 0xffu), b, accu);
+    };
+    auto load = [&](Frag& f, int k) { load1(f.c[0], k); load1(f.c[1], k + 128); };
+    auto compute = [&](const Frag& f) { compute1(f.c[0]); compute1(f.c[1]); };
+    const int nst = K / 256;  // whole two-chunk steps; an odd last chunk follows
+    if (nst > 0) {
+        const int rot = (gw * kRot + blk * 5) % nst;
+        auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
+        // two fragments in turn, no copies; loads past the end repeat the
+        // last step (never multiplied), so every wait count is exact
+        Frag fa, fb;
+        load(fa, kstep(0));
+        for (int j = 0; j < nst; j += 2) {
+            load(fb, kstep(j + 1));
+            compute(fa);
+            load(fa, kstep(j + 2));
+            if (j + 1 < nst) compute(fb);
+        }
+    }
+    if (K % 256) {
+        Chunk last;
+        load1(last, K - 128);
+        compute1(last);
+    }
+    pin(accg);
+    pin(accu);
+
+    float m = 0.0f;
+    if (valid) {
+        const float sx = xscale[t];
+        f32x4_t o;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            o[v] = silu(accg[v] * sx) * (accu[v] * sx);
+            m = fmaxf(m, fabsf(o[v]));
+        }
+        *reinterpret_cast<f32x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 4 * kq) = o;
+    }
+    const uint32_t mb = col_max_bits(__float_as_uint(m));
+    if (valid && kq == 0) atomicMax(amax + blk * kDecRows + i, mb);
+}
+
+__global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
+    const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
+    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2e8,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
+    int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
+    const int blk = (int)blockIdx.y;
+    if (blk * kDecRows >= *num_padded) return;
+    const int e = block_expert[blk];
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
+    const int gw = (int)blockIdx.x * 4 + wave;
+    const int c0 = gw * 32;
+    const int i = lane & 15, kq = lane >> 4;
+    const int z = (int)blockIdx.z;
+    const int nlen = N / nsplit;
+    const int nbeg = z * nlen;
+    const int r = blk * kDecRows + i;
+    const int p = sorted_ids[r];
+    const bool valid = p < nslots;
+
+    const size_t row_bytes = (size_t)N / 2;
+    const size_t srow = (size_t)N / 32;
+    const size_t r0 = (size_t)e * K + c0;
+    const rsrc_t rw = make_rsrc(w2 + r0 * row_bytes, (uint32_t)(32 * row_bytes));
+    const rsrc_t rs = make_rsrc(w2e8 + r0 * srow, (uint32_t)(32 * srow));
+    const rsrc_t ra = make_rsrc(act_q, (uint32_t)((size_t)cap * N));
+    const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg / 2 + kq * 16;
+    const uint32_t wo1 = wo + (uint32_t)(16 * row_bytes);
+    const uint32_t so = (uint32_t)(i * srow) + nbeg / 32;
+    const uint32_t so1 = so + (uint32_t)(16 * srow);
+    const uint32_t ao = valid ? (uint32_t)((size_t)r * N) + nbeg + kq * 16 : kOob;
+    const int sh = 8 * kq;
+
+    struct Chunk { i32x4_t a0, a1, b0, b1; uint32_t s0, s1; };
+    struct Frag { Chunk c[2]; };
+    auto load1 = [&](Chunk& f, int n) {
+        f.a0 = bload(rw, wo + n / 2);
+        f.a1 = bload(rw, wo1 + n / 2);
+        f.b0 = bload(ra, ao + n);
+        f.b1 = bload(ra, ao + n + 64);
+        f.s0 = bload_u32(rs, so + n / 32);
+        f.s1 = bload_u32(rs, so1 + n / 32);
+    };
+    f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    auto compute1 = [&](const Chunk& f) {
+        const i32x8_t b = {f.b0[0], f.b0[1], f.b0[2], f.b0[3], f.b1[0], f.b1[1], f.b1[2], f.b1[3]};
+        acc0 = mfma_fp4_fp8(f.a0, (int)((f.s0 >> sh) & 0xffu), b, acc0);
+        acc1 = mfma_fp4_fp8(f.a1, (int)((f.s1 >> sh) & 0xffu), b, acc1);
+    };
+    auto load = [&](Frag& f, int n) { load1(f.c[0], n); load1(f.c[1], n + 128); };
+    auto compute = [&](const Frag& f) { compute1(f.c[0]); compute1(f.c[1]); };
+    const int nst = nlen / 256;  // whole two-chunk steps; an odd last chunk follows
+    if (nst > 0) {
+        const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
+        auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
+        Frag fa, fb;
+        load(fa, kstep(0));
+        for (int j = 0; j < nst; j += 2) {
+            load(fb, kstep(j + 1));
+            compute(fa);
+            load(fa, kstep(j + 2));
+            if (j + 1 < nst) compute(fb);
+        }
+    }
+    if (nlen % 256) {
+        Chunk last;
+        load1(last, nlen - 128);
+        compute1(last);
+    }
+    pin(acc0);
+    pin(acc1);
+
+    if (valid) {
+        const float w = topk_w[p] * ascale[r];
+        float* yr = ypart + ((size_t)z * nslots + p) * K + c0 + 4 * kq;
+        *reinterpret_cast<f32x4_t*>(yr) = acc0 * w;
+        *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * w;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
@@ -435,8 +628,11 @@ void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void*
 void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sorted_ids,
                       const int32_t* num_padded, int nslots, int N, int cap, uint8_t* act_q,
                       float* ascale, hipStream_t s) {
-    act_quant_kernel<<<(cap + 3) / 4, 256, 0, s>>>(act, amax, sorted_ids, num_padded, nslots, N,
-                                                   act_q, ascale);
+    const int nchunk = (N + kActChunk - 1) / kActChunk;
+    const long waves = (long)cap * nchunk;
+    act_quant_kernel<<<(int)((waves + 3) / 4), 256, 0, s>>>(act, amax, sorted_ids, num_padded,
+                                                             nslots, N, nchunk, cap, act_q,
+                                                             ascale);
 }
 
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
@@ -448,6 +644,28 @@ void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const vo
     gemm2_decode_fp8_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale,
                                                  rowwise, topk_w, sorted_ids, block_expert, num_padded,
                                                  cap, nslots, K, N, nsplit, ypart);
+}
+
+void launch_gemm1_decode_mxfp4(const uint8_t* xq, const float* xscale, const void* w1,
+                               const uint8_t* w1e8, const int32_t* sorted_ids,
+                               const int32_t* block_expert, const int32_t* num_padded, int M,
+                               int topk, int nslots, int K, int N, int max_blocks, float* act,
+                               uint32_t* amax, hipStream_t s) {
+    dim3 grid(N / 64, max_blocks);
+    gemm1_decode_mxfp4_kernel<<<grid, 256, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1e8,
+                                                   sorted_ids, block_expert, num_padded, M, topk,
+                                                   nslots, K, N, act, amax);
+}
+
+void launch_gemm2_decode_mxfp4(const uint8_t* act_q, const float* ascale, const void* w2,
+                               const uint8_t* w2e8, const float* topk_w,
+                               const int32_t* sorted_ids, const int32_t* block_expert,
+                               const int32_t* num_padded, int cap, int nslots, int K, int N,
+                               int nsplit, int max_blocks, float* ypart, hipStream_t s) {
+    dim3 grid(K / 128, max_blocks, nsplit);
+    gemm2_decode_mxfp4_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2e8,
+                                                   topk_w, sorted_ids, block_expert, num_padded,
+                                                   cap, nslots, K, N, nsplit, ypart);
 }
 
 }  // namespace moe

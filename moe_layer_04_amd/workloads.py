@@ -44,6 +44,7 @@ class Workload:
     topk: int
     fp8: bool = False
     fp8_rowwise: bool = False   # e4m3 scales per output row instead of per tensor
+    mxfp4: bool = False         # MXFP4 weights (implies e4m3 activations)
     bias_var: Optional[float] = None
     seed: int = 0
 
@@ -83,13 +84,38 @@ def _quant_tensor(w32: torch.Tensor, rowwise: bool = False):
     return q.to(torch.float8_e4m3fn).view(torch.uint8), scale
 
 
+_E2M1 = (0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0)
+
+
+def _quant_mxfp4(w32: torch.Tensor):
+    """OCP MXFP4 of a [rows, cols] matrix: per 32-element block of a row the
+    E8M0 scale 2^(floor(log2 amax) - 2) (6 = 1.5 * 2^2 is e2m1's largest
+    value), elements rounded to the nearest e2m1 value (saturating at 6),
+    packed two per byte with the even element in the low nibble.  Returns
+    (packed uint8 [rows, cols/2], scales uint8 [rows, cols/32])."""
+    rows, cols = w32.shape
+    blk = w32.reshape(rows, cols // 32, 32)
+    amax = blk.abs().amax(dim=2)
+    ex = torch.where(amax > 0, torch.floor(torch.log2(amax)) - 2, torch.full_like(amax, -127))
+    ex = ex.clamp(-127, 127)
+    scales = (ex + 127).to(torch.uint8)
+    v = blk / torch.exp2(ex)[..., None]
+    table = torch.tensor(_E2M1, device=w32.device)
+    mag = (v.abs()[..., None] - table).abs().argmin(dim=-1).to(torch.uint8)  # nearest value
+    code = mag | ((v < 0).to(torch.uint8) << 3)
+    code = code.reshape(rows, cols)
+    packed = code[:, 0::2] | (code[:, 1::2] << 4)
+    return packed.contiguous(), scales.contiguous()
+
+
 def generate(wl: Workload, device="cpu") -> dict:
     """Draw all tensors of ``wl`` on ``device``.
 
     Returns a dict with x [M,K] bf16, w_router [E,K] bf16, bias [E] fp32 or
     None, w1 [E,2N,K] and w2 [E,K,N] (bf16, or uint8 e4m3 codes), and
     w1_scale / w2_scale fp32: [E] per tensor, or [E,2N] / [E,K] per output
-    row with ``fp8_rowwise`` (None for bf16)."""
+    row with ``fp8_rowwise`` (None for bf16).  With ``mxfp4``: w1 [E,2N,K/2]
+    and w2 [E,K,N/2] packed e2m1, scales uint8 E8M0 [E,2N,K/32] / [E,K,N/32]."""
     device = torch.device(device)
     g = torch.Generator(device=device)
     g.manual_seed(wl.seed)
@@ -102,6 +128,17 @@ def generate(wl: Workload, device="cpu") -> dict:
     x = normal((M, K), 1.0).to(torch.bfloat16)
     w_router = normal((E, K), 1.0 / K).to(torch.bfloat16)
     bias = normal((E,), wl.bias_var) if wl.bias_var is not None else None
+    if wl.mxfp4:
+        w1 = torch.empty((E, 2 * N, K // 2), dtype=torch.uint8, device=device)
+        w2 = torch.empty((E, K, N // 2), dtype=torch.uint8, device=device)
+        w1_scale = torch.empty((E, 2 * N, K // 32), dtype=torch.uint8, device=device)
+        w2_scale = torch.empty((E, K, N // 32), dtype=torch.uint8, device=device)
+        for e in range(E):
+            w1[e], w1_scale[e] = _quant_mxfp4(normal((2 * N, K), 1.0 / K))
+        for e in range(E):
+            w2[e], w2_scale[e] = _quant_mxfp4(normal((K, N), 1.0 / N))
+        return {"x": x, "w_router": w_router, "bias": bias, "w1": w1, "w2": w2,
+                "w1_scale": w1_scale, "w2_scale": w2_scale}
     wdt = torch.uint8 if wl.fp8 else torch.bfloat16
     w1 = torch.empty((E, 2 * N, K), dtype=wdt, device=device)
     w2 = torch.empty((E, K, N), dtype=wdt, device=device)

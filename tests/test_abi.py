@@ -82,7 +82,9 @@ def fused(lib, *, x=FAKE, wr=FAKE, bias=None, w1=FAKE, w2=FAKE, s1=None, s2=None
 
 def test_fused_validation(lib):
     INV, UNS, WSP = B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE
-    assert fused(lib, dtype=3)[0] == INV
+    assert fused(lib, dtype=4)[0] == INV
+    assert fused(lib, dtype=3)[0] == INV                              # MXFP4 without scales
+    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
     assert fused(lib, dtype=2)[0] == INV                              # rowwise fp8 without scales
     assert fused(lib, dtype=2, s1=FAKE, s2=None)[0] == INV
     assert fused(lib, dtype=2, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
@@ -124,3 +126,4 @@ def test_workspace_query_sizes(lib):
     assert moe.workspace_size(moe.MOE_BF16, 8, 4096, 14336, 8, 2, moe.MOE_REGIME_PREFILL) > s_dec
     # per-channel scales change no workspace region
     assert moe.workspace_size(moe.MOE_FP8_E4M3_ROWWISE, 128, 7168, 2048, 256, 8) == s_fp8
+    assert moe.workspace_size(moe.MOE_MXFP4_E2M1, 128, 7168, 2048, 256, 8) == s_fp8

@@ -51,7 +51,8 @@ def gen_small(wl, seed=None):
 
 
 def run_layer(moe, g, wl, regime=0, poison=True):
-    dtype = moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16
+    dtype = (moe.MOE_MXFP4_E2M1 if wl.mxfp4 else
+             moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
     need = moe.workspace_size(dtype, wl.M, wl.K, wl.N, wl.E, wl.topk, regime)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     if poison:
@@ -70,7 +71,7 @@ def oracle_layer(d, wl, tokens=None):
     return oracle.moe_forward(bits(d["x"]), bits(d["w_router"]),
                               None if d["bias"] is None else d["bias"].numpy(),
                               bits(d["w1"]), bits(d["w2"]), wl.topk, w1_scale=s1, w2_scale=s2,
-                              tokens=tokens, fp8=wl.fp8)
+                              tokens=tokens, fp8=wl.fp8, mxfp4=wl.mxfp4)
 
 
 def out_f64(out):
@@ -226,6 +227,10 @@ SMALL = [
     ("fp8_rowwise_tiny", 16, 512, 256, 16, 4, "rowwise", None, 0),
     ("fp8_rowwise_ragged", 7, 384, 640, 32, 8, "rowwise", None, 0),
     ("fp8_rowwise_many_rows", 300, 256, 384, 8, 2, "rowwise", None, 0),
+    # MXFP4 weights (e2m1, E8M0 per 32 elements) with e4m3 activations
+    ("mxfp4_tiny", 16, 512, 256, 16, 4, "mxfp4", None, 0),
+    ("mxfp4_ragged", 7, 384, 640, 32, 8, "mxfp4", None, 0),
+    ("mxfp4_many_rows", 300, 256, 384, 8, 2, "mxfp4", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
 ]
 
@@ -235,9 +240,10 @@ def test_fused_small(moe, case):
     name, M, K, N, E, k, fp8, bias_var, regime = case
     note(f"fused small {case}")
     rowwise = fp8 == "rowwise"
-    fp8 = bool(fp8)
+    mx = fp8 == "mxfp4"
+    fp8 = bool(fp8) and not mx
     wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, fp8_rowwise=rowwise,
-                      bias_var=bias_var, seed=3)
+                      mxfp4=mx, bias_var=bias_var, seed=3)
     d, g = gen_small(wl)
     out = run_layer(moe, g, wl, regime)
     ref, _, _ = oracle_layer(d, wl)
@@ -245,7 +251,7 @@ def test_fused_small(moe, case):
     assert np.isfinite(got).all()
     err = row_rel_err(got, ref)
     note(f"  err={err:.3e}")
-    assert err <= (TOL_FP8 if fp8 else TOL_BF16)
+    assert err <= (TOL_FP8 if (fp8 or mx) else TOL_BF16)
 
 
 def test_fused_m0_is_noop(moe):
@@ -298,11 +304,14 @@ def sample_tokens(M, n=6):
     return [0] + mid + [M - 1]
 
 
-# the DeepSeek-shaped batch also with per-channel e4m3 weight scales
-@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise"])
+# the DeepSeek-shaped batch also with per-channel e4m3 weight scales and with
+# MXFP4 weights
+@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise", "dsv3_mxfp4"])
 def test_fused_full_size_sampled(moe, name):
     if name == "dsv3_fp8_rowwise":
         wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, fp8_rowwise=True)
+    elif name == "dsv3_mxfp4":
+        wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, fp8=False, mxfp4=True)
     else:
         wl = wlm.WORKLOADS[name]
     note(f"full size {name}: generate on GPU")
@@ -328,9 +337,9 @@ def test_fused_full_size_sampled(moe, name):
     s1 = None if g["w1_scale"] is None else g["w1_scale"].cpu().numpy()
     s2 = None if g["w2_scale"] is None else g["w2_scale"].cpu().numpy()
     ref, _, _ = oracle.moe_forward(x_h, wr_h, bias_h, w1, w2, wl.topk, w1_scale=s1,
-                                   w2_scale=s2, tokens=toks, fp8=wl.fp8)
+                                   w2_scale=s2, tokens=toks, fp8=wl.fp8, mxfp4=wl.mxfp4)
     err = row_rel_err(got[toks], ref)
     note(f"  err={err:.3e}")
-    assert err <= (TOL_FP8 if wl.fp8 else TOL_BF16)
+    assert err <= (TOL_FP8 if (wl.fp8 or wl.mxfp4) else TOL_BF16)
     del g
     torch.cuda.empty_cache()
