@@ -81,7 +81,9 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         // the weight stream spreads over all CUs
         const long est_blocks = slots < E ? slots : E;
         const long tiles = est_blocks * (K / 128);
-        while (tiles * p.nsplit < 2048 && p.nsplit < 16 && (N / (p.nsplit * 2)) % 128 == 0)
+        // each split's reduction length stays a multiple of the kernels' step
+        const int gran = dtype == MOE_MXFP4_E2M1 ? 256 : 128;
+        while (tiles * p.nsplit < 2048 && p.nsplit < 16 && (N / (p.nsplit * 2)) % gran == 0)
             p.nsplit *= 2;
     } else {
         p.nsplit = moe::prefill_gemm2_splits(K, N);
@@ -195,6 +197,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     if (is_fp8(dtype) && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
     if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
+    if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256)) return MOE_ERR_UNSUPPORTED;
     if (is_fp8(dtype) && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
     const long kn = K > N ? K : N;

@@ -420,19 +420,32 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
 // e4m3 operand's lane group q holds K 16q .. 16q+15 and 64+16q .. 64+16q+15
 // (its two 16-byte halves).  Both layouts were measured on gfx950.
 // ---------------------------------------------------------------------------
+// Each wave covers RT 16-row tiles of gate rows and the matching up rows
+// (GEMM1) or RT 16-row tiles of output rows (GEMM2) with one token fragment;
+// a step is two 128-deep chunks, the scale bytes of a step are one 8-byte
+// load per row tile, and the steps alternate between two fragments.
+constexpr int kMxTiles1 = 1;  // GEMM1: 16 gate + 16 up rows per wave
+constexpr int kMxTiles2 = 4;  // GEMM2: 64 output rows per wave
+
+__device__ __forceinline__ uint64_t bload_u64(rsrc_t r, uint32_t off) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0);
+    return ((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0];
+}
+
 __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1e8,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     float* __restrict__ act, uint32_t* __restrict__ amax) {
+    constexpr int RT = kMxTiles1;
     const int blk = (int)blockIdx.y;
     if (blk * kDecRows >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
-    const int n0 = gw * 16;
+    const int n0 = gw * 16 * RT;
     const int i = lane & 15, kq = lane >> 4;
     const int p = sorted_ids[blk * kDecRows + i];
     const bool valid = p < nslots;
@@ -441,70 +454,89 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const size_t row_bytes = (size_t)K / 2;   // packed e2m1
     const size_t srow = (size_t)K / 32;       // E8M0 scales per row
     const size_t g0 = (size_t)e * 2 * N + n0, u0 = g0 + N;
-    const rsrc_t rg = make_rsrc(w1 + g0 * row_bytes, (uint32_t)(16 * row_bytes));
-    const rsrc_t ru = make_rsrc(w1 + u0 * row_bytes, (uint32_t)(16 * row_bytes));
-    const rsrc_t rsg = make_rsrc(w1e8 + g0 * srow, (uint32_t)(16 * srow));
-    const rsrc_t rsu = make_rsrc(w1e8 + u0 * srow, (uint32_t)(16 * srow));
+    const rsrc_t rg = make_rsrc(w1 + g0 * row_bytes, (uint32_t)(16 * RT * row_bytes));
+    const rsrc_t ru = make_rsrc(w1 + u0 * row_bytes, (uint32_t)(16 * RT * row_bytes));
+    const rsrc_t rsg = make_rsrc(w1e8 + g0 * srow, (uint32_t)(16 * RT * srow));
+    const rsrc_t rsu = make_rsrc(w1e8 + u0 * srow, (uint32_t)(16 * RT * srow));
     const rsrc_t rx = make_rsrc(xq, (uint32_t)((size_t)M * K));
     const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 16;
     const uint32_t so = (uint32_t)(i * srow);
     const uint32_t xo = valid ? (uint32_t)((size_t)t * K) + kq * 16 : kOob;
     const int sh = 8 * kq;
 
-    // A 128-deep chunk carries a quarter of the bf16 kernels' weight bytes,
-    // so a step is two chunks and the next step's loads are in flight while
-    // the current one is multiplied.
-    struct Chunk { i32x4_t g, u, b0, b1; uint32_t sg, su; };
-    struct Frag { Chunk c[2]; };
-    auto load1 = [&](Chunk& f, int k) {
-        f.g = bload(rg, wo + k / 2);
-        f.u = bload(ru, wo + k / 2);
-        f.b0 = bload(rx, xo + k);
-        f.b1 = bload(rx, xo + k + 64);
-        f.sg = bload_u32(rsg, so + k / 32);
-        f.su = bload_u32(rsu, so + k / 32);
+    // one step = chunks k and k+128 of every row tile
+    struct Frag {
+        i32x4_t g[2][RT], u[2][RT], b[2][2];
+        uint64_t sg[RT], su[RT];
     };
-    f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
-    auto compute1 = [&](const Chunk& f) {
-        const i32x8_t b = {f.b0[0], f.b0[1], f.b0[2], f.b0[3], f.b1[0], f.b1[1], f.b1[2], f.b1[3]};
-        accg = mfma_fp4_fp8(f.g, (int)((f.sg >> sh) & 0xffu), b, accg);
-        accu = mfma_fp4_fp8(f.u, (int)((f.su >> sh) & 0xffu), b, accu);
-    };
-    auto load = [&](Frag& f, int k) { load1(f.c[0], k); load1(f.c[1], k + 128); };
-    auto compute = [&](const Frag& f) { compute1(f.c[0]); compute1(f.c[1]); };
-    const int nst = K / 256;  // whole two-chunk steps; an odd last chunk follows
-    if (nst > 0) {
-        const int rot = (gw * kRot + blk * 5) % nst;
-        auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
-        // two fragments in turn, no copies; loads past the end repeat the
-        // last step (never multiplied), so every wait count is exact
-        Frag fa, fb;
-        load(fa, kstep(0));
-        for (int j = 0; j < nst; j += 2) {
-            load(fb, kstep(j + 1));
-            compute(fa);
-            load(fa, kstep(j + 2));
-            if (j + 1 < nst) compute(fb);
+    auto load = [&](Frag& f, int k) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int kc = k + 128 * c;
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                f.g[c][r] = bload(rg, wo + (uint32_t)(16 * r * row_bytes) + kc / 2);
+                f.u[c][r] = bload(ru, wo + (uint32_t)(16 * r * row_bytes) + kc / 2);
+            }
+            f.b[c][0] = bload(rx, xo + kc);
+            f.b[c][1] = bload(rx, xo + kc + 64);
         }
+#pragma unroll
+        for (int r = 0; r < RT; ++r) {
+            f.sg[r] = bload_u64(rsg, so + (uint32_t)(16 * r * srow) + k / 32);
+            f.su[r] = bload_u64(rsu, so + (uint32_t)(16 * r * srow) + k / 32);
+        }
+    };
+    f32x4_t accg[RT], accu[RT];
+#pragma unroll
+    for (int r = 0; r < RT; ++r) accg[r] = accu[r] = f32x4_t{0, 0, 0, 0};
+    auto compute = [&](const Frag& f) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const i32x4_t b0 = f.b[c][0], b1 = f.b[c][1];
+            const i32x8_t b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                accg[r] = mfma_fp4_fp8(f.g[c][r], (int)((f.sg[r] >> (32 * c + sh)) & 0xffu), b,
+                                       accg[r]);
+                accu[r] = mfma_fp4_fp8(f.u[c][r], (int)((f.su[r] >> (32 * c + sh)) & 0xffu), b,
+                                       accu[r]);
+            }
+        }
+    };
+    const int nst = K / 256;  // K is a multiple of 256 here (checked by the launcher)
+    const int rot = (gw * kRot + blk * 5) % nst;
+    auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
+    // two fragments in turn, no copies; loads past the end repeat the last
+    // step (never multiplied), so every wait count is exact
+    Frag fa, fb;
+    load(fa, kstep(0));
+    for (int j = 0; j < nst; j += 2) {
+        load(fb, kstep(j + 1));
+        compute(fa);
+        load(fa, kstep(j + 2));
+        if (j + 1 < nst) compute(fb);
     }
-    if (K % 256) {
-        Chunk last;
-        load1(last, K - 128);
-        compute1(last);
+#pragma unroll
+    for (int r = 0; r < RT; ++r) {
+        pin(accg[r]);
+        pin(accu[r]);
     }
-    pin(accg);
-    pin(accu);
 
     float m = 0.0f;
     if (valid) {
         const float sx = xscale[t];
-        f32x4_t o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            o[v] = silu(accg[v] * sx) * (accu[v] * sx);
-            m = fmaxf(m, fabsf(o[v]));
+        for (int r = 0; r < RT; ++r) {
+            f32x4_t o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                o[v] = silu(accg[r][v] * sx) * (accu[r][v] * sx);
+                m = fmaxf(m, fabsf(o[v]));
+            }
+            *reinterpret_cast<f32x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 16 * r +
+                                        4 * kq) = o;
         }
-        *reinterpret_cast<f32x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 4 * kq) = o;
     }
     const uint32_t mb = col_max_bits(__float_as_uint(m));
     if (valid && kq == 0) atomicMax(amax + blk * kDecRows + i, mb);
@@ -516,13 +548,14 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
+    constexpr int RT = kMxTiles2;
     const int blk = (int)blockIdx.y;
     if (blk * kDecRows >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
-    const int c0 = gw * 32;
+    const int c0 = gw * 16 * RT;
     const int i = lane & 15, kq = lane >> 4;
     const int z = (int)blockIdx.z;
     const int nlen = N / nsplit;
@@ -534,60 +567,64 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const size_t row_bytes = (size_t)N / 2;
     const size_t srow = (size_t)N / 32;
     const size_t r0 = (size_t)e * K + c0;
-    const rsrc_t rw = make_rsrc(w2 + r0 * row_bytes, (uint32_t)(32 * row_bytes));
-    const rsrc_t rs = make_rsrc(w2e8 + r0 * srow, (uint32_t)(32 * srow));
+    const rsrc_t rw = make_rsrc(w2 + r0 * row_bytes, (uint32_t)(16 * RT * row_bytes));
+    const rsrc_t rs = make_rsrc(w2e8 + r0 * srow, (uint32_t)(16 * RT * srow));
     const rsrc_t ra = make_rsrc(act_q, (uint32_t)((size_t)cap * N));
     const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg / 2 + kq * 16;
-    const uint32_t wo1 = wo + (uint32_t)(16 * row_bytes);
     const uint32_t so = (uint32_t)(i * srow) + nbeg / 32;
-    const uint32_t so1 = so + (uint32_t)(16 * srow);
     const uint32_t ao = valid ? (uint32_t)((size_t)r * N) + nbeg + kq * 16 : kOob;
     const int sh = 8 * kq;
 
-    struct Chunk { i32x4_t a0, a1, b0, b1; uint32_t s0, s1; };
-    struct Frag { Chunk c[2]; };
-    auto load1 = [&](Chunk& f, int n) {
-        f.a0 = bload(rw, wo + n / 2);
-        f.a1 = bload(rw, wo1 + n / 2);
-        f.b0 = bload(ra, ao + n);
-        f.b1 = bload(ra, ao + n + 64);
-        f.s0 = bload_u32(rs, so + n / 32);
-        f.s1 = bload_u32(rs, so1 + n / 32);
+    struct Frag {
+        i32x4_t a[2][RT], b[2][2];
+        uint64_t s[RT];
     };
-    f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
-    auto compute1 = [&](const Chunk& f) {
-        const i32x8_t b = {f.b0[0], f.b0[1], f.b0[2], f.b0[3], f.b1[0], f.b1[1], f.b1[2], f.b1[3]};
-        acc0 = mfma_fp4_fp8(f.a0, (int)((f.s0 >> sh) & 0xffu), b, acc0);
-        acc1 = mfma_fp4_fp8(f.a1, (int)((f.s1 >> sh) & 0xffu), b, acc1);
-    };
-    auto load = [&](Frag& f, int n) { load1(f.c[0], n); load1(f.c[1], n + 128); };
-    auto compute = [&](const Frag& f) { compute1(f.c[0]); compute1(f.c[1]); };
-    const int nst = nlen / 256;  // whole two-chunk steps; an odd last chunk follows
-    if (nst > 0) {
-        const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
-        auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
-        Frag fa, fb;
-        load(fa, kstep(0));
-        for (int j = 0; j < nst; j += 2) {
-            load(fb, kstep(j + 1));
-            compute(fa);
-            load(fa, kstep(j + 2));
-            if (j + 1 < nst) compute(fb);
+    auto load = [&](Frag& f, int n) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int nc = n + 128 * c;
+#pragma unroll
+            for (int q = 0; q < RT; ++q)
+                f.a[c][q] = bload(rw, wo + (uint32_t)(16 * q * row_bytes) + nc / 2);
+            f.b[c][0] = bload(ra, ao + nc);
+            f.b[c][1] = bload(ra, ao + nc + 64);
         }
+#pragma unroll
+        for (int q = 0; q < RT; ++q) f.s[q] = bload_u64(rs, so + (uint32_t)(16 * q * srow) + n / 32);
+    };
+    f32x4_t acc[RT];
+#pragma unroll
+    for (int q = 0; q < RT; ++q) acc[q] = f32x4_t{0, 0, 0, 0};
+    auto compute = [&](const Frag& f) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const i32x4_t b0 = f.b[c][0], b1 = f.b[c][1];
+            const i32x8_t b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+            for (int q = 0; q < RT; ++q)
+                acc[q] = mfma_fp4_fp8(f.a[c][q], (int)((f.s[q] >> (32 * c + sh)) & 0xffu), b,
+                                      acc[q]);
+        }
+    };
+    const int nst = nlen / 256;  // nlen is a multiple of 256 here (checked by the launcher)
+    const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
+    auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
+    Frag fa, fb;
+    load(fa, kstep(0));
+    for (int j = 0; j < nst; j += 2) {
+        load(fb, kstep(j + 1));
+        compute(fa);
+        load(fa, kstep(j + 2));
+        if (j + 1 < nst) compute(fb);
     }
-    if (nlen % 256) {
-        Chunk last;
-        load1(last, nlen - 128);
-        compute1(last);
-    }
-    pin(acc0);
-    pin(acc1);
+#pragma unroll
+    for (int q = 0; q < RT; ++q) pin(acc[q]);
 
     if (valid) {
         const float w = topk_w[p] * ascale[r];
         float* yr = ypart + ((size_t)z * nslots + p) * K + c0 + 4 * kq;
-        *reinterpret_cast<f32x4_t*>(yr) = acc0 * w;
-        *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * w;
+#pragma unroll
+        for (int q = 0; q < RT; ++q) *reinterpret_cast<f32x4_t*>(yr + 16 * q) = acc[q] * w;
     }
 }
 
@@ -651,7 +688,7 @@ void launch_gemm1_decode_mxfp4(const uint8_t* xq, const float* xscale, const voi
                                const int32_t* block_expert, const int32_t* num_padded, int M,
                                int topk, int nslots, int K, int N, int max_blocks, float* act,
                                uint32_t* amax, hipStream_t s) {
-    dim3 grid(N / 64, max_blocks);
+    dim3 grid(N / (64 * kMxTiles1), max_blocks);
     gemm1_decode_mxfp4_kernel<<<grid, 256, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1e8,
                                                    sorted_ids, block_expert, num_padded, M, topk,
                                                    nslots, K, N, act, amax);
@@ -662,7 +699,7 @@ void launch_gemm2_decode_mxfp4(const uint8_t* act_q, const float* ascale, const 
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int nsplit, int max_blocks, float* ypart, hipStream_t s) {
-    dim3 grid(K / 128, max_blocks, nsplit);
+    dim3 grid(K / (64 * kMxTiles2), max_blocks, nsplit);
     gemm2_decode_mxfp4_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2e8,
                                                    topk_w, sorted_ids, block_expert, num_padded,
                                                    cap, nslots, K, N, nsplit, ypart);

@@ -229,8 +229,10 @@ SMALL = [
     ("fp8_rowwise_many_rows", 300, 256, 384, 8, 2, "rowwise", None, 0),
     # MXFP4 weights (e2m1, E8M0 per 32 elements) with e4m3 activations
     ("mxfp4_tiny", 16, 512, 256, 16, 4, "mxfp4", None, 0),
-    ("mxfp4_ragged", 7, 384, 640, 32, 8, "mxfp4", None, 0),
-    ("mxfp4_many_rows", 300, 256, 384, 8, 2, "mxfp4", None, 0),
+    ("mxfp4_ragged", 7, 768, 512, 32, 8, "mxfp4", None, 0),
+    ("mxfp4_many_rows", 300, 256, 512, 8, 2, "mxfp4", None, 0),
+    # many experts and a wider intermediate dimension
+    ("mxfp4_wide_grid", 32, 512, 1024, 64, 4, "mxfp4", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
 ]
 
