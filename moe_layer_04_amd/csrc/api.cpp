@@ -88,7 +88,7 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         while (tiles * p.nsplit < 256 && p.nsplit < 16 && (N / (p.nsplit * 2)) % gran == 0)
             p.nsplit *= 2;
     } else {
-        p.nsplit = moe::prefill_gemm2_splits(K, N);
+        p.nsplit = moe::prefill_gemm2_splits(K, N, p.grid_blocks);
     }
     size_t o = 0;
     auto take = [&](size_t bytes) {

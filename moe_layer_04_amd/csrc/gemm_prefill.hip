@@ -481,9 +481,16 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
 
-int prefill_gemm2_splits(int K, int N) {
-    (void)K;
-    return (N % (4 * 32) == 0) ? 4 : 1;
+int prefill_gemm2_splits(int K, int N, int blocks) {
+    // split the reduction until about four workgroups per CU exist: at one
+    // per CU a grid of 2.5 rounds leaves its last round half empty, while
+    // every split adds a partial row per slot for the combine to read
+    // (8 experts x 4096 x 14336, 39 blocks: 1118 us unsplit, 999 us in two
+    // splits, 1007 us in four, whose combine takes twice as long)
+    const long tiles = (long)(K % 256 == 0 ? K / 256 : K / 128) * blocks;
+    int ns = 1;
+    while (tiles * ns < 1024 && ns < 4 && (N / (2 * ns)) % 64 == 0) ns *= 2;
+    return ns;
 }
 
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
@@ -493,7 +500,8 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
     if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
         // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 8><<<grid, 512, 0, s>>>(
+        // four weight tiles per group (measured against 1, 2, 8 and 16)
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 4><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else if (K % 256 == 0) {

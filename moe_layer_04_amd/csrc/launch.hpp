@@ -81,9 +81,9 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                const int32_t* block_expert, const int32_t* num_padded, int M,
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s);
-// reduction splits the full-tile GEMM2 uses for (K, N); its partial rows go
-// to ypart[split] like the decode kernel's
-int prefill_gemm2_splits(int K, int N);
+// reduction splits the full-tile GEMM2 uses for (K, N) over `blocks` token
+// blocks; its partial rows go to ypart[split] like the decode kernel's
+int prefill_gemm2_splits(int K, int N, int blocks);
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
