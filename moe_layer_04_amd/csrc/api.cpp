@@ -52,6 +52,8 @@ struct Plan {
     // (number of such experts), and that number is <= min(E, slots).
     int grid_blocks = 0;
     int nsplit = 1;      // GEMM2 reduction split (decode)
+    int lsplit = 1;      // router-logit reduction split (fp64 partials in lpart)
+    size_t lpart = 0;
     size_t logits = 0, ids = 0, wts = 0, sorted = 0, bexp = 0, offs = 0, npad = 0;
     size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
 };
@@ -97,6 +99,10 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         return at;
     };
     p.logits = take((size_t)M * E * 4);
+    // the fused top-k + align kernel reads finished logits: split only when
+    // the separate top-k kernel runs
+    p.lsplit = moe::topk_align_fits(M, topk) ? 1 : moe::router_logit_splits(M, K, E);
+    if (p.lsplit > 1) p.lpart = take((size_t)p.lsplit * M * E * 8);
     p.ids = take((size_t)slots * 4);
     p.wts = take((size_t)slots * 4);
     p.sorted = take((size_t)p.cap * 4);
@@ -148,8 +154,10 @@ MOE_API moe_status moe_topk(const void* x, const void* w_router, const float* ro
         return MOE_ERR_INVALID_ARG;
     hipStream_t s = (hipStream_t)stream;
     (void)hipGetLastError();
-    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, nullptr, nullptr, s);
-    moe::launch_router_topk(logits, M, E, topk, topk_ids, topk_weights, s);
+    // no workspace here: the logits are finished by the logits kernel itself
+    moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, nullptr, nullptr, 1,
+                              nullptr, s);
+    moe::launch_router_topk(logits, M, E, topk, topk_ids, topk_weights, nullptr, 1, nullptr, s);
     return finish_launches();
 }
 
@@ -255,15 +263,17 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         // and short (a wave per token there; a workgroup per token otherwise)
         const bool q_late = fp8 && M <= kLateQuantRows && K <= kLateQuantCols;
         moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits,
-                                  q_late ? nullptr : xq, xs, s);
+                                  q_late ? nullptr : xq, xs, 1, nullptr, s);
         mark(1);
         moe::launch_topk_align(logits, x, M, K, E, topk, ids, wts, q_late ? xq : nullptr, xs,
                                p.block, p.cap, sorted, bexp, offs, npad, amax, amax_words, s);
         mark(2);
     } else {
-        moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, xq, xs, s);
+        double* lpart = p.lsplit > 1 ? (double*)(ws + p.lpart) : nullptr;
+        moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits, xq, xs, p.lsplit,
+                                  lpart, s);
         mark(1);
-        moe::launch_router_topk(logits, M, E, topk, ids, wts, s);
+        moe::launch_router_topk(logits, M, E, topk, ids, wts, lpart, p.lsplit, router_bias, s);
         mark(2);
         moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax,
                           amax_words, s);

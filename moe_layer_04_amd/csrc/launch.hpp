@@ -19,11 +19,16 @@ constexpr int kPrefillRows = 256;
 namespace moe {
 
 // logits [M,E]; with xq/xscale non-null also the per-token e4m3 codes and
-// scales (a second kernel; K % 8 == 0)
+// scales (a second kernel; K % 8 == 0).  With nks > 1 (a value from
+// router_logit_splits) the logits are left as nks fp64 partial sums in
+// lpart [nks,M,E], which launch_router_topk (same nks, lpart and bias)
+// turns into the logits before selecting.
+int router_logit_splits(int M, int K, int E);
 void launch_router_logits(const void* x, const void* wr, const float* bias, int M, int K, int E,
-                          float* logits, uint8_t* xq, float* xscale, hipStream_t s);
-void launch_router_topk(const float* logits, int M, int E, int topk, int32_t* ids, float* w,
-                        hipStream_t s);
+                          float* logits, uint8_t* xq, float* xscale, int nks, double* lpart,
+                          hipStream_t s);
+void launch_router_topk(float* logits, int M, int E, int topk, int32_t* ids, float* w,
+                        const double* lpart, int nks, const float* bias, hipStream_t s);
 void launch_quant_rows(const void* x, int M, int K, uint8_t* q, float* scale, hipStream_t s);
 
 void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,

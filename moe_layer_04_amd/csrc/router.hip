@@ -118,7 +118,11 @@ __global__ __launch_bounds__(256) void router_logits_kernel(
 // 16-token x 16-expert tile with v_mfma_f64_16x16x4_f64; its 16 waves split
 // K into contiguous ranges (K % 512 == 0) and the per-wave fp64 sums are
 // added in wave order through LDS (deterministic), then the bias and one
-// fp32 rounding.  Operand layout: lane l supplies token / expert row l % 16
+// fp32 rounding.  The kernel is bound by the fp64 matrix rate of the CU a
+// tile runs on, so with fewer tiles than CUs the reduction is also split
+// over nks workgroups per tile (ks-th contiguous range of K each), which
+// store fp64 partial sums; the top-k kernel then adds them in ks order,
+// adds the bias and rounds once.  Operand layout: lane l supplies token / expert row l % 16
 // at k-slot l / 16, and each 16-byte load of a row gives the elements of 8
 // successive MFMAs (MFMA m takes element m of every lane's 8-element run,
 // the same k for both operands).  Accumulator element q of lane l is tile
@@ -129,19 +133,21 @@ constexpr int kLogitWaves = 16;
 
 __global__ __launch_bounds__(kLogitWaves * 64) void router_logits_f64mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int M, int K, int E, float* __restrict__ logits) {
+    const float* __restrict__ bias, int M, int K, int E, float* __restrict__ logits, int nks,
+    double* __restrict__ lpart) {
     __shared__ double part[kLogitWaves][256];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int tiles_e = (E + 15) / 16;
-    const int t0 = ((int)blockIdx.x / tiles_e) * 16;
-    const int e0 = ((int)blockIdx.x % tiles_e) * 16;
+    const int tile = (int)blockIdx.x / nks, ks = (int)blockIdx.x % nks;
+    const int t0 = (tile / tiles_e) * 16;
+    const int e0 = (tile % tiles_e) * 16;
     const int r = lane & 15, kq = lane >> 4;
     // rows past M / E are clamped to a valid row; their sums are discarded
     const uint16_t* xr = x + (size_t)min(t0 + r, M - 1) * K + kq * 8;
     const uint16_t* wrr = wr + (size_t)min(e0 + r, E - 1) * K + kq * 8;
-    const int kw = K / kLogitWaves;
-    const int kb = wave * kw;
+    const int kw = K / nks / kLogitWaves;
+    const int kb = ks * (K / nks) + wave * kw;
     const int nblk = kw / 32;
 
     f64x4_t acc = {0.0, 0.0, 0.0, 0.0};
@@ -184,8 +190,12 @@ __global__ __launch_bounds__(kLogitWaves * 64) void router_logits_f64mfma_kernel
             double s = part[0][tid];
 #pragma unroll
             for (int w = 1; w < kLogitWaves; ++w) s += part[w][tid];
-            if (bias) s += (double)bias[e];
-            logits[(size_t)t * E + e] = (float)s;
+            if (nks > 1) {
+                lpart[((size_t)ks * M + t) * E + e] = s;
+            } else {
+                if (bias) s += (double)bias[e];
+                logits[(size_t)t * E + e] = (float)s;
+            }
         }
     }
 }
@@ -234,11 +244,24 @@ __global__ __launch_bounds__(256) void quant_rows_vec_kernel(const uint16_t* __r
 // ---------------------------------------------------------------------------
 // Top-k + weights: one wave per token (topk_wave in routing.hpp).
 // ---------------------------------------------------------------------------
+// With nks > 1 the wave first forms its token's logits from the fp64
+// partial sums (ascending ks, then the bias, one fp32 rounding) and stores
+// them; lane l handles experts l, l+64, ..., the same lanes that read them
+// back in topk_wave.
 __global__ __launch_bounds__(256) void router_topk_kernel(
-    const float* __restrict__ logits, int M, int E, int topk,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights) {
+    float* __restrict__ logits, int M, int E, int topk,
+    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    const double* __restrict__ lpart, int nks, const float* __restrict__ bias) {
     const int t = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
     if (t >= M) return;  // wave-uniform
+    if (nks > 1) {
+        for (int e = lane_id(); e < E; e += kWave) {
+            double s = lpart[(size_t)t * E + e];
+            for (int ks = 1; ks < nks; ++ks) s += lpart[((size_t)ks * M + t) * E + e];
+            if (bias) s += (double)bias[e];
+            logits[(size_t)t * E + e] = (float)s;
+        }
+    }
     topk_wave(logits + (size_t)t * E, E, topk, topk_ids + (size_t)t * topk,
               topk_weights + (size_t)t * topk, nullptr);
 }
@@ -266,8 +289,18 @@ __global__ __launch_bounds__(256) void quant_rows_kernel(const uint16_t* __restr
 // ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
+int router_logit_splits(int M, int K, int E) {
+    if ((long)M * E <= 8192 || K % (kLogitWaves * 32)) return 1;
+    // fp64 matrix work is the bound: split K until every CU holds a tile
+    const long tiles = (long)((M + 15) / 16) * ((E + 15) / 16);
+    int nks = 1;
+    while (tiles * nks < 256 && nks < 4 && K % (kLogitWaves * 32 * nks * 2) == 0) nks *= 2;
+    return nks;
+}
+
 void launch_router_logits(const void* x, const void* wr, const float* bias, int M, int K, int E,
-                          float* logits, uint8_t* xq, float* xscale, hipStream_t s) {
+                          float* logits, uint8_t* xq, float* xscale, int nks, double* lpart,
+                          hipStream_t s) {
     const uint16_t* xp = (const uint16_t*)x;
     const uint16_t* wp = (const uint16_t*)wr;
     if ((long)M * E <= 8192) {
@@ -277,9 +310,9 @@ void launch_router_logits(const void* x, const void* wr, const float* bias, int 
         else
             router_logits_kernel<1, 1, false><<<grid, 256, 0, s>>>(xp, wp, bias, M, K, E, logits);
     } else if (K % (kLogitWaves * 32) == 0) {
-        const int grid = ((M + 15) / 16) * ((E + 15) / 16);
+        const int grid = ((M + 15) / 16) * ((E + 15) / 16) * nks;
         router_logits_f64mfma_kernel<<<grid, kLogitWaves * 64, 0, s>>>(xp, wp, bias, M, K, E,
-                                                                      logits);
+                                                                      logits, nks, lpart);
     } else {
         const int grid = ((M + 3) / 4) * ((E + 3) / 4);
         if (K % 8 == 0)
@@ -290,10 +323,10 @@ void launch_router_logits(const void* x, const void* wr, const float* bias, int 
     if (xq) quant_rows_vec_kernel<<<M, 256, 0, s>>>(xp, M, K, xq, xscale);
 }
 
-void launch_router_topk(const float* logits, int M, int E, int topk, int32_t* ids, float* w,
-                        hipStream_t s) {
+void launch_router_topk(float* logits, int M, int E, int topk, int32_t* ids, float* w,
+                        const double* lpart, int nks, const float* bias, hipStream_t s) {
     const int grid = (M + 3) / 4;
-    router_topk_kernel<<<grid, 256, 0, s>>>(logits, M, E, topk, ids, w);
+    router_topk_kernel<<<grid, 256, 0, s>>>(logits, M, E, topk, ids, w, lpart, nks, bias);
 }
 
 void launch_quant_rows(const void* x, int M, int K, uint8_t* q, float* scale, hipStream_t s) {

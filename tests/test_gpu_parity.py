@@ -231,6 +231,9 @@ SMALL = [
     ("mxfp4_tiny", 16, 512, 256, 16, 4, "mxfp4", None, 0),
     ("mxfp4_ragged", 7, 768, 512, 32, 8, "mxfp4", None, 0),
     ("mxfp4_many_rows", 300, 256, 512, 8, 2, "mxfp4", None, 0),
+    # router logits on the fp64 matrix cores with K split over 4 workgroups
+    # per 16x16 tile (finished by the top-k kernel)
+    ("router_split_k", 80, 2048, 256, 128, 4, False, 0.5, 0),
     # many experts and a wider intermediate dimension
     ("mxfp4_wide_grid", 32, 512, 1024, 64, 4, "mxfp4", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
