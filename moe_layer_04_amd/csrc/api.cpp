@@ -79,16 +79,26 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         p.grid_blocks = (int)(bound < p.max_blocks ? bound : p.max_blocks);
     }
     if (regime == MOE_REGIME_DECODE) {
-        // split GEMM2's reduction until the grid holds about one workgroup
-        // per CU; past that, longer per-wave streams measured faster (e.g.
-        // 8 experts x 4096 x 14336: 160 us unsplit, 167 us in 8 splits)
+        // GEMM2's reduction split (measured on three shapes, two weight
+        // formats): a grid that already holds a workgroup per CU stays
+        // unsplit (8 experts x 4096 x 14336 bf16: 160 us unsplit, 166-171 us
+        // in 2-16 splits); a smaller one splits until about two workgroups
+        // per CU, while each wave still streams at least 32 KB of weights
+        // (2 experts x 4096 x 8192: bf16 best in 8 splits, MXFP4 in 8, its
+        // 16 splits leaving 16 KB per wave measured 12 % slower)
         const long est_blocks = slots < E ? slots : E;
         const int mx = dtype == MOE_MXFP4_E2M1;
         const long tiles = est_blocks * (K / (mx ? 256 : 128));  // output rows per workgroup
+        // weight bytes per output row of a wave's tile, per reduction element
+        // (bf16: 32 rows x 2 B; e4m3: 32 x 1 B; MXFP4: 64 rows x 1/2 B)
+        const long row_bytes = dtype == MOE_BF16 ? 64 : 32;
         // each split's reduction length stays a multiple of the kernels' step
         const int gran = mx ? 256 : 128;
-        while (tiles * p.nsplit < 256 && p.nsplit < 16 && (N / (p.nsplit * 2)) % gran == 0)
-            p.nsplit *= 2;
+        if (tiles < 256)
+            while (tiles * p.nsplit < 512 && p.nsplit < 16 &&
+                   (N / (p.nsplit * 2)) % gran == 0 &&
+                   row_bytes * (N / (p.nsplit * 2)) >= 32 * 1024)
+                p.nsplit *= 2;
     } else {
         p.nsplit = moe::prefill_gemm2_splits(K, N, p.grid_blocks);
     }

@@ -476,7 +476,8 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 2><<<grid, 512, 0, s>>>(
+    // four weight tiles per XCD tile group (measured against 1, 2, 3 and 8)
+    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 4><<<grid, 512, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
