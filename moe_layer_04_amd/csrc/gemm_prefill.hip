@@ -166,14 +166,26 @@ struct PrefillCore {
         return (lane % kCPR) ^ swz<BK>(row);
     }
 
-    // woff[q] / xoff[q]: byte offset at k = kbeg of this lane's source chunk;
-    // the loop covers klen reduction elements.  With COMPUTE false the wave
-    // only takes its share of the copies and barriers (its token columns are
-    // all padding): no LDS reads, no MFMAs, accumulators stay zero.
-    template <bool COMPUTE>
-    __device__ __forceinline__ void run(char* lds, prsrc_t rw, const uint32_t* woff, prsrc_t rx,
-                                        const uint32_t* xoff, int klen, int wave, int wb,
-                                        const int* arow) {
+    // Source offsets at k = kbeg of this lane's chunk: weight copy q reads
+    // wvoff + wsoff[q] (wsoff wave-uniform, a scalar operand: the weight rows
+    // of a wave's copies differ by whole-row amounts the same for every
+    // lane), token copy q reads xoff[q] (gathered rows, per lane).  The A
+    // fragments of the wave are LDS rows arow0 + (a % AH)*32 + (a / AH)*AJUMP
+    // with AH = FW/2 when AJUMP is non-zero (GEMM1's gate and up halves),
+    // else FW; those rows differ by multiples of 16, so they share one
+    // swizzle and their LDS offsets differ by constants.  The loop covers
+    // klen reduction elements.  With COMPUTE false the wave only takes its
+    // share of the copies and barriers (its token columns are all padding):
+    // no LDS reads, no MFMAs, accumulators stay zero.
+    template <int AJUMP>
+    __device__ static constexpr int arow_delta(int a) {
+        return AJUMP ? (a % (FW / 2)) * 32 + (a / (FW / 2)) * AJUMP : a * 32;
+    }
+    template <bool COMPUTE, int AJUMP>
+    __device__ __forceinline__ void run(char* lds, prsrc_t rw, uint32_t wvoff,
+                                        const uint32_t* wsoff, prsrc_t rx, const uint32_t* xoff,
+                                        int klen, int wave, int wb, int arow0) {
+        static_assert(AJUMP % 16 == 0, "fragment rows must share one swizzle");
         const int lane = lane_id();
 #pragma unroll
         for (int a = 0; a < FW; ++a)
@@ -189,7 +201,8 @@ struct PrefillCore {
 #pragma unroll
             for (int q = 0; q < kWInstr; ++q)
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                    rw, (lds_ptr_t)(base + (q * NW + wave) * 1024), 16, woff[q] + kb, 0, 0, 0);
+                    rw, (lds_ptr_t)(base + (q * NW + wave) * 1024), 16, wvoff + kb, wsoff[q], 0,
+                    0);
         };
         auto dma_x = [&](int step, int slot) {
             const uint32_t kb = (uint32_t)step * kRowBytes;
@@ -200,34 +213,31 @@ struct PrefillCore {
                     rx, (lds_ptr_t)(base + (q * NW + wave) * 1024), 16, xoff[q] + kb, 0, 0, 0);
         };
 
-        // per-lane LDS read offsets (bytes within a slot) for each k16 slice
+        // per-lane LDS read offsets (bytes within a slot) of the first A and
+        // B fragment for each k16 slice; the others are constant offsets
         const int li = lane & 31, half = lane >> 5;
-        int aoff[KS][FW], boff[KS][FT];
+        int aoff[KS], boff[KS];
+        {
+            const int ra = arow0 + li, rb = wb * (TT / WT) + li;
 #pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int c = 2 * ks + half;
-#pragma unroll
-            for (int a = 0; a < FW; ++a) {
-                const int r = arow[a] + li;
-                aoff[ks][a] = r * kRowBytes + ((c ^ swz<BK>(r)) << 4);
-            }
-#pragma unroll
-            for (int b = 0; b < FT; ++b) {
-                const int r = wb * (TT / WT) + b * 32 + li;
-                boff[ks][b] = r * kRowBytes + ((c ^ swz<BK>(r)) << 4);
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = 2 * ks + half;
+                aoff[ks] = ra * kRowBytes + ((c ^ swz<BK>(ra)) << 4);
+                boff[ks] = rb * kRowBytes + ((c ^ swz<BK>(rb)) << 4);
             }
         }
         struct Frags { bf16x8_t a[FW], b[FT]; };
         auto read = [&](Frags& f, int wslot, int xslot, int ks) {
             if constexpr (!COMPUTE) return;
-            const char* wbase = lds + wslot * kWSlot;
-            const char* xbase = lds + kXBase + xslot * kXSlot;
+            const char* wbase = lds + wslot * kWSlot + aoff[ks];
+            const char* xbase = lds + kXBase + xslot * kXSlot + boff[ks];
 #pragma unroll
             for (int a = 0; a < FW; ++a)
-                f.a[a] = *reinterpret_cast<const bf16x8_t*>(wbase + aoff[ks][a]);
+                f.a[a] = *reinterpret_cast<const bf16x8_t*>(wbase +
+                                                            arow_delta<AJUMP>(a) * kRowBytes);
 #pragma unroll
             for (int b = 0; b < FT; ++b)
-                f.b[b] = *reinterpret_cast<const bf16x8_t*>(xbase + boff[ks][b]);
+                f.b[b] = *reinterpret_cast<const bf16x8_t*>(xbase + b * 32 * kRowBytes);
         };
         auto mfmas = [&](const Frags& f) {
             if constexpr (!COMPUTE) return;
@@ -336,12 +346,18 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const size_t row_bytes = (size_t)K * 2;
     const prsrc_t rw = pmake_rsrc(w1 + (size_t)e * 2 * N * K, (uint32_t)(2 * (size_t)N * row_bytes));
     const prsrc_t rx = pmake_rsrc(x, (uint32_t)((size_t)M * row_bytes));
-    uint32_t woff[Core::kWInstr], xoff[Core::kXInstr];
+    // weight copy q covers LDS rows q*NW*R + wave*R .. +R (R rows per copy,
+    // a multiple of 8 never straddling the gate/up boundary HW): its global
+    // rows are those of copy 0 moved by a wave-uniform amount
+    uint32_t wsoff[Core::kWInstr], xoff[Core::kXInstr];
+    const int row0 = Core::dma_row(wave, 0, lane);
+    const uint32_t wvoff = (uint32_t)((wt * HW + row0) * row_bytes) +
+                           Core::dma_chunk(row0, lane) * 16;
 #pragma unroll
     for (int q = 0; q < Core::kWInstr; ++q) {
-        const int row = Core::dma_row(wave, q, lane);
-        const int wrow = (row < HW) ? (wt * HW + row) : (N + wt * HW + row - HW);
-        woff[q] = (uint32_t)(wrow * row_bytes) + Core::dma_chunk(row, lane) * 16;
+        const int first = (q * NW + wave) * Core::kRowsPerInstr;  // wave-uniform
+        const int shift = q * NW * Core::kRowsPerInstr + (first >= HW ? N - HW : 0);
+        wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * row_bytes));
     }
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
@@ -350,20 +366,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
         const int t = p < nslots ? p / topk : 0;
         xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
-    // A tiles of this wave: its gate frags, then the matching up frags
-    int arow[Core::FW];
-#pragma unroll
-    for (int a = 0; a < Core::FW / 2; ++a) {
-        arow[a] = wa * WN + a * 32;
-        arow[a + Core::FW / 2] = HW + wa * WN + a * 32;
-    }
+    // A tiles of this wave: its gate frags (LDS rows wa*WN + 32a), then the
+    // matching up frags HW rows further
     Core core;
     // a wave whose token rows are all padding (the tail of an expert's last
     // block) skips its MFMAs
     if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
-        core.template run<true>(lds, rw, woff, rx, xoff, K, wave, wb, arow);
+        core.template run<true, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
     else
-        core.template run<false>(lds, rw, woff, rx, xoff, K, wave, wb, arow);
+        core.template run<false, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
 
     const int li = lane & 31;
 #pragma unroll
@@ -419,12 +430,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const prsrc_t rw = pmake_rsrc(w2 + ((size_t)e * K + (size_t)wt * TW) * N,
                                   (uint32_t)(TW * row_bytes));
     const prsrc_t ra = pmake_rsrc(act, (uint32_t)((size_t)cap * row_bytes));
-    uint32_t woff[Core::kWInstr], aoff[Core::kXInstr];
+    uint32_t wsoff[Core::kWInstr], aoff[Core::kXInstr];
+    const int row0 = Core::dma_row(wave, 0, lane);
+    const uint32_t wvoff = (uint32_t)(row0 * row_bytes) + nbeg * 2 +
+                           Core::dma_chunk(row0, lane) * 16;
 #pragma unroll
-    for (int q = 0; q < Core::kWInstr; ++q) {
-        const int row = Core::dma_row(wave, q, lane);
-        woff[q] = (uint32_t)(row * row_bytes) + nbeg * 2 + Core::dma_chunk(row, lane) * 16;
-    }
+    for (int q = 0; q < Core::kWInstr; ++q)
+        wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(q * NW * Core::kRowsPerInstr * row_bytes));
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
@@ -433,14 +446,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
         const int src = sorted_ids[blk * TT + row] < nslots ? blk * TT + row : blk * TT;
         aoff[q] = (uint32_t)(src * row_bytes) + nbeg * 2 + Core::dma_chunk(row, lane) * 16;
     }
-    int arow[Core::FW];
-#pragma unroll
-    for (int a = 0; a < Core::FW; ++a) arow[a] = wa * WR + a * 32;
     Core core;
+    // A tiles of this wave: LDS rows wa*WR + 32a
     if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
-        core.template run<true>(lds, rw, woff, ra, aoff, nlen, wave, wb, arow);
+        core.template run<true, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
     else
-        core.template run<false>(lds, rw, woff, ra, aoff, nlen, wave, wb, arow);
+        core.template run<false, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
 
     const int li = lane & 31;
 #pragma unroll
