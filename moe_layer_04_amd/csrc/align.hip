@@ -15,10 +15,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int n, int E, int B, int cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded,
-    uint32_t* __restrict__ zero_buf, int zero_words) {
+    uint32_t* __restrict__ zero_buf, int zero_words, int32_t* __restrict__ inv) {
     __shared__ AlignShared sh;
     align_body(sh, ids, n, E, B, cap, sorted_ids, block_expert, expert_offsets, num_padded,
-               zero_buf, zero_words);
+               zero_buf, zero_words, inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -35,7 +35,7 @@ __global__ __launch_bounds__(kAlignThreads) void topk_align_kernel(
     uint8_t* __restrict__ xq, float* __restrict__ xscale, int B, int cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded,
-    uint32_t* __restrict__ zero_buf, int zero_words) {
+    uint32_t* __restrict__ zero_buf, int zero_words, int32_t* __restrict__ inv) {
     __shared__ int32_t sid[kRouteSmallMaxSlots];
     __shared__ AlignShared sh;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
@@ -47,14 +47,15 @@ __global__ __launch_bounds__(kAlignThreads) void topk_align_kernel(
                   topk_weights + (size_t)t * topk, sid + t * topk);
     __syncthreads();
     align_body(sh, sid, M * topk, E, B, cap, sorted_ids, block_expert, expert_offsets,
-               num_padded, zero_buf, zero_words);
+               num_padded, zero_buf, zero_words, inv);
 }
 
 void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,
                   int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
-                  uint32_t* zero_buf, int zero_words, hipStream_t s) {
+                  uint32_t* zero_buf, int zero_words, int32_t* inv, hipStream_t s) {
     align_kernel<<<1, kAlignThreads, 0, s>>>(ids, n, E, B, cap, sorted_ids, block_expert,
-                                             expert_offsets, num_padded, zero_buf, zero_words);
+                                             expert_offsets, num_padded, zero_buf, zero_words,
+                                             inv);
 }
 
 bool topk_align_fits(int M, int topk) {
@@ -65,10 +66,11 @@ bool topk_align_fits(int M, int topk) {
 void launch_topk_align(const float* logits, const void* x, int M, int K, int E, int topk,
                        int32_t* ids, float* w, uint8_t* xq, float* xscale, int B, int cap,
                        int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
-                       int32_t* num_padded, uint32_t* zero_buf, int zero_words, hipStream_t s) {
+                       int32_t* num_padded, uint32_t* zero_buf, int zero_words, int32_t* inv,
+                       hipStream_t s) {
     topk_align_kernel<<<1, kAlignThreads, 0, s>>>(
         logits, (const uint16_t*)x, M, K, E, topk, ids, w, xq, xscale, B, cap, sorted_ids,
-        block_expert, expert_offsets, num_padded, zero_buf, zero_words);
+        block_expert, expert_offsets, num_padded, zero_buf, zero_words, inv);
 }
 
 }  // namespace moe

@@ -55,6 +55,7 @@ struct Plan {
     int lsplit = 1;      // router-logit reduction split (fp64 partials in lpart)
     size_t lpart = 0;
     size_t logits = 0, ids = 0, wts = 0, sorted = 0, bexp = 0, offs = 0, npad = 0;
+    size_t inv = 0;  // FP8 activations: sorted position of each slot
     size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
 };
 
@@ -123,6 +124,7 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         p.xq = take((size_t)M * K);
         p.xs = take((size_t)M * 4);
         p.amax = take((size_t)p.cap * 4);
+        p.inv = take((size_t)slots * 4);
         p.act = take((size_t)p.cap * N * 4);
         p.actq = take((size_t)p.cap * N);
         p.as = take((size_t)p.cap * 4);
@@ -199,7 +201,7 @@ MOE_API moe_status moe_align(const int32_t* topk_ids, int M, int topk, int E, in
     const int cap = n + E * (block_m - 1);
     (void)hipGetLastError();
     moe::launch_align(topk_ids, n, E, block_m, cap, sorted_ids, block_expert, expert_offsets,
-                      num_padded, nullptr, 0, (hipStream_t)stream);
+                      num_padded, nullptr, 0, nullptr, (hipStream_t)stream);
     return finish_launches();
 }
 
@@ -267,6 +269,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     // routing clears on the way
     uint32_t* amax = fp8 ? (uint32_t*)(ws + p.amax) : nullptr;
     const int amax_words = fp8 ? p.cap : 0;
+    int32_t* inv = fp8 ? (int32_t*)(ws + p.inv) : nullptr;
     mark(0);
     if (moe::topk_align_fits(M, topk)) {
         // the FP8 token codes go with top-k + align when the tokens are few
@@ -276,7 +279,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                   q_late ? nullptr : xq, xs, 1, nullptr, s);
         mark(1);
         moe::launch_topk_align(logits, x, M, K, E, topk, ids, wts, q_late ? xq : nullptr, xs,
-                               p.block, p.cap, sorted, bexp, offs, npad, amax, amax_words, s);
+                               p.block, p.cap, sorted, bexp, offs, npad, amax, amax_words, inv,
+                               s);
         mark(2);
     } else {
         double* lpart = p.lsplit > 1 ? (double*)(ws + p.lpart) : nullptr;
@@ -286,7 +290,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         moe::launch_router_topk(logits, M, E, topk, ids, wts, lpart, p.lsplit, router_bias, s);
         mark(2);
         moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax,
-                          amax_words, s);
+                          amax_words, inv, s);
     }
     mark(3);
     if (fp8) {
@@ -302,7 +306,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
             moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
                                          topk, nslots, K, N, p.grid_blocks, act, amax, s);
         mark(4);
-        moe::launch_act_quant(act, amax, sorted, npad, nslots, N, p.cap, actq, as, s);
+        moe::launch_act_quant(act, amax, inv, nslots, N, actq, as, s);
         mark(5);
         if (mx)
             moe::launch_gemm2_decode_mxfp4(actq, as, w2, (const uint8_t*)w2_scale, wts, sorted,

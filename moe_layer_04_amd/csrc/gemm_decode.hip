@@ -306,12 +306,14 @@ constexpr int kActChunk = 8 * kWave * 4;
 
 __global__ __launch_bounds__(256) void act_quant_kernel(
     const float* __restrict__ act, const uint32_t* __restrict__ amax,
-    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ num_padded, int nslots,
-    int N, int nchunk, int cap, uint8_t* __restrict__ act_q, float* __restrict__ ascale) {
+    const int32_t* __restrict__ inv, int nslots, int N, int nchunk,
+    uint8_t* __restrict__ act_q, float* __restrict__ ascale) {
+    // waves cover the slots (padding rows are never read): slot p's row is
+    // its sorted position inv[p], written by the align step
     const int w = (int)(blockIdx.x * 4 + threadIdx.x / kWave);
-    const int r = w / nchunk, ch = w % nchunk;
-    if (r >= cap || r >= *num_padded) return;
-    if (sorted_ids[r] >= nslots) return;
+    const int p = w / nchunk, ch = w % nchunk;
+    if (p >= nslots) return;
+    const int r = inv[p];
     const int lane = lane_id();
     const float a = __uint_as_float(amax[r]);
     const float s = (a == 0.0f) ? 1.0f : a / 448.0f;
@@ -662,14 +664,12 @@ void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void*
                                                  nslots, K, N, act, amax);
 }
 
-void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sorted_ids,
-                      const int32_t* num_padded, int nslots, int N, int cap, uint8_t* act_q,
-                      float* ascale, hipStream_t s) {
+void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* inv, int nslots,
+                      int N, uint8_t* act_q, float* ascale, hipStream_t s) {
     const int nchunk = (N + kActChunk - 1) / kActChunk;
-    const long waves = (long)cap * nchunk;
-    act_quant_kernel<<<(int)((waves + 3) / 4), 256, 0, s>>>(act, amax, sorted_ids, num_padded,
-                                                             nslots, N, nchunk, cap, act_q,
-                                                             ascale);
+    const long waves = (long)nslots * nchunk;
+    act_quant_kernel<<<(int)((waves + 3) / 4), 256, 0, s>>>(act, amax, inv, nslots, N, nchunk,
+                                                             act_q, ascale);
 }
 
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,

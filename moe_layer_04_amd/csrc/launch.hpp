@@ -31,9 +31,10 @@ void launch_router_topk(float* logits, int M, int E, int topk, int32_t* ids, flo
                         const double* lpart, int nks, const float* bias, hipStream_t s);
 void launch_quant_rows(const void* x, int M, int K, uint8_t* q, float* scale, hipStream_t s);
 
+// inv (optional): inv[p] = sorted position of slot p
 void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,
                   int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
-                  uint32_t* zero_buf, int zero_words, hipStream_t s);
+                  uint32_t* zero_buf, int zero_words, int32_t* inv, hipStream_t s);
 
 // Top-k + align (and, with xq not null, the FP8 token codes; meant for a
 // few tokens) in one single-workgroup launch, for at most kRouteSmallMaxTokens
@@ -44,7 +45,8 @@ bool topk_align_fits(int M, int topk);
 void launch_topk_align(const float* logits, const void* x, int M, int K, int E, int topk,
                        int32_t* ids, float* w, uint8_t* xq, float* xscale, int B, int cap,
                        int32_t* sorted_ids, int32_t* block_expert, int32_t* expert_offsets,
-                       int32_t* num_padded, uint32_t* zero_buf, int zero_words, hipStream_t s);
+                       int32_t* num_padded, uint32_t* zero_buf, int zero_words, int32_t* inv,
+                       hipStream_t s);
 
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded, int M,
@@ -60,9 +62,9 @@ void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void*
                              const int32_t* block_expert, const int32_t* num_padded, int M,
                              int topk, int nslots, int K, int N, int max_blocks, float* act,
                              uint32_t* amax, hipStream_t s);
-void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* sorted_ids,
-                      const int32_t* num_padded, int nslots, int N, int cap, uint8_t* act_q,
-                      float* ascale, hipStream_t s);
+// rows of the nslots slots only: slot p is sorted row inv[p]
+void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* inv, int nslots,
+                      int N, uint8_t* act_q, float* ascale, hipStream_t s);
 void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
                              const float* w2_scale, int rowwise, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,

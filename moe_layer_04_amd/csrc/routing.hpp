@@ -140,13 +140,15 @@ struct AlignShared {
 // each lane's rank among earlier lanes of the same expert comes from 8
 // ballots over the bits of the expert id (a wave-level match) plus the
 // per-wave counts of earlier waves, so the order never depends on atomics.
-// zero_buf[0 .. zero_words) is cleared on the way (a caller buffer).
+// zero_buf[0 .. zero_words) is cleared on the way (a caller buffer); with
+// inv not null, inv[p] receives the sorted position of slot p.
 __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* ids, int n, int E,
                                            int B, int cap, int32_t* __restrict__ sorted_ids,
                                            int32_t* __restrict__ block_expert,
                                            int32_t* __restrict__ expert_offsets,
                                            int32_t* __restrict__ num_padded,
-                                           uint32_t* __restrict__ zero_buf, int zero_words) {
+                                           uint32_t* __restrict__ zero_buf, int zero_words,
+                                           int32_t* __restrict__ inv) {
     const int tid = (int)threadIdx.x;
     const int lane = lane_id();
     const int wave = tid / kWave;
@@ -242,7 +244,9 @@ __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* ids, 
         if (valid) {
             int before = 0;
             for (int w = 0; w < wave; ++w) before += sh.wc[w][e];
-            sorted_ids[sh.off[e] + sh.run[e] + before + rank] = p;
+            const int pos = sh.off[e] + sh.run[e] + before + rank;
+            sorted_ids[pos] = p;
+            if (inv) inv[p] = pos;
         }
         __syncthreads();
         for (int x = tid; x < E; x += kAlignThreads) {
