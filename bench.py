@@ -389,7 +389,9 @@ def main():
         "dtype": dtype_name,
         "data": "synthetic (seeded N(0,1/fan_in) weights, random init; no dataset)",
         "config": {"workload": wl.name, "M": wl.M, "K": wl.K, "N": wl.N, "E": wl.E,
-                   "topk": wl.topk, "weights": ("e4m3 per-channel" if wl.fp8_rowwise else "e4m3 per-tensor") if wl.fp8 else "bf16",
+                   "topk": wl.topk, "weights": ("mxfp4 (e2m1, E8M0 per 32)" if wl.mxfp4 else
+                               ("e4m3 per-channel" if wl.fp8_rowwise else "e4m3 per-tensor")
+                               if wl.fp8 else "bf16"),
                    "router_bias_var": wl.bias_var, "seed": wl.seed, "layers": layers,
                    "active_experts": active},
         "step_hbm_GBps": round(alg_bytes / step_s / 1e9, 1),
@@ -425,7 +427,8 @@ def main():
         t0 = time.perf_counter()
         while True:
             ref, _, _ = oracle.moe_forward(x_h, wr_h, bias_h, w1h, w2h, wl.topk, w1_scale=s1,
-                                           w2_scale=s2, tokens=toks, fp8=wl.fp8)
+                                           w2_scale=s2, tokens=toks, fp8=wl.fp8,
+                                           mxfp4=wl.mxfp4)
             reps += 1
             if time.perf_counter() - t0 >= CPU_SECONDS:
                 break
@@ -440,7 +443,7 @@ def main():
                       f"({n_tok * wl.topk} token-slots, fp64), evaluated {reps} times",
             "seconds": round(cpu_s, 3)}
         result["parity_vs_oracle"] = {"max_row_rel_err": err, "tokens": n_tok,
-                                      "tol": 6e-2 if wl.fp8 else 2e-2}
+                                      "tol": 6e-2 if (wl.fp8 or wl.mxfp4) else 2e-2}
     print(json.dumps(result), flush=True)
 
 
