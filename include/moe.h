@@ -88,7 +88,7 @@ typedef enum {
 
 /* Supported envelope: 1 <= E <= 256, 1 <= topk <= min(E,16), K >= 1 and
  * N >= 1; moe_fused_forward additionally needs K and N multiples of 128
- * (of 256 for MOE_MXFP4_E2M1),
+ * (of 256, and K <= 16384, for MOE_MXFP4_E2M1),
  * M*topk < 2^30, (M*topk + 256*E) * max(K,N) * 4 < 2^31 (the sorted
  * activation rows), M*K*2 < 2^31 and 2*N*K*2 < 2^31 (one expert's W1). */
 #define MOE_MAX_EXPERTS 256

@@ -219,7 +219,10 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     if (is_fp8(dtype) && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
     if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
-    if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256)) return MOE_ERR_UNSUPPORTED;
+    // MXFP4: 256-deep steps; GEMM1 keeps K/32 scale bytes per row of its
+    // waves in LDS (K <= 16384: 64 KB per workgroup)
+    if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256 || K > 16384))
+        return MOE_ERR_UNSUPPORTED;
     if (is_fp8(dtype) && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
     const long kn = K > N ? K : N;

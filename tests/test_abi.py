@@ -86,6 +86,7 @@ def test_fused_validation(lib):
     assert fused(lib, dtype=3)[0] == INV                              # MXFP4 without scales
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=384)[0] == UNS       # MXFP4: multiples of 256
+    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, K=16640)[0] == UNS     # MXFP4: K <= 16384
     assert fused(lib, dtype=2)[0] == INV                              # rowwise fp8 without scales
     assert fused(lib, dtype=2, s1=FAKE, s2=None)[0] == INV
     assert fused(lib, dtype=2, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
