@@ -100,6 +100,11 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
                    (N / (p.nsplit * 2)) % gran == 0 &&
                    row_bytes * (N / (p.nsplit * 2)) >= 32 * 1024)
                 p.nsplit *= 2;
+        // MXFP4's GEMM2 keeps each split's scale bytes in LDS: at most 8192
+        // reduction elements per split (64 KB per workgroup)
+        if (mx)
+            while (N / p.nsplit > 8192 && p.nsplit < 16 && (N / (p.nsplit * 2)) % gran == 0)
+                p.nsplit *= 2;
     } else {
         p.nsplit = moe::prefill_gemm2_splits(K, N, p.grid_blocks);
     }
@@ -234,6 +239,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         return MOE_ERR_UNSUPPORTED;
     const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
     if (p.max_blocks > 65535) return MOE_ERR_UNSUPPORTED;
+    // MXFP4 GEMM2: a split's scale bytes must fit its LDS copy
+    if (dtype == MOE_MXFP4_E2M1 && N / p.nsplit > 8192) return MOE_ERR_UNSUPPORTED;
     if (!workspace) {
         *workspace_bytes = p.total;
         return MOE_OK;

@@ -429,7 +429,8 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
 constexpr int kMxTiles1 = 1;  // GEMM1: 16 gate + 16 up rows per wave
 constexpr int kMxTiles2 = 4;  // GEMM2: 64 output rows per wave
 
-// GEMM1's per-wave E8M0 scale copies (dynamic LDS, sized by the launcher)
+// per-wave E8M0 scale copies of the MXFP4 kernels (dynamic LDS, sized by
+// the launchers)
 extern __shared__ __attribute__((aligned(16))) char mx_scale_lds[];
 
 __device__ __forceinline__ uint64_t bload_u64(rsrc_t r, uint32_t off) {
@@ -590,9 +591,22 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const rsrc_t rs = make_rsrc(w2e8 + r0 * srow, (uint32_t)(16 * RT * srow));
     const rsrc_t ra = make_rsrc(act_q, (uint32_t)((size_t)cap * N));
     const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg / 2 + kq * 16;
-    const uint32_t so = (uint32_t)(i * srow) + nbeg / 32;
     const uint32_t ao = valid ? (uint32_t)((size_t)r * N) + nbeg + kq * 16 : kOob;
     const int sh = 8 * kq;
+
+    // the split's E8M0 bytes of the wave's 16*RT rows (nlen/32 per row),
+    // copied once into the wave's LDS region in 8-byte pieces, row-major
+    const int sspan = nlen / 32;  // a multiple of 8 (nlen % 256 == 0)
+    char* sl = mx_scale_lds + (size_t)wave * 16 * RT * sspan;
+    {
+        const int upr = sspan / 8;
+        for (int u = lane; u < 16 * RT * upr; u += kWave) {
+            const int row = u / upr, col = u - row * upr;
+            *reinterpret_cast<uint64_t*>(sl + row * sspan + col * 8) =
+                bload_u64(rs, (uint32_t)(row * srow) + nbeg / 32 + col * 8);
+        }
+    }
+    __syncthreads();
 
     struct Frag {
         i32x4_t a[2][RT], b[2][2];
@@ -609,7 +623,8 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
             f.b[c][1] = bload(ra, ao + nc + 64);
         }
 #pragma unroll
-        for (int q = 0; q < RT; ++q) f.s[q] = bload_u64(rs, so + (uint32_t)(16 * q * srow) + n / 32);
+        for (int q = 0; q < RT; ++q)
+            f.s[q] = *reinterpret_cast<const uint64_t*>(sl + (i + 16 * q) * sspan + n / 32);
     };
     f32x4_t acc[RT];
 #pragma unroll
@@ -720,7 +735,10 @@ void launch_gemm2_decode_mxfp4(const uint8_t* act_q, const float* ascale, const 
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     dim3 grid(K / (64 * kMxTiles2), max_blocks, nsplit);
-    gemm2_decode_mxfp4_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2e8,
+    // 4 waves x 16*RT rows x (N/nsplit)/32 scale bytes; N/nsplit <= 8192
+    // keeps it within 64 KB (ensured by the caller's split choice)
+    const size_t lds = (size_t)4 * 16 * kMxTiles2 * (N / nsplit / 32);
+    gemm2_decode_mxfp4_kernel<<<grid, 256, lds, s>>>(act_q, ascale, (const uint8_t*)w2, w2e8,
                                                    topk_w, sorted_ids, block_expert, num_padded,
                                                    cap, nslots, K, N, nsplit, ypart);
 }
