@@ -87,6 +87,10 @@ def test_fused_validation(lib):
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=384)[0] == UNS       # MXFP4: multiples of 256
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, K=16640)[0] == UNS     # MXFP4: K <= 16384
+    # MXFP4: GEMM2 splits must hold <= 8192 reduction elements; 8448 = 33*256
+    # cannot be halved into multiples of 256
+    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=8448)[0] == UNS
+    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=8192, ws=None)[0] == 0  # size query succeeds
     assert fused(lib, dtype=2)[0] == INV                              # rowwise fp8 without scales
     assert fused(lib, dtype=2, s1=FAKE, s2=None)[0] == INV
     assert fused(lib, dtype=2, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
