@@ -231,6 +231,10 @@ SMALL = [
     ("mxfp4_tiny", 16, 512, 256, 16, 4, "mxfp4", None, 0),
     ("mxfp4_ragged", 7, 768, 512, 32, 8, "mxfp4", None, 0),
     ("mxfp4_many_rows", 300, 256, 512, 8, 2, "mxfp4", None, 0),
+    # tiny batches through the single-workgroup routing, with router bias;
+    # FP8 with K > 1024 quantises the token rows in their own kernel
+    ("tiny_route_bias", 8, 768, 512, 8, 2, False, 0.5, 0),
+    ("tiny_route_fp8", 4, 1536, 256, 8, 2, True, 0.5, 0),
     # router logits on the fp64 matrix cores with K split over 4 workgroups
     # per 16x16 tile (finished by the top-k kernel)
     ("router_split_k", 80, 2048, 256, 128, 4, False, 0.5, 0),
