@@ -184,6 +184,8 @@ def main():
                     help="distinct weight copies stepped round-robin (0 = enough to exceed "
                          "the 256 MB last-level cache several times)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--tokens", type=int, default=0,
+                    help="run the workload's shapes with this many tokens M instead")
     ap.add_argument("--cpu-tokens", type=int, default=0,
                     help="tokens in the oracle's sample (0 = whole batch up to 8)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -230,6 +232,8 @@ def main():
         wl = wl.resized(name=wl.name + "_rowwise", fp8_rowwise=True)
     if args.mxfp4:
         wl = wl.resized(name=wl.name + "_mxfp4", fp8=False, fp8_rowwise=False, mxfp4=True)
+    if args.tokens:
+        wl = wl.resized(name=f"{wl.name}_M{args.tokens}", M=args.tokens)
     if not torch.cuda.is_available():
         sys.exit("no GPU visible")
     dev = torch.device("cuda:0")

@@ -11,6 +11,7 @@
 //   4 GEMM1 + SiLU*up
 //   5 (e4m3) per-row activation quantisation  6 GEMM2 * routing weight, scattered
 //   7 combine into bf16 out
+#include <cmath>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <string.h>
@@ -73,6 +74,19 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
                      : MOE_REGIME_PREFILL;
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
+    if (regime == MOE_REGIME_DECODE && (dtype == MOE_FP8_E4M3 || dtype == MOE_FP8_E4M3_ROWWISE)) {
+        // e4m3 weights have only the Swap-AB kernels: with more rows per
+        // active expert, 32- or 64-row blocks (2 or 4 token tiles per wave)
+        // stream each expert's weights once instead of once per 16 rows.
+        // Blocks are sized for the mean rows per expert plus two standard
+        // deviations of a Poisson count (DeepSeek shape, 7168 x 2048 x 256
+        // experts, top-8: 16 rows on average best in 32-row blocks, 2.44
+        // against 2.82 ms; 32 rows in 64-row blocks, 3.09 against 4.35 ms)
+        const double active = (double)(slots < E ? slots : E);
+        const double rows = active > 0 ? (double)slots / active : 0.0;
+        const double need = rows + 2.0 * std::sqrt(rows);
+        p.block = need > 32 ? 4 * kDecodeBlock : (need > 16 ? 2 * kDecodeBlock : kDecodeBlock);
+    }
     p.cap = (int)(slots + (long)E * (p.block - 1));
     p.max_blocks = p.cap / p.block;
     {
@@ -314,7 +328,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                            s);
         else
             moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
-                                         topk, nslots, K, N, p.grid_blocks, act, amax, s);
+                                         topk, nslots, K, N, p.grid_blocks, p.block / kDecodeBlock,
+                                         act, amax, s);
         mark(4);
         moe::launch_act_quant(act, amax, inv, nslots, N, actq, as, s);
         mark(5);
@@ -325,7 +340,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         else
             moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
                                          npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
-                                         ypart, s);
+                                         p.block / kDecodeBlock, ypart, s);
         mark(6);
     } else {
         void* act = ws + p.act;

@@ -225,41 +225,59 @@ __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
 // |act| max into amax[r] (float bits, atomicMax: exact and order-free for
 // non-negative floats).
 // ---------------------------------------------------------------------------
+// NT token tiles of 16 rows per block (block = 16*NT sorted rows): every
+// wave multiplies its weight fragment by all NT token fragments, so an
+// expert with up to 16*NT rows streams its weights once.
+template <int NT>
 __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
     const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale, int rowwise,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     float* __restrict__ act, uint32_t* __restrict__ amax) {
+    constexpr int BR = kDecRows * NT;  // sorted rows per block
     const int blk = (int)blockIdx.y;
-    if (blk * kDecRows >= *num_padded) return;
+    if (blk * BR >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
     const int n0 = gw * 16;
     const int i = lane & 15, kq = lane >> 4;
-    const int p = sorted_ids[blk * kDecRows + i];
-    const bool valid = p < nslots;
-    const int t = valid ? p / topk : 0;
 
     const size_t row_bytes = (size_t)K;
     const rsrc_t rg = make_rsrc(w1 + ((size_t)e * 2 * N + n0) * K, (uint32_t)(16 * row_bytes));
     const rsrc_t ru = make_rsrc(w1 + ((size_t)e * 2 * N + N + n0) * K, (uint32_t)(16 * row_bytes));
     const rsrc_t rx = make_rsrc(xq, (uint32_t)((size_t)M * row_bytes));
     const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 32;
-    const uint32_t xo = valid ? (uint32_t)((size_t)t * row_bytes) + kq * 32 : kOob;
+    // token tile j: sorted row blk*BR + 16j + i
+    int tj[NT];
+    bool vj[NT];
+    uint32_t xo[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int p = sorted_ids[blk * BR + 16 * j + i];
+        vj[j] = p < nslots;
+        tj[j] = vj[j] ? p / topk : 0;
+        xo[j] = vj[j] ? (uint32_t)((size_t)tj[j] * row_bytes) + kq * 32 : kOob;
+    }
 
-    struct Frag { i32x8_t g, u, b; };
+    struct Frag { i32x8_t g, u, b[NT]; };
     auto load = [&](Frag& f, int k) {
         f.g = bload32(rg, wo + k);
         f.u = bload32(ru, wo + k);
-        f.b = bload32(rx, xo + k);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) f.b[j] = bload32(rx, xo[j] + k);
     };
-    f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    f32x4_t accg[NT], accu[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) accg[j] = accu[j] = f32x4_t{0, 0, 0, 0};
     auto compute = [&](const Frag& f) {
-        accg = mfma_fp8(f.g, f.b, accg);
-        accu = mfma_fp8(f.u, f.b, accu);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            accg[j] = mfma_fp8(f.g, f.b[j], accg[j]);
+            accu[j] = mfma_fp8(f.u, f.b[j], accu[j]);
+        }
     };
     const int nst = K / 128;
     const int rot = (gw * kRot + blk * 5) % nst;
@@ -272,31 +290,41 @@ __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
         cur = nxt;
     }
     compute(cur);
-    pin(accg);
-    pin(accu);
-
-    float m = 0.0f;
-    if (valid) {
-        // accumulator element v is gate row n0 + 4*kq + v (and that up row)
-        const float sx = xscale[t];
-        f32x4_t o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) {
-            float sg, su;
-            if (rowwise) {
-                const float* sr = w1_scale + (size_t)e * 2 * N + n0 + 4 * kq + v;
-                sg = sx * sr[0];
-                su = sx * sr[N];
-            } else {
-                sg = su = sx * w1_scale[e];
-            }
-            o[v] = silu(accg[v] * sg) * (accu[v] * su);
-            m = fmaxf(m, fabsf(o[v]));
-        }
-        *reinterpret_cast<f32x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 4 * kq) = o;
+    for (int j = 0; j < NT; ++j) {
+        pin(accg[j]);
+        pin(accu[j]);
     }
-    const uint32_t mb = col_max_bits(__float_as_uint(m));
-    if (valid && kq == 0) atomicMax(amax + blk * kDecRows + i, mb);
+
+    // accumulator element v is gate row n0 + 4*kq + v (and that up row)
+    float sg[4], su[4];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+        if (rowwise) {
+            const float* sr = w1_scale + (size_t)e * 2 * N + n0 + 4 * kq + v;
+            sg[v] = sr[0];
+            su[v] = sr[N];
+        } else {
+            sg[v] = su[v] = w1_scale[e];
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int row = blk * BR + 16 * j + i;
+        float m = 0.0f;
+        if (vj[j]) {
+            const float sx = xscale[tj[j]];
+            f32x4_t o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                o[v] = silu(accg[j][v] * (sx * sg[v])) * (accu[j][v] * (sx * su[v]));
+                m = fmaxf(m, fabsf(o[v]));
+            }
+            *reinterpret_cast<f32x4_t*>(act + (size_t)row * N + n0 + 4 * kq) = o;
+        }
+        const uint32_t mb = col_max_bits(__float_as_uint(m));
+        if (vj[j] && kq == 0) atomicMax(amax + row, mb);
+    }
 }
 
 // act32 [cap,N] + amax [cap] -> act_q [cap,N] e4m3 and s_a [cap]; one wave per row.
@@ -341,14 +369,16 @@ __global__ __launch_bounds__(256) void act_quant_kernel(
     if (ch == 0 && lane == 0) ascale[r] = s;
 }
 
+template <int NT>
 __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
     const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale, int rowwise,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
+    constexpr int BR = kDecRows * NT;
     const int blk = (int)blockIdx.y;
-    if (blk * kDecRows >= *num_padded) return;
+    if (blk * BR >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
@@ -358,27 +388,37 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     const int z = (int)blockIdx.z;
     const int nlen = N / nsplit;
     const int nbeg = z * nlen;
-    const int r = blk * kDecRows + i;
-    const int p = sorted_ids[r];
-    const bool valid = p < nslots;
 
     const size_t row_bytes = (size_t)N;
     const rsrc_t rw = make_rsrc(w2 + ((size_t)e * K + c0) * N, (uint32_t)(32 * row_bytes));
     const rsrc_t ra = make_rsrc(act_q, (uint32_t)((size_t)cap * row_bytes));
     const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg + kq * 32;
     const uint32_t wo1 = wo + (uint32_t)(16 * row_bytes);
-    const uint32_t ao = valid ? (uint32_t)((size_t)r * row_bytes) + nbeg + kq * 32 : kOob;
+    int rj[NT], pj[NT];
+    uint32_t ao[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        rj[j] = blk * BR + 16 * j + i;
+        pj[j] = sorted_ids[rj[j]];
+        ao[j] = pj[j] < nslots ? (uint32_t)((size_t)rj[j] * row_bytes) + nbeg + kq * 32 : kOob;
+    }
 
-    struct Frag { i32x8_t a0, a1, b; };
+    struct Frag { i32x8_t a0, a1, b[NT]; };
     auto load = [&](Frag& f, int n) {
         f.a0 = bload32(rw, wo + n);
         f.a1 = bload32(rw, wo1 + n);
-        f.b = bload32(ra, ao + n);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) f.b[j] = bload32(ra, ao[j] + n);
     };
-    f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    f32x4_t acc0[NT], acc1[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc0[j] = acc1[j] = f32x4_t{0, 0, 0, 0};
     auto compute = [&](const Frag& f) {
-        acc0 = mfma_fp8(f.a0, f.b, acc0);
-        acc1 = mfma_fp8(f.a1, f.b, acc1);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+            acc0[j] = mfma_fp8(f.a0, f.b[j], acc0[j]);
+            acc1[j] = mfma_fp8(f.a1, f.b[j], acc1[j]);
+        }
     };
     const int nst = nlen / 128;
     const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
@@ -391,24 +431,30 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
         cur = nxt;
     }
     compute(cur);
-    pin(acc0);
-    pin(acc1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        pin(acc0[j]);
+        pin(acc1[j]);
+    }
 
-    if (valid) {
-        const float w = topk_w[p] * ascale[r];
-        float* yr = ypart + ((size_t)z * nslots + p) * K + c0 + 4 * kq;
-        if (rowwise) {
-            // accumulator element v of acc0 / acc1 is output column
-            // c0 + 4*kq + v / c0 + 16 + 4*kq + v
-            const float* sr = w2_scale + (size_t)e * K + c0 + 4 * kq;
-            const f32x4_t s0 = *reinterpret_cast<const f32x4_t*>(sr);
-            const f32x4_t s1 = *reinterpret_cast<const f32x4_t*>(sr + 16);
-            *reinterpret_cast<f32x4_t*>(yr) = acc0 * (s0 * w);
-            *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * (s1 * w);
-        } else {
-            const float ws = w * w2_scale[e];
-            *reinterpret_cast<f32x4_t*>(yr) = acc0 * ws;
-            *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * ws;
+    // accumulator element v of acc0 / acc1 is output column
+    // c0 + 4*kq + v / c0 + 16 + 4*kq + v
+    f32x4_t s0, s1;
+    if (rowwise) {
+        const float* sr = w2_scale + (size_t)e * K + c0 + 4 * kq;
+        s0 = *reinterpret_cast<const f32x4_t*>(sr);
+        s1 = *reinterpret_cast<const f32x4_t*>(sr + 16);
+    } else {
+        const float ws = w2_scale[e];
+        s0 = s1 = f32x4_t{ws, ws, ws, ws};
+    }
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        if (pj[j] < nslots) {
+            const float w = topk_w[pj[j]] * ascale[rj[j]];
+            float* yr = ypart + ((size_t)z * nslots + pj[j]) * K + c0 + 4 * kq;
+            *reinterpret_cast<f32x4_t*>(yr) = acc0[j] * (s0 * w);
+            *reinterpret_cast<f32x4_t*>(yr + 16) = acc1[j] * (s1 * w);
         }
     }
 }
@@ -688,12 +734,17 @@ void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
                              const float* w1_scale, int rowwise, const int32_t* sorted_ids,
                              const int32_t* block_expert, const int32_t* num_padded, int M,
-                             int topk, int nslots, int K, int N, int max_blocks, float* act,
-                             uint32_t* amax, hipStream_t s) {
+                             int topk, int nslots, int K, int N, int max_blocks, int nt,
+                             float* act, uint32_t* amax, hipStream_t s) {
     dim3 grid(N / 64, max_blocks);
-    gemm1_decode_fp8_kernel<<<grid, 256, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale,
-                                                 rowwise, sorted_ids, block_expert, num_padded, M, topk,
-                                                 nslots, K, N, act, amax);
+#define MOE_G1F8(NT)                                                                         \
+    gemm1_decode_fp8_kernel<NT><<<grid, 256, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale, \
+                                                     rowwise, sorted_ids, block_expert,        \
+                                                     num_padded, M, topk, nslots, K, N, act, amax)
+    if (nt == 4) MOE_G1F8(4);
+    else if (nt == 2) MOE_G1F8(2);
+    else MOE_G1F8(1);
+#undef MOE_G1F8
 }
 
 void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* inv, int nslots,
@@ -708,11 +759,17 @@ void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const vo
                              const float* w2_scale, int rowwise, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,
                              const int32_t* num_padded, int cap, int nslots, int K, int N,
-                             int nsplit, int max_blocks, float* ypart, hipStream_t s) {
+                             int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s) {
     dim3 grid(K / 128, max_blocks, nsplit);
-    gemm2_decode_fp8_kernel<<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale,
-                                                 rowwise, topk_w, sorted_ids, block_expert, num_padded,
-                                                 cap, nslots, K, N, nsplit, ypart);
+#define MOE_G2F8(NT)                                                                          \
+    gemm2_decode_fp8_kernel<NT><<<grid, 256, 0, s>>>(act_q, ascale, (const uint8_t*)w2,         \
+                                                     w2_scale, rowwise, topk_w, sorted_ids,    \
+                                                     block_expert, num_padded, cap, nslots, K, \
+                                                     N, nsplit, ypart)
+    if (nt == 4) MOE_G2F8(4);
+    else if (nt == 2) MOE_G2F8(2);
+    else MOE_G2F8(1);
+#undef MOE_G2F8
 }
 
 void launch_gemm1_decode_mxfp4(const uint8_t* xq, const float* xscale, const void* w1,

@@ -57,11 +57,12 @@ void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
                               int nsplit, int max_blocks, float* ypart, hipStream_t s);
 // rowwise: w1_scale [E,2N] / w2_scale [E,K] (one per output row) instead of [E]
+// nt: 16-row token tiles per block (1, 2 or 4; the align block size is 16*nt)
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,
                              const float* w1_scale, int rowwise, const int32_t* sorted_ids,
                              const int32_t* block_expert, const int32_t* num_padded, int M,
-                             int topk, int nslots, int K, int N, int max_blocks, float* act,
-                             uint32_t* amax, hipStream_t s);
+                             int topk, int nslots, int K, int N, int max_blocks, int nt,
+                             float* act, uint32_t* amax, hipStream_t s);
 // rows of the nslots slots only: slot p is sorted row inv[p]
 void launch_act_quant(const float* act, const uint32_t* amax, const int32_t* inv, int nslots,
                       int N, uint8_t* act_q, float* ascale, hipStream_t s);
@@ -69,7 +70,7 @@ void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const vo
                              const float* w2_scale, int rowwise, const float* topk_w,
                              const int32_t* sorted_ids, const int32_t* block_expert,
                              const int32_t* num_padded, int cap, int nslots, int K, int N,
-                             int nsplit, int max_blocks, float* ypart, hipStream_t s);
+                             int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s);
 
 // MXFP4 weights: w1 [E,2N,K/2] / w2 [E,K,N/2] packed e2m1 with E8M0 scales
 // w1e8 [E,2N,K/32] / w2e8 [E,K,N/32]; activations as the e4m3 path

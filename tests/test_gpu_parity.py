@@ -223,6 +223,10 @@ SMALL = [
     ("fp8_tiny", 16, 512, 256, 16, 4, True, None, 0),
     ("fp8_ragged", 7, 384, 640, 32, 8, True, None, 0),
     ("fp8_many_rows", 300, 256, 384, 8, 2, True, None, 0),
+    # more rows per expert: 32-row (2 token tiles) and 64-row (4) blocks
+    ("fp8_two_tiles", 48, 512, 256, 8, 2, True, None, 0),
+    ("fp8_four_tiles", 160, 512, 384, 8, 2, True, 0.5, 0),
+    ("fp8_rowwise_four_tiles", 200, 256, 256, 4, 2, "rowwise", None, 0),
     # e4m3 weights with per-channel scales (one per output row)
     ("fp8_rowwise_tiny", 16, 512, 256, 16, 4, "rowwise", None, 0),
     ("fp8_rowwise_ragged", 7, 384, 640, 32, 8, "rowwise", None, 0),
