@@ -74,8 +74,8 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
                      : MOE_REGIME_PREFILL;
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
-    if (regime == MOE_REGIME_DECODE && (dtype == MOE_FP8_E4M3 || dtype == MOE_FP8_E4M3_ROWWISE)) {
-        // e4m3 weights have only the Swap-AB kernels: with more rows per
+    if (regime == MOE_REGIME_DECODE && is_fp8(dtype)) {
+        // e4m3 and MXFP4 weights have only the Swap-AB kernels: with more rows per
         // active expert, 32- or 64-row blocks (2 or 4 token tiles per wave)
         // stream each expert's weights once instead of once per 16 rows.
         // Blocks are sized for the mean rows per expert plus two standard
@@ -324,8 +324,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         const bool mx = dtype == MOE_MXFP4_E2M1;
         if (mx)
             moe::launch_gemm1_decode_mxfp4(xq, xs, w1, (const uint8_t*)w1_scale, sorted, bexp,
-                                           npad, M, topk, nslots, K, N, p.grid_blocks, act, amax,
-                                           s);
+                                           npad, M, topk, nslots, K, N, p.grid_blocks,
+                                           p.block / kDecodeBlock, act, amax, s);
         else
             moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
                                          topk, nslots, K, N, p.grid_blocks, p.block / kDecodeBlock,
@@ -336,7 +336,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         if (mx)
             moe::launch_gemm2_decode_mxfp4(actq, as, w2, (const uint8_t*)w2_scale, wts, sorted,
                                            bexp, npad, p.cap, nslots, K, N, p.nsplit,
-                                           p.grid_blocks, ypart, s);
+                                           p.grid_blocks, p.block / kDecodeBlock, ypart, s);
         else
             moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
                                          npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,

@@ -484,6 +484,7 @@ __device__ __forceinline__ uint64_t bload_u64(rsrc_t r, uint32_t off) {
     return ((uint64_t)(uint32_t)v[1] << 32) | (uint32_t)v[0];
 }
 
+template <int NT>
 __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
     const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1e8,
@@ -491,17 +492,23 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     float* __restrict__ act, uint32_t* __restrict__ amax) {
     constexpr int RT = kMxTiles1;
+    constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * kDecRows >= *num_padded) return;
+    if (blk * BR >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
     const int n0 = gw * 16 * RT;
     const int i = lane & 15, kq = lane >> 4;
-    const int p = sorted_ids[blk * kDecRows + i];
-    const bool valid = p < nslots;
-    const int t = valid ? p / topk : 0;
+    int tj[NT];
+    bool vj[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int p = sorted_ids[blk * BR + 16 * j + i];
+        vj[j] = p < nslots;
+        tj[j] = vj[j] ? p / topk : 0;
+    }
 
     const size_t row_bytes = (size_t)K / 2;   // packed e2m1
     const size_t srow = (size_t)K / 32;       // E8M0 scales per row
@@ -513,7 +520,9 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const rsrc_t rx = make_rsrc(xq, (uint32_t)((size_t)M * K));
     const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 16;
     const uint32_t so = (uint32_t)(i * srow);
-    const uint32_t xo = valid ? (uint32_t)((size_t)t * K) + kq * 16 : kOob;
+    uint32_t xo[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) xo[j] = vj[j] ? (uint32_t)((size_t)tj[j] * K) + kq * 16 : kOob;
     const int sh = 8 * kq;
 
     // The E8M0 scales of this wave's gate rows and of its up rows (each
@@ -531,7 +540,7 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
 
     // one step = chunks k and k+128 of every row tile
     struct Frag {
-        i32x4_t g[2][RT], u[2][RT], b[2][2];
+        i32x4_t g[2][RT], u[2][RT], b[2][NT][2];
         uint64_t sg[RT], su[RT];
     };
     auto load = [&](Frag& f, int k) {
@@ -543,8 +552,11 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
                 f.g[c][r] = bload(rg, wo + (uint32_t)(16 * r * row_bytes) + kc / 2);
                 f.u[c][r] = bload(ru, wo + (uint32_t)(16 * r * row_bytes) + kc / 2);
             }
-            f.b[c][0] = bload(rx, xo + kc);
-            f.b[c][1] = bload(rx, xo + kc + 64);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                f.b[c][j][0] = bload(rx, xo[j] + kc);
+                f.b[c][j][1] = bload(rx, xo[j] + kc + 64);
+            }
         }
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
@@ -553,22 +565,26 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
             f.su[r] = *reinterpret_cast<const uint64_t*>(q + sbytes);
         }
     };
-    f32x4_t accg[RT], accu[RT];
+    f32x4_t accg[NT][RT], accu[NT][RT];
 #pragma unroll
-    for (int r = 0; r < RT; ++r) accg[r] = accu[r] = f32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int r = 0; r < RT; ++r) accg[j][r] = accu[j][r] = f32x4_t{0, 0, 0, 0};
     auto compute = [&](const Frag& f) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const i32x4_t b0 = f.b[c][0], b1 = f.b[c][1];
-            const i32x8_t b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int r = 0; r < RT; ++r) {
-                accg[r] = mfma_fp4_fp8(f.g[c][r], (int)((f.sg[r] >> (32 * c + sh)) & 0xffu), b,
-                                       accg[r]);
-                accu[r] = mfma_fp4_fp8(f.u[c][r], (int)((f.su[r] >> (32 * c + sh)) & 0xffu), b,
-                                       accu[r]);
+            for (int j = 0; j < NT; ++j) {
+                const i32x4_t b0 = f.b[c][j][0], b1 = f.b[c][j][1];
+                const i32x8_t b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+                for (int r = 0; r < RT; ++r) {
+                    accg[j][r] = mfma_fp4_fp8(f.g[c][r], (int)((f.sg[r] >> (32 * c + sh)) & 0xffu),
+                                              b, accg[j][r]);
+                    accu[j][r] = mfma_fp4_fp8(f.u[c][r], (int)((f.su[r] >> (32 * c + sh)) & 0xffu),
+                                              b, accu[j][r]);
+                }
             }
-        }
     };
     const int nst = K / 256;  // K is a multiple of 256 here (checked by the launcher)
     const int rot = (gw * kRot + blk * 5) % nst;
@@ -584,30 +600,36 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
         if (j + 1 < nst) compute(fb);
     }
 #pragma unroll
-    for (int r = 0; r < RT; ++r) {
-        pin(accg[r]);
-        pin(accu[r]);
-    }
-
-    float m = 0.0f;
-    if (valid) {
-        const float sx = xscale[t];
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int r = 0; r < RT; ++r) {
-            f32x4_t o;
-#pragma unroll
-            for (int v = 0; v < 4; ++v) {
-                o[v] = silu(accg[r][v] * sx) * (accu[r][v] * sx);
-                m = fmaxf(m, fabsf(o[v]));
-            }
-            *reinterpret_cast<f32x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 16 * r +
-                                        4 * kq) = o;
+            pin(accg[j][r]);
+            pin(accu[j][r]);
         }
+
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int row = blk * BR + 16 * j + i;
+        float m = 0.0f;
+        if (vj[j]) {
+            const float sx = xscale[tj[j]];
+#pragma unroll
+            for (int r = 0; r < RT; ++r) {
+                f32x4_t o;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    o[v] = silu(accg[j][r][v] * sx) * (accu[j][r][v] * sx);
+                    m = fmaxf(m, fabsf(o[v]));
+                }
+                *reinterpret_cast<f32x4_t*>(act + (size_t)row * N + n0 + 16 * r + 4 * kq) = o;
+            }
+        }
+        const uint32_t mb = col_max_bits(__float_as_uint(m));
+        if (vj[j] && kq == 0) atomicMax(amax + row, mb);
     }
-    const uint32_t mb = col_max_bits(__float_as_uint(m));
-    if (valid && kq == 0) atomicMax(amax + blk * kDecRows + i, mb);
 }
 
+template <int NT>
 __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
     const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2e8,
@@ -615,8 +637,9 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
     constexpr int RT = kMxTiles2;
+    constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * kDecRows >= *num_padded) return;
+    if (blk * BR >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
@@ -626,9 +649,12 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const int z = (int)blockIdx.z;
     const int nlen = N / nsplit;
     const int nbeg = z * nlen;
-    const int r = blk * kDecRows + i;
-    const int p = sorted_ids[r];
-    const bool valid = p < nslots;
+    int rj[NT], pj[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        rj[j] = blk * BR + 16 * j + i;
+        pj[j] = sorted_ids[rj[j]];
+    }
 
     const size_t row_bytes = (size_t)N / 2;
     const size_t srow = (size_t)N / 32;
@@ -637,7 +663,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     const rsrc_t rs = make_rsrc(w2e8 + r0 * srow, (uint32_t)(16 * RT * srow));
     const rsrc_t ra = make_rsrc(act_q, (uint32_t)((size_t)cap * N));
     const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg / 2 + kq * 16;
-    const uint32_t ao = valid ? (uint32_t)((size_t)r * N) + nbeg + kq * 16 : kOob;
+    uint32_t ao[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+        ao[j] = pj[j] < nslots ? (uint32_t)((size_t)rj[j] * N) + nbeg + kq * 16 : kOob;
     const int sh = 8 * kq;
 
     // the split's E8M0 bytes of the wave's 16*RT rows (nlen/32 per row),
@@ -655,7 +684,7 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     __syncthreads();
 
     struct Frag {
-        i32x4_t a[2][RT], b[2][2];
+        i32x4_t a[2][RT], b[2][NT][2];
         uint64_t s[RT];
     };
     auto load = [&](Frag& f, int n) {
@@ -665,26 +694,33 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
 #pragma unroll
             for (int q = 0; q < RT; ++q)
                 f.a[c][q] = bload(rw, wo + (uint32_t)(16 * q * row_bytes) + nc / 2);
-            f.b[c][0] = bload(ra, ao + nc);
-            f.b[c][1] = bload(ra, ao + nc + 64);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                f.b[c][j][0] = bload(ra, ao[j] + nc);
+                f.b[c][j][1] = bload(ra, ao[j] + nc + 64);
+            }
         }
 #pragma unroll
         for (int q = 0; q < RT; ++q)
             f.s[q] = *reinterpret_cast<const uint64_t*>(sl + (i + 16 * q) * sspan + n / 32);
     };
-    f32x4_t acc[RT];
+    f32x4_t acc[NT][RT];
 #pragma unroll
-    for (int q = 0; q < RT; ++q) acc[q] = f32x4_t{0, 0, 0, 0};
+    for (int j = 0; j < NT; ++j)
+#pragma unroll
+        for (int q = 0; q < RT; ++q) acc[j][q] = f32x4_t{0, 0, 0, 0};
     auto compute = [&](const Frag& f) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const i32x4_t b0 = f.b[c][0], b1 = f.b[c][1];
-            const i32x8_t b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+        for (int c = 0; c < 2; ++c)
 #pragma unroll
-            for (int q = 0; q < RT; ++q)
-                acc[q] = mfma_fp4_fp8(f.a[c][q], (int)((f.s[q] >> (32 * c + sh)) & 0xffu), b,
-                                      acc[q]);
-        }
+            for (int j = 0; j < NT; ++j) {
+                const i32x4_t b0 = f.b[c][j][0], b1 = f.b[c][j][1];
+                const i32x8_t b = {b0[0], b0[1], b0[2], b0[3], b1[0], b1[1], b1[2], b1[3]};
+#pragma unroll
+                for (int q = 0; q < RT; ++q)
+                    acc[j][q] = mfma_fp4_fp8(f.a[c][q], (int)((f.s[q] >> (32 * c + sh)) & 0xffu),
+                                             b, acc[j][q]);
+            }
     };
     const int nst = nlen / 256;  // nlen is a multiple of 256 here (checked by the launcher)
     const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
@@ -698,13 +734,19 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
         if (j + 1 < nst) compute(fb);
     }
 #pragma unroll
-    for (int q = 0; q < RT; ++q) pin(acc[q]);
-
-    if (valid) {
-        const float w = topk_w[p] * ascale[r];
-        float* yr = ypart + ((size_t)z * nslots + p) * K + c0 + 4 * kq;
+    for (int j = 0; j < NT; ++j)
 #pragma unroll
-        for (int q = 0; q < RT; ++q) *reinterpret_cast<f32x4_t*>(yr + 16 * q) = acc[q] * w;
+        for (int q = 0; q < RT; ++q) pin(acc[j][q]);
+
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        if (pj[j] < nslots) {
+            const float w = topk_w[pj[j]] * ascale[rj[j]];
+            float* yr = ypart + ((size_t)z * nslots + pj[j]) * K + c0 + 4 * kq;
+#pragma unroll
+            for (int q = 0; q < RT; ++q)
+                *reinterpret_cast<f32x4_t*>(yr + 16 * q) = acc[j][q] * w;
+        }
     }
 }
 
@@ -775,29 +817,40 @@ void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const vo
 void launch_gemm1_decode_mxfp4(const uint8_t* xq, const float* xscale, const void* w1,
                                const uint8_t* w1e8, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,
-                               int topk, int nslots, int K, int N, int max_blocks, float* act,
-                               uint32_t* amax, hipStream_t s) {
+                               int topk, int nslots, int K, int N, int max_blocks, int nt,
+                               float* act, uint32_t* amax, hipStream_t s) {
     dim3 grid(N / (64 * kMxTiles1), max_blocks);
     // 4 waves x (gate + up) x 16*RT rows x K/32 scale bytes; K <= 16384 keeps
     // it within the default 64 KB (checked by the caller)
     const size_t lds = (size_t)4 * 2 * 16 * kMxTiles1 * (K / 32);
-    gemm1_decode_mxfp4_kernel<<<grid, 256, lds, s>>>(xq, xscale, (const uint8_t*)w1, w1e8,
-                                                   sorted_ids, block_expert, num_padded, M, topk,
-                                                   nslots, K, N, act, amax);
+#define MOE_G1MX(NT)                                                                          \
+    gemm1_decode_mxfp4_kernel<NT><<<grid, 256, lds, s>>>(xq, xscale, (const uint8_t*)w1, w1e8, \
+                                                         sorted_ids, block_expert, num_padded, \
+                                                         M, topk, nslots, K, N, act, amax)
+    if (nt == 4) MOE_G1MX(4);
+    else if (nt == 2) MOE_G1MX(2);
+    else MOE_G1MX(1);
+#undef MOE_G1MX
 }
 
 void launch_gemm2_decode_mxfp4(const uint8_t* act_q, const float* ascale, const void* w2,
                                const uint8_t* w2e8, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
-                               int nsplit, int max_blocks, float* ypart, hipStream_t s) {
+                               int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s) {
     dim3 grid(K / (64 * kMxTiles2), max_blocks, nsplit);
     // 4 waves x 16*RT rows x (N/nsplit)/32 scale bytes; N/nsplit <= 8192
     // keeps it within 64 KB (ensured by the caller's split choice)
     const size_t lds = (size_t)4 * 16 * kMxTiles2 * (N / nsplit / 32);
-    gemm2_decode_mxfp4_kernel<<<grid, 256, lds, s>>>(act_q, ascale, (const uint8_t*)w2, w2e8,
-                                                   topk_w, sorted_ids, block_expert, num_padded,
-                                                   cap, nslots, K, N, nsplit, ypart);
+#define MOE_G2MX(NT)                                                                          \
+    gemm2_decode_mxfp4_kernel<NT><<<grid, 256, lds, s>>>(act_q, ascale, (const uint8_t*)w2,     \
+                                                         w2e8, topk_w, sorted_ids, block_expert,\
+                                                         num_padded, cap, nslots, K, N, nsplit, \
+                                                         ypart)
+    if (nt == 4) MOE_G2MX(4);
+    else if (nt == 2) MOE_G2MX(2);
+    else MOE_G2MX(1);
+#undef MOE_G2MX
 }
 
 }  // namespace moe

@@ -77,13 +77,13 @@ void launch_gemm2_decode_fp8(const uint8_t* act_q, const float* ascale, const vo
 void launch_gemm1_decode_mxfp4(const uint8_t* xq, const float* xscale, const void* w1,
                                const uint8_t* w1e8, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,
-                               int topk, int nslots, int K, int N, int max_blocks, float* act,
+                               int topk, int nslots, int K, int N, int max_blocks, int nt, float* act,
                                uint32_t* amax, hipStream_t s);
 void launch_gemm2_decode_mxfp4(const uint8_t* act_q, const float* ascale, const void* w2,
                                const uint8_t* w2e8, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
-                               int nsplit, int max_blocks, float* ypart, hipStream_t s);
+                               int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s);
 
 void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,

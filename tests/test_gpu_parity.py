@@ -242,6 +242,9 @@ SMALL = [
     # router logits on the fp64 matrix cores with K split over 4 workgroups
     # per 16x16 tile (finished by the top-k kernel)
     ("router_split_k", 80, 2048, 256, 128, 4, False, 0.5, 0),
+    # MXFP4 with 32- and 64-row blocks
+    ("mxfp4_two_tiles", 48, 512, 512, 8, 2, "mxfp4", None, 0),
+    ("mxfp4_four_tiles", 160, 256, 512, 8, 2, "mxfp4", 0.5, 0),
     # many experts and a wider intermediate dimension
     ("mxfp4_wide_grid", 32, 512, 1024, 64, 4, "mxfp4", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
