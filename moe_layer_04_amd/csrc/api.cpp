@@ -74,10 +74,11 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
                      : MOE_REGIME_PREFILL;
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
-    if (regime == MOE_REGIME_DECODE && is_fp8(dtype)) {
-        // e4m3 and MXFP4 weights have only the Swap-AB kernels: with more rows per
-        // active expert, 32- or 64-row blocks (2 or 4 token tiles per wave)
-        // stream each expert's weights once instead of once per 16 rows.
+    if (regime == MOE_REGIME_DECODE) {
+        // With more rows per active expert the Swap-AB kernels take 32- or
+        // 64-row blocks (2 or 4 token tiles per wave), so each expert's
+        // weights stream once instead of once per 16 rows (e4m3 and MXFP4
+        // weights have only these kernels).
         // Blocks are sized for the mean rows per expert plus two standard
         // deviations of a Poisson count (DeepSeek shape, 7168 x 2048 x 256
         // experts, top-8: 16 rows on average best in 32-row blocks, 2.44
@@ -346,7 +347,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         void* act = ws + p.act;
         if (p.regime == MOE_REGIME_DECODE)
             moe::launch_gemm1_decode_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
-                                          p.grid_blocks, act, s);
+                                          p.grid_blocks, p.block / kDecodeBlock, act, s);
         else
             moe::launch_gemm1_prefill_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
                                            p.grid_blocks, act, s);
@@ -354,7 +355,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         mark(5);
         if (p.regime == MOE_REGIME_DECODE)
             moe::launch_gemm2_decode_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
-                                          p.nsplit, p.grid_blocks, ypart, s);
+                                          p.nsplit, p.grid_blocks, p.block / kDecodeBlock, ypart,
+                                          s);
         else
             moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
                                            p.nsplit, p.grid_blocks, ypart, s);

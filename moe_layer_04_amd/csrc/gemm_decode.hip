@@ -83,46 +83,58 @@ __device__ __forceinline__ int rotated(int j, int rot, int n) {
 // gate rows n0..n0+15 with n0 = (4x + w)*16 and up rows N+n0..N+n0+15.
 // A K-step is 128 elements: 4 MFMAs per row tile.
 // ---------------------------------------------------------------------------
+template <int NT>
 __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     uint16_t* __restrict__ act) {
+    constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * kDecRows >= *num_padded) return;
+    if (blk * BR >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
     const int n0 = gw * 16;
     const int i = lane & 15, kq = lane >> 4;
-    const int p = sorted_ids[blk * kDecRows + i];
-    const bool valid = p < nslots;
 
     const size_t row_bytes = (size_t)K * 2;
     const rsrc_t rg = make_rsrc(w1 + ((size_t)e * 2 * N + n0) * K, (uint32_t)(16 * row_bytes));
     const rsrc_t ru = make_rsrc(w1 + ((size_t)e * 2 * N + N + n0) * K, (uint32_t)(16 * row_bytes));
     const rsrc_t rx = make_rsrc(x, (uint32_t)((size_t)M * row_bytes));
     const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 16;
-    const uint32_t xo = valid ? (uint32_t)((size_t)(p / topk) * row_bytes) + kq * 16 : kOob;
+    bool vj[NT];
+    uint32_t xo[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int p = sorted_ids[blk * BR + 16 * j + i];
+        vj[j] = p < nslots;
+        xo[j] = vj[j] ? (uint32_t)((size_t)(p / topk) * row_bytes) + kq * 16 : kOob;
+    }
 
-    struct Frag { i32x4_t g[4], u[4], b[4]; };
+    struct Frag { i32x4_t g[4], u[4], b[NT][4]; };
     auto load = [&](Frag& f, int k) {
         const uint32_t kb = (uint32_t)k * 2;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             f.g[s] = bload(rg, wo + kb + s * 64);
             f.u[s] = bload(ru, wo + kb + s * 64);
-            f.b[s] = bload(rx, xo + kb + s * 64);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) f.b[j][s] = bload(rx, xo[j] + kb + s * 64);
         }
     };
-    f32x4_t accg = {0, 0, 0, 0}, accu = {0, 0, 0, 0};
+    f32x4_t accg[NT], accu[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) accg[j] = accu[j] = f32x4_t{0, 0, 0, 0};
     auto compute = [&](const Frag& f) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            accg = mfma_bf16(f.g[s], f.b[s], accg);
-            accu = mfma_bf16(f.u[s], f.b[s], accu);
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                accg[j] = mfma_bf16(f.g[s], f.b[j][s], accg[j]);
+                accu[j] = mfma_bf16(f.u[s], f.b[j][s], accu[j]);
+            }
     };
     const int nst = K / 128;
     const int rot = (gw * kRot + blk * 5) % nst;
@@ -135,14 +147,21 @@ __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
         cur = nxt;
     }
     compute(cur);
-    pin(accg);
-    pin(accu);
-
-    if (valid) {
-        u16x4_t o;
 #pragma unroll
-        for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_bits(silu(accg[v]) * accu[v]);
-        *reinterpret_cast<u16x4_t*>(act + (size_t)(blk * kDecRows + i) * N + n0 + 4 * kq) = o;
+    for (int j = 0; j < NT; ++j) {
+        pin(accg[j]);
+        pin(accu[j]);
+    }
+
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        if (vj[j]) {
+            u16x4_t o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) o[v] = f32_to_bf16_bits(silu(accg[j][v]) * accu[j][v]);
+            *reinterpret_cast<u16x4_t*>(act + (size_t)(blk * BR + 16 * j + i) * N + n0 +
+                                        4 * kq) = o;
+        }
     }
 }
 
@@ -151,13 +170,15 @@ __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
 // workgroup x owns output rows c0..c0+31, c0 = (4x + w)*32, over the
 // reduction range [z*N/nsplit, (z+1)*N/nsplit).
 // ---------------------------------------------------------------------------
+template <int NT>
 __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
+    constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * kDecRows >= *num_padded) return;
+    if (blk * BR >= *num_padded) return;
     const int e = block_expert[blk];
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
@@ -167,34 +188,43 @@ __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
     const int z = (int)blockIdx.z;
     const int nlen = N / nsplit;
     const int nbeg = z * nlen;
-    const int r = blk * kDecRows + i;
-    const int p = sorted_ids[r];
-    const bool valid = p < nslots;
 
     const size_t row_bytes = (size_t)N * 2;
     const rsrc_t rw = make_rsrc(w2 + ((size_t)e * K + c0) * N, (uint32_t)(32 * row_bytes));
     const rsrc_t ra = make_rsrc(act, (uint32_t)((size_t)cap * row_bytes));
     const uint32_t wo = (uint32_t)(i * row_bytes) + nbeg * 2 + kq * 16;
     const uint32_t wo1 = wo + (uint32_t)(16 * row_bytes);
-    const uint32_t ao = valid ? (uint32_t)((size_t)r * row_bytes) + nbeg * 2 + kq * 16 : kOob;
+    int pj[NT];
+    uint32_t ao[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        const int r = blk * BR + 16 * j + i;
+        pj[j] = sorted_ids[r];
+        ao[j] = pj[j] < nslots ? (uint32_t)((size_t)r * row_bytes) + nbeg * 2 + kq * 16 : kOob;
+    }
 
-    struct Frag { i32x4_t a0[4], a1[4], b[4]; };
+    struct Frag { i32x4_t a0[4], a1[4], b[NT][4]; };
     auto load = [&](Frag& f, int n) {
         const uint32_t nb = (uint32_t)n * 2;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
             f.a0[s] = bload(rw, wo + nb + s * 64);
             f.a1[s] = bload(rw, wo1 + nb + s * 64);
-            f.b[s] = bload(ra, ao + nb + s * 64);
+#pragma unroll
+            for (int j = 0; j < NT; ++j) f.b[j][s] = bload(ra, ao[j] + nb + s * 64);
         }
     };
-    f32x4_t acc0 = {0, 0, 0, 0}, acc1 = {0, 0, 0, 0};
+    f32x4_t acc0[NT], acc1[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j) acc0[j] = acc1[j] = f32x4_t{0, 0, 0, 0};
     auto compute = [&](const Frag& f) {
 #pragma unroll
-        for (int s = 0; s < 4; ++s) {
-            acc0 = mfma_bf16(f.a0[s], f.b[s], acc0);
-            acc1 = mfma_bf16(f.a1[s], f.b[s], acc1);
-        }
+        for (int s = 0; s < 4; ++s)
+#pragma unroll
+            for (int j = 0; j < NT; ++j) {
+                acc0[j] = mfma_bf16(f.a0[s], f.b[j][s], acc0[j]);
+                acc1[j] = mfma_bf16(f.a1[s], f.b[j][s], acc1[j]);
+            }
     };
     const int nst = nlen / 128;
     const int rot = (gw * kRot + blk * 5 + z * 3) % nst;
@@ -207,14 +237,20 @@ __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
         cur = nxt;
     }
     compute(cur);
-    pin(acc0);
-    pin(acc1);
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        pin(acc0[j]);
+        pin(acc1[j]);
+    }
 
-    if (valid) {
-        const float w = topk_w[p];
-        float* yr = ypart + ((size_t)z * nslots + p) * K + c0 + 4 * kq;
-        *reinterpret_cast<f32x4_t*>(yr) = acc0 * w;
-        *reinterpret_cast<f32x4_t*>(yr + 16) = acc1 * w;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+        if (pj[j] < nslots) {
+            const float w = topk_w[pj[j]];
+            float* yr = ypart + ((size_t)z * nslots + pj[j]) * K + c0 + 4 * kq;
+            *reinterpret_cast<f32x4_t*>(yr) = acc0[j] * w;
+            *reinterpret_cast<f32x4_t*>(yr + 16) = acc1[j] * w;
+        }
     }
 }
 
@@ -755,22 +791,33 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
 // ---------------------------------------------------------------------------
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded, int M,
-                              int topk, int nslots, int K, int N, int max_blocks, void* act,
-                              hipStream_t s) {
+                              int topk, int nslots, int K, int N, int max_blocks, int nt,
+                              void* act, hipStream_t s) {
     dim3 grid(N / 64, max_blocks);
-    gemm1_decode_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)w1,
-                                                  sorted_ids, block_expert, num_padded, M, topk,
-                                                  nslots, K, N, (uint16_t*)act);
+#define MOE_G1BF(NT)                                                                          \
+    gemm1_decode_bf16_kernel<NT><<<grid, 256, 0, s>>>((const uint16_t*)x, (const uint16_t*)w1, \
+                                                      sorted_ids, block_expert, num_padded, M, \
+                                                      topk, nslots, K, N, (uint16_t*)act)
+    if (nt == 4) MOE_G1BF(4);
+    else if (nt == 2) MOE_G1BF(2);
+    else MOE_G1BF(1);
+#undef MOE_G1BF
 }
 
 void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk_w,
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
-                              int nsplit, int max_blocks, float* ypart, hipStream_t s) {
+                              int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s) {
     dim3 grid(K / 128, max_blocks, nsplit);
-    gemm2_decode_bf16_kernel<<<grid, 256, 0, s>>>((const uint16_t*)act, (const uint16_t*)w2,
-                                                  topk_w, sorted_ids, block_expert, num_padded,
-                                                  cap, nslots, K, N, nsplit, ypart);
+#define MOE_G2BF(NT)                                                                          \
+    gemm2_decode_bf16_kernel<NT><<<grid, 256, 0, s>>>((const uint16_t*)act, (const uint16_t*)w2,\
+                                                      topk_w, sorted_ids, block_expert,        \
+                                                      num_padded, cap, nslots, K, N, nsplit,   \
+                                                      ypart)
+    if (nt == 4) MOE_G2BF(4);
+    else if (nt == 2) MOE_G2BF(2);
+    else MOE_G2BF(1);
+#undef MOE_G2BF
 }
 
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,

@@ -50,12 +50,12 @@ void launch_topk_align(const float* logits, const void* x, int M, int K, int E, 
 
 void launch_gemm1_decode_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded, int M,
-                              int topk, int nslots, int K, int N, int max_blocks, void* act,
+                              int topk, int nslots, int K, int N, int max_blocks, int nt, void* act,
                               hipStream_t s);
 void launch_gemm2_decode_bf16(const void* act, const void* w2, const float* topk_w,
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
-                              int nsplit, int max_blocks, float* ypart, hipStream_t s);
+                              int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s);
 // rowwise: w1_scale [E,2N] / w2_scale [E,K] (one per output row) instead of [E]
 // nt: 16-row token tiles per block (1, 2 or 4; the align block size is 16*nt)
 void launch_gemm1_decode_fp8(const uint8_t* xq, const float* xscale, const void* w1,

@@ -223,6 +223,9 @@ SMALL = [
     ("fp8_tiny", 16, 512, 256, 16, 4, True, None, 0),
     ("fp8_ragged", 7, 384, 640, 32, 8, True, None, 0),
     ("fp8_many_rows", 300, 256, 384, 8, 2, True, None, 0),
+    # bf16 Swap-AB kernels forced on 32-row (2 token tiles) and 64-row (4) blocks
+    ("decode_two_tiles", 48, 512, 512, 8, 2, False, None, 1),
+    ("decode_four_tiles", 160, 256, 384, 8, 2, False, 0.5, 1),
     # more rows per expert: 32-row (2 token tiles) and 64-row (4) blocks
     ("fp8_two_tiles", 48, 512, 256, 8, 2, True, None, 0),
     ("fp8_four_tiles", 160, 512, 384, 8, 2, True, 0.5, 0),
