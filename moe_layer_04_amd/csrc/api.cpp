@@ -18,6 +18,7 @@
 
 #include "../../include/moe.h"
 #include "launch.hpp"
+#include "tuning.hpp"
 
 #define MOE_API extern "C" __attribute__((visibility("default")))
 
@@ -26,19 +27,6 @@ namespace {
 constexpr int kDecodeBlock = moe::kDecodeRows;
 constexpr int kPrefillBlock = moe::kPrefillRows;
 constexpr size_t kAlign = 256;
-// Kernel family chosen per token bucket, from a sweep of both families over
-// batch sizes on one MI355X (bf16; K, N, E, k = 4096, 14336, 8, 2 /
-// 4096, 8192, 16, 2 / 7168, 2048, 256, 8; M = 8 .. 1024): the Swap-AB decode
-// kernels are faster up to 8 token-slots per expert on all three shapes, the
-// full-tile kernels from 12 on (8-12 is the crossover).  Past 16 rows an
-// expert takes a second 16-row decode block and its weights are streamed
-// again.  The e4m3 weights have only the decode kernels.
-constexpr long kDecodeMaxRowsPerExpert = 8;
-// up to this many tokens the FP8 token quantisation runs inside the
-// single-workgroup top-k + align launch (a wave per token)
-constexpr int kLateQuantRows = 16;
-constexpr int kLateQuantCols = 1024;
-
 bool misaligned(const void* p) { return p && ((uintptr_t)p & 15u); }
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
@@ -69,25 +57,14 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     Plan p;
     const long slots = (long)M * topk;
     if (regime == MOE_REGIME_AUTO)
-        regime = (is_fp8(dtype) || slots <= (long)kDecodeMaxRowsPerExpert * E)
+        regime = (is_fp8(dtype) || slots <= moe::tune::kDecodeMaxRowsPerExpert * E)
                      ? MOE_REGIME_DECODE
                      : MOE_REGIME_PREFILL;
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
-    if (regime == MOE_REGIME_DECODE) {
-        // With more rows per active expert the Swap-AB kernels take 32- or
-        // 64-row blocks (2 or 4 token tiles per wave), so each expert's
-        // weights stream once instead of once per 16 rows (e4m3 and MXFP4
-        // weights have only these kernels).
-        // Blocks are sized for the mean rows per expert plus two standard
-        // deviations of a Poisson count (DeepSeek shape, 7168 x 2048 x 256
-        // experts, top-8: 16 rows on average best in 32-row blocks, 2.44
-        // against 2.82 ms; 32 rows in 64-row blocks, 3.09 against 4.35 ms)
-        const double active = (double)(slots < E ? slots : E);
-        const double rows = active > 0 ? (double)slots / active : 0.0;
-        const double need = rows + 2.0 * std::sqrt(rows);
-        p.block = need > 32 ? 4 * kDecodeBlock : (need > 16 ? 2 * kDecodeBlock : kDecodeBlock);
-    }
+    // larger decode blocks when experts receive more rows (e4m3 and MXFP4
+    // weights have only the decode kernels)
+    if (regime == MOE_REGIME_DECODE) p.block = moe::tune::decode_block_rows(slots, E);
     p.cap = (int)(slots + (long)E * (p.block - 1));
     p.max_blocks = p.cap / p.block;
     {
@@ -95,13 +72,7 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         p.grid_blocks = (int)(bound < p.max_blocks ? bound : p.max_blocks);
     }
     if (regime == MOE_REGIME_DECODE) {
-        // GEMM2's reduction split (measured on three shapes, two weight
-        // formats): a grid that already holds a workgroup per CU stays
-        // unsplit (8 experts x 4096 x 14336 bf16: 160 us unsplit, 166-171 us
-        // in 2-16 splits); a smaller one splits until about two workgroups
-        // per CU, while each wave still streams at least 32 KB of weights
-        // (2 experts x 4096 x 8192: bf16 best in 8 splits, MXFP4 in 8, its
-        // 16 splits leaving 16 KB per wave measured 12 % slower)
+        // GEMM2's reduction split: the rule and its measurements are in tuning.hpp
         const long est_blocks = slots < E ? slots : E;
         const int mx = dtype == MOE_MXFP4_E2M1;
         const long tiles = est_blocks * (K / (mx ? 256 : 128));  // output rows per workgroup
@@ -110,15 +81,14 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         const long row_bytes = dtype == MOE_BF16 ? 64 : 32;
         // each split's reduction length stays a multiple of the kernels' step
         const int gran = mx ? 256 : 128;
-        if (tiles < 256)
-            while (tiles * p.nsplit < 512 && p.nsplit < 16 &&
+        if (tiles < moe::tune::kDecodeSplitUnsplitTiles)
+            while (tiles * p.nsplit < moe::tune::kDecodeSplitTargetTiles && p.nsplit < 16 &&
                    (N / (p.nsplit * 2)) % gran == 0 &&
-                   row_bytes * (N / (p.nsplit * 2)) >= 32 * 1024)
+                   row_bytes * (N / (p.nsplit * 2)) >= moe::tune::kDecodeSplitMinWaveBytes)
                 p.nsplit *= 2;
-        // MXFP4's GEMM2 keeps each split's scale bytes in LDS: at most 8192
-        // reduction elements per split (64 KB per workgroup)
         if (mx)
-            while (N / p.nsplit > 8192 && p.nsplit < 16 && (N / (p.nsplit * 2)) % gran == 0)
+            while (N / p.nsplit > moe::tune::kMxMaxSplitLen && p.nsplit < 16 &&
+                   (N / (p.nsplit * 2)) % gran == 0)
                 p.nsplit *= 2;
     } else {
         p.nsplit = moe::prefill_gemm2_splits(K, N, p.grid_blocks);
@@ -241,7 +211,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
     // MXFP4: 256-deep steps; GEMM1 keeps K/32 scale bytes per row of its
     // waves in LDS (K <= 16384: 64 KB per workgroup)
-    if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256 || K > 16384))
+    if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256 || K > moe::tune::kMxMaxK))
         return MOE_ERR_UNSUPPORTED;
     if (is_fp8(dtype) && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
@@ -255,7 +225,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
     if (p.max_blocks > 65535) return MOE_ERR_UNSUPPORTED;
     // MXFP4 GEMM2: a split's scale bytes must fit its LDS copy
-    if (dtype == MOE_MXFP4_E2M1 && N / p.nsplit > 8192) return MOE_ERR_UNSUPPORTED;
+    if (dtype == MOE_MXFP4_E2M1 && N / p.nsplit > moe::tune::kMxMaxSplitLen)
+        return MOE_ERR_UNSUPPORTED;
     if (!workspace) {
         *workspace_bytes = p.total;
         return MOE_OK;
@@ -299,7 +270,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     if (moe::topk_align_fits(M, topk)) {
         // the FP8 token codes go with top-k + align when the tokens are few
         // and short (a wave per token there; a workgroup per token otherwise)
-        const bool q_late = fp8 && M <= kLateQuantRows && K <= kLateQuantCols;
+        const bool q_late = fp8 && M <= moe::tune::kLateQuantRows && K <= moe::tune::kLateQuantCols;
         moe::launch_router_logits(x, w_router, router_bias, M, K, E, logits,
                                   q_late ? nullptr : xq, xs, 1, nullptr, s);
         mark(1);

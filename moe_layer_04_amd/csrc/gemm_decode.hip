@@ -34,6 +34,7 @@
 // accumulator lane l holds D[4*(l/16) + v][l % 16], v = 0..3.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tuning.hpp"
 
 namespace moe {
 
@@ -508,8 +509,8 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
 // (GEMM1) or RT 16-row tiles of output rows (GEMM2) with one token fragment;
 // a step is two 128-deep chunks, the scale bytes of a step are one 8-byte
 // load per row tile, and the steps alternate between two fragments.
-constexpr int kMxTiles1 = 1;  // GEMM1: 16 gate + 16 up rows per wave
-constexpr int kMxTiles2 = 4;  // GEMM2: 64 output rows per wave
+constexpr int kMxTiles1 = tune::kMxTiles1;  // GEMM1: 16 gate + 16 up rows per wave
+constexpr int kMxTiles2 = tune::kMxTiles2;  // GEMM2: 64 output rows per wave
 
 // per-wave E8M0 scale copies of the MXFP4 kernels (dynamic LDS, sized by
 // the launchers)

@@ -42,6 +42,7 @@
 // D[8*(v/4) + 4*(l/32) + v%4][l % 32], v = 0..15.
 #include "common.hpp"
 #include "launch.hpp"
+#include "tuning.hpp"
 
 #include <type_traits>
 
@@ -487,21 +488,21 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    // four weight tiles per XCD tile group (measured against 1, 2, 3 and 8)
-    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, 4><<<grid, 512, 0, s>>>(
+    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm1WeightSlots,
+                              tune::kPrefillGemm1TokenSlots, 2, 8, 1, tune::kPrefillGemm1Group>
+        <<<grid, 512, 0, s>>>(
         (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
 
 int prefill_gemm2_splits(int K, int N, int blocks) {
-    // split the reduction until about four workgroups per CU exist: at one
-    // per CU a grid of 2.5 rounds leaves its last round half empty, while
-    // every split adds a partial row per slot for the combine to read
-    // (8 experts x 4096 x 14336, 39 blocks: 1118 us unsplit, 999 us in two
-    // splits, 1007 us in four, whose combine takes twice as long)
+    // split the reduction until the target tile count (tuning.hpp): fewer
+    // tiles leave the last round of workgroups part-empty, every split adds
+    // a partial row per slot for the combine to read
     const long tiles = (long)(K % 256 == 0 ? K / 256 : K / 128) * blocks;
     int ns = 1;
-    while (tiles * ns < 1024 && ns < 4 && (N / (2 * ns)) % 64 == 0) ns *= 2;
+    while (tiles * ns < tune::kPrefillSplitTargetTiles && ns < 4 && (N / (2 * ns)) % 64 == 0)
+        ns *= 2;
     return ns;
 }
 
@@ -512,10 +513,9 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
     if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
         // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        // four weight tiles per group (measured against 1, 2, 8 and 16); the
-        // token (activation) ring one slot longer than the weight ring
-        // (933-935 us against 946-950 with the rings the other way round)
-        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 2, 3, 2, 8, 1, 4><<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm2WeightSlots,
+                                  tune::kPrefillGemm2TokenSlots, 2, 8, 1, tune::kPrefillGemm2Group>
+            <<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else if (K % 256 == 0) {

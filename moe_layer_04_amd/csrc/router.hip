@@ -10,6 +10,7 @@
 // the weights are the softmax over the picked logits (equal to the full
 // softmax renormalised over them).
 #include "routing.hpp"
+#include "tuning.hpp"
 
 namespace moe {
 
@@ -294,7 +295,9 @@ int router_logit_splits(int M, int K, int E) {
     // fp64 matrix work is the bound: split K until every CU holds a tile
     const long tiles = (long)((M + 15) / 16) * ((E + 15) / 16);
     int nks = 1;
-    while (tiles * nks < 256 && nks < 4 && K % (kLogitWaves * 32 * nks * 2) == 0) nks *= 2;
+    while (tiles * nks < tune::kRouterSplitTargetTiles && nks < 4 &&
+           K % (kLogitWaves * 32 * nks * 2) == 0)
+        nks *= 2;
     return nks;
 }
 

@@ -1,0 +1,84 @@
+// tuning.hpp -- the launch choices of the fused MoE layer, per token bucket
+// and shape, frozen from measurements on one MI355X (the batch sweep is
+// `bench.py --regime-sweep`; the other figures are quoted at each entry).
+// Everything that picks a kernel family, a block size, a reduction split, a
+// tile order or a ring shape reads it from here.
+#pragma once
+
+#include <cmath>
+
+namespace moe {
+namespace tune {
+
+// ---- kernel family per token bucket -----------------------------------------
+// bf16 weights: the Swap-AB decode kernels up to this many token-slots per
+// expert, the full-tile kernels above.  Sweep of both families over
+// M = 8 .. 1024 (K, N, E, k = 4096, 14336, 8, 2 / 4096, 8192, 16, 2 /
+// 7168, 2048, 256, 8): decode faster up to 8 rows per expert on all three
+// shapes, full tiles from 12 on; re-measured with the 32- and 64-row decode
+// blocks (Mixtral shape, 16 rows: 0.586 ms decode against 0.548 tiles).
+// e4m3 and MXFP4 weights have only the decode kernels.
+constexpr long kDecodeMaxRowsPerExpert = 8;
+
+// ---- decode block rows ------------------------------------------------------
+// 16, 32 or 64 sorted rows per block (1, 2 or 4 token tiles multiplied by
+// every weight fragment), sized for the mean rows per active expert plus two
+// Poisson standard deviations, so most experts stream their weights once.
+// DeepSeek shape, e4m3: 16 rows on average best in 32-row blocks (2.44 ms
+// against 2.82 ms in 16-row ones), 32 rows in 64-row blocks (3.09 / 4.35).
+inline int decode_block_rows(long slots, int E) {
+    const double active = (double)(slots < E ? slots : E);
+    const double rows = active > 0 ? (double)slots / active : 0.0;
+    const double need = rows + 2.0 * std::sqrt(rows);
+    return need > 32 ? 64 : (need > 16 ? 32 : 16);
+}
+
+// ---- decode GEMM2 reduction split ----------------------------------------
+// tiles = (block, output-row tile) pairs of one split.  A grid already
+// holding a workgroup per CU stays unsplit (8 experts x 4096 x 14336 bf16:
+// 160 us unsplit, 166-171 us in 2-16 splits); a smaller one splits until
+// about two workgroups per CU while each wave keeps at least 32 KB of
+// weights (2 experts x 4096 x 8192: bf16 and MXFP4 best in 8 splits; 16
+// splits, 16 KB per wave, measured 12 % slower for MXFP4).
+constexpr long kDecodeSplitUnsplitTiles = 256;
+constexpr long kDecodeSplitTargetTiles = 512;
+constexpr long kDecodeSplitMinWaveBytes = 32 * 1024;
+// MXFP4 GEMM2 keeps a split's E8M0 bytes in LDS: at most this many reduction
+// elements per split (64 KB of dynamic LDS per workgroup)
+constexpr int kMxMaxSplitLen = 8192;
+// MXFP4 GEMM1 keeps K/32 scale bytes per row of its waves in LDS
+constexpr int kMxMaxK = 16384;
+
+// ---- MXFP4 row tiles per wave -------------------------------------------------
+// GEMM1: one 16-row gate tile and its up tile (two: 12-30 % slower as the
+// grid halves); GEMM2: four 16-row output tiles (two: 1-2 % slower).
+constexpr int kMxTiles1 = 1;
+constexpr int kMxTiles2 = 4;
+
+// ---- prefill ------------------------------------------------------------------
+// GEMM2 reduction split until about four workgroups per CU exist (Mixtral
+// prefill, 39 blocks: 1118 us unsplit, 999 us in 2 splits, 1007 us in 4
+// with a combine twice as long).
+constexpr long kPrefillSplitTargetTiles = 1024;
+// weight tiles varying fastest in a tile group of the XCD-aware order
+// (GEMM1: 1705-1715 us with 4 against 1725-1740 with 2; GEMM2: 936 us with
+// 4 against 990 with 8 and 1042 with 16)
+constexpr int kPrefillGemm1Group = 4;
+constexpr int kPrefillGemm2Group = 4;
+// LDS ring slots (weight, token) of the 64-deep steps: GEMM1 3 + 2; GEMM2
+// 2 + 3 (933-935 us against 946-950 with 3 + 2)
+constexpr int kPrefillGemm1WeightSlots = 3, kPrefillGemm1TokenSlots = 2;
+constexpr int kPrefillGemm2WeightSlots = 2, kPrefillGemm2TokenSlots = 3;
+
+// ---- router -------------------------------------------------------------------
+// fp64-MFMA logits: split K until the tiles x splits cover every CU (the
+// DeepSeek shape's 128 tiles in 2 splits: its logits + e4m3-rows stage
+// 32 -> 23 us)
+constexpr long kRouterSplitTargetTiles = 256;
+// up to this many tokens (of at most this width) the FP8 token quantisation
+// runs inside the single-workgroup top-k + align launch (a wave per token)
+constexpr int kLateQuantRows = 16;
+constexpr int kLateQuantCols = 1024;
+
+}  // namespace tune
+}  // namespace moe
