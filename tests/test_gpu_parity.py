@@ -226,6 +226,9 @@ SMALL = [
     # bf16 Swap-AB kernels forced on 32-row (2 token tiles) and 64-row (4) blocks
     ("decode_two_tiles", 48, 512, 512, 8, 2, False, None, 1),
     ("decode_four_tiles", 160, 256, 384, 8, 2, False, 0.5, 1),
+    # FP8 with fp64-MFMA logits (split over K) and the token rows quantised
+    # by their own kernel
+    ("fp8_router_mfma", 78, 1024, 256, 128, 4, True, None, 0),
     # more rows per expert: 32-row (2 token tiles) and 64-row (4) blocks
     ("fp8_two_tiles", 48, 512, 256, 8, 2, True, None, 0),
     ("fp8_four_tiles", 160, 512, 384, 8, 2, True, 0.5, 0),
