@@ -13,12 +13,15 @@
 // weights read from HBM feeds a full MFMA row.  Decode is bound by that HBM
 // stream; the kernels load weights straight into registers.
 //
-// Work split: one workgroup (4 waves) per (16-row block of one expert, tile
-// of weight rows).  GEMM1 waves own 16 gate rows and the matching 16 up rows,
-// so SiLU(gate)*up is formed in registers (the fused epilogue); GEMM2 waves
-// own 32 output rows and may split the reduction (N) across workgroups,
-// writing fp32 partial rows scattered back to slot order and already
-// multiplied by the routing weight.
+// Work split: one workgroup (4 waves) per (block of one expert's sorted
+// rows, tile of weight rows).  A block holds 16, 32 or 64 rows (NT = 1, 2 or
+// 4 token tiles of 16): every weight fragment is multiplied by all NT token
+// fragments, so an expert with up to 16*NT rows streams its weights once.
+// GEMM1 waves own 16 gate rows and the matching 16 up rows, so
+// SiLU(gate)*up is formed in registers (the fused epilogue); GEMM2 waves own
+// 32 output rows and may split the reduction (N) across workgroups, writing
+// fp32 partial rows scattered back to slot order and already multiplied by
+// the routing weight.
 //
 // Memory access: all operands go through buffer loads.  A buffer resource is
 // bounds-checked by the hardware, so padding lanes of a block (sentinel rows)

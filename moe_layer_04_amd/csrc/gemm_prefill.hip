@@ -18,11 +18,13 @@
 // both halves, so SiLU(gate)*up is formed from its own accumulators.
 //
 // Staging: both operand tiles are copied global -> LDS by the gfx950 buffer
-// loads with an LDS destination (no register round trip) into a ring of
-// STAGES slots.  Each K-step waits (vmcnt) for its own slot, meets the
-// workgroup at one raw s_barrier (the __syncthreads fence would wait for
-// every in-flight copy), issues the copy STAGES-1 steps ahead and runs its
-// MFMAs.  Padding token rows (sentinels) copy token row 0 for GEMM1 / the
+// loads with an LDS destination (no register round trip) into rings of
+// slots (one for the weights, one for the tokens; their lengths may differ
+// by one).
+// Each K-step waits (vmcnt) for its own slots, meets the workgroup at one raw
+// s_barrier (the __syncthreads fence would wait for every in-flight copy),
+// issues each operand's copy as many steps ahead as its ring allows and runs
+// its MFMAs.  Padding token rows (sentinels) copy token row 0 for GEMM1 / the
 // block's first act row for GEMM2: an MFMA output column depends only on its
 // own B column, and those columns are never stored.
 //
@@ -34,8 +36,7 @@
 // the hardware; each XCD is given a contiguous range of tiles, and tiles are
 // numbered so that a run of consecutive ids covers G weight tiles for
 // successive token blocks, so workgroups resident on one XCD share both
-// operands in its L2 (G = 4 for GEMM1, 8 for GEMM2: the measured minima of
-// time and HBM fetch).
+// operands in its L2 (G = 4 for both GEMMs: the measured minimum of time).
 //
 // 32x32x16 layouts (gfx950): lane l supplies row/column (l % 32) with the
 // K-slice 8*(l/32)..+8 for both operands; the accumulator lane l holds
