@@ -80,9 +80,11 @@ typedef enum {
  * summation order whichever is picked. */
 typedef enum {
     MOE_REGIME_AUTO = 0,    /* DECODE while M*topk <= 8*E (at most 8 token-slots
-                               per expert on average) or for e4m3 weights,
-                               else PREFILL: the measured crossover */
-    MOE_REGIME_DECODE = 1,  /* Swap-AB: weight rows on the MFMA row dimension */
+                               per expert on average) or for e4m3 / MXFP4
+                               weights, else PREFILL: the measured crossover */
+    MOE_REGIME_DECODE = 1,  /* Swap-AB: weight rows on the MFMA row dimension;
+                               blocks of 16, 32 or 64 sorted rows sized from
+                               the expected rows per expert */
     MOE_REGIME_PREFILL = 2  /* full MFMA tiles of token rows x weight rows */
 } moe_regime;
 
@@ -181,8 +183,9 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  * expert aggregation fused, for per-tensor FP8 models).
  *
  *   x, w_router, router_bias   as moe_topk
- *   w1        [E,2N,K] bf16 or e4m3 (dtype)
- *   w2        [E,K,N]  bf16 or e4m3
+ *   w1        [E,2N,K] bf16 or e4m3 (dtype); MXFP4: [E,2N,K/2] bytes, two
+ *             e2m1 codes each (even element in the low nibble)
+ *   w2        [E,K,N]  bf16 or e4m3; MXFP4: [E,K,N/2] bytes
  *   w1_scale  fp32 [E] (MOE_FP8_E4M3), [E,2N] (MOE_FP8_E4M3_ROWWISE), uint8
  *             E8M0 [E,2N,K/32] (MOE_MXFP4_E2M1) or NULL (MOE_BF16); w2_scale
  *             likewise [E], [E,K], [E,K,N/32] or NULL
@@ -199,7 +202,10 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  *
  * Errors: as moe_topk, plus INVALID_ARG for null w1/w2/out/workspace_bytes,
  * N < 1, a bad dtype, scales given for bf16 or missing for fp8;
- * UNSUPPORTED for K or N not a multiple of 128 or the size limits above;
+ * UNSUPPORTED for K or N not a multiple of 128 or the size limits above
+ * (MXFP4 also: K or N not a multiple of 256, K > 16384, or N that cannot be
+ * split into GEMM2 reduction ranges of at most 8192 multiples of 256), and
+ * for MOE_REGIME_PREFILL with e4m3 or MXFP4 weights;
  * WORKSPACE if *workspace_bytes is below the required size.
  */
 moe_status moe_fused_forward(const void *x, const void *w_router, const float *router_bias,
