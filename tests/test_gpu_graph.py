@@ -18,10 +18,12 @@ from tests.test_gpu_parity import (TOL_BF16, TOL_FP8, gen_small, note, oracle_la
 pytestmark = pytest.mark.gpu
 
 CASES = [
-    # name, M, K, N, E, k, fp8, regime
-    ("decode_bf16", 8, 512, 768, 8, 2, False, 0),
-    ("decode_fp8", 6, 512, 384, 16, 4, True, 0),
-    ("full_tiles_bf16", 96, 512, 512, 6, 2, False, 2),
+    # name, M, K, N, E, k, weights ("bf16" / "fp8" / "mxfp4"), regime
+    ("decode_bf16", 8, 512, 768, 8, 2, "bf16", 0),
+    ("decode_fp8", 6, 512, 384, 16, 4, "fp8", 0),
+    ("full_tiles_bf16", 96, 512, 512, 6, 2, "bf16", 2),
+    ("decode_mxfp4", 8, 512, 512, 8, 2, "mxfp4", 0),
+    ("fp8_32_row_blocks", 48, 512, 256, 8, 2, "fp8", 0),
 ]
 
 
@@ -34,9 +36,10 @@ def moe():
 
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
 def test_graph_replays_match_eager(moe, case):
-    name, M, K, N, E, k, fp8, regime = case
+    name, M, K, N, E, k, weights, regime = case
     note(f"graph {case}")
-    wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, seed=21)
+    fp8, mx = weights == "fp8", weights == "mxfp4"
+    wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, mxfp4=mx, seed=21)
     d, g = gen_small(wl)
     x = g["x"].clone()
     graph = moe.FusedForwardGraph(x, g["w_router"], g["bias"], g["w1"], g["w2"], k,
@@ -63,4 +66,4 @@ def test_graph_replays_match_eager(moe, case):
             err = row_rel_err(out_f64(got), want)
             note(f"  replay {rep} err={err:.3e}")
             assert np.isfinite(out_f64(got)).all()
-            assert err <= (TOL_FP8 if fp8 else TOL_BF16)
+            assert err <= (TOL_FP8 if (fp8 or mx) else TOL_BF16)
