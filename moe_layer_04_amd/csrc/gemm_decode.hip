@@ -95,8 +95,10 @@ __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
     uint16_t* __restrict__ act) {
     constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * BR >= *num_padded) return;
+    // a block past the padded end has no owner (-1 from the align step): the
+    // owner alone decides, one dependent load fewer than reading num_padded
     const int e = block_expert[blk];
+    if (e < 0) return;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
@@ -182,8 +184,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_bf16_kernel(
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
     constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * BR >= *num_padded) return;
+    // a block past the padded end has no owner (-1 from the align step): the
+    // owner alone decides, one dependent load fewer than reading num_padded
     const int e = block_expert[blk];
+    if (e < 0) return;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
@@ -277,8 +281,10 @@ __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
     float* __restrict__ act, uint32_t* __restrict__ amax) {
     constexpr int BR = kDecRows * NT;  // sorted rows per block
     const int blk = (int)blockIdx.y;
-    if (blk * BR >= *num_padded) return;
+    // a block past the padded end has no owner (-1 from the align step): the
+    // owner alone decides, one dependent load fewer than reading num_padded
     const int e = block_expert[blk];
+    if (e < 0) return;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
@@ -418,8 +424,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
     int nslots, int K, int N, int nsplit, float* __restrict__ ypart) {
     constexpr int BR = kDecRows * NT;
     const int blk = (int)blockIdx.y;
-    if (blk * BR >= *num_padded) return;
+    // a block past the padded end has no owner (-1 from the align step): the
+    // owner alone decides, one dependent load fewer than reading num_padded
     const int e = block_expert[blk];
+    if (e < 0) return;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
@@ -534,8 +542,10 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     constexpr int RT = kMxTiles1;
     constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * BR >= *num_padded) return;
+    // a block past the padded end has no owner (-1 from the align step): the
+    // owner alone decides, one dependent load fewer than reading num_padded
     const int e = block_expert[blk];
+    if (e < 0) return;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
@@ -679,8 +689,10 @@ __global__ __launch_bounds__(256) void gemm2_decode_mxfp4_kernel(
     constexpr int RT = kMxTiles2;
     constexpr int BR = kDecRows * NT;  // sorted rows per block (NT token tiles)
     const int blk = (int)blockIdx.y;
-    if (blk * BR >= *num_padded) return;
+    // a block past the padded end has no owner (-1 from the align step): the
+    // owner alone decides, one dependent load fewer than reading num_padded
     const int e = block_expert[blk];
+    if (e < 0) return;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);  // wave-uniform
     const int gw = (int)blockIdx.x * 4 + wave;
