@@ -57,6 +57,7 @@ CPU_SECONDS = 10.0  # oracle work timed for the CPU baseline
 # the library's automatic kernel-family choice (api.cpp): Swap-AB decode
 # kernels up to this many token-slots per expert, full tiles above
 DECODE_MAX_ROWS_PER_EXPERT = 8
+FP8_DECODE_MAX_ROWS_PER_EXPERT = 16   # e4m3 weights (MXFP4: decode kernels only)
 COPY_BYTES = 1 << 30
 
 
@@ -131,13 +132,16 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     print(json.dumps(rec))
 
 
-def regime_sweep(moe, wlm, wl, dev):
-    """Both kernel families (bf16 weights) on batches of M = 8 .. 1024 tokens
-    of this workload's shape: mean ms per layer call over 10 calls after 3."""
+def regime_sweep(moe, wlm, wl, dev, ms_list=None):
+    """Both kernel families (the workload's bf16 or e4m3 weights) on batches of
+    M = 8 .. 1024 tokens (or ms_list) of this workload's shape: mean ms per
+    layer call over 10 calls after 3."""
     import torch
-    ms_list = [8, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024]
+    ms_list = ms_list or [8, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024]
     big = wlm.Workload(wl.name + "_sweep", M=max(ms_list), K=wl.K, N=wl.N, E=wl.E,
-                       topk=wl.topk, seed=wl.seed)
+                       topk=wl.topk, fp8=wl.fp8, fp8_rowwise=wl.fp8_rowwise, seed=wl.seed)
+    dtype = (moe.MOE_FP8_E4M3_ROWWISE if wl.fp8_rowwise else
+             moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
     g = wlm.generate(big, dev)
     for M in ms_list:
         x = g["x"][:M].contiguous()
@@ -147,12 +151,13 @@ def regime_sweep(moe, wlm, wl, dev):
                             (moe.MOE_REGIME_PREFILL, "tiles_ms")):
             if regime == moe.MOE_REGIME_DECODE and rows > 256:
                 continue  # the decode kernels re-stream the weights per 16-row block
-            need = moe.workspace_size(moe.MOE_BF16, M, wl.K, wl.N, wl.E, wl.topk, regime)
+            need = moe.workspace_size(dtype, M, wl.K, wl.N, wl.E, wl.topk, regime)
             ws = torch.empty(need, dtype=torch.uint8, device=dev)
             out = torch.empty((M, wl.K), dtype=torch.bfloat16, device=dev)
 
             def call():
                 moe.moe_fused_forward(x, g["w_router"], None, g["w1"], g["w2"], wl.topk,
+                                      w1_scale=g["w1_scale"], w2_scale=g["w2_scale"],
                                       regime=regime, out=out, workspace=ws)
 
             for _ in range(3):
@@ -191,6 +196,9 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy 3 times (for scaling the "
                          "FETCH_SIZE / WRITE_SIZE counters) and exit")
+    ap.add_argument("--fp8", action="store_true",
+                    help="the workload with e4m3 weights (one fp32 scale per expert "
+                         "tensor) and per-token dynamic e4m3 activations")
     ap.add_argument("--fp8-rowwise", action="store_true",
                     help="with an e4m3 workload: per-channel weight scales (one per output "
                          "row) instead of one per expert tensor")
@@ -198,9 +206,12 @@ def main():
                     help="the workload with MXFP4 weights (e2m1, E8M0 scale per 32 "
                          "elements) and e4m3 activations")
     ap.add_argument("--regime-sweep", action="store_true",
-                    help="time the decode and full-tile kernel families (bf16) over batch "
-                         "sizes M = 8 .. 1024 at this workload's K, N, E, top-k; one JSON "
-                         "line per M, then exit")
+                    help="time the decode and full-tile kernel families (the workload's "
+                         "bf16 or e4m3 weights) over batch sizes M = 8 .. 1024 (or "
+                         "--sweep-tokens) at this workload's K, N, E, top-k; one JSON line "
+                         "per M, then exit")
+    ap.add_argument("--sweep-tokens", type=int, nargs="+", default=None,
+                    help="batch sizes M of --regime-sweep")
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [REQ_CSV COPY_REQ_CSV]: "
                          "turn rocprofv3 --pmc counter CSVs of this workload and of the copy "
@@ -226,6 +237,8 @@ def main():
     if args.workload not in wlm.WORKLOADS:
         sys.exit(f"unknown workload {args.workload}; one of {list(wlm.WORKLOADS)}")
     wl = wlm.WORKLOADS[args.workload]
+    if args.fp8 and not wl.fp8:
+        wl = wl.resized(name=wl.name + "_fp8", fp8=True)
     if args.fp8_rowwise:
         if not wl.fp8:
             sys.exit("--fp8-rowwise needs an e4m3 workload")
@@ -248,7 +261,7 @@ def main():
         return
     moe.load_library(build_if_missing=True)
     if args.regime_sweep:
-        regime_sweep(moe, wlm, wl, dev)
+        regime_sweep(moe, wlm, wl, dev, args.sweep_tokens)
         return
 
     log(f"generating {wl}")
@@ -353,7 +366,8 @@ def main():
                     if wl.fp8 else 0))
     alg_flops = 6.0 * slots * wl.N * wl.K
     step_s = ms_per_step / 1e3
-    decode = (slots <= DECODE_MAX_ROWS_PER_EXPERT * wl.E) or wl.fp8 or wl.mxfp4
+    decode = (wl.mxfp4 or slots <= (FP8_DECODE_MAX_ROWS_PER_EXPERT if wl.fp8
+                                    else DECODE_MAX_ROWS_PER_EXPERT) * wl.E)
     g1_s = kern_us["gemm1"] / 1e6
     if decode:
         # GEMM1 reads W1 of every active expert once plus the token rows

@@ -79,9 +79,10 @@ typedef enum {
 /* Kernel family used by the expert GEMMs; results agree up to fp32
  * summation order whichever is picked. */
 typedef enum {
-    MOE_REGIME_AUTO = 0,    /* DECODE while M*topk <= 8*E (at most 8 token-slots
-                               per expert on average) or for e4m3 / MXFP4
-                               weights, else PREFILL: the measured crossover */
+    MOE_REGIME_AUTO = 0,    /* DECODE while M*topk <= 8*E (bf16: at most 8
+                               token-slots per expert on average) or
+                               M*topk <= 16*E (e4m3), always for MXFP4
+                               weights, else PREFILL: the measured crossovers */
     MOE_REGIME_DECODE = 1,  /* Swap-AB: weight rows on the MFMA row dimension;
                                blocks of 16, 32 or 64 sorted rows sized from
                                the expected rows per expert */
@@ -91,8 +92,9 @@ typedef enum {
 /* Supported envelope: 1 <= E <= 256, 1 <= topk <= min(E,16), K >= 1 and
  * N >= 1; moe_fused_forward additionally needs K and N multiples of 128
  * (of 256, and K <= 16384, for MOE_MXFP4_E2M1),
- * M*topk < 2^30, (M*topk + 256*E) * max(K,N) * 4 < 2^31 (the sorted
- * activation rows), M*K*2 < 2^31 and 2*N*K*2 < 2^31 (one expert's W1). */
+ * M*topk < 2^30, (M*topk + 256*E) * N * b < 2^31 with b = 2 for bf16 and
+ * 1 otherwise (the sorted activation rows GEMM2 reads), M*K*2 < 2^31 and
+ * 2*N*K*2 < 2^31 (one expert's W1). */
 #define MOE_MAX_EXPERTS 256
 #define MOE_MAX_TOPK 16
 
@@ -205,7 +207,7 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  * UNSUPPORTED for K or N not a multiple of 128 or the size limits above
  * (MXFP4 also: K or N not a multiple of 256, K > 16384, or N that cannot be
  * split into GEMM2 reduction ranges of at most 8192 multiples of 256), and
- * for MOE_REGIME_PREFILL with e4m3 or MXFP4 weights;
+ * for MOE_REGIME_PREFILL with MXFP4 weights;
  * WORKSPACE if *workspace_bytes is below the required size.
  */
 moe_status moe_fused_forward(const void *x, const void *w_router, const float *router_bias,

@@ -56,14 +56,16 @@ bool is_fp8(int dtype) {
 Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     Plan p;
     const long slots = (long)M * topk;
-    if (regime == MOE_REGIME_AUTO)
-        regime = (is_fp8(dtype) || slots <= moe::tune::kDecodeMaxRowsPerExpert * E)
-                     ? MOE_REGIME_DECODE
-                     : MOE_REGIME_PREFILL;
+    if (regime == MOE_REGIME_AUTO) {
+        // MXFP4 weights have only the decode kernels
+        const long rows = dtype == MOE_BF16 ? moe::tune::kDecodeMaxRowsPerExpert
+                                            : moe::tune::kFp8DecodeMaxRowsPerExpert;
+        regime = (dtype == MOE_MXFP4_E2M1 || slots <= rows * E) ? MOE_REGIME_DECODE
+                                                                : MOE_REGIME_PREFILL;
+    }
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
-    // larger decode blocks when experts receive more rows (e4m3 and MXFP4
-    // weights have only the decode kernels)
+    // larger decode blocks when experts receive more rows (sized in tuning.hpp)
     if (regime == MOE_REGIME_DECODE) p.block = moe::tune::decode_block_rows(slots, E);
     p.cap = (int)(slots + (long)E * (p.block - 1));
     p.max_blocks = p.cap / p.block;
@@ -91,7 +93,7 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
                    (N / (p.nsplit * 2)) % gran == 0)
                 p.nsplit *= 2;
     } else {
-        p.nsplit = moe::prefill_gemm2_splits(K, N, p.grid_blocks);
+        p.nsplit = moe::prefill_gemm2_splits(K, N, p.grid_blocks, is_fp8(dtype) ? 128 : 64);
     }
     size_t o = 0;
     auto take = [&](size_t bytes) {
@@ -213,12 +215,13 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     // waves in LDS (K <= 16384: 64 KB per workgroup)
     if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256 || K > moe::tune::kMxMaxK))
         return MOE_ERR_UNSUPPORTED;
-    if (is_fp8(dtype) && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
+    if (dtype == MOE_MXFP4_E2M1 && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
-    const long kn = K > N ? K : N;
-    // 32-bit buffer offsets: the sorted activation rows in fp32, the tokens
-    // and one expert's W1 must each stay below 2 GiB
-    if (slots >= (1L << 30) || (slots + (long)E * kPrefillBlock) * kn * 4 >= (1L << 31) ||
+    // 32-bit buffer offsets: the sorted activation rows GEMM2 reads (bf16, or
+    // e4m3 codes), the tokens and one expert's W1 must each stay below 2 GiB
+    // (the fp32 activation and the partial rows are addressed in 64 bits)
+    const long act_bytes = dtype == MOE_BF16 ? 2 : 1;
+    if (slots >= (1L << 30) || (slots + (long)E * kPrefillBlock) * N * act_bytes >= (1L << 31) ||
         (long)M * K * 2 >= (1L << 31) || (long)2 * N * K * 2 >= (1L << 31) ||
         (long)E * 2 * N >= (1L << 31))
         return MOE_ERR_UNSUPPORTED;
@@ -294,7 +297,11 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
         const bool mx = dtype == MOE_MXFP4_E2M1;
-        if (mx)
+        const bool tiles = p.regime == MOE_REGIME_PREFILL;  // e4m3 only
+        if (tiles)
+            moe::launch_gemm1_prefill_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
+                                          topk, nslots, K, N, p.grid_blocks, act, amax, s);
+        else if (mx)
             moe::launch_gemm1_decode_mxfp4(xq, xs, w1, (const uint8_t*)w1_scale, sorted, bexp,
                                            npad, M, topk, nslots, K, N, p.grid_blocks,
                                            p.block / kDecodeBlock, act, amax, s);
@@ -305,7 +312,11 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         mark(4);
         moe::launch_act_quant(act, amax, inv, nslots, N, actq, as, s);
         mark(5);
-        if (mx)
+        if (tiles)
+            moe::launch_gemm2_prefill_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
+                                          npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
+                                          ypart, s);
+        else if (mx)
             moe::launch_gemm2_decode_mxfp4(actq, as, w2, (const uint8_t*)w2_scale, wts, sorted,
                                            bexp, npad, p.cap, nslots, K, N, p.nsplit,
                                            p.grid_blocks, p.block / kDecodeBlock, ypart, s);

@@ -57,6 +57,10 @@ __device__ __forceinline__ prsrc_t pmake_rsrc(const void* base, uint32_t bytes) 
 __device__ __forceinline__ f32x16_t mfma32_bf16(bf16x8_t a, bf16x8_t b, f32x16_t c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// e4m3 x e4m3, 64-deep; block scales fixed at 2^0 (E8M0 code 127)
+__device__ __forceinline__ f32x16_t mfma32_fp8(i32x8_t a, i32x8_t b, f32x16_t c) {
+    return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
+}
 
 // Tile schedule.  The hardware deals workgroup g to XCD g % 8; each XCD is
 // given a contiguous range of tiles, numbered with G weight tiles varying
@@ -97,16 +101,18 @@ struct TileWalk {
     }
 };
 
-// LDS rows: each operand row of a K-step is BK bf16 (BK*2 bytes) without
-// padding, its 16-byte chunks permuted by an XOR of the row index (swz) so
+// LDS rows: each operand row of a K-step is its BK elements (64 or 128
+// bytes) without padding, its 16-byte chunks permuted by an XOR of the row
+// index (swz, keyed by the chunks per row) so
 // that the 16 consecutive rows an MFMA operand read touches in one LDS cycle
 // land in distinct banks.  The DMA writes 1 KB per wave instruction in lane
 // order, so lane l of an instruction covering rows r0.. stores physical
 // chunk (l % CPR) of row r0 + l / CPR and therefore fetches logical chunk
 // (l % CPR) ^ swz(row) from global memory.
-template <int BK>
+template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-    if constexpr (BK == 32) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
+    static_assert(CPR == 4 || CPR == 8, "64- or 128-byte LDS rows");
+    if constexpr (CPR == 4) return ((r >> 1) & 3) ^ ((r >> 3) & 1);
     else return (r & 7) ^ ((r >> 3) & 1);
 }
 
@@ -128,10 +134,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 // and reads the first fragments of step s+1, so those MFMAs cover the
 // barrier and the LDS latency.  The barrier also proves that every wave is
 // done reading step s, whose slots the copies issued at step s+1 overwrite.
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, bool F8 = false>
 struct PrefillCore {
-    static constexpr int kRowBytes = BK * 2;
-    static constexpr int kCPR = BK / 8;                     // 16-B chunks per row
+    static constexpr int kRowBytes = F8 ? BK : BK * 2;
+    static constexpr int kCPR = kRowBytes / 16;             // 16-B chunks per row
     static constexpr int kRowsPerInstr = 64 / kCPR;         // rows one wave instruction covers
     static constexpr int kWInstr = TW / kRowsPerInstr / NW; // per wave per step
     static constexpr int kXInstr = TT / kRowsPerInstr / NW;
@@ -142,7 +148,8 @@ struct PrefillCore {
     static constexpr int WT = NW / WW;                      // waves along the token dimension
     static constexpr int FW = TW / WW / 32;                 // 32-row A tiles per wave
     static constexpr int FT = TT / WT / 32;                 // 32-column B tiles per wave
-    static constexpr int KS = BK / 16;                      // MFMA k-slices per step
+    // MFMA k-slices per step: 16 bf16 (32x32x16) or 64 e4m3 (32x32x64)
+    static constexpr int KS = F8 ? BK / 64 : BK / 16;
     static_assert(kWInstr * kRowsPerInstr * NW == TW && kXInstr * kRowsPerInstr * NW == TT,
                   "tile rows must split evenly over the waves' DMA instructions");
     static_assert(WST >= 2 && XST >= 2 && WST - XST <= 1 && XST - WST <= 1,
@@ -165,7 +172,7 @@ struct PrefillCore {
         return (q * NW + wave) * kRowsPerInstr + lane / kCPR;
     }
     __device__ static __forceinline__ int dma_chunk(int row, int lane) {
-        return (lane % kCPR) ^ swz<BK>(row);
+        return (lane % kCPR) ^ swz<kCPR>(row);
     }
 
     // Source offsets at k = kbeg of this lane's chunk: weight copy q reads
@@ -216,37 +223,58 @@ struct PrefillCore {
         };
 
         // per-lane LDS read offsets (bytes within a slot) of the first A and
-        // B fragment for each k16 slice; the others are constant offsets
+        // B fragment for each k-slice; the other fragments are constant
+        // offsets away.  bf16: lane half h reads chunk 2*ks + h (8 elements);
+        // e4m3: chunks 4*ks + 2h and 4*ks + 2h + 1 (32 codes), two reads as
+        // the swizzle may separate them.  A and B fragments come from the
+        // same chunks of their rows, so whatever K order the MFMA assigns to
+        // a lane's bytes, each product pairs matching reduction indices.
         const int li = lane & 31, half = lane >> 5;
-        int aoff[KS], boff[KS];
+        constexpr int NC = F8 ? 2 : 1;  // 16-byte reads per fragment
+        int aoff[KS][NC], boff[KS][NC];
         {
             const int ra = arow0 + li, rb = wb * (TT / WT) + li;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c = 2 * ks + half;
-                aoff[ks] = ra * kRowBytes + ((c ^ swz<BK>(ra)) << 4);
-                boff[ks] = rb * kRowBytes + ((c ^ swz<BK>(rb)) << 4);
-            }
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int h = 0; h < NC; ++h) {
+                    const int c = F8 ? 4 * ks + 2 * half + h : 2 * ks + half;
+                    aoff[ks][h] = ra * kRowBytes + ((c ^ swz<kCPR>(ra)) << 4);
+                    boff[ks][h] = rb * kRowBytes + ((c ^ swz<kCPR>(rb)) << 4);
+                }
         }
-        struct Frags { bf16x8_t a[FW], b[FT]; };
+        typedef typename std::conditional<F8, i32x8_t, bf16x8_t>::type frag_t;
+        struct Frags { frag_t a[FW], b[FT]; };
+        auto ld = [&](const char* base, const int (&off)[NC]) {
+            if constexpr (F8) {
+                const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + off[0]);
+                const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + off[1]);
+                return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                return *reinterpret_cast<const bf16x8_t*>(base + off[0]);
+            }
+        };
         auto read = [&](Frags& f, int wslot, int xslot, int ks) {
             if constexpr (!COMPUTE) return;
-            const char* wbase = lds + wslot * kWSlot + aoff[ks];
-            const char* xbase = lds + kXBase + xslot * kXSlot + boff[ks];
+            const char* wbase = lds + wslot * kWSlot;
+            const char* xbase = lds + kXBase + xslot * kXSlot;
 #pragma unroll
             for (int a = 0; a < FW; ++a)
-                f.a[a] = *reinterpret_cast<const bf16x8_t*>(wbase +
-                                                            arow_delta<AJUMP>(a) * kRowBytes);
+                f.a[a] = ld(wbase + arow_delta<AJUMP>(a) * kRowBytes, aoff[ks]);
 #pragma unroll
-            for (int b = 0; b < FT; ++b)
-                f.b[b] = *reinterpret_cast<const bf16x8_t*>(xbase + b * 32 * kRowBytes);
+            for (int b = 0; b < FT; ++b) f.b[b] = ld(xbase + b * 32 * kRowBytes, boff[ks]);
         };
         auto mfmas = [&](const Frags& f) {
             if constexpr (!COMPUTE) return;
 #pragma unroll
             for (int a = 0; a < FW; ++a)
 #pragma unroll
-                for (int b = 0; b < FT; ++b) acc[a][b] = mfma32_bf16(f.a[a], f.b[b], acc[a][b]);
+                for (int b = 0; b < FT; ++b) {
+                    if constexpr (F8)
+                        acc[a][b] = mfma32_fp8(f.a[a], f.b[b], acc[a][b]);
+                    else
+                        acc[a][b] = mfma32_bf16(f.a[a], f.b[b], acc[a][b]);
+                }
         };
 
         const int steps = klen / BK;
@@ -479,6 +507,184 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// FP8 (OCP e4m3) weights and per-token e4m3 activations on the same tiles:
+// 128-code K-steps (128-byte LDS rows, as the bf16 kernels' 64-element
+// steps), two 32x32x64 MFMAs per step and fragment.  The epilogues apply the
+// scales where the decode FP8 kernels do: GEMM1 multiplies the gate and up
+// accumulators by s_x[t] times the row's (or the expert's) W1 scale, forms
+// SiLU(gate)*up in fp32, stores it and folds each row's |act| max into
+// amax[r] (float bits, atomicMax: exact and order-free for non-negative
+// values); GEMM2 multiplies by the output row's (or expert's) W2 scale, the
+// sorted row's activation scale s_a[r] and the routing weight.
+// ---------------------------------------------------------------------------
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
+    const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale, int rowwise,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
+    int max_blocks, float* __restrict__ act, uint32_t* __restrict__ amax) {
+    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW, true>;
+    __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
+    constexpr int HW = TW / 2;  // n-values per tile
+    constexpr int WN = HW / WW; // n-values per wave
+
+    const int npad = *num_padded;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wa = wave % WW, wb = wave / WW;
+    TileWalk<GROUP> walk(N / HW, max_blocks);
+    int wt, blk;
+    while (walk.next(wt, blk)) {
+    if (blk * TT >= npad) continue;
+    const int e = block_expert[blk];
+
+    const size_t row_bytes = (size_t)K;
+    const prsrc_t rw = pmake_rsrc(w1 + (size_t)e * 2 * N * K, (uint32_t)(2 * (size_t)N * row_bytes));
+    const prsrc_t rx = pmake_rsrc(xq, (uint32_t)((size_t)M * row_bytes));
+    uint32_t wsoff[Core::kWInstr], xoff[Core::kXInstr];
+    const int row0 = Core::dma_row(wave, 0, lane);
+    const uint32_t wvoff = (uint32_t)((wt * HW + row0) * row_bytes) +
+                           Core::dma_chunk(row0, lane) * 16;
+#pragma unroll
+    for (int q = 0; q < Core::kWInstr; ++q) {
+        const int first = (q * NW + wave) * Core::kRowsPerInstr;  // wave-uniform
+        const int shift = q * NW * Core::kRowsPerInstr + (first >= HW ? N - HW : 0);
+        wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * row_bytes));
+    }
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
+        const int p = sorted_ids[blk * TT + row];
+        const int t = p < nslots ? p / topk : 0;
+        xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
+    }
+    Core core;
+    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+        core.template run<true, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
+    else
+        core.template run<false, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
+
+    const int li = lane & 31;
+    const float ws = rowwise ? 0.0f : w1_scale[e];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
+        const int p = sorted_ids[r];
+        const bool valid = p < nslots;
+        const float sx = valid ? xscale[p / topk] : 0.0f;
+        float m = 0.0f;
+#pragma unroll
+        for (int a = 0; a < Core::FW / 2; ++a) {
+            // accumulator element 4*vg + v is gate row n0 + 8*vg + v (and that up row)
+            const int n0 = wt * HW + wa * WN + a * 32 + 4 * (lane >> 5);
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+                f32x4_t sg, su;
+                if (rowwise) {
+                    const float* sr = w1_scale + (size_t)e * 2 * N + n0 + 8 * vg;
+                    sg = *reinterpret_cast<const f32x4_t*>(sr);
+                    su = *reinterpret_cast<const f32x4_t*>(sr + N);
+                } else {
+                    sg = su = f32x4_t{ws, ws, ws, ws};
+                }
+                f32x4_t o;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) {
+                    o[v] = silu(core.acc[a][b][vg * 4 + v] * (sx * sg[v])) *
+                           (core.acc[a + Core::FW / 2][b][vg * 4 + v] * (sx * su[v]));
+                    m = fmaxf(m, fabsf(o[v]));
+                }
+                if (valid)
+                    *reinterpret_cast<f32x4_t*>(act + (size_t)r * N + n0 + 8 * vg) = o;
+            }
+        }
+        // lanes l and l ^ 32 hold the same token row
+        const uint32_t mb = max(__float_as_uint(m), (uint32_t)__shfl_xor((int)__float_as_uint(m), 32));
+        if (valid && lane < 32) atomicMax(amax + r, mb);
+    }
+    }  // tiles
+}
+
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
+__global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
+    const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
+    const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale, int rowwise,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
+    int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
+    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW, true>;
+    __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
+    constexpr int WR = TW / WW;  // output rows per wave
+
+    const int n_wt = K / TW;
+    const int npad = *num_padded;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wa = wave % WW, wb = wave / WW;
+    TileWalk<GROUP> walk(n_wt * nsplit, max_blocks);
+    int wtz, blk;
+    while (walk.next(wtz, blk)) {
+    if (blk * TT >= npad) continue;
+    const int wt = wtz % n_wt, z = wtz / n_wt;
+    const int nlen = N / nsplit, nbeg = z * nlen;
+    const int e = block_expert[blk];
+
+    const size_t row_bytes = (size_t)N;
+    const prsrc_t rw = pmake_rsrc(w2 + ((size_t)e * K + (size_t)wt * TW) * N,
+                                  (uint32_t)(TW * row_bytes));
+    const prsrc_t ra = pmake_rsrc(act_q, (uint32_t)((size_t)cap * row_bytes));
+    uint32_t wsoff[Core::kWInstr], aoff[Core::kXInstr];
+    const int row0 = Core::dma_row(wave, 0, lane);
+    const uint32_t wvoff = (uint32_t)(row0 * row_bytes) + nbeg +
+                           Core::dma_chunk(row0, lane) * 16;
+#pragma unroll
+    for (int q = 0; q < Core::kWInstr; ++q)
+        wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)(q * NW * Core::kRowsPerInstr * row_bytes));
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
+        // padding rows (never quantised) copy the block's first row instead
+        const int src = sorted_ids[blk * TT + row] < nslots ? blk * TT + row : blk * TT;
+        aoff[q] = (uint32_t)(src * row_bytes) + nbeg + Core::dma_chunk(row, lane) * 16;
+    }
+    Core core;
+    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+        core.template run<true, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
+    else
+        core.template run<false, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
+
+    const int li = lane & 31;
+    const float ws = rowwise ? 0.0f : w2_scale[e];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
+        const int p = sorted_ids[r];
+        if (p >= nslots) continue;
+        const float w = topk_w[p] * ascale[r];
+#pragma unroll
+        for (int a = 0; a < Core::FW; ++a) {
+            const int c0 = wt * TW + wa * WR + a * 32 + 4 * (lane >> 5);
+            float* dst = ypart + ((size_t)z * nslots + p) * K + c0;
+#pragma unroll
+            for (int vg = 0; vg < 4; ++vg) {
+                f32x4_t sc;
+                if (rowwise)
+                    sc = *reinterpret_cast<const f32x4_t*>(w2_scale + (size_t)e * K + c0 + 8 * vg);
+                else
+                    sc = f32x4_t{ws, ws, ws, ws};
+                f32x4_t o;
+#pragma unroll
+                for (int v = 0; v < 4; ++v) o[v] = core.acc[a][b][vg * 4 + v] * (sc[v] * w);
+                *reinterpret_cast<f32x4_t*>(dst + 8 * vg) = o;
+            }
+        }
+    }
+    }  // tiles
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 // One workgroup per tile, rounded up to whole XCD groups of 8.
@@ -496,13 +702,13 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
         nslots, K, N, max_blocks, (uint16_t*)act);
 }
 
-int prefill_gemm2_splits(int K, int N, int blocks) {
+int prefill_gemm2_splits(int K, int N, int blocks, int gran) {
     // split the reduction until the target tile count (tuning.hpp): fewer
     // tiles leave the last round of workgroups part-empty, every split adds
     // a partial row per slot for the combine to read
     const long tiles = (long)(K % 256 == 0 ? K / 256 : K / 128) * blocks;
     int ns = 1;
-    while (tiles * ns < tune::kPrefillSplitTargetTiles && ns < 4 && (N / (2 * ns)) % 64 == 0)
+    while (tiles * ns < tune::kPrefillSplitTargetTiles && ns < 4 && (N / (2 * ns)) % gran == 0)
         ns *= 2;
     return ns;
 }
@@ -529,6 +735,42 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
         gemm2_prefill_bf16_kernel<128, kPrefillRows, 32, 3, 3, 4, 8, 1, 8><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
+    }
+}
+
+
+// e4m3: 128-code K-steps; GEMM2's reduction split keeps each split a
+// multiple of 128 codes (the caller's split choice)
+void launch_gemm1_prefill_fp8(const uint8_t* xq, const float* xscale, const void* w1,
+                              const float* w1_scale, int rowwise, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded, int M,
+                              int topk, int nslots, int K, int N, int max_blocks, float* act,
+                              uint32_t* amax, hipStream_t s) {
+    const int grid = tile_grid((N / 128) * max_blocks);
+    gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillGemm1WeightSlots,
+                             tune::kPrefillGemm1TokenSlots, 2, 8, 1, tune::kPrefillGemm1Group>
+        <<<grid, 512, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids,
+                              block_expert, num_padded, M, topk, nslots, K, N, max_blocks, act,
+                              amax);
+}
+
+void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
+                              const float* w2_scale, int rowwise, const float* topk_w,
+                              const int32_t* sorted_ids, const int32_t* block_expert,
+                              const int32_t* num_padded, int cap, int nslots, int K, int N,
+                              int nsplit, int max_blocks, float* ypart, hipStream_t s) {
+    if (K % 256 == 0) {
+        const int grid = tile_grid((K / 256) * nsplit * max_blocks);
+        gemm2_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillGemm2WeightSlots,
+                                 tune::kPrefillGemm2TokenSlots, 2, 8, 1, tune::kPrefillGemm2Group>
+            <<<grid, 512, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale, rowwise, topk_w,
+                                  sorted_ids, block_expert, num_padded, cap, nslots, K, N, nsplit,
+                                  max_blocks, ypart);
+    } else {
+        const int grid = tile_grid((K / 128) * nsplit * max_blocks);
+        gemm2_prefill_fp8_kernel<128, kPrefillRows, 128, 3, 3, 4, 8, 1, 8><<<grid, 512, 0, s>>>(
+            act_q, ascale, (const uint8_t*)w2, w2_scale, rowwise, topk_w, sorted_ids,
+            block_expert, num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     }
 }
 

@@ -90,12 +90,29 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                int topk, int nslots, int K, int N, int max_blocks, void* act,
                                hipStream_t s);
 // reduction splits the full-tile GEMM2 uses for (K, N) over `blocks` token
-// blocks; its partial rows go to ypart[split] like the decode kernel's
-int prefill_gemm2_splits(int K, int N, int blocks);
+// blocks, each split a multiple of `gran` reduction elements (the kernel's
+// K-step: 64 bf16, 128 e4m3); its partial rows go to ypart[split] like the
+// decode kernel's
+int prefill_gemm2_splits(int K, int N, int blocks, int gran);
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int nsplit, int max_blocks, float* ypart, hipStream_t s);
+
+// e4m3 weights on the full tiles (K % 128 == 0, N % 128 == 0; with nsplit
+// > 1, (N / nsplit) % 128 == 0): GEMM1 writes the fp32 activation rows and
+// their |act| maxima (amax cleared by the align step), GEMM2 reads act_q /
+// ascale from launch_act_quant; scales as the decode FP8 kernels
+void launch_gemm1_prefill_fp8(const uint8_t* xq, const float* xscale, const void* w1,
+                              const float* w1_scale, int rowwise, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded, int M,
+                              int topk, int nslots, int K, int N, int max_blocks, float* act,
+                              uint32_t* amax, hipStream_t s);
+void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
+                              const float* w2_scale, int rowwise, const float* topk_w,
+                              const int32_t* sorted_ids, const int32_t* block_expert,
+                              const int32_t* num_padded, int cap, int nslots, int K, int N,
+                              int nsplit, int max_blocks, float* ypart, hipStream_t s);
 
 void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
                     hipStream_t s);

@@ -17,8 +17,16 @@ namespace tune {
 // 7168, 2048, 256, 8): decode faster up to 8 rows per expert on all three
 // shapes, full tiles from 12 on; re-measured with the 32- and 64-row decode
 // blocks (Mixtral shape, 16 rows: 0.586 ms decode against 0.548 tiles).
-// e4m3 and MXFP4 weights have only the decode kernels.
 constexpr long kDecodeMaxRowsPerExpert = 8;
+// e4m3 weights: the decode kernels up to this many token-slots per expert,
+// the full tiles above (MXFP4 weights have only the decode kernels).  Sweep
+// of both families (bench.py --fp8 --regime-sweep), ms per layer call at
+// 8 / 16 / 32 / 64 rows per expert, decode against tiles:
+//   K, N, E, k = 4096, 14336, 8, 2: 0.300/0.330, 0.332/0.338, 0.422/0.353,
+//                                   0.735/0.378 (128 rows: 1.198/0.441)
+//   K, N, E, k = 7168, 2048, 256, 8: 2.14/2.42, 2.43/2.54, 3.09/2.82,
+//                                   4.85/3.20 (128 rows: 8.73/4.16)
+constexpr long kFp8DecodeMaxRowsPerExpert = 16;
 
 // ---- decode block rows ------------------------------------------------------
 // 16, 32 or 64 sorted rows per block (1, 2 or 4 token tiles multiplied by

@@ -93,7 +93,8 @@ def test_fused_validation(lib):
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=8192, ws=None)[0] == 0  # size query succeeds
     assert fused(lib, dtype=2)[0] == INV                              # rowwise fp8 without scales
     assert fused(lib, dtype=2, s1=FAKE, s2=None)[0] == INV
-    assert fused(lib, dtype=2, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
+    # e4m3 weights have full-tile kernels too (size query only: no launch here)
+    assert fused(lib, dtype=2, s1=FAKE, s2=FAKE, regime=2, ws=None)[0] == B.MOE_OK
     assert fused(lib, regime=3)[0] == INV
     assert fused(lib, M=-1)[0] == INV
     assert fused(lib, N=0)[0] == INV
@@ -105,7 +106,14 @@ def test_fused_validation(lib):
     assert fused(lib, E=64, k=17)[0] == UNS
     assert fused(lib, K=200)[0] == UNS                               # not a multiple of 128
     assert fused(lib, N=192)[0] == UNS
-    assert fused(lib, dtype=1, s1=FAKE, s2=FAKE, regime=2)[0] == UNS  # no fp8 full-tile kernels
+    assert fused(lib, dtype=1, s1=FAKE, s2=FAKE, regime=2, ws=None)[0] == B.MOE_OK
+    # 32-bit offsets of the sorted activation rows GEMM2 reads: 2 bytes each
+    # for bf16, 1 for the e4m3 codes
+    assert fused(lib, M=65536, K=4096, N=14336, E=8, k=2, ws=None)[0] == UNS
+    assert fused(lib, dtype=1, s1=FAKE, s2=FAKE, M=65536, K=4096, N=14336, E=8, k=2,
+                 ws=None)[0] == B.MOE_OK
+    assert fused(lib, dtype=1, s1=FAKE, s2=FAKE, M=4096, K=7168, N=2048, E=256, k=8,
+                 ws=None)[0] == B.MOE_OK
     assert fused(lib, x=None)[0] == INV
     assert fused(lib, out=None)[0] == INV
     assert fused(lib, w2=MISALIGNED)[0] == INV

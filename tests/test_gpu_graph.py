@@ -24,6 +24,7 @@ CASES = [
     ("full_tiles_bf16", 96, 512, 512, 6, 2, "bf16", 2),
     ("decode_mxfp4", 8, 512, 512, 8, 2, "mxfp4", 0),
     ("fp8_32_row_blocks", 48, 512, 256, 8, 2, "fp8", 0),
+    ("full_tiles_fp8", 96, 512, 512, 6, 2, "fp8", 2),
 ]
 
 

@@ -229,10 +229,11 @@ SMALL = [
     # FP8 with fp64-MFMA logits (split over K) and the token rows quantised
     # by their own kernel
     ("fp8_router_mfma", 78, 1024, 256, 128, 4, True, None, 0),
-    # more rows per expert: 32-row (2 token tiles) and 64-row (4) blocks
+    # more rows per expert: 32-row (2 token tiles) and 64-row (4) blocks (the
+    # latter forced: the automatic choice takes the full tiles there)
     ("fp8_two_tiles", 48, 512, 256, 8, 2, True, None, 0),
-    ("fp8_four_tiles", 160, 512, 384, 8, 2, True, 0.5, 0),
-    ("fp8_rowwise_four_tiles", 200, 256, 256, 4, 2, "rowwise", None, 0),
+    ("fp8_four_tiles", 160, 512, 384, 8, 2, True, 0.5, 1),
+    ("fp8_rowwise_four_tiles", 200, 256, 256, 4, 2, "rowwise", None, 1),
     # e4m3 weights with per-channel scales (one per output row)
     ("fp8_rowwise_tiny", 16, 512, 256, 16, 4, "rowwise", None, 0),
     ("fp8_rowwise_ragged", 7, 384, 640, 32, 8, "rowwise", None, 0),
@@ -254,6 +255,16 @@ SMALL = [
     # many experts and a wider intermediate dimension
     ("mxfp4_wide_grid", 32, 512, 1024, 64, 4, "mxfp4", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
+    # e4m3 weights on the full tiles: forced, ragged (GEMM2 with 128 output
+    # rows per tile as K % 256 != 0), reduction split in 2 and 4, per-channel
+    # scales, and the automatic choice at many rows per expert
+    ("fp8_prefill_tiles", 300, 256, 384, 8, 2, True, None, 2),
+    ("fp8_prefill_ragged", 333, 384, 640, 5, 3, True, None, 2),
+    ("fp8_prefill_split2", 150, 256, 256, 4, 2, True, None, 2),
+    ("fp8_prefill_split4", 260, 512, 512, 4, 2, True, None, 2),
+    ("fp8_rowwise_prefill", 200, 256, 256, 4, 2, "rowwise", None, 2),
+    ("fp8_rowwise_prefill_ragged", 97, 384, 384, 3, 2, "rowwise", 0.5, 2),
+    ("fp8_prefill_auto_skewed", 700, 256, 384, 8, 2, True, 0.5, 0),
 ]
 
 
@@ -299,6 +310,23 @@ def test_swap_ab_identity_decode_vs_prefill(moe):
     assert row_rel_err(a, b) <= 1e-2
 
 
+def test_fp8_decode_vs_tiles(moe):
+    """The e4m3 Swap-AB decode kernels and the e4m3 full-tile kernels on
+    identical inputs: both within tolerance of the oracle, and close to each
+    other (they differ by fp32 summation order, which can move an activation
+    code across an e4m3 rounding boundary)."""
+    note("fp8 decode vs full tiles")
+    wl = wlm.Workload("xcheck8", M=96, K=512, N=768, E=6, topk=2, fp8=True, seed=12)
+    d, g = gen_small(wl)
+    a = out_f64(run_layer(moe, g, wl, 1))
+    b = out_f64(run_layer(moe, g, wl, 2))
+    ref, _, _ = oracle_layer(d, wl)
+    ea, eb, eab = row_rel_err(a, ref), row_rel_err(b, ref), row_rel_err(a, b)
+    note(f"  decode {ea:.3e} tiles {eb:.3e} between {eab:.3e}")
+    assert ea <= TOL_FP8 and eb <= TOL_FP8
+    assert eab <= 2e-2
+
+
 def test_fused_deterministic(moe):
     note("determinism")
     wl = wlm.Workload("det", M=40, K=512, N=512, E=8, topk=2, seed=4)
@@ -308,9 +336,10 @@ def test_fused_deterministic(moe):
         assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
     wl8 = wl.resized(fp8=True)
     d8, g8 = gen_small(wl8)
-    o8 = [run_layer(moe, g8, wl8).clone() for _ in range(3)]
-    for o in o8[1:]:
-        assert torch.equal(o.view(torch.int16), o8[0].view(torch.int16))
+    for regime in (0, 2):
+        o8 = [run_layer(moe, g8, wl8, regime).clone() for _ in range(3)]
+        for o in o8[1:]:
+            assert torch.equal(o.view(torch.int16), o8[0].view(torch.int16))
 
 
 # --------------------------------------------------------------------------
@@ -327,10 +356,14 @@ def sample_tokens(M, n=6):
 
 
 # the DeepSeek-shaped batch also with per-channel e4m3 weight scales and with
-# MXFP4 weights
-@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise", "dsv3_mxfp4"])
+# MXFP4 weights; the prefill batch also with e4m3 weights
+@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise", "dsv3_mxfp4",
+                                                      "mixtral_prefill_fp8"])
 def test_fused_full_size_sampled(moe, name):
-    if name == "dsv3_fp8_rowwise":
+    if name == "mixtral_prefill_fp8":
+        # the prefill batch with e4m3 weights: the e4m3 full-tile kernels
+        wl = wlm.WORKLOADS["mixtral_prefill"].resized(name=name, fp8=True)
+    elif name == "dsv3_fp8_rowwise":
         wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, fp8_rowwise=True)
     elif name == "dsv3_mxfp4":
         wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, fp8=False, mxfp4=True)
