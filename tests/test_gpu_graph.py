@@ -25,6 +25,7 @@ CASES = [
     ("decode_mxfp4", 8, 512, 512, 8, 2, "mxfp4", 0),
     ("fp8_32_row_blocks", 48, 512, 256, 8, 2, "fp8", 0),
     ("full_tiles_fp8", 96, 512, 512, 6, 2, "fp8", 2),
+    ("single_token_one_launch_routing", 1, 512, 512, 16, 2, "fp8", 0),
 ]
 
 

@@ -265,6 +265,12 @@ SMALL = [
     ("fp8_rowwise_prefill", 200, 256, 256, 4, 2, "rowwise", None, 2),
     ("fp8_rowwise_prefill_ragged", 97, 384, 384, 3, 2, "rowwise", 0.5, 2),
     ("fp8_prefill_auto_skewed", 700, 256, 384, 8, 2, True, 0.5, 0),
+    # logits, (FP8) token codes, top-k and align in one launch for at most
+    # two tokens and 16 (token, expert) pairs
+    ("tiny_route_fused_bias", 2, 768, 512, 8, 2, False, 0.5, 0),
+    ("tiny_route_fused_fp8", 1, 1536, 256, 8, 2, True, 0.5, 0),
+    ("tiny_route_fused_fp8_rowwise", 2, 512, 256, 4, 3, "rowwise", None, 0),
+    ("tiny_route_fused_mxfp4", 1, 512, 512, 12, 4, "mxfp4", None, 0),
 ]
 
 
@@ -285,6 +291,34 @@ def test_fused_small(moe, case):
     err = row_rel_err(got, ref)
     note(f"  err={err:.3e}")
     assert err <= (TOL_FP8 if (fp8 or mx) else TOL_BF16)
+
+
+@pytest.mark.parametrize("M,E,fp8", [(1, 16, False), (2, 8, False), (1, 8, True)])
+def test_fused_tiny_routing_ties(moe, M, E, fp8):
+    """The one-launch routing of tiny batches breaks ties to the lower expert
+    id: with every router row equal all logits of a token tie and experts 0
+    and 1 must serve it; with some rows duplicated the oracle's tie rule
+    decides.  A wrong pick routes through other experts' weights, which the
+    output comparison sees."""
+    note(f"fused tiny routing ties M={M} E={E} fp8={fp8}")
+    wl = wlm.Workload("tiny_ties", M=M, K=256, N=256, E=E, topk=2, fp8=fp8, seed=8)
+    for dup in ("all", "pairs"):
+        d, g = gen_small(wl)
+        wr = d["w_router"].clone()
+        if dup == "all":
+            wr[:] = wr[0]
+        else:
+            wr[E - 1] = wr[1]
+            wr[E - 2] = wr[0]
+        d["w_router"] = wr
+        g["w_router"] = wr.cuda()
+        got = out_f64(run_layer(moe, g, wl))
+        ref, ids, _ = oracle_layer(d, wl)
+        if dup == "all":
+            assert np.array_equal(np.asarray(ids).reshape(M, 2), np.tile([0, 1], (M, 1)))
+        err = row_rel_err(got, ref)
+        note(f"  {dup}: err={err:.3e}")
+        assert err <= (TOL_FP8 if fp8 else TOL_BF16)
 
 
 def test_fused_m0_is_noop(moe):
