@@ -747,8 +747,8 @@ void launch_gemm1_prefill_fp8(const uint8_t* xq, const float* xscale, const void
                               int topk, int nslots, int K, int N, int max_blocks, float* act,
                               uint32_t* amax, hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillGemm1WeightSlots,
-                             tune::kPrefillGemm1TokenSlots, 2, 8, 1, tune::kPrefillGemm1Group>
+    gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm1WeightSlots,
+                             tune::kPrefillFp8Gemm1TokenSlots, 2, 8, 1, tune::kPrefillFp8Gemm1Group>
         <<<grid, 512, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids,
                               block_expert, num_padded, M, topk, nslots, K, N, max_blocks, act,
                               amax);
@@ -761,8 +761,9 @@ void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const v
                               int nsplit, int max_blocks, float* ypart, hipStream_t s) {
     if (K % 256 == 0) {
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillGemm2WeightSlots,
-                                 tune::kPrefillGemm2TokenSlots, 2, 8, 1, tune::kPrefillGemm2Group>
+        gemm2_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm2WeightSlots,
+                                 tune::kPrefillFp8Gemm2TokenSlots, 2, 8, 1,
+                                 tune::kPrefillFp8Gemm2Group>
             <<<grid, 512, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale, rowwise, topk_w,
                                   sorted_ids, block_expert, num_padded, cap, nslots, K, N, nsplit,
                                   max_blocks, ypart);

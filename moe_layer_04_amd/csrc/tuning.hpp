@@ -77,6 +77,17 @@ constexpr int kPrefillGemm2Group = 4;
 // 2 + 3 (933-935 us against 946-950 with 3 + 2)
 constexpr int kPrefillGemm1WeightSlots = 3, kPrefillGemm1TokenSlots = 2;
 constexpr int kPrefillGemm2WeightSlots = 2, kPrefillGemm2TokenSlots = 3;
+// the e4m3 full tiles (same bytes per K-step as the bf16 ones).  GEMM1
+// group, rings (weight + token slots), us on the Mixtral shape with 4096
+// tokens / the DeepSeek shape with 4096 tokens (two runs where given):
+// 2, 3+2: 983-1011 / 1679-1733; 4, 3+2: 1003 / 2163; 4, 2+3: 990 / 2330;
+// 8, 2+3: 1001 / 2327; 1, 3+2: 1031 / 1791; 1, 2+2: 1059 / 1750;
+// 2, 2+3: 1016 / 1844; 3, 3+2: 1014 / 2267.  GEMM2: 4, 2+3: 520 / 1148;
+// 4, 3+2: 555 / 1112; 2, 3+2: 582 / 1216; 2, 2+3: 542 / 1326; 8, 2+2:
+// 593 / 1440; 8, 2+3: 579 / 1564.
+constexpr int kPrefillFp8Gemm1Group = 2, kPrefillFp8Gemm2Group = 4;
+constexpr int kPrefillFp8Gemm1WeightSlots = 3, kPrefillFp8Gemm1TokenSlots = 2;
+constexpr int kPrefillFp8Gemm2WeightSlots = 2, kPrefillFp8Gemm2TokenSlots = 3;
 
 // ---- router -------------------------------------------------------------------
 // fp64-MFMA logits: split K until the tiles x splits cover every CU (the
