@@ -260,6 +260,171 @@ __global__ __launch_bounds__(kRouteTinyWaves * kWave) void route_tiny_kernel(
                              block_expert, expert_offsets, num_padded, zero_buf, zero_words, inv);
 }
 
+// ---------------------------------------------------------------------------
+// The same permutation for large batches over many workgroups, in three
+// launches.  The slots are cut into chunks of kAlignThreads, as the single
+// workgroup walks them; (1) a workgroup per chunk counts its slots per
+// expert; (2) one workgroup adds the counts up, scans the padded totals into
+// the experts' offsets and gives every (chunk, expert) its first position:
+// the expert's offset plus that expert's slots in earlier chunks -- exactly
+// the running count the single workgroup carries from chunk to chunk; (3) a
+// workgroup per chunk places its slots at that base plus their rank inside
+// the chunk (the same ballot ranks), and all workgroups share the sentinel
+// and block-owner writes.  The result is identical to align_kernel's.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(kAlignThreads) void align_count_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int32_t* __restrict__ chunk_cnt) {
+    __shared__ int cnt[MOE_KERNEL_MAX_EXPERTS];
+    const int tid = (int)threadIdx.x;
+    const int c = (int)blockIdx.x;
+    for (int e = tid; e < E; e += kAlignThreads) cnt[e] = 0;
+    __syncthreads();
+    const int p = c * kAlignThreads + tid;
+    if (p < n) atomicAdd(&cnt[min(max(ids[p], 0), E - 1)], 1);  // counts are order-free
+    __syncthreads();
+    for (int e = tid; e < E; e += kAlignThreads) chunk_cnt[(size_t)c * E + e] = cnt[e];
+}
+
+// One workgroup; chunk_cnt [nchunk,E] becomes the chunk bases; cnt_total [E]
+// receives each expert's slot count.
+__global__ __launch_bounds__(kAlignThreads) void align_scan_kernel(
+    int nchunk, int E, int B, int32_t* __restrict__ chunk_cnt, int32_t* __restrict__ cnt_total,
+    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded) {
+    __shared__ int tot[MOE_KERNEL_MAX_EXPERTS];
+    __shared__ int off[MOE_KERNEL_MAX_EXPERTS + 1];
+    const int tid = (int)threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    // per expert: exclusive prefix of its counts over the chunks (in place)
+    for (int e = tid; e < E; e += kAlignThreads) {
+        int run = 0;
+        for (int c = 0; c < nchunk; ++c) {
+            const int v = chunk_cnt[(size_t)c * E + e];
+            chunk_cnt[(size_t)c * E + e] = run;
+            run += v;
+        }
+        tot[e] = run;
+    }
+    __syncthreads();
+    if (wave == 0) {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            v[i] = (e < E) ? (tot[e] + B - 1) / B * B : 0;
+            sum += v[i];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        int base = incl - sum;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int e = lane * 4 + i;
+            if (e < E) off[e] = base;
+            base += v[i];
+        }
+        if (lane == kWave - 1) off[E] = incl;
+    }
+    __syncthreads();
+    for (int e = tid; e <= E; e += kAlignThreads) expert_offsets[e] = off[e];
+    for (int e = tid; e < E; e += kAlignThreads) cnt_total[e] = tot[e];
+    if (tid == 0) *num_padded = off[E];
+    for (int i = tid; i < nchunk * E; i += kAlignThreads) chunk_cnt[i] += off[i % E];
+}
+
+__global__ __launch_bounds__(kAlignThreads) void align_scatter_kernel(
+    const int32_t* __restrict__ ids, int n, int E, int B, int cap,
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ cnt_total,
+    const int32_t* __restrict__ expert_offsets, int32_t* __restrict__ sorted_ids,
+    int32_t* __restrict__ block_expert, uint32_t* __restrict__ zero_buf, int zero_words,
+    int32_t* __restrict__ inv) {
+    __shared__ int cnt[MOE_KERNEL_MAX_EXPERTS];
+    __shared__ int off[MOE_KERNEL_MAX_EXPERTS + 1];
+    __shared__ int wc[kAlignWaves][MOE_KERNEL_MAX_EXPERTS];
+    const int tid = (int)threadIdx.x;
+    const int lane = lane_id();
+    const int wave = tid / kWave;
+    const int c = (int)blockIdx.x;
+    const int nthreads = (int)gridDim.x * kAlignThreads;
+    const int gtid = c * kAlignThreads + tid;
+    for (int i = gtid; i < zero_words; i += nthreads) zero_buf[i] = 0u;
+    for (int e = tid; e < E; e += kAlignThreads) cnt[e] = cnt_total[e];
+    for (int e = tid; e <= E; e += kAlignThreads) off[e] = expert_offsets[e];
+    for (int i = tid; i < kAlignWaves * MOE_KERNEL_MAX_EXPERTS; i += kAlignThreads)
+        (&wc[0][0])[i] = 0;
+    __syncthreads();
+    const int npad = off[E];
+    // sentinels and block owners, shared by all workgroups
+    for (int i = gtid; i < cap; i += nthreads) {
+        bool pad = (i >= npad);
+        if (!pad) {
+            int lo = 0, hi = E - 1;  // last e with off[e] <= i
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            pad = (i - off[lo]) >= cnt[lo];
+        }
+        if (pad) sorted_ids[i] = n;
+    }
+    for (int b = gtid; b < cap / B; b += nthreads) {
+        const int i = b * B;
+        int owner = -1;
+        if (i < npad) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        block_expert[b] = owner;
+    }
+    // this chunk's slots: rank among earlier slots of the same expert
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    const int p = c * kAlignThreads + tid;
+    const bool valid = p < n;
+    const int e = valid ? min(max(ids[p], 0), E - 1) : 0;
+    uint64_t match = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+        const bool on = (e >> bit) & 1;
+        const uint64_t bb = __ballot(valid && on);
+        match &= on ? bb : ~bb;
+    }
+    const int rank = __popcll(match & lt_mask);
+    if (valid && (match >> lane) == 1ull) wc[wave][e] = __popcll(match);  // last lane of its group
+    __syncthreads();
+    if (valid) {
+        int before = 0;
+        for (int w = 0; w < wave; ++w) before += wc[w][e];
+        const int pos = chunk_base[(size_t)c * E + e] + before + rank;
+        sorted_ids[pos] = p;
+        if (inv) inv[p] = pos;
+    }
+}
+
+static_assert(kAlignThreads == 1024, "align_chunks counts chunks of 1024 slots");
+
+bool align_multi_fits(int n) { return n > kAlignMultiMinSlots; }
+
+void launch_align_multi(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
+                        uint32_t* zero_buf, int zero_words, int32_t* inv, int32_t* chunk_cnt,
+                        int32_t* cnt_total, hipStream_t s) {
+    const int nchunk = align_chunks(n);
+    align_count_kernel<<<nchunk, kAlignThreads, 0, s>>>(ids, n, E, chunk_cnt);
+    align_scan_kernel<<<1, kAlignThreads, 0, s>>>(nchunk, E, B, chunk_cnt, cnt_total,
+                                                  expert_offsets, num_padded);
+    align_scatter_kernel<<<nchunk, kAlignThreads, 0, s>>>(ids, n, E, B, cap, chunk_cnt, cnt_total,
+                                                          expert_offsets, sorted_ids, block_expert,
+                                                          zero_buf, zero_words, inv);
+}
+
 void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,
                   int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
                   uint32_t* zero_buf, int zero_words, int32_t* inv, hipStream_t s) {

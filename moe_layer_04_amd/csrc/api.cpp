@@ -46,6 +46,8 @@ struct Plan {
     size_t lpart = 0;
     size_t logits = 0, ids = 0, wts = 0, sorted = 0, bexp = 0, offs = 0, npad = 0;
     size_t inv = 0;  // FP8 activations: sorted position of each slot
+    bool align_multi = false;  // the multi-workgroup align (scratch achunk, atot)
+    size_t achunk = 0, atot = 0;
     size_t xq = 0, xs = 0, amax = 0, act = 0, actq = 0, as = 0, ypart = 0, total = 0;
 };
 
@@ -113,6 +115,11 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     p.bexp = take((size_t)p.max_blocks * 4);
     p.offs = take((size_t)(E + 1) * 4);
     p.npad = take(4);
+    p.align_multi = !moe::topk_align_fits(M, topk) && moe::align_multi_fits((int)slots);
+    if (p.align_multi) {
+        p.achunk = take((size_t)moe::align_chunks((int)slots) * E * 4);
+        p.atot = take((size_t)E * 4);
+    }
     if (is_fp8(dtype)) {
         p.xq = take((size_t)M * K);
         p.xs = take((size_t)M * 4);
@@ -296,8 +303,13 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         mark(1);
         moe::launch_router_topk(logits, M, E, topk, ids, wts, lpart, p.lsplit, router_bias, s);
         mark(2);
-        moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax,
-                          amax_words, inv, s);
+        if (p.align_multi)
+            moe::launch_align_multi(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad,
+                                    amax, amax_words, inv, (int32_t*)(ws + p.achunk),
+                                    (int32_t*)(ws + p.atot), s);
+        else
+            moe::launch_align(ids, nslots, E, p.block, p.cap, sorted, bexp, offs, npad, amax,
+                              amax_words, inv, s);
     }
     mark(3);
     if (fp8) {

@@ -47,6 +47,17 @@ void launch_route_tiny(const void* x, const void* wr, const float* bias, int M, 
                        int32_t* expert_offsets, int32_t* num_padded, uint32_t* zero_buf,
                        int zero_words, int32_t* inv, hipStream_t s);
 
+// The align of launch_align over many workgroups (three launches, identical
+// result) for batches of more than kAlignMultiMinSlots slots; scratch:
+// chunk_cnt [align_chunks(n) * E] and cnt_total [E] int32.
+constexpr int kAlignMultiMinSlots = 2048;
+inline int align_chunks(int n) { return (n + 1023) / 1024; }
+bool align_multi_fits(int n);
+void launch_align_multi(const int32_t* ids, int n, int E, int B, int cap, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
+                        uint32_t* zero_buf, int zero_words, int32_t* inv, int32_t* chunk_cnt,
+                        int32_t* cnt_total, hipStream_t s);
+
 // Top-k + align (and, with xq not null, the FP8 token codes; meant for a
 // few tokens) in one single-workgroup launch, for at most kRouteSmallMaxTokens
 // tokens and kRouteSmallMaxSlots token-slots.

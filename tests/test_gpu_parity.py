@@ -265,6 +265,17 @@ SMALL = [
     ("fp8_rowwise_prefill", 200, 256, 256, 4, 2, "rowwise", None, 2),
     ("fp8_rowwise_prefill_ragged", 97, 384, 384, 3, 2, "rowwise", 0.5, 2),
     ("fp8_prefill_auto_skewed", 700, 256, 384, 8, 2, True, 0.5, 0),
+    # full tiles over 256 experts with a few rows each (one mostly-padding
+    # block per expert, block owners and sentinels over a long sorted list)
+    ("fp8_prefill_many_experts", 300, 256, 256, 256, 8, True, None, 2),
+    ("prefill_many_experts", 100, 256, 256, 256, 8, False, None, 2),
+    # more than 2048 token-slots: the multi-workgroup align (per-chunk counts,
+    # one scan, per-chunk scatter), with decode blocks, FP8 (its amax rows
+    # cleared and inverse permutation written by all workgroups) and a last
+    # chunk of one slot
+    ("decode_many_slots", 300, 256, 256, 256, 8, False, None, 1),
+    ("fp8_decode_many_slots", 300, 256, 256, 128, 8, True, None, 1),
+    ("align_multi_ragged", 683, 256, 256, 16, 3, False, None, 0),
     # logits, (FP8) token codes, top-k and align in one launch for at most
     # two tokens and 16 (token, expert) pairs
     ("tiny_route_fused_bias", 2, 768, 512, 8, 2, False, 0.5, 0),
