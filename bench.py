@@ -132,6 +132,46 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     print(json.dumps(rec))
 
 
+def mfma_summary(csv_path):
+    """MFMA utilisation per kernel from one rocprofv3 --pmc run of
+    SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F8 and
+    GRBM_GUI_ACTIVE: the busy cycles (summed over the 1024 SIMDs) over the
+    active cycles of one XCD (the aggregated GRBM count covers the 8 XCDs)
+    times the SIMDs, the clock those cycles imply over the dispatch, and the
+    MFMA FLOPs the hardware executed (512 per MOP, padding rows included)."""
+    import csv
+    import statistics
+    rows = {}
+    for r in csv.DictReader(open(csv_path)):
+        k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+        d = rows.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
+        d[r["Counter_Name"]] = float(r["Counter_Value"])
+        d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    out = []
+    for k, disp in rows.items():
+        util, clk, flops, rate = [], [], [], []
+        for d in disp.values():
+            gui = d.get("GRBM_GUI_ACTIVE", 0.0) / 8
+            if gui <= 0 or d["ns"] <= 0:
+                continue
+            util.append(d.get("SQ_VALU_MFMA_BUSY_CYCLES", 0.0) / (gui * 1024))
+            clk.append(gui / d["ns"])
+            f = 512.0 * (d.get("SQ_INSTS_VALU_MFMA_MOPS_BF16", 0.0) +
+                         d.get("SQ_INSTS_VALU_MFMA_MOPS_F8", 0.0))
+            flops.append(f)
+            rate.append(f / d["ns"] / 1e3)
+        if not util:
+            continue
+        rec = {"kernel": k, "dispatches": len(util),
+               "mfma_busy_frac": round(statistics.median(util), 4),
+               "clock_GHz": round(statistics.median(clk), 3),
+               "mfma_flops": statistics.median(flops),
+               "mfma_TFLOPs": round(statistics.median(rate), 1)}
+        out.append(rec)
+        print(json.dumps(rec))
+    return out
+
+
 def regime_sweep(moe, wlm, wl, dev, ms_list=None):
     """Both kernel families (the workload's bf16 or e4m3 weights) on batches of
     M = 8 .. 1024 tokens (or ms_list) of this workload's shape: mean ms per
@@ -212,12 +252,20 @@ def main():
                          "per M, then exit")
     ap.add_argument("--sweep-tokens", type=int, nargs="+", default=None,
                     help="batch sizes M of --regime-sweep")
+    ap.add_argument("--mfma-summary", metavar="CSV",
+                    help="MFMA busy fraction, clock and executed MFMA FLOPs per kernel from "
+                         "a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
+                         "SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F8 and "
+                         "GRBM_GUI_ACTIVE; one JSON line per kernel, then exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [REQ_CSV COPY_REQ_CSV]: "
                          "turn rocprofv3 --pmc counter CSVs of this workload and of the copy "
                          "calibration (FETCH_SIZE, WRITE_SIZE, and optionally the TCC_EA0_RDREQ "
                          "request-size counters) into profiles/gemm1_<workload>_pmc.json and exit")
     args = ap.parse_args()
+    if args.mfma_summary:
+        mfma_summary(args.mfma_summary)
+        return
     if args.pmc_summary:
         if len(args.pmc_summary) not in (4, 6):
             ap.error("--pmc-summary takes 4 or 6 CSV paths")
