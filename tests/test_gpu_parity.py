@@ -276,6 +276,9 @@ SMALL = [
     ("decode_many_slots", 300, 256, 256, 256, 8, False, None, 1),
     ("fp8_decode_many_slots", 300, 256, 256, 128, 8, True, None, 1),
     ("align_multi_ragged", 683, 256, 256, 16, 3, False, None, 0),
+    # the largest top-k (16), on the decode kernels and on the e4m3 full tiles
+    ("topk16", 20, 256, 256, 64, 16, False, None, 0),
+    ("fp8_topk16_tiles", 40, 256, 256, 32, 16, True, None, 2),
     # logits, (FP8) token codes, top-k and align in one launch for at most
     # two tokens and 16 (token, expert) pairs
     ("tiny_route_fused_bias", 2, 768, 512, 8, 2, False, 0.5, 0),
