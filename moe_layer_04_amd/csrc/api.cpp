@@ -68,6 +68,11 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     }
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
+    // full tiles: 128-row token blocks when the experts receive few rows
+    // (tuning.hpp); those kernels are built for K % 256 == 0
+    if (regime == MOE_REGIME_PREFILL && K % 256 == 0 &&
+        slots <= moe::tune::kPrefillSmallTileMaxRows * (slots < E ? slots : E))
+        p.block = moe::kPrefillSmallRows;
     // larger decode blocks when experts receive more rows (sized in tuning.hpp)
     if (regime == MOE_REGIME_DECODE) p.block = moe::tune::decode_block_rows(slots, E);
     p.cap = (int)(slots + (long)E * (p.block - 1));
@@ -320,7 +325,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         const bool tiles = p.regime == MOE_REGIME_PREFILL;  // e4m3 only
         if (tiles)
             moe::launch_gemm1_prefill_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
-                                          topk, nslots, K, N, p.grid_blocks, act, amax, s);
+                                          topk, nslots, K, N, p.grid_blocks, p.block, act, amax,
+                                          s);
         else if (mx)
             moe::launch_gemm1_decode_mxfp4(xq, xs, w1, (const uint8_t*)w1_scale, sorted, bexp,
                                            npad, M, topk, nslots, K, N, p.grid_blocks,
@@ -335,7 +341,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         if (tiles)
             moe::launch_gemm2_prefill_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
                                           npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
-                                          ypart, s);
+                                          p.block, ypart, s);
         else if (mx)
             moe::launch_gemm2_decode_mxfp4(actq, as, w2, (const uint8_t*)w2_scale, wts, sorted,
                                            bexp, npad, p.cap, nslots, K, N, p.nsplit,
@@ -352,7 +358,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                           p.grid_blocks, p.block / kDecodeBlock, act, s);
         else
             moe::launch_gemm1_prefill_bf16(x, w1, sorted, bexp, npad, M, topk, nslots, K, N,
-                                           p.grid_blocks, act, s);
+                                           p.grid_blocks, p.block, act, s);
         mark(4);
         mark(5);
         if (p.regime == MOE_REGIME_DECODE)
@@ -361,7 +367,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                           s);
         else
             moe::launch_gemm2_prefill_bf16(act, w2, wts, sorted, bexp, npad, p.cap, nslots, K, N,
-                                           p.nsplit, p.grid_blocks, ypart, s);
+                                           p.nsplit, p.grid_blocks, p.block, ypart, s);
         mark(6);
     }
     moe::launch_combine(ypart, M, K, topk, p.nsplit, out, s);

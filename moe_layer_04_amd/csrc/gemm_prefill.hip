@@ -690,16 +690,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
 // One workgroup per tile, rounded up to whole XCD groups of 8.
 static int tile_grid(int tiles) { return (tiles + 7) / 8 * 8; }
 
+// Token blocks of tt = 256 rows, or 128 for batches with few rows per expert
+// (the plan's choice, tuning.hpp): 128-row tiles put 4 waves along the weight
+// rows and 2 along the tokens, with a 3-slot weight ring and a 4-slot token
+// ring (160 KB of LDS).
 void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,
-                               int topk, int nslots, int K, int N, int max_blocks, void* act,
-                               hipStream_t s) {
+                               int topk, int nslots, int K, int N, int max_blocks, int tt,
+                               void* act, hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm1WeightSlots,
-                              tune::kPrefillGemm1TokenSlots, 2, 8, 1, tune::kPrefillGemm1Group>
-        <<<grid, 512, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M, topk,
-        nslots, K, N, max_blocks, (uint16_t*)act);
+    if (tt == kPrefillSmallRows)
+        gemm1_prefill_bf16_kernel<256, kPrefillSmallRows, 64, 3, 4, 4, 8, 1,
+                                  tune::kPrefillGemm1Group><<<grid, 512, 0, s>>>(
+            (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
+            topk, nslots, K, N, max_blocks, (uint16_t*)act);
+    else
+        gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm1WeightSlots,
+                                  tune::kPrefillGemm1TokenSlots, 2, 8, 1, tune::kPrefillGemm1Group>
+            <<<grid, 512, 0, s>>>(
+            (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
+            topk, nslots, K, N, max_blocks, (uint16_t*)act);
 }
 
 int prefill_gemm2_splits(int K, int N, int blocks, int gran) {
@@ -716,8 +726,16 @@ int prefill_gemm2_splits(int K, int N, int blocks, int gran) {
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
-                               int nsplit, int max_blocks, float* ypart, hipStream_t s) {
-    if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
+                               int nsplit, int max_blocks, int tt, float* ypart, hipStream_t s) {
+    if (tt == kPrefillSmallRows) {
+        // the plan picks 128-row blocks only with K % 256 == 0; its splits
+        // keep N / nsplit a multiple of 64
+        const int grid = tile_grid((K / 256) * nsplit * max_blocks);
+        gemm2_prefill_bf16_kernel<256, kPrefillSmallRows, 64, 3, 4, 4, 8, 1,
+                                  tune::kPrefillGemm2Group><<<grid, 512, 0, s>>>(
+            (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
+            num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
+    } else if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
         // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
         gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm2WeightSlots,
@@ -744,22 +762,35 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
 void launch_gemm1_prefill_fp8(const uint8_t* xq, const float* xscale, const void* w1,
                               const float* w1_scale, int rowwise, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded, int M,
-                              int topk, int nslots, int K, int N, int max_blocks, float* act,
-                              uint32_t* amax, hipStream_t s) {
+                              int topk, int nslots, int K, int N, int max_blocks, int tt,
+                              float* act, uint32_t* amax, hipStream_t s) {
     const int grid = tile_grid((N / 128) * max_blocks);
-    gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm1WeightSlots,
-                             tune::kPrefillFp8Gemm1TokenSlots, 2, 8, 1, tune::kPrefillFp8Gemm1Group>
-        <<<grid, 512, 0, s>>>(xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids,
-                              block_expert, num_padded, M, topk, nslots, K, N, max_blocks, act,
-                              amax);
+    if (tt == kPrefillSmallRows)
+        gemm1_prefill_fp8_kernel<256, kPrefillSmallRows, 128, 3, 4, 4, 8, 1,
+                                 tune::kPrefillFp8Gemm1Group><<<grid, 512, 0, s>>>(
+            xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids, block_expert,
+            num_padded, M, topk, nslots, K, N, max_blocks, act, amax);
+    else
+        gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm1WeightSlots,
+                                 tune::kPrefillFp8Gemm1TokenSlots, 2, 8, 1,
+                                 tune::kPrefillFp8Gemm1Group><<<grid, 512, 0, s>>>(
+            xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids, block_expert,
+            num_padded, M, topk, nslots, K, N, max_blocks, act, amax);
 }
 
 void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
                               const float* w2_scale, int rowwise, const float* topk_w,
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
-                              int nsplit, int max_blocks, float* ypart, hipStream_t s) {
-    if (K % 256 == 0) {
+                              int nsplit, int max_blocks, int tt, float* ypart, hipStream_t s) {
+    if (tt == kPrefillSmallRows) {
+        // 128-row blocks come with K % 256 == 0 (the plan's choice)
+        const int grid = tile_grid((K / 256) * nsplit * max_blocks);
+        gemm2_prefill_fp8_kernel<256, kPrefillSmallRows, 128, 3, 4, 4, 8, 1,
+                                 tune::kPrefillFp8Gemm2Group><<<grid, 512, 0, s>>>(
+            act_q, ascale, (const uint8_t*)w2, w2_scale, rowwise, topk_w, sorted_ids,
+            block_expert, num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
+    } else if (K % 256 == 0) {
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
         gemm2_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm2WeightSlots,
                                  tune::kPrefillFp8Gemm2TokenSlots, 2, 8, 1,

@@ -14,6 +14,7 @@ namespace moe {
 // Swap-AB decode kernels and for the full-tile kernels
 constexpr int kDecodeRows = 16;
 constexpr int kPrefillRows = 256;
+constexpr int kPrefillSmallRows = 128;  // full-tile blocks for few rows per expert
 }
 
 namespace moe {
@@ -107,10 +108,12 @@ void launch_gemm2_decode_mxfp4(const uint8_t* act_q, const float* ascale, const 
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
                                int nsplit, int max_blocks, int nt, float* ypart, hipStream_t s);
 
+// Full tiles: tt = token rows per block, kPrefillRows or kPrefillSmallRows
+// (the latter only with K % 256 == 0).
 void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int32_t* num_padded, int M,
-                               int topk, int nslots, int K, int N, int max_blocks, void* act,
-                               hipStream_t s);
+                               int topk, int nslots, int K, int N, int max_blocks, int tt,
+                               void* act, hipStream_t s);
 // reduction splits the full-tile GEMM2 uses for (K, N) over `blocks` token
 // blocks, each split a multiple of `gran` reduction elements (the kernel's
 // K-step: 64 bf16, 128 e4m3); its partial rows go to ypart[split] like the
@@ -119,7 +122,7 @@ int prefill_gemm2_splits(int K, int N, int blocks, int gran);
 void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* topk_w,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, int cap, int nslots, int K, int N,
-                               int nsplit, int max_blocks, float* ypart, hipStream_t s);
+                               int nsplit, int max_blocks, int tt, float* ypart, hipStream_t s);
 
 // e4m3 weights on the full tiles (K % 128 == 0, N % 128 == 0; with nsplit
 // > 1, (N / nsplit) % 128 == 0): GEMM1 writes the fp32 activation rows and
@@ -128,13 +131,13 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
 void launch_gemm1_prefill_fp8(const uint8_t* xq, const float* xscale, const void* w1,
                               const float* w1_scale, int rowwise, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded, int M,
-                              int topk, int nslots, int K, int N, int max_blocks, float* act,
-                              uint32_t* amax, hipStream_t s);
+                              int topk, int nslots, int K, int N, int max_blocks, int tt,
+                              float* act, uint32_t* amax, hipStream_t s);
 void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const void* w2,
                               const float* w2_scale, int rowwise, const float* topk_w,
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
-                              int nsplit, int max_blocks, float* ypart, hipStream_t s);
+                              int nsplit, int max_blocks, int tt, float* ypart, hipStream_t s);
 
 void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
                     hipStream_t s);

@@ -64,6 +64,14 @@ constexpr int kMxTiles1 = 1;
 constexpr int kMxTiles2 = 4;
 
 // ---- prefill ------------------------------------------------------------------
+// token rows per full-tile block: 128 while the mean rows per active expert
+// stay at or below this, else 256.  Full-tile ms per layer call with 128- /
+// 256-row blocks at 16, 32, 64, 128 rows per expert:
+//   e4m3, K, N, E, k = 7168, 2048, 256, 8: 2.18/2.44, 2.35/2.63, 2.63/2.95, 3.58/3.57
+//   e4m3, K, N, E, k = 4096, 14336, 8, 2: 0.301/0.351, 0.315/0.365, 0.348/0.384, 0.424/0.444
+//   bf16, K, N, E, k = 4096, 14336, 8, 2: 0.513/0.551, 0.525/0.562, 0.562/0.604, 0.701/0.697
+constexpr long kPrefillSmallTileMaxRows = 128;
+
 // GEMM2 reduction split until about four workgroups per CU exist (Mixtral
 // prefill, 39 blocks: 1118 us unsplit, 999 us in 2 splits, 1007 us in 4
 // with a combine twice as long).
