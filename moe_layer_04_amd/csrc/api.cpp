@@ -70,8 +70,10 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
     // full tiles: 128-row token blocks when the experts receive few rows
     // (tuning.hpp); those kernels are built for K % 256 == 0
+    const long small_rows = dtype == MOE_BF16 ? moe::tune::kPrefillSmallTileMaxRows
+                                              : moe::tune::kPrefillFp8SmallTileMaxRows;
     if (regime == MOE_REGIME_PREFILL && K % 256 == 0 &&
-        slots <= moe::tune::kPrefillSmallTileMaxRows * (slots < E ? slots : E))
+        slots <= small_rows * (slots < E ? slots : E))
         p.block = moe::kPrefillSmallRows;
     // larger decode blocks when experts receive more rows (sized in tuning.hpp)
     if (regime == MOE_REGIME_DECODE) p.block = moe::tune::decode_block_rows(slots, E);

@@ -71,6 +71,12 @@ constexpr int kMxTiles2 = 4;
 //   e4m3, K, N, E, k = 4096, 14336, 8, 2: 0.301/0.351, 0.315/0.365, 0.348/0.384, 0.424/0.444
 //   bf16, K, N, E, k = 4096, 14336, 8, 2: 0.513/0.551, 0.525/0.562, 0.562/0.604, 0.701/0.697
 constexpr long kPrefillSmallTileMaxRows = 128;
+// e4m3 weights: the same bound.  128-row blocks at every size measured
+// worse on the skewed Mixtral-shaped prefill (1.82 -> 1.87 ms per layer
+// call, 1024 rows per expert on average) and better on the DeepSeek shape
+// with 8192 tokens (256 rows per expert: 6.01 -> 5.82 ms; GEMM1 faster by
+// 11 %, GEMM2 slower by 5 %).
+constexpr long kPrefillFp8SmallTileMaxRows = 128;
 
 // GEMM2 reduction split until about four workgroups per CU exist (Mixtral
 // prefill, 39 blocks: 1118 us unsplit, 999 us in 2 splits, 1007 us in 4
