@@ -467,6 +467,11 @@ def main():
         "algorithmic_flops": alg_flops,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
         "timed_pass_ms_per_step": round(float(np.mean(total_ms)), 4),
+        # per-call spread of the same pass: HIP events before the first and
+        # after the last kernel of each call (back to back, weights cycled
+        # over the layer copies)
+        "call_ms": {q: round(float(np.percentile(total_ms, v)), 4)
+                    for q, v in (("p10", 10), ("p50", 50), ("p90", 90))},
         "graph_ms_per_step": round(graph_ms, 4),
         "graph_tokens_per_s": round(wl.M / (graph_ms / 1e3), 1),
         "roofline": roofline,
