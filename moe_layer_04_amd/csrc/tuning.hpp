@@ -70,6 +70,9 @@ constexpr int kMxTiles2 = 4;
 //   e4m3, K, N, E, k = 7168, 2048, 256, 8: 2.18/2.44, 2.35/2.63, 2.63/2.95, 3.58/3.57
 //   e4m3, K, N, E, k = 4096, 14336, 8, 2: 0.301/0.351, 0.315/0.365, 0.348/0.384, 0.424/0.444
 //   bf16, K, N, E, k = 4096, 14336, 8, 2: 0.513/0.551, 0.525/0.562, 0.562/0.604, 0.701/0.697
+// and on the skewed Mixtral-shaped prefill (1024 rows per expert on
+// average) 3.15 against 2.78 ms (GEMM1 1908/1720 us, GEMM2 unsplit
+// 1167/945 us although the combine halves, 30/53 us).
 constexpr long kPrefillSmallTileMaxRows = 128;
 // e4m3 weights: the same bound.  128-row blocks at every size measured
 // worse on the skewed Mixtral-shaped prefill (1.82 -> 1.87 ms per layer
