@@ -58,46 +58,31 @@ __global__ __launch_bounds__(kAlignThreads) void topk_align_kernel(
 // over the expert-id bits.  The order is the stable one of the workgroup
 // version, so the results are identical.
 // ---------------------------------------------------------------------------
-// Orders one wave's LDS writes before its own later LDS reads of other
-// lanes' words (the body below runs in a single wave of a larger workgroup
-// too, so it cannot use a workgroup barrier): the wave's LDS operations
-// complete in order once lgkmcnt reaches zero; the fences keep the compiler
-// from moving LDS accesses across.
-__device__ __forceinline__ void wave_lds_sync() {
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0)
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-struct WaveAlignShared {
-    int32_t sid[kWave];
-    int cnt[MOE_KERNEL_MAX_EXPERTS];
-    int off[MOE_KERNEL_MAX_EXPERTS + 1];
-};
-
-// Run by one wave (the only one touching sh): logits may point to global or
-// shared memory.
-__device__ __forceinline__ void topk_align_wave_body(
-    WaveAlignShared& sh, const float* logits, int M, int E, int topk,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights, int B, int cap,
+__global__ __launch_bounds__(kWave) void topk_align_wave_kernel(
+    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int K, int E,
+    int topk, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
+    uint8_t* __restrict__ xq, float* __restrict__ xscale, int B, int cap,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded,
     uint32_t* __restrict__ zero_buf, int zero_words, int32_t* __restrict__ inv) {
-    int32_t* sid = sh.sid;
-    int* cnt = sh.cnt;
-    int* off = sh.off;
+    __shared__ int32_t sid[kWave];
+    __shared__ int cnt[MOE_KERNEL_MAX_EXPERTS];
+    __shared__ int off[MOE_KERNEL_MAX_EXPERTS + 1];
     const int lane = lane_id();
     for (int i = lane; i < zero_words; i += kWave) zero_buf[i] = 0u;
     for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+    if (xq)
+        for (int t = 0; t < M; ++t)
+            quant_row_wave(x + (size_t)t * K, K, xq + (size_t)t * K, xscale + t);
     for (int t = 0; t < M; ++t)
         topk_wave(logits + (size_t)t * E, E, topk, topk_ids + (size_t)t * topk,
                   topk_weights + (size_t)t * topk, sid + t * topk);
-    wave_lds_sync();  // the LDS writes above before the reads below
+    __syncthreads();  // one wave: orders the LDS writes above before the reads below
     const int n = M * topk;
     const bool valid = lane < n;
     const int e = valid ? min(max(sid[lane], 0), E - 1) : 0;
     if (valid) atomicAdd(&cnt[e], 1);
-    wave_lds_sync();
+    __syncthreads();
     {
         int v[4], sum = 0;
 #pragma unroll
@@ -121,7 +106,7 @@ __device__ __forceinline__ void topk_align_wave_body(
         }
         if (lane == kWave - 1) off[E] = incl;
     }
-    wave_lds_sync();
+    __syncthreads();
     for (int ex = lane; ex <= E; ex += kWave) expert_offsets[ex] = off[ex];
     const int npad = off[E];
     if (lane == 0) *num_padded = npad;
@@ -165,99 +150,6 @@ __device__ __forceinline__ void topk_align_wave_body(
         sorted_ids[pos] = lane;
         if (inv) inv[lane] = pos;
     }
-}
-
-__global__ __launch_bounds__(kWave) void topk_align_wave_kernel(
-    const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int K, int E,
-    int topk, int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
-    uint8_t* __restrict__ xq, float* __restrict__ xscale, int B, int cap,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded,
-    uint32_t* __restrict__ zero_buf, int zero_words, int32_t* __restrict__ inv) {
-    __shared__ WaveAlignShared sh;
-    if (xq)
-        for (int t = 0; t < M; ++t)
-            quant_row_wave(x + (size_t)t * K, K, xq + (size_t)t * K, xscale + t);
-    topk_align_wave_body(sh, logits, M, E, topk, topk_ids, topk_weights, B, cap, sorted_ids,
-                         block_expert, expert_offsets, num_padded, zero_buf, zero_words, inv);
-}
-
-// ---------------------------------------------------------------------------
-// The whole routing of a tiny batch (at most kRouteTinyPairs (token, expert)
-// pairs, at most two tokens) in one launch: wave w computes the logit of pair
-// w = t*E + e with exactly the arithmetic of router_logits_kernel<1, 1>
-// (the four K-quarters that kernel gives its four waves, here four fp64
-// accumulators of one wave, each wave-summed, added in quarter order, plus
-// the bias, rounded once), so the logits are bit-identical to the logits
-// kernel's; waves past the pairs quantise the FP8 token rows; then wave 0
-// runs the single-wave top-k + align on the logits in LDS.
-// ---------------------------------------------------------------------------
-constexpr int kRouteTinyWaves = 16;
-constexpr int kRouteTinyPairs = 16;
-
-// K % 8 == 0 (the fused layer's K is a multiple of 128): the vector path of
-// router_logits_kernel, 8 elements (16 bytes) per lane and step
-__device__ __forceinline__ float logit_one_wave(const uint16_t* xr, const uint16_t* wrr, int K,
-                                                const float* bias, int e) {
-    const int lane = lane_id();
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    const int kq = ((K / 8 + 3) / 4) * 8;
-    // step i of quarter w reads k = w*kq + lane*8 + i*512: each accumulator
-    // sees its quarter's products in ascending k, as that kernel's wave w
-    const int iters = (kq + kWave * 8 - 1) / (kWave * 8);
-    for (int i = 0; i < iters; ++i) {
-#pragma unroll
-        for (int w = 0; w < 4; ++w) {
-            const int k = w * kq + lane * 8 + i * kWave * 8;
-            if (k < min(K, (w + 1) * kq)) {
-                const i32x4_t xv = *reinterpret_cast<const i32x4_t*>(xr + k);
-                const i32x4_t wv = *reinterpret_cast<const i32x4_t*>(wrr + k);
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    acc[w] = __fma_rn((double)bf16_bits_to_f32((uint32_t)xv[q] & 0xffffu),
-                                      (double)bf16_bits_to_f32((uint32_t)wv[q] & 0xffffu),
-                                      acc[w]);
-                    acc[w] = __fma_rn((double)bf16_bits_to_f32((uint32_t)xv[q] >> 16),
-                                      (double)bf16_bits_to_f32((uint32_t)wv[q] >> 16), acc[w]);
-                }
-            }
-        }
-    }
-    double p[4];
-#pragma unroll
-    for (int w = 0; w < 4; ++w) p[w] = wave_sum_f64(acc[w]);
-    double s = ((p[0] + p[1]) + p[2]) + p[3];
-    if (bias) s += (double)bias[e];
-    return (float)s;
-}
-
-__global__ __launch_bounds__(kRouteTinyWaves * kWave) void route_tiny_kernel(
-    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr,
-    const float* __restrict__ bias, int M, int K, int E, int topk, float* __restrict__ logits,
-    int32_t* __restrict__ topk_ids, float* __restrict__ topk_weights,
-    uint8_t* __restrict__ xq, float* __restrict__ xscale, int B, int cap,
-    int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded,
-    uint32_t* __restrict__ zero_buf, int zero_words, int32_t* __restrict__ inv) {
-    __shared__ float lg[kRouteTinyPairs];
-    __shared__ WaveAlignShared sh;
-    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int pairs = M * E;
-    if (wave < pairs) {
-        const int t = wave / E, e = wave % E;
-        const float l = logit_one_wave(x + (size_t)t * K, wr + (size_t)e * K, K, bias, e);
-        if (lane_id() == 0) {
-            lg[wave] = l;
-            logits[wave] = l;
-        }
-    } else if (xq && wave - pairs < M) {
-        const int t = wave - pairs;
-        quant_row_wave(x + (size_t)t * K, K, xq + (size_t)t * K, xscale + t);
-    }
-    __syncthreads();
-    if (wave == 0)
-        topk_align_wave_body(sh, lg, M, E, topk, topk_ids, topk_weights, B, cap, sorted_ids,
-                             block_expert, expert_offsets, num_padded, zero_buf, zero_words, inv);
 }
 
 // ---------------------------------------------------------------------------
@@ -431,22 +323,6 @@ void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sor
     align_kernel<<<1, kAlignThreads, 0, s>>>(ids, n, E, B, cap, sorted_ids, block_expert,
                                              expert_offsets, num_padded, zero_buf, zero_words,
                                              inv);
-}
-
-bool route_tiny_fits(int M, int E, int topk) {
-    // the FP8 token rows take waves past the pairs; callers have K % 8 == 0
-    return M <= 2 && M * E <= kRouteTinyPairs && M * E + M <= kRouteTinyWaves &&
-           M * topk <= kWave;
-}
-
-void launch_route_tiny(const void* x, const void* wr, const float* bias, int M, int K, int E,
-                       int topk, float* logits, int32_t* ids, float* w, uint8_t* xq,
-                       float* xscale, int B, int cap, int32_t* sorted_ids, int32_t* block_expert,
-                       int32_t* expert_offsets, int32_t* num_padded, uint32_t* zero_buf,
-                       int zero_words, int32_t* inv, hipStream_t s) {
-    route_tiny_kernel<<<1, kRouteTinyWaves * kWave, 0, s>>>(
-        (const uint16_t*)x, (const uint16_t*)wr, bias, M, K, E, topk, logits, ids, w, xq, xscale,
-        B, cap, sorted_ids, block_expert, expert_offsets, num_padded, zero_buf, zero_words, inv);
 }
 
 bool topk_align_fits(int M, int topk) {

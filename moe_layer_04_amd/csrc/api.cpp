@@ -7,8 +7,7 @@
 // value is read back):
 //   1 router logits (fp64 dot products) (+ x -> e4m3)
 //   2 top-k + weights                         3 align (sorted rows, block owners)
-//     (2-3 are one single-workgroup launch for up to 1024 token-slots, 1-3
-//     one launch for at most two tokens and 16 (token, expert) pairs)
+//     (2-3 are one single-workgroup launch for up to 1024 token-slots)
 //   4 GEMM1 + SiLU*up
 //   5 (e4m3) per-row activation quantisation  6 GEMM2 * routing weight, scattered
 //   7 combine into bf16 out
@@ -285,14 +284,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     const int amax_words = fp8 ? p.cap : 0;
     int32_t* inv = fp8 ? (int32_t*)(ws + p.inv) : nullptr;
     mark(0);
-    if (moe::route_tiny_fits(M, E, topk)) {
-        // logits, FP8 token codes, top-k and align in one launch
-        moe::launch_route_tiny(x, w_router, router_bias, M, K, E, topk, logits, ids, wts, xq, xs,
-                               p.block, p.cap, sorted, bexp, offs, npad, amax, amax_words, inv,
-                               s);
-        mark(1);
-        mark(2);
-    } else if (moe::topk_align_fits(M, topk)) {
+    if (moe::topk_align_fits(M, topk)) {
         // the FP8 token codes go with top-k + align when the tokens are few
         // and short (a wave per token there; a workgroup per token otherwise)
         const bool q_late = fp8 && M <= moe::tune::kLateQuantRows && K <= moe::tune::kLateQuantCols;

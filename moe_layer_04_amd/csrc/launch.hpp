@@ -37,17 +37,6 @@ void launch_align(const int32_t* ids, int n, int E, int B, int cap, int32_t* sor
                   int32_t* block_expert, int32_t* expert_offsets, int32_t* num_padded,
                   uint32_t* zero_buf, int zero_words, int32_t* inv, hipStream_t s);
 
-// The whole routing of a tiny batch in one single-workgroup launch: logits
-// (bit-identical to launch_router_logits'), FP8 token codes when xq is not
-// null, top-k and align, for batches route_tiny_fits accepts (at most two
-// tokens and 16 (token, expert) pairs) with K % 8 == 0.
-bool route_tiny_fits(int M, int E, int topk);
-void launch_route_tiny(const void* x, const void* wr, const float* bias, int M, int K, int E,
-                       int topk, float* logits, int32_t* ids, float* w, uint8_t* xq,
-                       float* xscale, int B, int cap, int32_t* sorted_ids, int32_t* block_expert,
-                       int32_t* expert_offsets, int32_t* num_padded, uint32_t* zero_buf,
-                       int zero_words, int32_t* inv, hipStream_t s);
-
 // The align of launch_align over many workgroups (three launches, identical
 // result) for batches of more than kAlignMultiMinSlots slots; scratch:
 // chunk_cnt [align_chunks(n) * E] and cnt_total [E] int32.

@@ -279,8 +279,8 @@ SMALL = [
     # the largest top-k (16), on the decode kernels and on the e4m3 full tiles
     ("topk16", 20, 256, 256, 64, 16, False, None, 0),
     ("fp8_topk16_tiles", 40, 256, 256, 32, 16, True, None, 2),
-    # logits, (FP8) token codes, top-k and align in one launch for at most
-    # two tokens and 16 (token, expert) pairs
+    # one or two tokens: the single-wave top-k + align, with bias, e4m3
+    # (per-tensor and per-channel) and MXFP4 weights
     ("tiny_route_fused_bias", 2, 768, 512, 8, 2, False, 0.5, 0),
     ("tiny_route_fused_fp8", 1, 1536, 256, 8, 2, True, 0.5, 0),
     ("tiny_route_fused_fp8_rowwise", 2, 512, 256, 4, 3, "rowwise", None, 0),
@@ -309,11 +309,12 @@ def test_fused_small(moe, case):
 
 @pytest.mark.parametrize("M,E,fp8", [(1, 16, False), (2, 8, False), (1, 8, True)])
 def test_fused_tiny_routing_ties(moe, M, E, fp8):
-    """The one-launch routing of tiny batches breaks ties to the lower expert
-    id: with every router row equal all logits of a token tie and experts 0
-    and 1 must serve it; with some rows duplicated the oracle's tie rule
-    decides.  A wrong pick routes through other experts' weights, which the
-    output comparison sees."""
+    """The routing of one or two tokens (the single-wave top-k + align)
+    breaks ties to the lower expert id inside the fused layer: with every
+    router row equal all logits of a token tie and experts 0 and 1 must serve
+    it; with some rows duplicated the oracle's tie rule decides.  A wrong
+    pick routes through other experts' weights, which the output comparison
+    sees."""
     note(f"fused tiny routing ties M={M} E={E} fp8={fp8}")
     wl = wlm.Workload("tiny_ties", M=M, K=256, N=256, E=E, topk=2, fp8=fp8, seed=8)
     for dup in ("all", "pairs"):
