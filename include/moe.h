@@ -155,6 +155,31 @@ moe_status moe_align(const int32_t *topk_ids, int M, int topk, int E, int block_
                      int32_t *expert_offsets, int32_t *num_padded, void *stream);
 
 /*
+ * moe_align_ex -- moe_align with a caller workspace, for large batches: the
+ * same outputs, bit for bit.  Above 2048 token-slots it runs over many
+ * workgroups -- per 1024-slot chunk a count of the slots of each expert,
+ * one scan that turns the counts into the padded segment starts and each
+ * chunk's first position per expert, then per chunk the stable scatter --
+ * instead of one workgroup walking all chunks, and keeps the chunk counts in
+ * the workspace.  The fused layer runs this align on its own workspace.
+ *
+ *   topk_ids ... num_padded   as moe_align
+ *   workspace        device buffer of at least *workspace_bytes bytes
+ *                    (256-byte aligned), or NULL to query: the call stores the
+ *                    required size (0 up to 2048 slots) in *workspace_bytes,
+ *                    enqueues nothing and returns MOE_OK
+ *   workspace_bytes  host pointer: in = size of `workspace`, out = required
+ *
+ * Errors: as moe_align, plus INVALID_ARG for a null workspace_bytes or a
+ * workspace not 256-byte aligned; WORKSPACE if *workspace_bytes is below the
+ * required size.
+ */
+moe_status moe_align_ex(const int32_t *topk_ids, int M, int topk, int E, int block_m,
+                        int32_t *sorted_ids, int32_t *block_expert,
+                        int32_t *expert_offsets, int32_t *num_padded, void *workspace,
+                        size_t *workspace_bytes, void *stream);
+
+/*
  * moe_quant_rows_e4m3 -- per-row dynamic FP8 quantisation of bf16 rows, the
  * step the fused forward applies to the tokens before GEMM1 in the e4m3 path.
  *

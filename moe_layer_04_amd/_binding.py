@@ -34,7 +34,7 @@ MOE_REGIME_AUTO = 0
 MOE_REGIME_DECODE = 1
 MOE_REGIME_PREFILL = 2
 
-EXPORTS = ("moe_topk", "moe_align", "moe_quant_rows_e4m3", "moe_fused_forward",
+EXPORTS = ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3", "moe_fused_forward",
            "moe_fused_forward_ex", "moe_fused_forward_timed", "moe_status_string")
 
 _lock = threading.Lock()
@@ -62,13 +62,15 @@ def load_library(build_if_missing: bool = False):
         P, I, SZP = ctypes.c_void_p, ctypes.c_int, ctypes.POINTER(ctypes.c_size_t)
         lib.moe_topk.argtypes = [P, P, P, I, I, I, I, P, P, P, P]
         lib.moe_align.argtypes = [P, I, I, I, I, P, P, P, P, P]
+        lib.moe_align_ex.argtypes = [P, I, I, I, I, P, P, P, P, P, SZP, P]
         lib.moe_quant_rows_e4m3.argtypes = [P, I, I, P, P, P]
         lib.moe_fused_forward.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P, SZP, P]
         lib.moe_fused_forward_ex.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
                                              SZP, P]
         lib.moe_fused_forward_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
                                                 SZP, P, P]
-        for name in ("moe_topk", "moe_align", "moe_quant_rows_e4m3", "moe_fused_forward",
+        for name in ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3",
+                     "moe_fused_forward",
                      "moe_fused_forward_ex", "moe_fused_forward_timed"):
             getattr(lib, name).restype = ctypes.c_int
         lib.moe_status_string.argtypes = [I]
@@ -144,6 +146,29 @@ def moe_align(topk_ids: torch.Tensor, num_experts: int, block_m: int):
     _check(lib.moe_align(_ptr(topk_ids), M, k, num_experts, block_m, _ptr(sorted_ids),
                          _ptr(block_expert), _ptr(offsets), _ptr(npad), _stream(dev)),
            "moe_align")
+    return sorted_ids, block_expert[: cap // block_m], offsets, npad
+
+
+def moe_align_ex(topk_ids: torch.Tensor, num_experts: int, block_m: int):
+    """moe_align through moe_align_ex (many workgroups above 2048 slots, with
+    a workspace allocated here); the same outputs."""
+    lib = load_library()
+    _dev(topk_ids, "topk_ids", torch.int32)
+    M, k = topk_ids.shape
+    cap = M * k + num_experts * (block_m - 1)
+    dev = topk_ids.device
+    nbytes = ctypes.c_size_t(0)
+    _check(lib.moe_align_ex(None, M, k, num_experts, block_m, None, None, None, None, None,
+                            ctypes.byref(nbytes), None), "moe_align_ex (size query)")
+    ws = torch.empty(max(nbytes.value, 256), dtype=torch.uint8, device=dev)
+    nbytes = ctypes.c_size_t(ws.numel())
+    sorted_ids = torch.empty(cap, dtype=torch.int32, device=dev)
+    block_expert = torch.empty(max(cap // block_m, 1), dtype=torch.int32, device=dev)
+    offsets = torch.empty(num_experts + 1, dtype=torch.int32, device=dev)
+    npad = torch.empty(1, dtype=torch.int32, device=dev)
+    _check(lib.moe_align_ex(_ptr(topk_ids), M, k, num_experts, block_m, _ptr(sorted_ids),
+                            _ptr(block_expert), _ptr(offsets), _ptr(npad), _ptr(ws),
+                            ctypes.byref(nbytes), _stream(dev)), "moe_align_ex")
     return sorted_ids, block_expert[: cap // block_m], offsets, npad
 
 

@@ -191,9 +191,9 @@ MOE_API moe_status moe_quant_rows_e4m3(const void* x, int M, int K, uint8_t* q, 
     return finish_launches();
 }
 
-MOE_API moe_status moe_align(const int32_t* topk_ids, int M, int topk, int E, int block_m,
-                             int32_t* sorted_ids, int32_t* block_expert,
-                             int32_t* expert_offsets, int32_t* num_padded, void* stream) {
+static moe_status align_check(const int32_t* topk_ids, int M, int topk, int E, int block_m,
+                              int32_t* sorted_ids, int32_t* block_expert,
+                              int32_t* expert_offsets, int32_t* num_padded) {
     if (M < 0 || topk < 1 || E < 1 || block_m < 1) return MOE_ERR_INVALID_ARG;
     if (E > MOE_MAX_EXPERTS || block_m > 1024 || (long)M * topk >= (1L << 30))
         return MOE_ERR_UNSUPPORTED;
@@ -203,11 +203,56 @@ MOE_API moe_status moe_align(const int32_t* topk_ids, int M, int topk, int E, in
     if (misaligned(topk_ids) || misaligned(sorted_ids) || misaligned(block_expert) ||
         misaligned(expert_offsets) || misaligned(num_padded))
         return MOE_ERR_INVALID_ARG;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_align(const int32_t* topk_ids, int M, int topk, int E, int block_m,
+                             int32_t* sorted_ids, int32_t* block_expert,
+                             int32_t* expert_offsets, int32_t* num_padded, void* stream) {
+    const moe_status st = align_check(topk_ids, M, topk, E, block_m, sorted_ids, block_expert,
+                                      expert_offsets, num_padded);
+    if (st != MOE_OK) return st;
     const int n = M * topk;
     const int cap = n + E * (block_m - 1);
     (void)hipGetLastError();
     moe::launch_align(topk_ids, n, E, block_m, cap, sorted_ids, block_expert, expert_offsets,
                       num_padded, nullptr, 0, nullptr, (hipStream_t)stream);
+    return finish_launches();
+}
+
+MOE_API moe_status moe_align_ex(const int32_t* topk_ids, int M, int topk, int E, int block_m,
+                                int32_t* sorted_ids, int32_t* block_expert,
+                                int32_t* expert_offsets, int32_t* num_padded, void* workspace,
+                                size_t* workspace_bytes, void* stream) {
+    if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+    if (M < 0 || topk < 1 || E < 1 || block_m < 1) return MOE_ERR_INVALID_ARG;
+    if (E > MOE_MAX_EXPERTS || block_m > 1024 || (long)M * topk >= (1L << 30))
+        return MOE_ERR_UNSUPPORTED;
+    const int n = M * topk;
+    const bool multi = moe::align_multi_fits(n);
+    // chunk counts [chunks, E], then the experts' totals [E]
+    const size_t chunk_bytes = round_up((size_t)moe::align_chunks(n) * E * 4);
+    const size_t need = multi ? chunk_bytes + round_up((size_t)E * 4) : 0;
+    if (!workspace) {
+        *workspace_bytes = need;
+        return MOE_OK;
+    }
+    const moe_status st = align_check(topk_ids, M, topk, E, block_m, sorted_ids, block_expert,
+                                      expert_offsets, num_padded);
+    if (st != MOE_OK) return st;
+    if ((uintptr_t)workspace & (kAlign - 1)) return MOE_ERR_INVALID_ARG;
+    if (*workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    const int cap = n + E * (block_m - 1);
+    hipStream_t s = (hipStream_t)stream;
+    (void)hipGetLastError();
+    if (multi)
+        moe::launch_align_multi(topk_ids, n, E, block_m, cap, sorted_ids, block_expert,
+                                expert_offsets, num_padded, nullptr, 0, nullptr,
+                                (int32_t*)workspace, (int32_t*)((char*)workspace + chunk_bytes),
+                                s);
+    else
+        moe::launch_align(topk_ids, n, E, block_m, cap, sorted_ids, block_expert, expert_offsets,
+                          num_padded, nullptr, 0, nullptr, s);
     return finish_launches();
 }
 

@@ -60,6 +60,29 @@ def test_topk_validation(lib):
     assert topk_call(lib, M=0, x=None, ids=None, w=None, lg=None) == B.MOE_OK   # no-op
 
 
+def test_align_ex_validation(lib):
+    f = lib.moe_align_ex
+    n = ctypes.c_size_t(0)
+    # size queries make no HIP call: none up to 2048 slots, chunk counts above
+    assert f(None, 1024, 2, 8, 16, None, None, None, None, None, ctypes.byref(n), None) == 0
+    assert n.value == 0
+    assert f(None, 4096, 2, 256, 16, None, None, None, None, None, ctypes.byref(n), None) == 0
+    assert n.value >= (8 * 256 + 256) * 4
+    need = n.value
+    assert f(FAKE, 4096, 2, 256, 16, FAKE, FAKE, FAKE, FAKE, None, None, None) == \
+        B.MOE_ERR_INVALID_ARG                                          # null size pointer
+    small = ctypes.c_size_t(need - 1)
+    assert f(FAKE, 4096, 2, 256, 16, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(small),
+             None) == B.MOE_ERR_WORKSPACE
+    big = ctypes.c_size_t(need)
+    assert f(FAKE, 4096, 2, 256, 16, FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(0x10010),
+             ctypes.byref(big), None) == B.MOE_ERR_INVALID_ARG       # workspace not aligned
+    assert f(FAKE, 4, 2, 257, 16, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(big), None) == \
+        B.MOE_ERR_UNSUPPORTED
+    assert f(FAKE, -1, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, FAKE, ctypes.byref(big), None) == \
+        B.MOE_ERR_INVALID_ARG
+
+
 def test_align_validation(lib):
     f = lib.moe_align
     assert f(FAKE, -1, 2, 8, 16, FAKE, FAKE, FAKE, FAKE, None) == B.MOE_ERR_INVALID_ARG

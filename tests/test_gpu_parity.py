@@ -185,7 +185,8 @@ def test_router_ties_lower_id(moe):
 @pytest.mark.parametrize("M,k,E,B", [(64, 2, 8, 16), (8, 2, 8, 16), (1, 2, 16, 16),
                                      (4096, 2, 8, 128), (128, 8, 256, 16), (0, 2, 8, 16),
                                      (37, 3, 17, 64), (20000, 4, 64, 128), (300, 1, 256, 1),
-                                     (9, 5, 5, 1024)])
+                                     (9, 5, 5, 1024), (1024, 2, 8, 256), (683, 3, 16, 256),
+                                     (4096, 8, 256, 128), (2500, 1, 3, 1)])
 def test_align_bit_exact(moe, M, k, E, B):
     note(f"align M={M} k={k} E={E} B={B}")
     rng = np.random.default_rng(M * 7 + E)
@@ -196,13 +197,15 @@ def test_align_bit_exact(moe, M, k, E, B):
     else:
         ids = np.zeros((0, k))
     ids = ids.astype(np.int32)
-    s, b, o, npad = moe.moe_align(torch.from_numpy(ids).cuda(), E, B)
-    torch.cuda.synchronize()
     rs, rb, ro, rn = oracle.align(ids, E, B)
-    assert int(npad.item()) == rn
-    assert np.array_equal(o.cpu().numpy(), ro)
-    assert np.array_equal(b.cpu().numpy(), rb)
-    assert np.array_equal(s.cpu().numpy(), rs)
+    # one workgroup (moe_align) and, above 2048 slots, many (moe_align_ex)
+    for fn in (moe.moe_align, moe.moe_align_ex):
+        s, b, o, npad = fn(torch.from_numpy(ids).cuda(), E, B)
+        torch.cuda.synchronize()
+        assert int(npad.item()) == rn
+        assert np.array_equal(o.cpu().numpy(), ro)
+        assert np.array_equal(b.cpu().numpy(), rb)
+        assert np.array_equal(s.cpu().numpy(), rs)
 
 
 # --------------------------------------------------------------------------
