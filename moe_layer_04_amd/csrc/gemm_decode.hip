@@ -639,15 +639,31 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const int nst = K / 256;  // K is a multiple of 256 here (checked by the launcher)
     const int rot = (gw * kRot + blk * 5) % nst;
     auto kstep = [&](int j) { return rotated(j < nst ? j : nst - 1, rot, nst) * 256; };
-    // two fragments in turn, no copies; loads past the end repeat the last
-    // step (never multiplied), so every wait count is exact
-    Frag fa, fb;
-    load(fa, kstep(0));
-    for (int j = 0; j < nst; j += 2) {
-        load(fb, kstep(j + 1));
-        compute(fa);
-        load(fa, kstep(j + 2));
-        if (j + 1 < nst) compute(fb);
+    // fragments in turn, no copies; loads past the end repeat the last step
+    // (never multiplied), so every wait count is exact.  One token tile:
+    // three fragments (loads two steps ahead); more tiles: two, as a third
+    // would cost occupancy.
+    if constexpr (NT == 1) {
+        Frag fa, fb, fc;
+        load(fa, kstep(0));
+        load(fb, kstep(1));
+        for (int j = 0; j < nst; j += 3) {
+            load(fc, kstep(j + 2));
+            compute(fa);
+            load(fa, kstep(j + 3));
+            if (j + 1 < nst) compute(fb);
+            load(fb, kstep(j + 4));
+            if (j + 2 < nst) compute(fc);
+        }
+    } else {
+        Frag fa, fb;
+        load(fa, kstep(0));
+        for (int j = 0; j < nst; j += 2) {
+            load(fb, kstep(j + 1));
+            compute(fa);
+            load(fa, kstep(j + 2));
+            if (j + 1 < nst) compute(fb);
+        }
     }
 #pragma unroll
     for (int j = 0; j < NT; ++j)
