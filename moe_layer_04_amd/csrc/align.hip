@@ -6,7 +6,9 @@
 //
 // Slot p = t*topk + j is sorted stably by expert; each expert's segment is
 // padded to a multiple of the block size with the sentinel n = M*topk.
-// One 1024-thread workgroup runs the align body of routing.hpp.
+// One 1024-thread workgroup runs the align body of routing.hpp; for more
+// than 2048 slots three launches spread the same work over a workgroup per
+// 1024-slot chunk (below), with an identical result.
 #include "routing.hpp"
 
 namespace moe {

@@ -537,7 +537,8 @@ __global__ __launch_bounds__(256) void gemm2_decode_fp8_kernel(
 // Each wave covers RT 16-row tiles of gate rows and the matching up rows
 // (GEMM1) or RT 16-row tiles of output rows (GEMM2) with one token fragment;
 // a step is two 128-deep chunks, the scale bytes of a step are one 8-byte
-// load per row tile, and the steps alternate between two fragments.
+// read per row tile from the wave's LDS copy of its rows' scales, and the
+// steps rotate through two fragments (three in GEMM1 with one token tile).
 constexpr int kMxTiles1 = tune::kMxTiles1;  // GEMM1: 16 gate + 16 up rows per wave
 constexpr int kMxTiles2 = tune::kMxTiles2;  // GEMM2: 64 output rows per wave
 

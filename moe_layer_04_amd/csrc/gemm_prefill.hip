@@ -5,9 +5,10 @@
 // SageMaker AI" (summary text) groups all active experts into one launch;
 // with hundreds of token rows per expert the GEMMs are MFMA-bound, so each
 // workgroup computes a full TW (weight rows) x TT (token rows) tile from
-// LDS with 32x32x16 bf16 MFMAs; the launchers use 256 x 256 tiles (each
-// token block re-reads its expert's weights, so the token tile sets the
-// weight traffic).  Weights stay in the pages' B^T layout
+// LDS with 32x32x16 bf16 (or 32x32x64 e4m3) MFMAs; the launchers use
+// 256 x 256 tiles, or 256 weight rows x 128 tokens when the experts receive
+// few rows (each token block re-reads its expert's weights, so the token
+// tile sets the weight traffic).  Weights stay in the pages' B^T layout
 // (output-major, reduction dimension contiguous) on the MFMA row dimension,
 // as in the decode kernels; tokens are the columns, gathered through the
 // expert-sorted row list for GEMM1 and contiguous for GEMM2.
