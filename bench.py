@@ -132,13 +132,14 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     print(json.dumps(rec))
 
 
-def mfma_summary(csv_path):
+def mfma_summary(csv_path, l2_csv=None):
     """MFMA utilisation per kernel from one rocprofv3 --pmc run of
     SQ_VALU_MFMA_BUSY_CYCLES, SQ_INSTS_VALU_MFMA_MOPS_BF16 / _F8 and
     GRBM_GUI_ACTIVE: the busy cycles (summed over the 1024 SIMDs) over the
     active cycles of one XCD (the aggregated GRBM count covers the 8 XCDs)
     times the SIMDs, the clock those cycles imply over the dispatch, and the
-    MFMA FLOPs the hardware executed (512 per MOP, padding rows included)."""
+    MFMA FLOPs the hardware executed (512 per MOP, padding rows included);
+    with l2_csv (a run of TCC_HIT_sum and TCC_MISS_sum) also the L2 hit rate."""
     import csv
     import statistics
     rows = {}
@@ -147,6 +148,18 @@ def mfma_summary(csv_path):
         d = rows.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})
         d[r["Counter_Name"]] = float(r["Counter_Value"])
         d["ns"] = float(r["End_Timestamp"]) - float(r["Start_Timestamp"])
+    hits = {}
+    if l2_csv:
+        l2 = {}
+        for r in csv.DictReader(open(l2_csv)):
+            k = r["Kernel_Name"].split("(")[0].replace("void ", "")
+            l2.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = \
+                float(r["Counter_Value"])
+        for k, disp in l2.items():
+            v = [d["TCC_HIT_sum"] / (d["TCC_HIT_sum"] + d["TCC_MISS_sum"]) for d in disp.values()
+                 if d.get("TCC_HIT_sum", 0.0) + d.get("TCC_MISS_sum", 0.0) > 0]
+            if v:
+                hits[k] = statistics.median(v)
     out = []
     for k, disp in rows.items():
         util, clk, flops, rate = [], [], [], []
@@ -167,6 +180,8 @@ def mfma_summary(csv_path):
                "clock_GHz": round(statistics.median(clk), 3),
                "mfma_flops": statistics.median(flops),
                "mfma_TFLOPs": round(statistics.median(rate), 1)}
+        if k in hits:
+            rec["l2_hit_rate"] = round(hits[k], 4)
         out.append(rec)
         print(json.dumps(rec))
     return out
@@ -252,11 +267,12 @@ def main():
                          "per M, then exit")
     ap.add_argument("--sweep-tokens", type=int, nargs="+", default=None,
                     help="batch sizes M of --regime-sweep")
-    ap.add_argument("--mfma-summary", metavar="CSV",
-                    help="MFMA busy fraction, clock and executed MFMA FLOPs per kernel from "
-                         "a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
+    ap.add_argument("--mfma-summary", nargs="+", metavar="CSV",
+                    help="MFMA_CSV [L2_CSV]: MFMA busy fraction, clock and executed MFMA FLOPs "
+                         "per kernel from a rocprofv3 --pmc run of SQ_VALU_MFMA_BUSY_CYCLES, "
                          "SQ_INSTS_VALU_MFMA_MOPS_BF16, SQ_INSTS_VALU_MFMA_MOPS_F8 and "
-                         "GRBM_GUI_ACTIVE; one JSON line per kernel, then exit")
+                         "GRBM_GUI_ACTIVE, and the L2 hit rate from a run of TCC_HIT_sum and "
+                         "TCC_MISS_sum; one JSON line per kernel, then exit")
     ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
                     help="FETCH_CSV WRITE_CSV COPY_FETCH_CSV COPY_WRITE_CSV [REQ_CSV COPY_REQ_CSV]: "
                          "turn rocprofv3 --pmc counter CSVs of this workload and of the copy "
@@ -264,7 +280,9 @@ def main():
                          "request-size counters) into profiles/gemm1_<workload>_pmc.json and exit")
     args = ap.parse_args()
     if args.mfma_summary:
-        mfma_summary(args.mfma_summary)
+        if len(args.mfma_summary) > 2:
+            sys.exit("--mfma-summary takes MFMA_CSV [L2_CSV]")
+        mfma_summary(*args.mfma_summary)
         return
     if args.pmc_summary:
         if len(args.pmc_summary) not in (4, 6):
