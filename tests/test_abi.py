@@ -164,3 +164,13 @@ def test_workspace_query_sizes(lib):
     # per-channel scales change no workspace region
     assert moe.workspace_size(moe.MOE_FP8_E4M3_ROWWISE, 128, 7168, 2048, 256, 8) == s_fp8
     assert moe.workspace_size(moe.MOE_MXFP4_E2M1, 128, 7168, 2048, 256, 8) == s_fp8
+    # e4m3 full tiles: 256-row blocks at 1024 rows per expert, 128-row blocks
+    # at 128 (the fp32 + e4m3 activations of [M*k + E*(B-1), N] dominate)
+    s_pre8 = moe.workspace_size(moe.MOE_FP8_E4M3, 4096, 4096, 14336, 8, 2)
+    assert s_pre8 >= (8192 + 8 * 255) * 14336 * 5
+    s_ds = moe.workspace_size(moe.MOE_FP8_E4M3, 4096, 7168, 2048, 256, 8)
+    assert (32768 + 256 * 127) * 2048 * 5 <= s_ds < (32768 + 256 * 255) * 2048 * 5
+    # forcing the decode kernels there sizes 64-row blocks
+    s_dsd = moe.workspace_size(moe.MOE_FP8_E4M3, 4096, 7168, 2048, 256, 8,
+                               moe.MOE_REGIME_DECODE)
+    assert (32768 + 256 * 63) * 2048 * 5 <= s_dsd < s_ds

@@ -408,11 +408,16 @@ def sample_tokens(M, n=6):
 
 
 # the DeepSeek-shaped batch also with per-channel e4m3 weight scales and with
-# MXFP4 weights; the prefill batch also with e4m3 weights
+# MXFP4 weights and at 4096 tokens; the prefill batch also with e4m3 weights
 @pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise", "dsv3_mxfp4",
-                                                      "mixtral_prefill_fp8"])
+                                                      "mixtral_prefill_fp8", "dsv3_fp8_4096"])
 def test_fused_full_size_sampled(moe, name):
-    if name == "mixtral_prefill_fp8":
+    if name == "dsv3_fp8_4096":
+        # 4096 tokens on the DeepSeek shape: 32 768 token-slots over 256
+        # experts (about 128 each): e4m3 full tiles with 128-row blocks and
+        # the multi-workgroup align
+        wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, M=4096)
+    elif name == "mixtral_prefill_fp8":
         # the prefill batch with e4m3 weights: the e4m3 full-tile kernels
         wl = wlm.WORKLOADS["mixtral_prefill"].resized(name=name, fp8=True)
     elif name == "dsv3_fp8_rowwise":
