@@ -104,7 +104,8 @@ def test_quant_rows_bit_exact_all_bf16_values(moe):
     assert np.array_equal(q.cpu().numpy(), rq)
 
 
-@pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (5, 4096), (2, 7168 + 3)])
+@pytest.mark.parametrize("M,K", [(1, 1), (3, 7), (5, 4096), (2, 7168 + 3), (4, 7168),
+                                 (3, 8192), (2, 8192 + 2048 + 8)])
 def test_quant_rows_ragged(moe, M, K):
     note(f"quant_rows M={M} K={K}")
     g = torch.Generator().manual_seed(M * 31 + K)
