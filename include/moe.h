@@ -156,7 +156,8 @@ moe_status moe_align(const int32_t *topk_ids, int M, int topk, int E, int block_
 
 /*
  * moe_align_ex -- moe_align with a caller workspace, for large batches: the
- * same outputs, bit for bit.  Above 2048 token-slots it runs over many
+ * same outputs, bit for bit.  Source: as moe_align (the fused op's data
+ * shuffling; per-expert batch sizes that change from call to call).  Above 2048 token-slots it runs over many
  * workgroups -- per 1024-slot chunk a count of the slots of each expert,
  * one scan that turns the counts into the padded segment starts and each
  * chunk's first position per expert, then per chunk the stable scatter --
