@@ -381,18 +381,20 @@ def test_fp8_decode_vs_tiles(moe):
 
 
 def test_fused_deterministic(moe):
+    """Ten calls on the same inputs are bitwise identical on every path: the
+    decode and full-tile kernels, bf16 and e4m3, and the multi-workgroup align
+    (no result depends on the order of atomics or on timing)."""
     note("determinism")
     wl = wlm.Workload("det", M=40, K=512, N=512, E=8, topk=2, seed=4)
-    d, g = gen_small(wl)
-    outs = [run_layer(moe, g, wl).clone() for _ in range(5)]
-    for o in outs[1:]:
-        assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16))
-    wl8 = wl.resized(fp8=True)
-    d8, g8 = gen_small(wl8)
-    for regime in (0, 2):
-        o8 = [run_layer(moe, g8, wl8, regime).clone() for _ in range(3)]
-        for o in o8[1:]:
-            assert torch.equal(o.view(torch.int16), o8[0].view(torch.int16))
+    big = wlm.Workload("det_big", M=1100, K=256, N=256, E=8, topk=2, seed=5)
+    for w, regimes in ((wl, (1, 2)), (wl.resized(fp8=True), (1, 2)), (big, (0,)),
+                       (big.resized(fp8=True), (0,))):
+        d, g = gen_small(w)
+        for regime in regimes:
+            outs = [run_layer(moe, g, w, regime).clone() for _ in range(10)]
+            for o in outs[1:]:
+                assert torch.equal(o.view(torch.int16), outs[0].view(torch.int16)), \
+                    (w.name, w.fp8, regime)
 
 
 # --------------------------------------------------------------------------
