@@ -285,10 +285,10 @@ SMALL = [
     ("fp8_topk16_tiles", 40, 256, 256, 32, 16, True, None, 2),
     # one or two tokens: the single-wave top-k + align, with bias, e4m3
     # (per-tensor and per-channel) and MXFP4 weights
-    ("tiny_route_fused_bias", 2, 768, 512, 8, 2, False, 0.5, 0),
-    ("tiny_route_fused_fp8", 1, 1536, 256, 8, 2, True, 0.5, 0),
-    ("tiny_route_fused_fp8_rowwise", 2, 512, 256, 4, 3, "rowwise", None, 0),
-    ("tiny_route_fused_mxfp4", 1, 512, 512, 12, 4, "mxfp4", None, 0),
+    ("two_tokens_wave_route_bias", 2, 768, 512, 8, 2, False, 0.5, 0),
+    ("one_token_wave_route_fp8", 1, 1536, 256, 8, 2, True, 0.5, 0),
+    ("two_tokens_wave_route_fp8_rowwise", 2, 512, 256, 4, 3, "rowwise", None, 0),
+    ("one_token_wave_route_mxfp4", 1, 512, 512, 12, 4, "mxfp4", None, 0),
 ]
 
 
