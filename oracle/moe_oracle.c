@@ -304,62 +304,68 @@ int orc_align(const int32_t *ids, int64_t M, int64_t k, int64_t E, int64_t B,
 
 static double silu(double z) { return z / (1.0 + exp(-z)); }
 
-/* One token-slot, bf16 weights: y[0:K] = W2 . (silu(W1g.x) * (W1u.x)). */
-static void expert_bf16(const uint16_t *xt, const uint16_t *w1, const uint16_t *w2,
-                        int64_t K, int64_t N, double *act, double *y)
+/* The expert MLP of one token-slot is written as two steps, so that the
+ * host's threads can share the work of a single slot: the activation
+ * element n (a function of the token row and two W1 rows) and the output
+ * element c (a function of the whole activation row and one W2 row).  Each
+ * element is one fixed-order fp64 sum, computed by one thread. */
+
+/* bf16 weights: act[n] = silu(W1g[n].x) * (W1u[n].x). */
+static double act_bf16(const uint16_t *xt, const uint16_t *w1, int64_t K, int64_t N, int64_t n)
 {
-    int64_t n, c, kk;
-    for (n = 0; n < N; ++n) {
-        const uint16_t *g = w1 + n * K;
-        const uint16_t *u = w1 + (N + n) * K;
-        double hg = 0.0, hu = 0.0;
-        for (kk = 0; kk < K; ++kk) {
-            double xv = orc_bf16_to_f64(xt[kk]);
-            hg += orc_bf16_to_f64(g[kk]) * xv;
-            hu += orc_bf16_to_f64(u[kk]) * xv;
-        }
-        act[n] = silu(hg) * hu;
+    const uint16_t *g = w1 + n * K;
+    const uint16_t *u = w1 + (N + n) * K;
+    double hg = 0.0, hu = 0.0;
+    int64_t kk;
+    for (kk = 0; kk < K; ++kk) {
+        double xv = orc_bf16_to_f64(xt[kk]);
+        hg += orc_bf16_to_f64(g[kk]) * xv;
+        hu += orc_bf16_to_f64(u[kk]) * xv;
     }
-    for (c = 0; c < K; ++c) {
-        const uint16_t *r = w2 + c * N;
-        double acc = 0.0;
-        for (n = 0; n < N; ++n)
-            acc += orc_bf16_to_f64(r[n]) * act[n];
-        y[c] = acc;
-    }
+    return silu(hg) * hu;
 }
 
-/* One token-slot, e4m3 weights: per-tensor scales (R7, rs = 0: every row
- * reads w1s[0] / w2s[0]) or per-channel scales (R8, rs = 1: row r reads
- * w1s[r] / w2s[r]). */
-static void expert_fp8(const uint8_t *xq, float sx, const uint8_t *w1, const float *w1s,
-                       const uint8_t *w2, const float *w2s, int64_t rs, int64_t K,
-                       int64_t N, double *act, float *act32, uint8_t *aq, double *y)
+/* bf16 weights: y[c] = W2[c] . act. */
+static double out_bf16(const double *act, const uint16_t *w2, int64_t N, int64_t c)
 {
-    int64_t n, c, kk;
-    float sa;
-    for (n = 0; n < N; ++n) {
-        const uint8_t *g = w1 + n * K;
-        const uint8_t *u = w1 + (N + n) * K;
-        double hg = 0.0, hu = 0.0;
-        for (kk = 0; kk < K; ++kk) {
-            double xv = e4m3_table[xq[kk]];
-            hg += e4m3_table[g[kk]] * xv;
-            hu += e4m3_table[u[kk]] * xv;
-        }
-        hg *= (double)sx * (double)w1s[n * rs];
-        hu *= (double)sx * (double)w1s[(N + n) * rs];
-        act[n] = silu(hg) * hu;
-        act32[n] = (float)act[n];
+    const uint16_t *r = w2 + c * N;
+    double acc = 0.0;
+    int64_t n;
+    for (n = 0; n < N; ++n)
+        acc += orc_bf16_to_f64(r[n]) * act[n];
+    return acc;
+}
+
+/* e4m3 weights, token codes xq with scale sx: per-tensor scales (R7,
+ * rs = 0: every row reads w1s[0] / w2s[0]) or per-channel scales (R8,
+ * rs = 1: row r reads w1s[r] / w2s[r]). */
+static double act_fp8(const uint8_t *xq, float sx, const uint8_t *w1, const float *w1s,
+                      int64_t rs, int64_t K, int64_t N, int64_t n)
+{
+    const uint8_t *g = w1 + n * K;
+    const uint8_t *u = w1 + (N + n) * K;
+    double hg = 0.0, hu = 0.0;
+    int64_t kk;
+    for (kk = 0; kk < K; ++kk) {
+        double xv = e4m3_table[xq[kk]];
+        hg += e4m3_table[g[kk]] * xv;
+        hu += e4m3_table[u[kk]] * xv;
     }
-    quant_row_f32(act32, N, aq, &sa);
-    for (c = 0; c < K; ++c) {
-        const uint8_t *r = w2 + c * N;
-        double acc = 0.0;
-        for (n = 0; n < N; ++n)
-            acc += e4m3_table[r[n]] * e4m3_table[aq[n]];
-        y[c] = acc * (double)sa * (double)w2s[c * rs];
-    }
+    hg *= (double)sx * (double)w1s[n * rs];
+    hu *= (double)sx * (double)w1s[(N + n) * rs];
+    return silu(hg) * hu;
+}
+
+/* e4m3 weights: y[c] = sa * w2s . (W2[c] . act codes aq). */
+static double out_fp8(const uint8_t *aq, float sa, const uint8_t *w2, const float *w2s,
+                      int64_t rs, int64_t N, int64_t c)
+{
+    const uint8_t *r = w2 + c * N;
+    double acc = 0.0;
+    int64_t n;
+    for (n = 0; n < N; ++n)
+        acc += e4m3_table[r[n]] * e4m3_table[aq[n]];
+    return acc * (double)sa * (double)w2s[c * rs];
 }
 
 /* e2m1 code (low 4 bits) -> value, from the format's definition (R9). */
@@ -384,33 +390,33 @@ static double mx_weight(const uint8_t *w, const uint8_t *sc, int64_t cols, int64
     return orc_e2m1_to_f64(code) * orc_e8m0_to_f64(sc[r * (cols / 32) + k / 32]);
 }
 
-/* One token-slot, MXFP4 weights (R9): w1 [2N, K/2] packed with scales
- * s1 [2N, K/32], w2 [K, N/2] with s2 [K, N/32]. */
-static void expert_mxfp4(const uint8_t *xq, float sx, const uint8_t *w1, const uint8_t *s1,
-                         const uint8_t *w2, const uint8_t *s2, int64_t K, int64_t N,
-                         double *act, float *act32, uint8_t *aq, double *y)
+/* MXFP4 weights (R9): w1 [2N, K/2] packed with scales s1 [2N, K/32];
+ * act[n] from the token codes xq with scale sx. */
+static double act_mxfp4(const uint8_t *xq, float sx, const uint8_t *w1, const uint8_t *s1,
+                        int64_t K, int64_t N, int64_t n)
 {
-    int64_t n, c, kk;
-    float sa;
-    for (n = 0; n < N; ++n) {
-        double hg = 0.0, hu = 0.0;
-        for (kk = 0; kk < K; ++kk) {
-            double xv = e4m3_table[xq[kk]];
-            hg += mx_weight(w1, s1, K, n, kk) * xv;
-            hu += mx_weight(w1, s1, K, N + n, kk) * xv;
-        }
-        hg *= (double)sx;
-        hu *= (double)sx;
-        act[n] = silu(hg) * hu;
-        act32[n] = (float)act[n];
+    double hg = 0.0, hu = 0.0;
+    int64_t kk;
+    for (kk = 0; kk < K; ++kk) {
+        double xv = e4m3_table[xq[kk]];
+        hg += mx_weight(w1, s1, K, n, kk) * xv;
+        hu += mx_weight(w1, s1, K, N + n, kk) * xv;
     }
-    quant_row_f32(act32, N, aq, &sa);
-    for (c = 0; c < K; ++c) {
-        double acc = 0.0;
-        for (n = 0; n < N; ++n)
-            acc += mx_weight(w2, s2, N, c, n) * e4m3_table[aq[n]];
-        y[c] = acc * (double)sa;
-    }
+    hg *= (double)sx;
+    hu *= (double)sx;
+    return silu(hg) * hu;
+}
+
+/* MXFP4 weights: w2 [K, N/2] with scales s2 [K, N/32]; y[c] from the
+ * activation codes aq with scale sa. */
+static double out_mxfp4(const uint8_t *aq, float sa, const uint8_t *w2, const uint8_t *s2,
+                        int64_t N, int64_t c)
+{
+    double acc = 0.0;
+    int64_t n;
+    for (n = 0; n < N; ++n)
+        acc += mx_weight(w2, s2, N, c, n) * e4m3_table[aq[n]];
+    return acc * (double)sa;
 }
 
 /* Per-token dynamic quantisation of bf16 rows (R7): xq [M,K], sx [M]. */
@@ -461,9 +467,10 @@ int orc_quant_rows_f32(const float *v, int64_t M, int64_t K, uint8_t *q, float *
  *   ids_out   int32 [n_tok, k] or NULL; wts_out fp64 [n_tok, k] or NULL
  *
  * Returns ORC_ERR_MISSING_EXPERT if a selected expert's weights are NULL.
- * Token-slots run in parallel; each writes its own y row, and the combine
- * then sums the k slots of a token in ascending j, so results do not depend
- * on the thread count.
+ * The threads share the (slot, element) pairs of each step; every element
+ * is one fixed-order sum written by one thread, and the combine then sums
+ * the k slots of a token in ascending j, so results do not depend on the
+ * thread count.
  */
 int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const float *bias,
                     const void *const *w1, const void *const *w2,
@@ -473,10 +480,12 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
                     double *out, int32_t *ids_out, double *wts_out)
 {
     int64_t i, nslot = n_tok * k;
-    int32_t *ids;
-    double *wts, *y;
-    float *lg;
+    int32_t *ids = NULL;
+    double *wts = NULL, *y = NULL, *act = NULL;
+    float *lg = NULL, *sx = NULL, *sa = NULL;
+    uint8_t *xq = NULL, *aq = NULL;
     int rc = ORC_OK;
+    const int quant = dtype != 0;
     if (dtype < 0 || dtype > 3 || M < 0 || K <= 0 || N <= 0 || E <= 0 ||
         k < 1 || k > E || n_tok < 0 || !x || !wr || !w1 || !w2 || !out ||
         (n_tok > 0 && !tokens) || (dtype != 0 && (!w1s || !w2s)) ||
@@ -486,11 +495,21 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
         if (tokens[i] < 0 || tokens[i] >= M)
             return ORC_ERR_ARG;
     init_e4m3_table();
-    ids = (int32_t *)malloc((size_t)(nslot > 0 ? nslot : 1) * sizeof *ids);
-    wts = (double *)malloc((size_t)(nslot > 0 ? nslot : 1) * sizeof *wts);
-    lg = (float *)malloc((size_t)(n_tok > 0 ? n_tok : 1) * (size_t)E * sizeof *lg);
-    y = (double *)malloc((size_t)(nslot > 0 ? nslot : 1) * (size_t)K * sizeof *y);
-    if (!ids || !wts || !lg || !y) {
+    {
+        const size_t ns = (size_t)(nslot > 0 ? nslot : 1), nt = (size_t)(n_tok > 0 ? n_tok : 1);
+        ids = (int32_t *)malloc(ns * sizeof *ids);
+        wts = (double *)malloc(ns * sizeof *wts);
+        lg = (float *)malloc(nt * (size_t)E * sizeof *lg);
+        y = (double *)malloc(ns * (size_t)K * sizeof *y);
+        act = (double *)malloc(ns * (size_t)N * sizeof *act);
+        if (quant) {
+            xq = (uint8_t *)malloc(nt * (size_t)K);
+            sx = (float *)malloc(nt * sizeof *sx);
+            aq = (uint8_t *)malloc(ns * (size_t)N);
+            sa = (float *)malloc(ns * sizeof *sa);
+        }
+    }
+    if (!ids || !wts || !lg || !y || !act || (quant && (!xq || !sx || !aq || !sa))) {
         rc = ORC_ERR_NOMEM;
         goto done;
     }
@@ -508,51 +527,98 @@ int orc_moe_forward(int dtype, const uint16_t *x, const uint16_t *wr, const floa
             rc = ORC_ERR_MISSING_EXPERT;
             goto done;
         }
-
+    /* FP8 and MXFP4: the per-token e4m3 codes of the token rows (R7) */
+    if (quant) {
+        rc = ORC_OK;
 #pragma omp parallel
-    {
-        double *act = (double *)malloc((size_t)N * sizeof *act);
-        float *act32 = (float *)malloc((size_t)N * sizeof *act32);
-        uint8_t *aq = (uint8_t *)malloc((size_t)N);
-        uint8_t *xq = (uint8_t *)malloc((size_t)K);
-        float *xrow = (float *)malloc((size_t)K * sizeof *xrow);
-        int64_t s;
-#pragma omp for schedule(dynamic, 1)
-        for (s = 0; s < nslot; ++s) {
-            int64_t t = tokens[s / k];
-            int e = ids[s];
-            const uint16_t *xt = x + t * K;
-            if (dtype == 0) {
-                expert_bf16(xt, (const uint16_t *)w1[e], (const uint16_t *)w2[e],
-                            K, N, act, y + s * K);
-            } else {
-                float sx;
-                int64_t kk;
-                for (kk = 0; kk < K; ++kk)
-                    xrow[kk] = bf16_to_f32(xt[kk]);
-                quant_row_f32(xrow, K, xq, &sx);
-                if (dtype == 1)
-                    expert_fp8(xq, sx, (const uint8_t *)w1[e], (const float *)w1s + e,
-                               (const uint8_t *)w2[e], (const float *)w2s + e, 0, K, N,
-                               act, act32, aq, y + s * K);
-                else if (dtype == 2)
-                    expert_fp8(xq, sx, (const uint8_t *)w1[e],
-                               (const float *)w1s + e * 2 * N, (const uint8_t *)w2[e],
-                               (const float *)w2s + e * K, 1, K, N, act, act32, aq,
-                               y + s * K);
-                else
-                    expert_mxfp4(xq, sx, (const uint8_t *)w1[e],
-                                 (const uint8_t *)w1s + e * 2 * N * (K / 32),
-                                 (const uint8_t *)w2[e],
-                                 (const uint8_t *)w2s + e * K * (N / 32), K, N, act, act32,
-                                 aq, y + s * K);
+        {
+            float *xrow = (float *)malloc((size_t)K * sizeof *xrow);
+            int64_t t, kk;
+            if (!xrow) {
+#pragma omp atomic write
+                rc = ORC_ERR_NOMEM;
             }
+#pragma omp for schedule(static)
+            for (t = 0; t < n_tok; ++t) {
+                if (!xrow)
+                    continue;
+                for (kk = 0; kk < K; ++kk)
+                    xrow[kk] = bf16_to_f32(x[tokens[t] * K + kk]);
+                quant_row_f32(xrow, K, xq + t * K, sx + t);
+            }
+            free(xrow);
         }
-        free(act);
-        free(act32);
-        free(aq);
-        free(xq);
-        free(xrow);
+        if (rc)
+            goto done;
+    }
+    /* the SiLU*up activation of every (slot, n) */
+    {
+        int64_t idx;
+#pragma omp parallel for schedule(static)
+        for (idx = 0; idx < nslot * N; ++idx) {
+            const int64_t s = idx / N, n = idx % N, tt = s / k;
+            const int e = ids[s];
+            double v;
+            if (dtype == 0)
+                v = act_bf16(x + tokens[tt] * K, (const uint16_t *)w1[e], K, N, n);
+            else if (dtype == 1)
+                v = act_fp8(xq + tt * K, sx[tt], (const uint8_t *)w1[e], (const float *)w1s + e,
+                            0, K, N, n);
+            else if (dtype == 2)
+                v = act_fp8(xq + tt * K, sx[tt], (const uint8_t *)w1[e],
+                            (const float *)w1s + e * 2 * N, 1, K, N, n);
+            else
+                v = act_mxfp4(xq + tt * K, sx[tt], (const uint8_t *)w1[e],
+                              (const uint8_t *)w1s + e * 2 * N * (K / 32), K, N, n);
+            act[idx] = v;
+        }
+    }
+    /* FP8 and MXFP4: per token-slot e4m3 codes of the activation, quantised
+     * from its fp64 value rounded to fp32 (R7) */
+    if (quant) {
+        rc = ORC_OK;
+#pragma omp parallel
+        {
+            float *row = (float *)malloc((size_t)N * sizeof *row);
+            int64_t s, n;
+            if (!row) {
+#pragma omp atomic write
+                rc = ORC_ERR_NOMEM;
+            }
+#pragma omp for schedule(static)
+            for (s = 0; s < nslot; ++s) {
+                if (!row)
+                    continue;
+                for (n = 0; n < N; ++n)
+                    row[n] = (float)act[s * N + n];
+                quant_row_f32(row, N, aq + s * N, sa + s);
+            }
+            free(row);
+        }
+        if (rc)
+            goto done;
+    }
+    /* the expert output of every (slot, c) */
+    {
+        int64_t idx;
+#pragma omp parallel for schedule(static)
+        for (idx = 0; idx < nslot * K; ++idx) {
+            const int64_t s = idx / K, c = idx % K;
+            const int e = ids[s];
+            double v;
+            if (dtype == 0)
+                v = out_bf16(act + s * N, (const uint16_t *)w2[e], N, c);
+            else if (dtype == 1)
+                v = out_fp8(aq + s * N, sa[s], (const uint8_t *)w2[e], (const float *)w2s + e, 0,
+                            N, c);
+            else if (dtype == 2)
+                v = out_fp8(aq + s * N, sa[s], (const uint8_t *)w2[e],
+                            (const float *)w2s + e * K, 1, N, c);
+            else
+                v = out_mxfp4(aq + s * N, sa[s], (const uint8_t *)w2[e],
+                              (const uint8_t *)w2s + e * K * (N / 32), N, c);
+            y[idx] = v;
+        }
     }
 
     /* weighted combine, slots in ascending j */
@@ -574,6 +640,11 @@ done:
     free(wts);
     free(lg);
     free(y);
+    free(act);
+    free(xq);
+    free(sx);
+    free(aq);
+    free(sa);
     return rc;
 }
 
