@@ -70,9 +70,8 @@ typedef enum {
                                   codes two per byte, the even element in the low
                                   nibble, w1 [E,2N,K/2], w2 [E,K,N/2]; one E8M0 scale
                                   byte (2^(e-127)) per 32 elements of a row,
-                                  w1_scale [E,2N,K/32], w2_scale [E,K,N/32], passed
-                                  through the float pointer parameters as uint8
-                                  arrays; activations are quantised per token to
+                                  w1_scale [E,2N,K/32], w2_scale [E,K,N/32] (uint8
+                                  arrays); activations are quantised per token to
                                   e4m3 as for MOE_FP8_E4M3 */
 } moe_dtype;
 
@@ -167,7 +166,8 @@ moe_status moe_align(const int32_t *topk_ids, int M, int topk, int E, int block_
  *   topk_ids ... num_padded   as moe_align
  *   workspace        device buffer of at least *workspace_bytes bytes
  *                    (256-byte aligned), or NULL to query: the call stores the
- *                    required size (0 up to 2048 slots) in *workspace_bytes,
+ *                    required size (256 bytes up to 2048 slots, where
+ *                    the buffer is not used) in *workspace_bytes,
  *                    enqueues nothing and returns MOE_OK
  *   workspace_bytes  host pointer: in = size of `workspace`, out = required
  *
@@ -214,9 +214,11 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  *   w1        [E,2N,K] bf16 or e4m3 (dtype); MXFP4: [E,2N,K/2] bytes, two
  *             e2m1 codes each (even element in the low nibble)
  *   w2        [E,K,N]  bf16 or e4m3; MXFP4: [E,K,N/2] bytes
- *   w1_scale  fp32 [E] (MOE_FP8_E4M3), [E,2N] (MOE_FP8_E4M3_ROWWISE), uint8
- *             E8M0 [E,2N,K/32] (MOE_MXFP4_E2M1) or NULL (MOE_BF16); w2_scale
- *             likewise [E], [E,K], [E,K,N/32] or NULL
+ *   w1_scale  per dtype: fp32 [E] (MOE_FP8_E4M3), fp32 [E,2N]
+ *             (MOE_FP8_E4M3_ROWWISE), uint8 E8M0 [E,2N,K/32] (MOE_MXFP4_E2M1)
+ *             or NULL (MOE_BF16); w2_scale likewise fp32 [E], fp32 [E,K],
+ *             uint8 [E,K,N/32] or NULL.  The element type follows dtype, so
+ *             the parameters are untyped.
  *   out       out bf16 [M,K]
  *   workspace device buffer of at least *workspace_bytes bytes (256-byte
  *             aligned), or NULL to query: with workspace == NULL the call
@@ -228,6 +230,14 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  * FP8: x is quantised per token to e4m3 with scale amax/448; the SiLU*up
  * activation per token-slot likewise; GEMM accumulation is fp32.
  *
+ * After the call completes (in stream order) the workspace holds the
+ * layer's own routing at the offsets moe_fused_plan reports: logits fp32
+ * [M,E], topk_ids int32 [M,topk], topk_weights fp32 [M,topk], sorted_ids
+ * int32 [sorted_rows], block_expert int32 [max_blocks], expert_offsets int32
+ * [E+1] and num_padded int32 [1], each with the meaning moe_topk and
+ * moe_align give it (block size block_m of the plan).  These are the values
+ * the GEMMs consumed, so a caller can check or reuse them.
+ *
  * Errors: as moe_topk, plus INVALID_ARG for null w1/w2/out/workspace_bytes,
  * N < 1, a bad dtype, scales given for bf16 or missing for fp8;
  * UNSUPPORTED for K or N not a multiple of 128 or the size limits above
@@ -238,7 +248,7 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  */
 moe_status moe_fused_forward(const void *x, const void *w_router, const float *router_bias,
                              const void *w1, const void *w2,
-                             const float *w1_scale, const float *w2_scale,
+                             const void *w1_scale, const void *w2_scale,
                              int dtype, int M, int K, int N, int E, int topk,
                              void *out, void *workspace, size_t *workspace_bytes,
                              void *stream);
@@ -249,7 +259,7 @@ moe_status moe_fused_forward(const void *x, const void *w_router, const float *r
  * page above). */
 moe_status moe_fused_forward_ex(const void *x, const void *w_router, const float *router_bias,
                                 const void *w1, const void *w2,
-                                const float *w1_scale, const float *w2_scale,
+                                const void *w1_scale, const void *w2_scale,
                                 int dtype, int M, int K, int N, int E, int topk,
                                 int regime, void *out, void *workspace,
                                 size_t *workspace_bytes, void *stream);
@@ -264,11 +274,45 @@ moe_status moe_fused_forward_ex(const void *x, const void *w_router, const float
  * INVALID_ARG for a NULL `events` when workspace is non-NULL. */
 moe_status moe_fused_forward_timed(const void *x, const void *w_router, const float *router_bias,
                                    const void *w1, const void *w2,
-                                   const float *w1_scale, const float *w2_scale,
+                                   const void *w1_scale, const void *w2_scale,
                                    int dtype, int M, int K, int N, int E, int topk,
                                    int regime, void *out, void *workspace,
                                    size_t *workspace_bytes, void *stream,
                                    void *const *events);
+
+/*
+ * moe_plan / moe_fused_plan -- the launch plan moe_fused_forward_ex takes for
+ * a shape: the kernel family (the Swap-AB decode kernels or full tiles,
+ * "Mixture-of-Experts kernel engineering on Amazon SageMaker AI", decode-
+ * phase passage and Figure 1), the block size of the expert-sorted rows, the
+ * reduction splits, the workspace size and where in the workspace the
+ * routing outputs of the call live (see moe_fused_forward).  The plan
+ * depends only on (dtype, M, K, N, E, topk, regime); the query makes no HIP
+ * call.
+ *
+ * Errors: INVALID_ARG for a NULL plan and the argument errors of
+ * moe_fused_forward_ex that concern these values; UNSUPPORTED as there.
+ */
+typedef struct {
+    int32_t regime;        /* kernel family used: MOE_REGIME_DECODE or MOE_REGIME_PREFILL */
+    int32_t block_m;       /* rows per block of the sorted list */
+    int32_t sorted_rows;   /* entries of sorted_ids: M*topk + E*(block_m-1) */
+    int32_t max_blocks;    /* entries of block_expert: sorted_rows / block_m */
+    int32_t gemm2_splits;  /* GEMM2 reduction split into fp32 partial rows */
+    int32_t logit_splits;  /* router reduction split (fp64 partials) */
+    int32_t reserved[2];   /* zero */
+    uint64_t workspace_bytes;
+    uint64_t logits_offset;          /* byte offsets into the workspace */
+    uint64_t topk_ids_offset;
+    uint64_t topk_weights_offset;
+    uint64_t sorted_ids_offset;
+    uint64_t block_expert_offset;
+    uint64_t expert_offsets_offset;
+    uint64_t num_padded_offset;
+} moe_plan;
+
+moe_status moe_fused_plan(int dtype, int M, int K, int N, int E, int topk, int regime,
+                          moe_plan *plan);
 
 /* Static, NUL-terminated name of a status code. */
 const char *moe_status_string(int status);

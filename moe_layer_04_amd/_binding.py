@@ -35,7 +35,22 @@ MOE_REGIME_DECODE = 1
 MOE_REGIME_PREFILL = 2
 
 EXPORTS = ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3", "moe_fused_forward",
-           "moe_fused_forward_ex", "moe_fused_forward_timed", "moe_status_string")
+           "moe_fused_forward_ex", "moe_fused_forward_timed", "moe_fused_plan",
+           "moe_status_string")
+
+
+class Plan(ctypes.Structure):
+    """moe_plan of include/moe.h: the launch plan of the fused forward for a
+    shape, and where its routing outputs sit in the workspace."""
+    _fields_ = [("regime", ctypes.c_int32), ("block_m", ctypes.c_int32),
+                ("sorted_rows", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
+                ("gemm2_splits", ctypes.c_int32), ("logit_splits", ctypes.c_int32),
+                ("reserved", ctypes.c_int32 * 2),
+                ("workspace_bytes", ctypes.c_uint64), ("logits_offset", ctypes.c_uint64),
+                ("topk_ids_offset", ctypes.c_uint64), ("topk_weights_offset", ctypes.c_uint64),
+                ("sorted_ids_offset", ctypes.c_uint64), ("block_expert_offset", ctypes.c_uint64),
+                ("expert_offsets_offset", ctypes.c_uint64),
+                ("num_padded_offset", ctypes.c_uint64)]
 
 _lock = threading.Lock()
 _lib = None
@@ -69,9 +84,10 @@ def load_library(build_if_missing: bool = False):
                                              SZP, P]
         lib.moe_fused_forward_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
                                                 SZP, P, P]
+        lib.moe_fused_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(Plan)]
         for name in ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3",
-                     "moe_fused_forward",
-                     "moe_fused_forward_ex", "moe_fused_forward_timed"):
+                     "moe_fused_forward", "moe_fused_forward_ex", "moe_fused_forward_timed",
+                     "moe_fused_plan"):
             getattr(lib, name).restype = ctypes.c_int
         lib.moe_status_string.argtypes = [I]
         lib.moe_status_string.restype = ctypes.c_char_p
@@ -194,6 +210,36 @@ def _weight_dtype(w1: torch.Tensor, w1_scale: Optional[torch.Tensor]) -> int:
     if w1_scale is not None and w1_scale.dim() == 2:
         return MOE_FP8_E4M3_ROWWISE
     return MOE_FP8_E4M3
+
+
+def fused_plan(dtype: int, M: int, K: int, N: int, E: int, topk: int,
+               regime: int = MOE_REGIME_AUTO) -> Plan:
+    """The library's launch plan for this shape (no GPU call is made)."""
+    plan = Plan()
+    _check(load_library().moe_fused_plan(dtype, M, K, N, E, topk, regime, ctypes.byref(plan)),
+           "moe_fused_plan")
+    return plan
+
+
+def fused_routing(workspace: torch.Tensor, plan: Plan, M: int, E: int, topk: int) -> dict:
+    """Views of the routing outputs a completed moe_fused_forward left in its
+    workspace (offsets from ``plan``): logits, topk_ids, topk_weights,
+    sorted_ids, block_expert, expert_offsets, num_padded."""
+    _dev(workspace, "workspace", torch.uint8)
+
+    def view(off, n, dt):
+        nbytes = n * 4
+        return workspace[off: off + nbytes].view(dt)
+
+    return {
+        "logits": view(plan.logits_offset, M * E, torch.float32).view(M, E),
+        "topk_ids": view(plan.topk_ids_offset, M * topk, torch.int32).view(M, topk),
+        "topk_weights": view(plan.topk_weights_offset, M * topk, torch.float32).view(M, topk),
+        "sorted_ids": view(plan.sorted_ids_offset, plan.sorted_rows, torch.int32),
+        "block_expert": view(plan.block_expert_offset, plan.max_blocks, torch.int32),
+        "expert_offsets": view(plan.expert_offsets_offset, E + 1, torch.int32),
+        "num_padded": view(plan.num_padded_offset, 1, torch.int32),
+    }
 
 
 def workspace_size(dtype: int, M: int, K: int, N: int, E: int, topk: int,

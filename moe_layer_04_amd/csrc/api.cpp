@@ -232,7 +232,10 @@ MOE_API moe_status moe_align_ex(const int32_t* topk_ids, int M, int topk, int E,
     const bool multi = moe::align_multi_fits(n);
     // chunk counts [chunks, E], then the experts' totals [E]
     const size_t chunk_bytes = round_up((size_t)moe::align_chunks(n) * E * 4);
-    const size_t need = multi ? chunk_bytes + round_up((size_t)E * 4) : 0;
+    // a non-zero size even where the single-workgroup align uses no
+    // scratch, so that a buffer sized from the query is never NULL (which
+    // would read as another size query)
+    const size_t need = multi ? chunk_bytes + round_up((size_t)E * 4) : kAlign;
     if (!workspace) {
         *workspace_bytes = need;
         return MOE_OK;
@@ -256,18 +259,12 @@ MOE_API moe_status moe_align_ex(const int32_t* topk_ids, int M, int topk, int E,
     return finish_launches();
 }
 
-static moe_status fused_impl(const void* x, const void* w_router, const float* router_bias,
-                             const void* w1, const void* w2, const float* w1_scale,
-                             const float* w2_scale, int dtype, int M, int K, int N, int E,
-                             int topk, int regime, void* out, void* workspace,
-                             size_t* workspace_bytes, void* stream, void* const* events,
-                             bool timed) {
-    if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+// Arguments that fix the plan (dtype, sizes, regime): the checks shared by
+// the fused forward and the plan query.
+static moe_status fused_shape_check(int dtype, int M, int K, int N, int E, int topk, int regime) {
     if (dtype != MOE_BF16 && !is_fp8(dtype)) return MOE_ERR_INVALID_ARG;
     if (regime < MOE_REGIME_AUTO || regime > MOE_REGIME_PREFILL) return MOE_ERR_INVALID_ARG;
     if (M < 0 || K < 1 || N < 1 || E < 1 || topk < 1 || topk > E) return MOE_ERR_INVALID_ARG;
-    if (dtype == MOE_BF16 && (w1_scale || w2_scale)) return MOE_ERR_INVALID_ARG;
-    if (is_fp8(dtype) && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
     if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
     // MXFP4: 256-deep steps; GEMM1 keeps K/32 scale bytes per row of its
@@ -289,6 +286,49 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     // MXFP4 GEMM2: a split's scale bytes must fit its LDS copy
     if (dtype == MOE_MXFP4_E2M1 && N / p.nsplit > moe::tune::kMxMaxSplitLen)
         return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_fused_plan(int dtype, int M, int K, int N, int E, int topk, int regime,
+                                  moe_plan* plan) {
+    if (!plan) return MOE_ERR_INVALID_ARG;
+    const moe_status st = fused_shape_check(dtype, M, K, N, E, topk, regime);
+    if (st != MOE_OK) return st;
+    const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
+    memset(plan, 0, sizeof(*plan));
+    plan->regime = p.regime;
+    plan->block_m = p.block;
+    plan->sorted_rows = p.cap;
+    plan->max_blocks = p.max_blocks;
+    plan->gemm2_splits = p.nsplit;
+    plan->logit_splits = p.lsplit;
+    plan->workspace_bytes = p.total;
+    plan->logits_offset = p.logits;
+    plan->topk_ids_offset = p.ids;
+    plan->topk_weights_offset = p.wts;
+    plan->sorted_ids_offset = p.sorted;
+    plan->block_expert_offset = p.bexp;
+    plan->expert_offsets_offset = p.offs;
+    plan->num_padded_offset = p.npad;
+    return MOE_OK;
+}
+
+static moe_status fused_impl(const void* x, const void* w_router, const float* router_bias,
+                             const void* w1, const void* w2, const void* w1_scale,
+                             const void* w2_scale, int dtype, int M, int K, int N, int E,
+                             int topk, int regime, void* out, void* workspace,
+                             size_t* workspace_bytes, void* stream, void* const* events,
+                             bool timed) {
+    if (!workspace_bytes) return MOE_ERR_INVALID_ARG;
+    if (dtype != MOE_BF16 && !is_fp8(dtype)) return MOE_ERR_INVALID_ARG;
+    if (dtype == MOE_BF16 && (w1_scale || w2_scale)) return MOE_ERR_INVALID_ARG;
+    if (is_fp8(dtype) && (!w1_scale || !w2_scale)) return MOE_ERR_INVALID_ARG;
+    {
+        const moe_status st = fused_shape_check(dtype, M, K, N, E, topk, regime);
+        if (st != MOE_OK) return st;
+    }
+    const long slots = (long)M * topk;
+    const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
     if (!workspace) {
         *workspace_bytes = p.total;
         return MOE_OK;
@@ -363,7 +403,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         const bool mx = dtype == MOE_MXFP4_E2M1;
         const bool tiles = p.regime == MOE_REGIME_PREFILL;  // e4m3 only
         if (tiles)
-            moe::launch_gemm1_prefill_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
+            moe::launch_gemm1_prefill_fp8(xq, xs, w1, (const float*)w1_scale, rowwise, sorted, bexp, npad, M,
                                           topk, nslots, K, N, p.grid_blocks, p.block, act, amax,
                                           s);
         else if (mx)
@@ -371,14 +411,14 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                            npad, M, topk, nslots, K, N, p.grid_blocks,
                                            p.block / kDecodeBlock, act, amax, s);
         else
-            moe::launch_gemm1_decode_fp8(xq, xs, w1, w1_scale, rowwise, sorted, bexp, npad, M,
+            moe::launch_gemm1_decode_fp8(xq, xs, w1, (const float*)w1_scale, rowwise, sorted, bexp, npad, M,
                                          topk, nslots, K, N, p.grid_blocks, p.block / kDecodeBlock,
                                          act, amax, s);
         mark(4);
         moe::launch_act_quant(act, amax, inv, nslots, N, actq, as, s);
         mark(5);
         if (tiles)
-            moe::launch_gemm2_prefill_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
+            moe::launch_gemm2_prefill_fp8(actq, as, w2, (const float*)w2_scale, rowwise, wts, sorted, bexp,
                                           npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
                                           p.block, ypart, s);
         else if (mx)
@@ -386,7 +426,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
                                            bexp, npad, p.cap, nslots, K, N, p.nsplit,
                                            p.grid_blocks, p.block / kDecodeBlock, ypart, s);
         else
-            moe::launch_gemm2_decode_fp8(actq, as, w2, w2_scale, rowwise, wts, sorted, bexp,
+            moe::launch_gemm2_decode_fp8(actq, as, w2, (const float*)w2_scale, rowwise, wts, sorted, bexp,
                                          npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
                                          p.block / kDecodeBlock, ypart, s);
         mark(6);
@@ -416,8 +456,8 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
 
 MOE_API moe_status moe_fused_forward_ex(const void* x, const void* w_router,
                                         const float* router_bias, const void* w1,
-                                        const void* w2, const float* w1_scale,
-                                        const float* w2_scale, int dtype, int M, int K, int N,
+                                        const void* w2, const void* w1_scale,
+                                        const void* w2_scale, int dtype, int M, int K, int N,
                                         int E, int topk, int regime, void* out,
                                         void* workspace, size_t* workspace_bytes,
                                         void* stream) {
@@ -427,8 +467,8 @@ MOE_API moe_status moe_fused_forward_ex(const void* x, const void* w_router,
 
 MOE_API moe_status moe_fused_forward_timed(const void* x, const void* w_router,
                                            const float* router_bias, const void* w1,
-                                           const void* w2, const float* w1_scale,
-                                           const float* w2_scale, int dtype, int M, int K,
+                                           const void* w2, const void* w1_scale,
+                                           const void* w2_scale, int dtype, int M, int K,
                                            int N, int E, int topk, int regime, void* out,
                                            void* workspace, size_t* workspace_bytes,
                                            void* stream, void* const* events) {
@@ -438,7 +478,7 @@ MOE_API moe_status moe_fused_forward_timed(const void* x, const void* w_router,
 
 MOE_API moe_status moe_fused_forward(const void* x, const void* w_router,
                                      const float* router_bias, const void* w1, const void* w2,
-                                     const float* w1_scale, const float* w2_scale, int dtype,
+                                     const void* w1_scale, const void* w2_scale, int dtype,
                                      int M, int K, int N, int E, int topk, void* out,
                                      void* workspace, size_t* workspace_bytes, void* stream) {
     return moe_fused_forward_ex(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K,

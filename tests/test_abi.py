@@ -63,9 +63,10 @@ def test_topk_validation(lib):
 def test_align_ex_validation(lib):
     f = lib.moe_align_ex
     n = ctypes.c_size_t(0)
-    # size queries make no HIP call: none up to 2048 slots, chunk counts above
+    # size queries make no HIP call: a minimal 256 bytes up to 2048 slots
+    # (never 0, so a buffer sized from the query is not NULL), chunk counts above
     assert f(None, 1024, 2, 8, 16, None, None, None, None, None, ctypes.byref(n), None) == 0
-    assert n.value == 0
+    assert n.value == 256
     assert f(None, 4096, 2, 256, 16, None, None, None, None, None, ctypes.byref(n), None) == 0
     assert n.value >= (8 * 256 + 256) * 4
     need = n.value
@@ -177,3 +178,43 @@ def test_workspace_query_sizes(lib):
     s_dsd = moe.workspace_size(moe.MOE_FP8_E4M3, 4096, 7168, 2048, 256, 8,
                                moe.MOE_REGIME_DECODE)
     assert (32768 + 256 * 63) * 2048 * 5 + ypart <= s_dsd < s_ds
+
+
+def test_fused_plan(lib):
+    """The plan query (no HIP call): kernel family per workload, block sizes,
+    and routing regions that lie inside the workspace without overlapping."""
+    P = B.Plan
+    assert lib.moe_fused_plan(0, 8, 256, 512, 8, 2, 0, None) == B.MOE_ERR_INVALID_ARG
+    p = P()
+    assert lib.moe_fused_plan(0, 8, 200, 512, 8, 2, 0, ctypes.byref(p)) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fused_plan(5, 8, 256, 512, 8, 2, 0, ctypes.byref(p)) == B.MOE_ERR_INVALID_ARG
+    assert lib.moe_fused_plan(3, 8, 256, 512, 8, 2, 2, ctypes.byref(p)) == B.MOE_ERR_UNSUPPORTED
+    cases = {  # (dtype, M, K, N, E, k): regime, block
+        (0, 64, 256, 512, 8, 2): (2, 128),      # 16 rows per expert: full tiles
+        (0, 8, 4096, 14336, 8, 2): (1, 16),
+        (0, 1, 4096, 8192, 16, 2): (1, 16),
+        (0, 4096, 4096, 14336, 8, 2): (2, 256),
+        (1, 128, 7168, 2048, 256, 8): (1, 16),
+        (1, 4096, 7168, 2048, 256, 8): (2, 128),
+    }
+    for (dt, M, K, N, E, k), (regime, block) in cases.items():
+        p = moe.fused_plan(dt, M, K, N, E, k)
+        assert p.regime == regime, (dt, M)
+        if block is not None:
+            assert p.block_m == block, (dt, M, p.block_m)
+        assert p.sorted_rows == M * k + E * (p.block_m - 1)
+        assert p.max_blocks == p.sorted_rows // p.block_m
+        assert p.workspace_bytes == moe.workspace_size(dt, M, K, N, E, k)
+        regions = sorted([(p.logits_offset, M * E * 4), (p.topk_ids_offset, M * k * 4),
+                          (p.topk_weights_offset, M * k * 4),
+                          (p.sorted_ids_offset, p.sorted_rows * 4),
+                          (p.block_expert_offset, p.max_blocks * 4),
+                          (p.expert_offsets_offset, (E + 1) * 4),
+                          (p.num_padded_offset, 4)])
+        for (a, na), (b, _) in zip(regions, regions[1:]):
+            assert a % 256 == 0 and a + na <= b
+        assert regions[-1][0] + regions[-1][1] <= p.workspace_bytes
+        assert list(p.reserved) == [0, 0]
+    # a forced family is reported as such
+    assert moe.fused_plan(0, 4096, 4096, 14336, 8, 2, moe.MOE_REGIME_DECODE).regime == 1
+    assert moe.fused_plan(0, 8, 4096, 14336, 8, 2, moe.MOE_REGIME_PREFILL).regime == 2
