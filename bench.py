@@ -3,17 +3,24 @@
 
 One step = one call of moe_fused_forward (router, permutation, GEMM1 +
 SiLU*up, GEMM2, combine) over one batch of synthetic tokens already resident
-in HBM.  The default workload is the Mixtral-shaped decode batch (M=8 tokens,
-K=4096, N=14336, E=8, top-2, bf16).  W untimed warm-up steps, then exactly K
-steps bracketed by torch.cuda.synchronize(); value = tokens per second.
+in HBM.  A default run times the five workloads of the layer's statement one
+after another: the Mixtral-shaped prefill batch (M=4096 tokens, K=4096,
+N=14336, E=8, top-2, bf16, skewed router) is the headline, and the tiny,
+Mixtral-shaped decode, single-token decode and DeepSeek-V3-shaped FP8
+batches follow under "workloads" with the same fields.  Per workload: W
+untimed warm-up steps, then exactly K steps bracketed by
+torch.cuda.synchronize(); value = tokens per second.
 
 The same K steps are then replayed from HIP graphs captured from the layer
 (graph_ms_per_step, graph_tokens_per_s), the launch mode of a serving loop.
 A third pass of K steps through moe_fused_forward_timed records HIP events
 between the kernels on the stream they run on; the dominant kernel's mean
 duration gives the roofline fraction (algorithmic bytes or FLOPs per launch
-/ duration vs the MI355X peak).  The CPU oracle is timed on this host's
-cores on a bounded sample of the same workload as a reference point.
+/ duration vs the MI355X peak), with the bound taken from the kernel family
+the library's plan reports.  The CPU oracle is timed on this host's cores
+on a bounded sample of the same workload as a reference point, and the
+sample's outputs are checked against it: a run whose output leaves the
+tolerance prints "parity_ok": false and exits with status 1.
 
 Prints ONE JSON line.  Only one GPU is used: --gpus N with N > 1 exits.
 """
@@ -53,11 +60,8 @@ def hip_runtime():
     return hip
 
 
-CPU_SECONDS = 10.0  # oracle work timed for the CPU baseline
-# the library's automatic kernel-family choice (api.cpp): Swap-AB decode
-# kernels up to this many token-slots per expert, full tiles above
-DECODE_MAX_ROWS_PER_EXPERT = 8
-FP8_DECODE_MAX_ROWS_PER_EXPERT = 16   # e4m3 weights (MXFP4: decode kernels only)
+CPU_SECONDS = 10.0        # oracle work timed for the headline workload's CPU baseline
+CPU_SECONDS_EXTRA = 5.0   # and for each of the other workloads of a full run
 COPY_BYTES = 1 << 30
 
 
@@ -239,7 +243,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="mixtral_decode")
+    ap.add_argument("--workload", default="all",
+                    help="one workload, or 'all' (default): the Mixtral-shaped prefill batch as "
+                         "the headline, then the tiny, Mixtral decode, single-token and "
+                         "DeepSeek-shaped FP8 batches under 'workloads'")
     ap.add_argument("--layers", type=int, default=0,
                     help="distinct weight copies stepped round-robin (0 = enough to exceed "
                          "the 256 MB last-level cache several times)")
@@ -287,6 +294,8 @@ def main():
     if args.pmc_summary:
         if len(args.pmc_summary) not in (4, 6):
             ap.error("--pmc-summary takes 4 or 6 CSV paths")
+        if args.workload == "all":
+            ap.error("--pmc-summary takes one --workload")
         pmc_summary(args.workload, *args.pmc_summary)
         return
     if args.gpus != 1:
@@ -300,9 +309,13 @@ def main():
     import moe_layer_04_amd as moe
     from moe_layer_04_amd import workloads as wlm
 
-    if args.workload not in wlm.WORKLOADS:
-        sys.exit(f"unknown workload {args.workload}; one of {list(wlm.WORKLOADS)}")
-    wl = wlm.WORKLOADS[args.workload]
+    if args.workload != "all" and args.workload not in wlm.WORKLOADS:
+        sys.exit(f"unknown workload {args.workload}; 'all' or one of {list(wlm.WORKLOADS)}")
+    if args.workload == "all" and (args.fp8 or args.fp8_rowwise or args.mxfp4 or args.tokens or
+                                   args.regime_sweep or args.pmc_summary):
+        sys.exit("--fp8, --fp8-rowwise, --mxfp4, --tokens, --regime-sweep and --pmc-summary "
+                 "take one --workload")
+    wl = wlm.WORKLOADS["mixtral_prefill" if args.workload == "all" else args.workload]
     if args.fp8 and not wl.fp8:
         wl = wl.resized(name=wl.name + "_fp8", fp8=True)
     if args.fp8_rowwise:
@@ -330,6 +343,55 @@ def main():
         regime_sweep(moe, wlm, wl, dev, args.sweep_tokens)
         return
 
+    hip = hip_runtime()
+    if args.workload == "all":
+        names = ["mixtral_prefill"] + [n for n in wlm.WORKLOADS if n != "mixtral_prefill"]
+        wls = [wlm.WORKLOADS[n] for n in names]
+    else:
+        wls = [wl]
+    records = []
+    for i, w in enumerate(wls):
+        cpu_s = 0.0 if args.no_cpu_baseline else (CPU_SECONDS if i == 0 else CPU_SECONDS_EXTRA)
+        records.append(bench_workload(moe, wlm, w, args, dev, hip, cpu_s))
+        torch.cuda.empty_cache()
+    result = dict(records[0])
+    if len(records) > 1:
+        # the headline is the first (the prefill batch, the matrix-core half of
+        # the metric); the other workloads of the same run follow with the
+        # same fields
+        result["workloads"] = {r["config"]["workload"]: {k: v for k, v in r.items()
+                                                          if k not in HEADLINE_ONLY}
+                               for r in records[1:]}
+    bad = [r["config"]["workload"] for r in records
+           if r.get("parity_vs_oracle") and not r["parity_vs_oracle"]["ok"]]
+    result["parity_ok"] = not bad
+    print(json.dumps(result), flush=True)
+    if bad:
+        log(f"output outside the oracle tolerance on {bad}")
+        sys.exit(1)
+
+
+HEADLINE_ONLY = ("metric", "unit", "n_gpus", "steps", "warmup", "higher_is_better", "scaling",
+                 "vs_baseline", "data")
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def bench_workload(moe, wlm, wl, args, dev, hip, cpu_seconds):
+    """One workload: K timed steps after W warm-up steps, the same steps from
+    captured HIP graphs, a pass with HIP events between the kernels, and the
+    oracle on a bounded sample.  Returns the workload's record."""
+    import numpy as np
+    import torch
+
     log(f"generating {wl}")
     g = wlm.generate(wl, dev)
     wbytes = 0.5 + 1 / 32 if wl.mxfp4 else (1 if wl.fp8 else 2)   # weight + block-scale bytes
@@ -337,6 +399,7 @@ def main():
     dtype = (moe.MOE_MXFP4_E2M1 if wl.mxfp4 else
              moe.MOE_FP8_E4M3_ROWWISE if wl.fp8_rowwise else
              moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
+    plan = moe.fused_plan(dtype, wl.M, wl.K, wl.N, wl.E, wl.topk)
 
     # routing of this batch (for the realised active-expert count)
     ids, _, _ = moe.moe_topk(g["x"], g["w_router"], g["bias"], wl.topk)
@@ -350,8 +413,7 @@ def main():
     w2s = [g["w2"]] + [g["w2"].clone() for _ in range(layers - 1)]
     log(f"active experts {active}, {touched / 1e9:.3f} GB of weights per step, {layers} layer(s)")
 
-    need = moe.workspace_size(dtype, wl.M, wl.K, wl.N, wl.E, wl.topk)
-    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    ws = torch.empty(plan.workspace_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((wl.M, wl.K), dtype=torch.bfloat16, device=dev)
 
     def step(i):
@@ -369,6 +431,7 @@ def main():
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
     tokens_per_s = wl.M * args.steps / elapsed
+    log(f"{wl.name}: {ms_per_step:.4f} ms per step")
 
     # ---- the same steps replayed from captured HIP graphs (one per weight copy)
     graphs = [moe.FusedForwardGraph(g["x"], g["w_router"], g["bias"], w1s[L], w2s[L], wl.topk,
@@ -385,7 +448,6 @@ def main():
     del graphs
 
     # ---- per-kernel durations from HIP events on the layer's stream --------
-    hip = hip_runtime()
     lib = moe.load_library()
     stream = ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
     nev = len(STAGES) + 1
@@ -432,8 +494,11 @@ def main():
                     if wl.fp8 else 0))
     alg_flops = 6.0 * slots * wl.N * wl.K
     step_s = ms_per_step / 1e3
-    decode = (wl.mxfp4 or slots <= (FP8_DECODE_MAX_ROWS_PER_EXPERT if wl.fp8
-                                    else DECODE_MAX_ROWS_PER_EXPERT) * wl.E)
+    # the bound of the dominant kernel follows the kernel family the library
+    # ran (its plan): the Swap-AB decode kernels stream weights, the full
+    # tiles are matrix-core bound
+    decode = plan.regime == moe.MOE_REGIME_DECODE
+    mfma_peak = MFMA_PEAK_TFLOPS["bf16" if dtype_name == "bf16" else "fp8"]
     g1_s = kern_us["gemm1"] / 1e6
     if decode:
         # GEMM1 reads W1 of every active expert once plus the token rows
@@ -446,9 +511,8 @@ def main():
     else:
         g1_flops = 4.0 * slots * wl.N * wl.K
         achieved = g1_flops / g1_s / 1e12
-        peak = MFMA_PEAK_TFLOPS[dtype_name]
         roofline = {"bound": "mfma", "kernel": "gemm1", "achieved": round(achieved, 1),
-                    "peak": peak, "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                    "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4),
                     "traffic": None, "units_per_launch": slots,
                     "flops_per_unit": 4.0 * wl.N * wl.K}
     # HBM traffic from committed counter runs, only while the kernels are unchanged
@@ -478,9 +542,14 @@ def main():
                                if wl.fp8 else "bf16"),
                    "router_bias_var": wl.bias_var, "seed": wl.seed, "layers": layers,
                    "active_experts": active},
+        "kernel_family": "swap-ab decode" if decode else "full tiles",
+        "block_m": plan.block_m,
+        # both fractions of the whole step: algorithmic bytes over the step
+        # time against 8 TB/s, algorithmic FLOPs against the dense MFMA peak
         "step_hbm_GBps": round(alg_bytes / step_s / 1e9, 1),
         "step_hbm_frac": round(alg_bytes / step_s / 1e9 / HBM_PEAK_GBS, 4),
         "step_tflops": round(alg_flops / step_s / 1e12, 2),
+        "step_mfma_frac": round(alg_flops / step_s / 1e12 / mfma_peak, 4),
         "algorithmic_bytes": alg_bytes,
         "algorithmic_flops": alg_flops,
         "kernel_us": {k: round(v, 2) for k, v in kern_us.items()},
@@ -497,7 +566,7 @@ def main():
     }
 
     # ---- CPU oracle on a bounded sample -------------------------------------
-    if not args.no_cpu_baseline:
+    if cpu_seconds > 0:
         import oracle
         n_tok = args.cpu_tokens or min(wl.M, 8)
         toks = list(range(n_tok))
@@ -511,7 +580,7 @@ def main():
         s1 = None if g["w1_scale"] is None else g["w1_scale"].cpu().numpy()
         s2 = None if g["w2_scale"] is None else g["w2_scale"].cpu().numpy()
         log(f"oracle on {n_tok} token(s), {len(need_e)} expert(s)")
-        # the sample is evaluated repeatedly until about CPU_SECONDS of work
+        # the sample is evaluated repeatedly until about cpu_seconds of work
         reps = 0
         t0 = time.perf_counter()
         while True:
@@ -519,21 +588,23 @@ def main():
                                            w2_scale=s2, tokens=toks, fp8=wl.fp8,
                                            mxfp4=wl.mxfp4)
             reps += 1
-            if time.perf_counter() - t0 >= CPU_SECONDS:
+            if time.perf_counter() - t0 >= cpu_seconds:
                 break
         cpu_s = time.perf_counter() - t0
         got = out.float().cpu().numpy()[toks].astype(np.float64)
         den = np.maximum(np.abs(ref).max(axis=1), 1e-300)
         err = float((np.abs(got - ref).max(axis=1) / den).max())
+        tol = 6e-2 if (wl.fp8 or wl.mxfp4) else 2e-2
         result["cpu_baseline"] = {
             "value": round(n_tok * reps / cpu_s, 3), "unit": "tokens/s",
-            "cores": min(oracle.num_threads(), n_tok * wl.topk), "kind": "oracle",
+            "cores": oracle.num_threads(), "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"first {n_tok} of the {wl.M} tokens of the same batch "
                       f"({n_tok * wl.topk} token-slots, fp64), evaluated {reps} times",
             "seconds": round(cpu_s, 3)}
-        result["parity_vs_oracle"] = {"max_row_rel_err": err, "tokens": n_tok,
-                                      "tol": 6e-2 if (wl.fp8 or wl.mxfp4) else 2e-2}
-    print(json.dumps(result), flush=True)
+        result["parity_vs_oracle"] = {"max_row_rel_err": err, "tokens": n_tok, "tol": tol,
+                                      "ok": bool(np.isfinite(got).all() and err <= tol)}
+    del g, w1s, w2s, ws, out
+    return result
 
 
 if __name__ == "__main__":

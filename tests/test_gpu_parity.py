@@ -50,10 +50,14 @@ def gen_small(wl, seed=None):
     return d, g
 
 
-def run_layer(moe, g, wl, regime=0, poison=True):
-    dtype = (moe.MOE_MXFP4_E2M1 if wl.mxfp4 else
-             moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
-    need = moe.workspace_size(dtype, wl.M, wl.K, wl.N, wl.E, wl.topk, regime)
+def dtype_of(moe, wl):
+    return (moe.MOE_MXFP4_E2M1 if wl.mxfp4 else
+            moe.MOE_FP8_E4M3_ROWWISE if wl.fp8_rowwise else
+            moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
+
+
+def run_layer(moe, g, wl, regime=0, poison=True, keep_ws=False):
+    need = moe.workspace_size(dtype_of(moe, wl), wl.M, wl.K, wl.N, wl.E, wl.topk, regime)
     ws = torch.empty(max(need, 256), dtype=torch.uint8, device="cuda")
     if poison:
         ws.fill_(0xFF)   # any read of a never-written workspace byte turns into NaN
@@ -62,7 +66,28 @@ def run_layer(moe, g, wl, regime=0, poison=True):
                           w1_scale=g["w1_scale"], w2_scale=g["w2_scale"], regime=regime,
                           out=out, workspace=ws)
     torch.cuda.synchronize()
-    return out
+    return (out, ws) if keep_ws else out
+
+
+def check_fused_routing(moe, ws, wl, regime, x_bits, wr_bits, bias):
+    """The routing the fused layer itself computed (left in its workspace at
+    the offsets moe_fused_plan reports) against the oracle: logits, top-k ids,
+    the sorted permutation, block owners, offsets and padded count bit for
+    bit, routing weights within 1e-6.  Returns (plan, oracle ids, oracle
+    sorted ids)."""
+    plan = moe.fused_plan(dtype_of(moe, wl), wl.M, wl.K, wl.N, wl.E, wl.topk, regime)
+    r = {k: v.cpu().numpy() for k, v in moe.fused_routing(ws, plan, wl.M, wl.E, wl.topk).items()}
+    rlg = oracle.logits(x_bits, wr_bits, bias)
+    assert np.array_equal(r["logits"], rlg), "fused logits"
+    rids, rw = oracle.topk(rlg, wl.topk)
+    assert np.array_equal(r["topk_ids"], rids), "fused top-k ids"
+    assert np.abs(r["topk_weights"] - rw).max() <= TOL_WEIGHTS, "fused routing weights"
+    rs, rb, ro, rn = oracle.align(rids, wl.E, plan.block_m)
+    assert int(r["num_padded"][0]) == rn, "fused num_padded"
+    assert np.array_equal(r["expert_offsets"], ro), "fused expert_offsets"
+    assert np.array_equal(r["block_expert"], rb), "fused block_expert"
+    assert np.array_equal(r["sorted_ids"], rs), "fused sorted_ids"
+    return plan, rids, rs
 
 
 def oracle_layer(d, wl, tokens=None):
@@ -302,12 +327,15 @@ def test_fused_small(moe, case):
     wl = wlm.Workload(name, M=M, K=K, N=N, E=E, topk=k, fp8=fp8, fp8_rowwise=rowwise,
                       mxfp4=mx, bias_var=bias_var, seed=3)
     d, g = gen_small(wl)
-    out = run_layer(moe, g, wl, regime)
+    out, ws = run_layer(moe, g, wl, regime, keep_ws=True)
+    plan, _, _ = check_fused_routing(moe, ws, wl, regime, bits(d["x"]), bits(d["w_router"]),
+                                     None if d["bias"] is None else d["bias"].numpy())
     ref, _, _ = oracle_layer(d, wl)
     got = out_f64(out)
     assert np.isfinite(got).all()
     err = row_rel_err(got, ref)
-    note(f"  err={err:.3e}")
+    note(f"  routing bit-exact (family {plan.regime}, block {plan.block_m}, "
+         f"logit splits {plan.logit_splits}); err={err:.3e}")
     assert err <= (TOL_FP8 if (fp8 or mx) else TOL_BF16)
 
 
@@ -331,7 +359,9 @@ def test_fused_tiny_routing_ties(moe, M, E, fp8):
             wr[E - 2] = wr[0]
         d["w_router"] = wr
         g["w_router"] = wr.cuda()
-        got = out_f64(run_layer(moe, g, wl))
+        out, ws = run_layer(moe, g, wl, keep_ws=True)
+        got = out_f64(out)
+        check_fused_routing(moe, ws, wl, 0, bits(d["x"]), bits(wr), None)
         ref, ids, _ = oracle_layer(d, wl)
         if dup == "all":
             assert np.array_equal(np.asarray(ids).reshape(M, 2), np.tile([0, 1], (M, 1)))
@@ -402,12 +432,32 @@ def test_fused_deterministic(moe):
 # times; the oracle evaluates sampled tokens one by one
 # --------------------------------------------------------------------------
 
-def sample_tokens(M, n=6):
-    if M <= n:
-        return list(range(M))
+def stratified_tokens(rids, E, B, M, k, n_min=64, max_experts=16):
+    """Tokens whose slots sit at telling rows of the token blocks: in the
+    segment of every expert (of at most max_experts, evenly spaced among
+    those routed to) the first row, the rows either side of the block middle
+    (the two halves of a 256-row block are different token waves) and the
+    last row of the first, a middle and the last (padded) block, then random
+    tokens up to n_min, plus the first and last token."""
+    rs, _, ro, _ = oracle.align(rids, E, B)
+    counts = np.bincount(rids.reshape(-1), minlength=E)
     rng = np.random.default_rng(M)
-    mid = sorted(rng.choice(np.arange(1, M - 1), size=n - 2, replace=False).tolist())
-    return [0] + mid + [M - 1]
+    toks = {0, M - 1}
+    used = [e for e in range(E) if counts[e] > 0]
+    n_pick = min(max_experts, len(used))
+    pick = [used[i * len(used) // n_pick] for i in range(n_pick)]
+    for e in pick:
+        c = int(counts[e])
+        nblk = (c + B - 1) // B
+        for b in sorted({0, nblk // 2, nblk - 1}):
+            for off in (0, B // 2 - 1, B // 2, B - 1):
+                r = b * B + off
+                if r < c:
+                    toks.add(int(rs[ro[e] + r]) // k)
+        toks.add(int(rs[ro[e] + c - 1]) // k)
+    while len(toks) < n_min:
+        toks.add(int(rng.integers(M)))
+    return sorted(toks)
 
 
 # the DeepSeek-shaped batch also with per-channel e4m3 weight scales and with
@@ -431,22 +481,27 @@ def test_fused_full_size_sampled(moe, name):
         wl = wlm.WORKLOADS[name]
     note(f"full size {name}: generate on GPU")
     g = wlm.generate(wl, "cuda")
-    out = run_layer(moe, g, wl, poison=False)
+    out, ws = run_layer(moe, g, wl, keep_ws=True)
     got = out_f64(out)
+    # the workspace was poisoned: a partial row never written would be NaN here
     assert np.isfinite(got).all()
-    # routing of every token is bit-exact with the oracle
-    ids, _, lg = moe.moe_topk(g["x"], g["w_router"], g["bias"], wl.topk)
-    torch.cuda.synchronize()
     x_h, wr_h = bits(g["x"]), bits(g["w_router"])
     bias_h = None if g["bias"] is None else g["bias"].cpu().numpy()
-    rlg = oracle.logits(x_h, wr_h, bias_h)
-    assert np.array_equal(lg.cpu().numpy(), rlg)
-    rids, _ = oracle.topk(rlg, wl.topk)
+    # the layer's own routing of every token is bit-exact with the oracle
+    plan, rids, _ = check_fused_routing(moe, ws, wl, 0, x_h, wr_h, bias_h)
+    del ws
+    # and so is the standalone router on the same batch
+    ids, _, lg = moe.moe_topk(g["x"], g["w_router"], g["bias"], wl.topk)
+    torch.cuda.synchronize()
     assert np.array_equal(ids.cpu().numpy(), rids)
-    # sampled tokens through the oracle, with only their experts copied to the host
-    toks = sample_tokens(wl.M)
+    # every token for the decode batches (at most 128 tokens), else tokens at
+    # the telling rows of every expert's blocks through the oracle
+    if wl.M <= 128:
+        toks = list(range(wl.M))
+    else:
+        toks = stratified_tokens(rids, wl.E, plan.block_m, wl.M, wl.topk)
     need = sorted(set(rids[toks].reshape(-1).tolist()))
-    note(f"  oracle on tokens {toks}, {len(need)} experts")
+    note(f"  oracle on {len(toks)} tokens, {len(need)} experts (block {plan.block_m})")
     w1 = [bits(g["w1"][e]) if e in need else None for e in range(wl.E)]
     w2 = [bits(g["w2"][e]) if e in need else None for e in range(wl.E)]
     s1 = None if g["w1_scale"] is None else g["w1_scale"].cpu().numpy()
@@ -456,5 +511,5 @@ def test_fused_full_size_sampled(moe, name):
     err = row_rel_err(got[toks], ref)
     note(f"  err={err:.3e}")
     assert err <= (TOL_FP8 if (wl.fp8 or wl.mxfp4) else TOL_BF16)
-    del g
+    del g, w1, w2
     torch.cuda.empty_cache()
