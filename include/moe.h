@@ -27,9 +27,10 @@
  * Conventions shared by every entry point:
  *   - Every pointer argument is a DEVICE pointer owned by the caller, except
  *     the size_t* of moe_fused_forward, which is a host pointer.  The library
- *     never allocates, frees or keeps device memory, keeps no mutable global
- *     state and is re-entrant; calls on different streams may overlap as long
- *     as their buffers do not.
+ *     never allocates or frees device memory and is re-entrant; calls on
+ *     different streams may overlap as long as their buffers do not.  The
+ *     one exception is moe_fused_forward_noalloc, whose scratch is a static
+ *     device array of the library (one per GPU, see there).
  *   - All work is enqueued asynchronously on `stream` (a hipStream_t; NULL is
  *     the default stream).  The library never synchronises the host.
  *   - Arguments are validated before any HIP call, so every error path is
@@ -313,6 +314,36 @@ typedef struct {
 
 moe_status moe_fused_plan(int dtype, int M, int K, int N, int E, int topk, int regime,
                           moe_plan *plan);
+
+/*
+ * moe_fused_forward_noalloc -- moe_fused_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, no allocation,
+ * no allocating library call.  The scratch is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES inside the library; every GPU the library runs
+ * on holds its own copy until the process ends.  Its device address is
+ * looked up (hipGetSymbolAddress) on the first call on each device, with
+ * that device current.
+ *
+ *   arguments as moe_fused_forward (regime automatic), without workspace
+ *
+ * The scratch keeps the last call's contents; every value the layer reads
+ * from it is written earlier in the same call.  Calls that overlap on one
+ * GPU (different streams, or different host threads) share the one array
+ * and race: the caller must order them, e.g. on a single stream.  The
+ * routing outputs of the last call can be read at the offsets
+ * moe_fused_plan reports, relative to the array.
+ *
+ * Errors: as moe_fused_forward; WORKSPACE when the shape needs more than
+ * MOE_NOALLOC_SCRATCH_BYTES (moe_fused_plan reports the size); HIP when the
+ * array's address cannot be obtained; UNSUPPORTED on a device ordinal >= 64.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES (128u << 20)
+moe_status moe_fused_forward_noalloc(const void *x, const void *w_router,
+                                     const float *router_bias, const void *w1, const void *w2,
+                                     const void *w1_scale, const void *w2_scale, int dtype,
+                                     int M, int K, int N, int E, int topk, void *out,
+                                     void *stream);
 
 /* Static, NUL-terminated name of a status code. */
 const char *moe_status_string(int status);

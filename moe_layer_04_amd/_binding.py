@@ -36,7 +36,9 @@ MOE_REGIME_PREFILL = 2
 
 EXPORTS = ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3", "moe_fused_forward",
            "moe_fused_forward_ex", "moe_fused_forward_timed", "moe_fused_plan",
-           "moe_status_string")
+           "moe_fused_forward_noalloc", "moe_status_string")
+
+NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
 
 class Plan(ctypes.Structure):
@@ -85,9 +87,10 @@ def load_library(build_if_missing: bool = False):
         lib.moe_fused_forward_timed.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
                                                 SZP, P, P]
         lib.moe_fused_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(Plan)]
+        lib.moe_fused_forward_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
         for name in ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3",
                      "moe_fused_forward", "moe_fused_forward_ex", "moe_fused_forward_timed",
-                     "moe_fused_plan"):
+                     "moe_fused_plan", "moe_fused_forward_noalloc"):
             getattr(lib, name).restype = ctypes.c_int
         lib.moe_status_string.argtypes = [I]
         lib.moe_status_string.restype = ctypes.c_char_p
@@ -310,6 +313,38 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
                                     topk, regime, _ptr(out), _ptr(workspace),
                                     ctypes.byref(nbytes), _stream(dev)),
            "moe_fused_forward")
+    return out
+
+
+def moe_fused_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor,
+                              router_bias: Optional[torch.Tensor], w1: torch.Tensor,
+                              w2: torch.Tensor, topk: int, *,
+                              w1_scale: Optional[torch.Tensor] = None,
+                              w2_scale: Optional[torch.Tensor] = None,
+                              out: Optional[torch.Tensor] = None) -> torch.Tensor:
+    """The layer through moe_fused_forward_noalloc: the library's static
+    per-device scratch instead of a workspace (shapes whose plan needs more
+    than NOALLOC_SCRATCH_BYTES raise MoEError with MOE_ERR_WORKSPACE).
+    Only ``out`` may be allocated here, when not given."""
+    lib = load_library()
+    dtype = _weight_dtype(w1, w1_scale)
+    M, K = x.shape
+    E, twoN, _ = w1.shape
+    N = twoN // 2
+    _dev(x, "x", torch.bfloat16)
+    _dev(w_router, "w_router", torch.bfloat16, (E, K))
+    _dev(w1, "w1")
+    _dev(w2, "w2")
+    for t, name in ((router_bias, "router_bias"), (w1_scale, "w1_scale"), (w2_scale, "w2_scale")):
+        if t is not None:
+            _dev(t, name)
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=x.device)
+    _dev(out, "out", torch.bfloat16, (M, K))
+    _check(lib.moe_fused_forward_noalloc(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1),
+                                         _ptr(w2), _ptr(w1_scale), _ptr(w2_scale), dtype, M, K,
+                                         N, E, topk, _ptr(out), _stream(x.device)),
+           "moe_fused_forward_noalloc")
     return out
 
 

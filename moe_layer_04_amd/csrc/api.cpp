@@ -13,6 +13,7 @@
 //   7 combine into bf16 out
 #include <cmath>
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stdint.h>
 #include <string.h>
 
@@ -313,6 +314,16 @@ MOE_API moe_status moe_fused_plan(int dtype, int M, int K, int N, int E, int top
     return MOE_OK;
 }
 
+// Required tensors present and 16-byte aligned.
+static bool fused_ptrs_ok(const void* x, const void* w_router, const float* router_bias,
+                          const void* w1, const void* w2, const void* w1_scale,
+                          const void* w2_scale, const void* out) {
+    if (!x || !w_router || !w1 || !w2 || !out) return false;
+    return !(misaligned(x) || misaligned(w_router) || misaligned(router_bias) ||
+             misaligned(w1) || misaligned(w2) || misaligned(w1_scale) || misaligned(w2_scale) ||
+             misaligned(out));
+}
+
 static moe_status fused_impl(const void* x, const void* w_router, const float* router_bias,
                              const void* w1, const void* w2, const void* w1_scale,
                              const void* w2_scale, int dtype, int M, int K, int N, int E,
@@ -334,9 +345,7 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         return MOE_OK;
     }
     if (M == 0) return MOE_OK;
-    if (!x || !w_router || !w1 || !w2 || !out) return MOE_ERR_INVALID_ARG;
-    if (misaligned(x) || misaligned(w_router) || misaligned(router_bias) || misaligned(w1) ||
-        misaligned(w2) || misaligned(w1_scale) || misaligned(w2_scale) || misaligned(out) ||
+    if (!fused_ptrs_ok(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, out) ||
         ((uintptr_t)workspace & (kAlign - 1)))
         return MOE_ERR_INVALID_ARG;
     if (*workspace_bytes < p.total) return MOE_ERR_WORKSPACE;
@@ -484,4 +493,58 @@ MOE_API moe_status moe_fused_forward(const void* x, const void* w_router,
     return moe_fused_forward_ex(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K,
                                 N, E, topk, MOE_REGIME_AUTO, out, workspace, workspace_bytes,
                                 stream);
+}
+
+// ---------------------------------------------------------------------------
+// The fused forward without a caller workspace, for callers that cannot
+// allocate device memory.  Its scratch is a file-scope device array: every
+// GPU the library runs on holds one copy (kNoAllocScratchBytes) until the
+// process ends.  In host code `scratch` only names the symbol; the device
+// address of the current GPU's copy comes from hipGetSymbolAddress, taken
+// once per device on the first call there and kept in g_scratch.
+// ---------------------------------------------------------------------------
+namespace moe {
+// external linkage (hidden by the library's default visibility), so the
+// runtime registers it under a stable name for hipGetSymbolAddress
+__device__ __attribute__((aligned(256))) char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+}  // namespace moe
+
+namespace {
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+constexpr int kMaxDevices = 64;
+void* g_scratch[kMaxDevices];
+hipError_t g_scratch_rc[kMaxDevices];
+std::once_flag g_scratch_once[kMaxDevices];
+}  // namespace
+
+MOE_API moe_status moe_fused_forward_noalloc(const void* x, const void* w_router,
+                                             const float* router_bias, const void* w1,
+                                             const void* w2, const void* w1_scale,
+                                             const void* w2_scale, int dtype, int M, int K,
+                                             int N, int E, int topk, void* out, void* stream) {
+    // the plan's size first: argument errors and oversized shapes are
+    // reported before any HIP call
+    size_t need = 0;
+    {
+        const moe_status st = fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale,
+                                         dtype, M, K, N, E, topk, MOE_REGIME_AUTO, out, nullptr,
+                                         &need, stream, nullptr, false);
+        if (st != MOE_OK) return st;
+    }
+    if (need > kNoAllocScratchBytes) return MOE_ERR_WORKSPACE;
+    if (M == 0) return MOE_OK;
+    if (!fused_ptrs_ok(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, out))
+        return MOE_ERR_INVALID_ARG;
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0) return MOE_ERR_HIP;
+    if (dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::call_once(g_scratch_once[dev], [dev]() {
+        void* ptr = nullptr;
+        g_scratch_rc[dev] = hipGetSymbolAddress(&ptr, HIP_SYMBOL(moe::scratch));
+        g_scratch[dev] = g_scratch_rc[dev] == hipSuccess ? ptr : nullptr;
+    });
+    if (g_scratch_rc[dev] != hipSuccess || !g_scratch[dev]) return MOE_ERR_HIP;
+    size_t have = kNoAllocScratchBytes;
+    return fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K, N, E,
+                      topk, MOE_REGIME_AUTO, out, g_scratch[dev], &have, stream, nullptr, false);
 }

@@ -218,3 +218,27 @@ def test_fused_plan(lib):
     # a forced family is reported as such
     assert moe.fused_plan(0, 4096, 4096, 14336, 8, 2, moe.MOE_REGIME_DECODE).regime == 1
     assert moe.fused_plan(0, 8, 4096, 14336, 8, 2, moe.MOE_REGIME_PREFILL).regime == 2
+
+
+def test_noalloc_validation(lib):
+    """moe_fused_forward_noalloc rejects bad arguments and shapes whose plan
+    needs more than its static scratch before any HIP call."""
+    f = lib.moe_fused_forward_noalloc
+
+    def call(x=FAKE, wr=FAKE, w1=FAKE, w2=FAKE, s1=None, s2=None, dtype=0, M=8, K=256, N=512,
+             E=8, k=2, out=FAKE):
+        return f(x, wr, None, w1, w2, s1, s2, dtype, M, K, N, E, k, out, None)
+
+    assert call(M=-1) == B.MOE_ERR_INVALID_ARG
+    assert call(K=200) == B.MOE_ERR_UNSUPPORTED
+    assert call(dtype=1) == B.MOE_ERR_INVALID_ARG                   # e4m3 without scales
+    assert call(x=None) == B.MOE_ERR_INVALID_ARG
+    assert call(out=MISALIGNED) == B.MOE_ERR_INVALID_ARG
+    assert call(M=0, x=None, out=None) == B.MOE_OK                  # no-op
+    # the Mixtral-shaped prefill batch needs ~536 MiB of scratch: rejected
+    p = moe.fused_plan(0, 4096, 4096, 14336, 8, 2)
+    assert p.workspace_bytes > B.NOALLOC_SCRATCH_BYTES
+    assert call(M=4096, K=4096, N=14336, E=8, k=2) == B.MOE_ERR_WORKSPACE
+    # the decode batches fit
+    for dt, M, K, N, E, k in ((0, 8, 4096, 14336, 8, 2), (0, 1, 4096, 8192, 16, 2)):
+        assert moe.fused_plan(dt, M, K, N, E, k).workspace_bytes <= B.NOALLOC_SCRATCH_BYTES
