@@ -99,7 +99,8 @@ def _request_bytes(path):
 
 def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
                 req_csv=None, copy_req_csv=None):
-    """Per-dispatch HBM traffic of the GEMM1 kernel from counter CSVs.
+    """Per-dispatch HBM traffic of the dominant kernel (GEMM1, for one or two
+    tokens the GEMM1 that also routes) from counter CSVs.
 
     Each counter is scaled by what it reads for the plain copy of COPY_BYTES.
     FETCH_SIZE counts a 128-byte read request as 64 bytes on this GPU, so its
@@ -116,7 +117,9 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
     w_scale = COPY_BYTES / (copy_w * 1024)
     kf = _pmc_rows(fetch_csv, "FETCH_SIZE")
     kw = _pmc_rows(write_csv, "WRITE_SIZE")
+    # the dominant kernel: GEMM1 (for one or two tokens the one that also routes)
     name = next(k for k in kf if "gemm1" in k)
+    tag = "route_gemm1" if "route_gemm1" in name else "gemm1"
     fetch_counter = statistics.median(kf[name]) * 1024
     fetch = fetch_counter * f_scale
     write = statistics.median(kw[name]) * 1024 * w_scale
@@ -130,7 +133,7 @@ def pmc_summary(workload, fetch_csv, write_csv, copy_fetch_csv, copy_write_csv,
         rec["fetch_scale_kernel"] = fetch / fetch_counter
     rec.update({"fetch_bytes_per_launch": fetch, "write_bytes_per_launch": write,
                 "bytes_per_launch": fetch + write, "source_digest": kernel_digest()})
-    path = os.path.join(ROOT, "profiles", f"gemm1_{workload}_pmc.json")
+    path = os.path.join(ROOT, "profiles", f"{tag}_{workload}_pmc.json")
     with open(path, "w") as f:
         json.dump(rec, f, indent=1)
     print(json.dumps(rec))
@@ -485,6 +488,11 @@ def bench_workload(moe, wlm, wl, args, dev, hip, cpu_seconds):
         for j in range(nev):
             hip.hipEventDestroy(arr[j])
     kern_us = {s: float(np.mean(v)) * 1e3 for s, v in stage_ms.items()}
+    if plan.fused_decode:
+        # three launches: router + top-k + align + GEMM1 in one kernel
+        # (recorded as the first stage; stages 2-5 are empty), GEMM2, combine
+        kern_us = {"route_gemm1": kern_us["router_logits"], "gemm2": kern_us["gemm2"],
+                   "combine": kern_us["combine"]}
 
     # ---- algorithmic work and roofline --------------------------------------
     slots = wl.M * wl.topk
@@ -499,16 +507,18 @@ def bench_workload(moe, wlm, wl, args, dev, hip, cpu_seconds):
     # tiles are matrix-core bound
     decode = plan.regime == moe.MOE_REGIME_DECODE
     mfma_peak = MFMA_PEAK_TFLOPS["bf16" if dtype_name == "bf16" else "fp8"]
-    g1_s = kern_us["gemm1"] / 1e6
     if decode:
+        g1_s = kern_us["route_gemm1" if plan.fused_decode else "gemm1"] / 1e6
         # GEMM1 reads W1 of every active expert once plus the token rows
         g1_bytes = active * w1_e + wl.M * wl.K * (1 if (wl.fp8 or wl.mxfp4) else 2)
         achieved = g1_bytes / g1_s / 1e9
-        roofline = {"bound": "hbm", "kernel": "gemm1", "achieved": round(achieved, 1),
+        roofline = {"bound": "hbm", "kernel": "route_gemm1" if plan.fused_decode else "gemm1",
+                    "achieved": round(achieved, 1),
                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
                     "units_per_launch": active, "bytes_per_unit": w1_e}
     else:
+        g1_s = kern_us["gemm1"] / 1e6
         g1_flops = 4.0 * slots * wl.N * wl.K
         achieved = g1_flops / g1_s / 1e12
         roofline = {"bound": "mfma", "kernel": "gemm1", "achieved": round(achieved, 1),
@@ -517,7 +527,7 @@ def bench_workload(moe, wlm, wl, args, dev, hip, cpu_seconds):
                     "flops_per_unit": 4.0 * wl.N * wl.K}
     # HBM traffic from committed counter runs, only while the kernels are unchanged
     digest = kernel_digest()
-    pmc = os.path.join(ROOT, "profiles", f"gemm1_{wl.name}_pmc.json")
+    pmc = os.path.join(ROOT, "profiles", f"{roofline['kernel']}_{wl.name}_pmc.json")
     if os.path.exists(pmc):
         rec = json.load(open(pmc))
         if rec.get("source_digest") == digest:
@@ -542,7 +552,8 @@ def bench_workload(moe, wlm, wl, args, dev, hip, cpu_seconds):
                                if wl.fp8 else "bf16"),
                    "router_bias_var": wl.bias_var, "seed": wl.seed, "layers": layers,
                    "active_experts": active},
-        "kernel_family": "swap-ab decode" if decode else "full tiles",
+        "kernel_family": ("swap-ab decode, routing inside GEMM1" if plan.fused_decode else
+                          "swap-ab decode" if decode else "full tiles"),
         "block_m": plan.block_m,
         # both fractions of the whole step: algorithmic bytes over the step
         # time against 8 TB/s, algorithmic FLOPs against the dense MFMA peak

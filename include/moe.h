@@ -301,7 +301,10 @@ typedef struct {
     int32_t max_blocks;    /* entries of block_expert: sorted_rows / block_m */
     int32_t gemm2_splits;  /* GEMM2 reduction split into fp32 partial rows */
     int32_t logit_splits;  /* router reduction split (fp64 partials) */
-    int32_t reserved[2];   /* zero */
+    int32_t fused_decode;  /* 1: one or two tokens with bf16 weights, the router
+                              (logits, top-k, align) computed inside the GEMM1 launch:
+                              three launches instead of five */
+    int32_t reserved;      /* zero */
     uint64_t workspace_bytes;
     uint64_t logits_offset;          /* byte offsets into the workspace */
     uint64_t topk_ids_offset;

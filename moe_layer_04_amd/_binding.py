@@ -47,7 +47,7 @@ class Plan(ctypes.Structure):
     _fields_ = [("regime", ctypes.c_int32), ("block_m", ctypes.c_int32),
                 ("sorted_rows", ctypes.c_int32), ("max_blocks", ctypes.c_int32),
                 ("gemm2_splits", ctypes.c_int32), ("logit_splits", ctypes.c_int32),
-                ("reserved", ctypes.c_int32 * 2),
+                ("fused_decode", ctypes.c_int32), ("reserved", ctypes.c_int32),
                 ("workspace_bytes", ctypes.c_uint64), ("logits_offset", ctypes.c_uint64),
                 ("topk_ids_offset", ctypes.c_uint64), ("topk_weights_offset", ctypes.c_uint64),
                 ("sorted_ids_offset", ctypes.c_uint64), ("block_expert_offset", ctypes.c_uint64),

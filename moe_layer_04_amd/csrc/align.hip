@@ -54,11 +54,7 @@ __global__ __launch_bounds__(kAlignThreads) void topk_align_kernel(
 
 // ---------------------------------------------------------------------------
 // The same top-k + align for one or two tokens in a single wave (no
-// workgroup barriers, a 64-thread launch): lane p holds slot p; an LDS
-// histogram, the padded exclusive scan over the experts (four per lane),
-// then each slot's rank among earlier slots of its expert from 8 ballots
-// over the expert-id bits.  The order is the stable one of the workgroup
-// version, so the results are identical.
+// workgroup barriers, a 64-thread launch); the align is align_wave.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(kWave) void topk_align_wave_kernel(
     const float* __restrict__ logits, const uint16_t* __restrict__ x, int M, int K, int E,
@@ -70,9 +66,6 @@ __global__ __launch_bounds__(kWave) void topk_align_wave_kernel(
     __shared__ int32_t sid[kWave];
     __shared__ int cnt[MOE_KERNEL_MAX_EXPERTS];
     __shared__ int off[MOE_KERNEL_MAX_EXPERTS + 1];
-    const int lane = lane_id();
-    for (int i = lane; i < zero_words; i += kWave) zero_buf[i] = 0u;
-    for (int e = lane; e < E; e += kWave) cnt[e] = 0;
     if (xq)
         for (int t = 0; t < M; ++t)
             quant_row_wave(x + (size_t)t * K, K, xq + (size_t)t * K, xscale + t);
@@ -80,78 +73,8 @@ __global__ __launch_bounds__(kWave) void topk_align_wave_kernel(
         topk_wave(logits + (size_t)t * E, E, topk, topk_ids + (size_t)t * topk,
                   topk_weights + (size_t)t * topk, sid + t * topk);
     __syncthreads();  // one wave: orders the LDS writes above before the reads below
-    const int n = M * topk;
-    const bool valid = lane < n;
-    const int e = valid ? min(max(sid[lane], 0), E - 1) : 0;
-    if (valid) atomicAdd(&cnt[e], 1);
-    __syncthreads();
-    {
-        int v[4], sum = 0;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ex = lane * 4 + q;
-            v[q] = (ex < E) ? (cnt[ex] + B - 1) / B * B : 0;
-            sum += v[q];
-        }
-        int incl = sum;
-#pragma unroll
-        for (int d = 1; d < kWave; d <<= 1) {
-            const int o = __shfl_up(incl, d);
-            if (lane >= d) incl += o;
-        }
-        int base = incl - sum;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-            const int ex = lane * 4 + q;
-            if (ex < E) off[ex] = base;
-            base += v[q];
-        }
-        if (lane == kWave - 1) off[E] = incl;
-    }
-    __syncthreads();
-    for (int ex = lane; ex <= E; ex += kWave) expert_offsets[ex] = off[ex];
-    const int npad = off[E];
-    if (lane == 0) *num_padded = npad;
-    // sentinels: padding inside a segment and everything past npad
-    for (int i = lane; i < cap; i += kWave) {
-        bool pad = (i >= npad);
-        if (!pad) {
-            int lo = 0, hi = E - 1;  // last expert with off <= i
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= i) lo = mid; else hi = mid - 1;
-            }
-            pad = (i - off[lo]) >= cnt[lo];
-        }
-        if (pad) sorted_ids[i] = n;
-    }
-    for (int b = lane; b < cap / B; b += kWave) {
-        const int i = b * B;
-        int owner = -1;
-        if (i < npad) {
-            int lo = 0, hi = E - 1;
-            while (lo < hi) {
-                const int mid = (lo + hi + 1) >> 1;
-                if (off[mid] <= i) lo = mid; else hi = mid - 1;
-            }
-            owner = lo;
-        }
-        block_expert[b] = owner;
-    }
-    // stable scatter: rank among the earlier slots of the same expert
-    uint64_t match = __ballot(valid);
-#pragma unroll
-    for (int b = 0; b < 8; ++b) {
-        const bool bit = (e >> b) & 1;
-        const uint64_t bb = __ballot(valid && bit);
-        match &= bit ? bb : ~bb;
-    }
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    if (valid) {
-        const int pos = off[e] + __popcll(match & lt_mask);
-        sorted_ids[pos] = lane;
-        if (inv) inv[lane] = pos;
-    }
+    align_wave(sid, M * topk, E, B, cap, cnt, off, sorted_ids, block_expert, expert_offsets,
+               num_padded, zero_buf, zero_words, inv);
 }
 
 // ---------------------------------------------------------------------------

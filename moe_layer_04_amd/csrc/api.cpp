@@ -43,6 +43,7 @@ struct Plan {
     int grid_blocks = 0;
     int nsplit = 1;      // GEMM2 reduction split (decode)
     int lsplit = 1;      // router-logit reduction split (fp64 partials in lpart)
+    bool fused = false;  // bf16, one or two tokens: the two-launch decode
     size_t lpart = 0;
     size_t logits = 0, ids = 0, wts = 0, sorted = 0, bexp = 0, offs = 0, npad = 0;
     size_t inv = 0;  // FP8 activations: sorted position of each slot
@@ -59,6 +60,10 @@ bool is_fp8(int dtype) {
 Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     Plan p;
     const long slots = (long)M * topk;
+    // the automatic choice routes one or two tokens with bf16 weights inside
+    // the GEMM1 launch; a forced family keeps the separate routing kernels
+    p.fused = regime == MOE_REGIME_AUTO && dtype == MOE_BF16 &&
+              moe::decode_fused_fits(M, K, N, E, topk);
     if (regime == MOE_REGIME_AUTO) {
         // MXFP4 weights have only the decode kernels
         const long rows = dtype == MOE_BF16 ? moe::tune::kDecodeMaxRowsPerExpert
@@ -77,6 +82,8 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
         p.block = moe::kPrefillSmallRows;
     // larger decode blocks when experts receive more rows (sized in tuning.hpp)
     if (regime == MOE_REGIME_DECODE) p.block = moe::tune::decode_block_rows(slots, E);
+    // the routing GEMM1 gives every routed expert one 16-row block
+    if (p.block != kDecodeBlock) p.fused = false;
     p.cap = (int)(slots + (long)E * (p.block - 1));
     p.max_blocks = p.cap / p.block;
     {
@@ -138,7 +145,8 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     } else {
         p.act = take((size_t)p.cap * N * 2);
     }
-    p.ypart = take((size_t)p.nsplit * slots * K * 4);
+    if (p.fused) p.nsplit = 1;  // GEMM2 and the combine in one launch: no partial rows
+    else p.ypart = take((size_t)p.nsplit * slots * K * 4);
     p.total = o;
     return p;
 }
@@ -303,6 +311,7 @@ MOE_API moe_status moe_fused_plan(int dtype, int M, int K, int N, int E, int top
     plan->max_blocks = p.max_blocks;
     plan->gemm2_splits = p.nsplit;
     plan->logit_splits = p.lsplit;
+    plan->fused_decode = p.fused ? 1 : 0;
     plan->workspace_bytes = p.total;
     plan->logits_offset = p.logits;
     plan->topk_ids_offset = p.ids;
@@ -378,6 +387,19 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
     const int amax_words = fp8 ? p.cap : 0;
     int32_t* inv = fp8 ? (int32_t*)(ws + p.inv) : nullptr;
     mark(0);
+    if (p.fused) {
+        // router, top-k, align and GEMM1 + SiLU*up in one launch, then GEMM2
+        // and the combine in another
+        void* act = ws + p.act;
+        moe::launch_decode_route_gemm1_bf16(x, w_router, router_bias, w1, M, K, N, E, topk, p.cap,
+                                            logits, ids, wts, sorted, bexp, offs, npad, act, s);
+        for (int i = 1; i <= 5; ++i) mark(i);
+        moe::launch_decode_gemm2_combine_bf16(act, w2, wts, sorted, bexp, M, K, N, E, topk, p.cap,
+                                              out, s);
+        mark(6);
+        mark(7);
+        return finish_launches();
+    }
     if (moe::topk_align_fits(M, topk)) {
         // the FP8 token codes go with top-k + align when the tokens are few
         // and short (a wave per token there; a workgroup per token otherwise)

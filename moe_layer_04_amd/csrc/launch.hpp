@@ -131,4 +131,21 @@ void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const v
 void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
                     hipStream_t s);
 
+// Router (logits, top-k), align (16-row blocks) and GEMM1 + SiLU*up of one
+// or two tokens with bf16 weights in one launch (decode_fused.hip): logits
+// [M,E], ids / weights [M*topk], the align outputs and act [cap,N] bf16 as
+// the separate launches write them.
+bool decode_fused_fits(int M, int K, int N, int E, int topk);
+void launch_decode_route_gemm1_bf16(const void* x, const void* wr, const float* bias,
+                                    const void* w1, int M, int K, int N, int E, int topk, int cap,
+                                    float* logits, int32_t* ids, float* wts, int32_t* sorted_ids,
+                                    int32_t* block_expert, int32_t* expert_offsets,
+                                    int32_t* num_padded, void* act, hipStream_t s);
+// GEMM2 and the combine of those tokens in one launch (no partial rows):
+// out [M,K] bf16 from act, the block owners and the routing weights.
+void launch_decode_gemm2_combine_bf16(const void* act, const void* w2, const float* topk_w,
+                                      const int32_t* sorted_ids, const int32_t* block_expert,
+                                      int M, int K, int N, int E, int topk, int cap, void* out,
+                                      hipStream_t s);
+
 }  // namespace moe

@@ -258,4 +258,99 @@ __device__ __forceinline__ void align_body(AlignShared& sh, const int32_t* ids, 
     }
 }
 
+// ---------------------------------------------------------------------------
+// The align of at most 64 slots by one wave (no workgroup barriers): lane p
+// holds slot p of sid (LDS); an LDS histogram in cnt, the padded exclusive
+// scan over the experts (four per lane) in off, then each slot's rank among
+// earlier slots of its expert from 8 ballots over the expert-id bits.  The
+// order is the stable one of align_body, so the results are identical.
+// cnt [E] and off [E+1] are LDS arrays of the caller.  Wave-uniform call.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void align_wave(const int32_t* sid, int n, int E, int B, int cap,
+                                           int* cnt, int* off, int32_t* __restrict__ sorted_ids,
+                                           int32_t* __restrict__ block_expert,
+                                           int32_t* __restrict__ expert_offsets,
+                                           int32_t* __restrict__ num_padded,
+                                           uint32_t* __restrict__ zero_buf, int zero_words,
+                                           int32_t* __restrict__ inv) {
+    const int lane = lane_id();
+    for (int i = lane; i < zero_words; i += kWave) zero_buf[i] = 0u;
+    for (int e = lane; e < E; e += kWave) cnt[e] = 0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    const bool valid = lane < n;
+    const int e = valid ? min(max(sid[lane], 0), E - 1) : 0;
+    if (valid) atomicAdd(&cnt[e], 1);
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    {
+        int v[4], sum = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ex = lane * 4 + q;
+            v[q] = (ex < E) ? (cnt[ex] + B - 1) / B * B : 0;
+            sum += v[q];
+        }
+        int incl = sum;
+#pragma unroll
+        for (int d = 1; d < kWave; d <<= 1) {
+            const int o = __shfl_up(incl, d);
+            if (lane >= d) incl += o;
+        }
+        int base = incl - sum;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int ex = lane * 4 + q;
+            if (ex < E) off[ex] = base;
+            base += v[q];
+        }
+        if (lane == kWave - 1) off[E] = incl;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "workgroup");
+    __builtin_amdgcn_wave_barrier();
+    for (int ex = lane; ex <= E; ex += kWave) expert_offsets[ex] = off[ex];
+    const int npad = off[E];
+    if (lane == 0) *num_padded = npad;
+    // sentinels: padding inside a segment and everything past npad
+    for (int i = lane; i < cap; i += kWave) {
+        bool pad = (i >= npad);
+        if (!pad) {
+            int lo = 0, hi = E - 1;  // last expert with off <= i
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            pad = (i - off[lo]) >= cnt[lo];
+        }
+        if (pad) sorted_ids[i] = n;
+    }
+    for (int b = lane; b < cap / B; b += kWave) {
+        const int i = b * B;
+        int owner = -1;
+        if (i < npad) {
+            int lo = 0, hi = E - 1;
+            while (lo < hi) {
+                const int mid = (lo + hi + 1) >> 1;
+                if (off[mid] <= i) lo = mid; else hi = mid - 1;
+            }
+            owner = lo;
+        }
+        block_expert[b] = owner;
+    }
+    // stable scatter: rank among the earlier slots of the same expert
+    uint64_t match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+        const bool bit = (e >> b) & 1;
+        const uint64_t bb = __ballot(valid && bit);
+        match &= bit ? bb : ~bb;
+    }
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    if (valid) {
+        const int pos = off[e] + __popcll(match & lt_mask);
+        sorted_ids[pos] = lane;
+        if (inv) inv[lane] = pos;
+    }
+}
+
 }  // namespace moe

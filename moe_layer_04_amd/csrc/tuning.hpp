@@ -106,6 +106,11 @@ constexpr int kPrefillFp8Gemm1Group = 2, kPrefillFp8Gemm2Group = 4;
 constexpr int kPrefillFp8Gemm1WeightSlots = 3, kPrefillFp8Gemm1TokenSlots = 2;
 constexpr int kPrefillFp8Gemm2WeightSlots = 2, kPrefillFp8Gemm2TokenSlots = 3;
 
+// ---- two-launch decode of one or two tokens (bf16) -----------------------------
+// every workgroup recomputes all router logits, M*E pairs of K-long fp64 dot
+// products, so the fused kernel is taken only while they stay few
+constexpr int kFusedDecodeMaxPairs = 32;
+
 // ---- router -------------------------------------------------------------------
 // fp64-MFMA logits: split K until the tiles x splits cover every CU (the
 // DeepSeek shape's 128 tiles in 2 splits: its logits + e4m3-rows stage

@@ -214,7 +214,10 @@ def test_fused_plan(lib):
         for (a, na), (b, _) in zip(regions, regions[1:]):
             assert a % 256 == 0 and a + na <= b
         assert regions[-1][0] + regions[-1][1] <= p.workspace_bytes
-        assert list(p.reserved) == [0, 0]
+        assert p.reserved == 0
+        assert p.fused_decode == (1 if (dt, M) == (0, 1) else 0)
+        if p.fused_decode:
+            assert p.gemm2_splits == 1
     # a forced family is reported as such
     assert moe.fused_plan(0, 4096, 4096, 14336, 8, 2, moe.MOE_REGIME_DECODE).regime == 1
     assert moe.fused_plan(0, 8, 4096, 14336, 8, 2, moe.MOE_REGIME_PREFILL).regime == 2

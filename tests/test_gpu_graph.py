@@ -28,8 +28,11 @@ CASES = [
     # more than 2048 token-slots: the multi-workgroup align in the graph
     ("multi_align_tiles", 1100, 256, 256, 8, 2, "bf16", 0),
     ("multi_align_tiles_fp8", 1100, 256, 256, 8, 2, "fp8", 0),
-    # one token: the single-wave top-k + align
+    # one token: routing inside GEMM1 (bf16) and the single-wave top-k +
+    # align (e4m3)
     ("single_token", 1, 512, 512, 16, 2, "bf16", 0),
+    # two tokens, bf16: routing inside GEMM1, GEMM2 + combine
+    ("two_tokens_fused", 2, 1024, 512, 8, 2, "bf16", 0),
     ("single_token_fp8", 1, 512, 512, 8, 2, "fp8", 0),
 ]
 

@@ -314,6 +314,17 @@ SMALL = [
     ("one_token_wave_route_fp8", 1, 1536, 256, 8, 2, True, 0.5, 0),
     ("two_tokens_wave_route_fp8_rowwise", 2, 512, 256, 4, 3, "rowwise", None, 0),
     ("one_token_wave_route_mxfp4", 1, 512, 512, 12, 4, "mxfp4", None, 0),
+    # bf16, one or two tokens, K and N multiples of 512, at most 32 router
+    # pairs and 4 routed experts: the router, top-k and align inside the
+    # GEMM1 launch and GEMM2 with the combine in one more; two tokens sharing
+    # experts, top-1, top-k = E (every expert serves both tokens), router bias
+    ("fused_decode_two_tokens_bias", 2, 1024, 512, 8, 2, False, 0.5, 0),
+    ("fused_decode_top1", 1, 512, 512, 4, 1, False, None, 0),
+    ("fused_decode_two_tokens_top1", 2, 512, 1024, 4, 1, False, None, 0),
+    ("fused_decode_top4", 1, 512, 512, 8, 4, False, 0.5, 0),
+    ("fused_decode_k_eq_e", 2, 512, 512, 4, 4, False, None, 0),
+    ("fused_decode_e16", 2, 1536, 1024, 16, 2, False, None, 0),
+    ("fused_decode_wide_k", 1, 4096, 512, 16, 2, False, 0.5, 0),
 ]
 
 
@@ -348,7 +359,8 @@ def test_fused_tiny_routing_ties(moe, M, E, fp8):
     pick routes through other experts' weights, which the output comparison
     sees."""
     note(f"fused tiny routing ties M={M} E={E} fp8={fp8}")
-    wl = wlm.Workload("tiny_ties", M=M, K=256, N=256, E=E, topk=2, fp8=fp8, seed=8)
+    # bf16 with K = N = 512: the routing GEMM1 of one or two tokens
+    wl = wlm.Workload("tiny_ties", M=M, K=512, N=512, E=E, topk=2, fp8=fp8, seed=8)
     for dup in ("all", "pairs"):
         d, g = gen_small(wl)
         wr = d["w_router"].clone()
@@ -412,13 +424,15 @@ def test_fp8_decode_vs_tiles(moe):
 
 def test_fused_deterministic(moe):
     """Ten calls on the same inputs are bitwise identical on every path: the
-    decode and full-tile kernels, bf16 and e4m3, and the multi-workgroup align
-    (no result depends on the order of atomics or on timing)."""
+    decode and full-tile kernels, bf16 and e4m3, the multi-workgroup align
+    and the routing GEMM1 with GEMM2 + combine of two tokens (no result
+    depends on the order of atomics or on timing)."""
     note("determinism")
     wl = wlm.Workload("det", M=40, K=512, N=512, E=8, topk=2, seed=4)
     big = wlm.Workload("det_big", M=1100, K=256, N=256, E=8, topk=2, seed=5)
+    two = wlm.Workload("det_two_tokens", M=2, K=512, N=512, E=8, topk=2, seed=6)
     for w, regimes in ((wl, (1, 2)), (wl.resized(fp8=True), (1, 2)), (big, (0,)),
-                       (big.resized(fp8=True), (0,))):
+                       (big.resized(fp8=True), (0,)), (two, (0,))):
         d, g = gen_small(w)
         for regime in regimes:
             outs = [run_layer(moe, g, w, regime).clone() for _ in range(10)]
