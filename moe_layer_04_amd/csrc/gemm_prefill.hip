@@ -21,7 +21,10 @@
 // Staging: both operand tiles are copied global -> LDS by the gfx950 buffer
 // loads with an LDS destination (no register round trip) into rings of
 // slots (one for the weights, one for the tokens; their lengths may differ
-// by one).
+// by one).  The bf16 256 x 256 tiles run the ping-pong core (PingPongCore:
+// two groups of four waves a phase apart, so one group's LDS reads, copies
+// and barrier waits overlap the other group's MFMAs); the other tiles run
+// PrefillCore, whose waves all read, copy and compute in step.
 // Each K-step waits (vmcnt) for its own slots, meets the workgroup at one raw
 // s_barrier (the __syncthreads fence would wait for every in-flight copy),
 // issues each operand's copy as many steps ahead as its ring allows and runs
@@ -172,6 +175,11 @@ struct PrefillCore {
     __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
         return (q * NW + wave) * kRowsPerInstr + lane / kCPR;
     }
+    // the wave's weight-row group (wa) and token-row group of TT/WT rows (wb)
+    __device__ static __forceinline__ int wave_a(int wave) { return wave % WW; }
+    __device__ static __forceinline__ int wave_b(int wave) { return wave / WW; }
+    // after the tile's epilogue (the ping-pong core's last barrier)
+    __device__ __forceinline__ void finish(int) {}
     __device__ static __forceinline__ int dma_chunk(int row, int lane) {
         return (lane % kCPR) ^ swz<kCPR>(row);
     }
@@ -350,16 +358,207 @@ struct PrefillCore {
 };
 
 // ---------------------------------------------------------------------------
+// The ping-pong main loop for TW x 256 tiles with 8 waves.  The waves form
+// two groups of four, A (waves 0-3) and B (waves 4-7), one wave of each per
+// SIMD; group A computes token rows 0-127, group B rows 128-255, each wave a
+// (TW/2) x 64 tile as in PrefillCore (2 x 2 waves per group).  A K-step is
+// two phases per group: a memory phase (read all of the step's fragments
+// from LDS into registers, issue DMA copies, wait for earlier copies) and a
+// compute phase (the step's MFMAs from registers).  Group B runs one phase
+// behind group A, and every phase ends at a workgroup barrier, so while one
+// group waits on LDS reads, copies and the barrier the other keeps its
+// SIMD's matrix core busy:
+//
+//   phase    1     2     3     4    ...   2s+1   2s+2  ...  2S+1
+//   A       M0    C0    M1    C1          Ms     Cs         (idle)
+//   B      (idle) M0    C0    M1          Cs-1   Ms          CS-1
+//
+// Group A copies the token rows (XST ring slots, issued one step ahead in
+// its memory phase, waited for at the end of its compute phase), group B the
+// weight rows (WST slots, issued two steps ahead in its memory phase and
+// waited for one step later).  A slot of step s is overwritten only after
+// the barrier that ends B's memory phase of step s, and a step's copies are
+// complete before the barrier that starts A's memory phase of it.
+// ---------------------------------------------------------------------------
+template <int TW, int BK, int WST, int XST>
+struct PingPongCore {
+    static constexpr int TT = 256, NW = 8;
+    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kCPR = kRowBytes / 16;
+    static constexpr int kRowsPerInstr = 64 / kCPR;
+    static constexpr int kWInstr = TW / kRowsPerInstr / 4;  // per wave of group B
+    static constexpr int kXInstr = TT / kRowsPerInstr / 4;  // per wave of group A
+    static constexpr int kWSlot = TW * kRowBytes;
+    static constexpr int kXSlot = TT * kRowBytes;
+    static constexpr int kXBase = WST * kWSlot;
+    static constexpr int kLdsBytes = WST * kWSlot + XST * kXSlot;
+    static constexpr int WW = 2;                // waves along the weight rows (per group)
+    static constexpr int WT = 4;                // 64-row token quarters of the tile
+    static constexpr int FW = TW / WW / 32;     // 32-row A tiles per wave
+    static constexpr int FT = 2;                // 32-column B tiles per wave
+    static constexpr int KS = BK / 16;          // 32x32x16 k-slices per step
+    static_assert(WST == 3 && XST == 2, "the copy schedule below is written for 3 + 2 slots");
+    static_assert(kWInstr * kRowsPerInstr * 4 == TW && kXInstr * kRowsPerInstr * 4 == TT,
+                  "tile rows must split evenly over a group's DMA instructions");
+
+    f32x16_t acc[FW][FT];
+
+    // rows copied by instruction q of a wave (its group copies one operand)
+    __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
+        return (q * 4 + (wave & 3)) * kRowsPerInstr + lane / kCPR;
+    }
+    __device__ static __forceinline__ int dma_chunk(int row, int lane) {
+        return (lane % kCPR) ^ swz<kCPR>(row);
+    }
+    __device__ static __forceinline__ int wave_a(int wave) { return (wave & 3) % WW; }
+    __device__ static __forceinline__ int wave_b(int wave) { return 2 * (wave >> 2) + (wave & 3) / WW; }
+    template <int AJUMP>
+    __device__ static constexpr int arow_delta(int a) {
+        return AJUMP ? (a % (FW / 2)) * 32 + (a / (FW / 2)) * AJUMP : a * 32;
+    }
+    // group A's last barrier, matching group B's last compute phase; taken
+    // after the tile's epilogue so that A's stores overlap B's last MFMAs
+    __device__ __forceinline__ void finish(int wave) {
+        if (wave < 4) __builtin_amdgcn_s_barrier();
+    }
+
+    template <bool COMPUTE, int AJUMP>
+    __device__ __forceinline__ void run(char* lds, prsrc_t rw, uint32_t wvoff,
+                                        const uint32_t* wsoff, prsrc_t rx, const uint32_t* xoff,
+                                        int klen, int wave, int wb, int arow0) {
+        static_assert(AJUMP % 16 == 0, "fragment rows must share one swizzle");
+        const int lane = lane_id();
+        const bool grp_b = wave >= 4;  // wave-uniform
+        const int gw = wave & 3;
+#pragma unroll
+        for (int a = 0; a < FW; ++a)
+#pragma unroll
+            for (int b = 0; b < FT; ++b)
+#pragma unroll
+                for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
+
+        typedef __attribute__((address_space(3))) void* lds_ptr_t;
+        auto dma_w = [&](int step, int slot) {
+            const uint32_t kb = (uint32_t)step * kRowBytes;
+            char* base = lds + slot * kWSlot;
+#pragma unroll
+            for (int q = 0; q < kWInstr; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (lds_ptr_t)(base + (q * 4 + gw) * 1024), 16, wvoff + kb, wsoff[q], 0, 0);
+        };
+        auto dma_x = [&](int step, int slot) {
+            const uint32_t kb = (uint32_t)step * kRowBytes;
+            char* base = lds + kXBase + slot * kXSlot;
+#pragma unroll
+            for (int q = 0; q < kXInstr; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (lds_ptr_t)(base + (q * 4 + gw) * 1024), 16, xoff[q] + kb, 0, 0, 0);
+        };
+        const int li = lane & 31, half = lane >> 5;
+        int aoff[KS], boff[KS];
+        {
+            const int ra = arow0 + li, rb = wb * (TT / WT) + li;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+                const int c = 2 * ks + half;
+                aoff[ks] = ra * kRowBytes + ((c ^ swz<kCPR>(ra)) << 4);
+                boff[ks] = rb * kRowBytes + ((c ^ swz<kCPR>(rb)) << 4);
+            }
+        }
+        bf16x8_t fa[KS][FW], fb[KS][FT];
+        auto read_all = [&](int wslot, int xslot) {
+            const char* wbase = lds + wslot * kWSlot;
+            const char* xbase = lds + kXBase + xslot * kXSlot;
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+                for (int a = 0; a < FW; ++a)
+                    fa[ks][a] = *reinterpret_cast<const bf16x8_t*>(
+                        wbase + arow_delta<AJUMP>(a) * kRowBytes + aoff[ks]);
+#pragma unroll
+                for (int b = 0; b < FT; ++b)
+                    fb[ks][b] = *reinterpret_cast<const bf16x8_t*>(xbase + b * 32 * kRowBytes +
+                                                                   boff[ks]);
+            }
+        };
+        auto mfma_all = [&]() {
+#pragma unroll
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int a = 0; a < FW; ++a)
+#pragma unroll
+                    for (int b = 0; b < FT; ++b) acc[a][b] = mfma32_bf16(fa[ks][a], fb[ks][b], acc[a][b]);
+        };
+        auto barrier = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        const int steps = klen / BK;
+        // the previous tile's last LDS reads are done before refilling
+        barrier();
+        // prologue: the token rows of step 0 (A), the weight rows of steps 0
+        // and 1 (B); step 0 complete at the first barrier
+        if (!grp_b) {
+            if (steps > 0) dma_x(0, 0);
+            wait_vmcnt<0>();
+        } else {
+            if (steps > 0) dma_w(0, 0);
+            if (steps > 1) {
+                dma_w(1, 1);
+                wait_vmcnt<kWInstr>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+        barrier();
+        if (grp_b) barrier();  // B sits out phase 1
+        int wsl = 0, xsl = 0;  // slots of step s
+        for (int s = 0; s < steps; ++s) {
+            // ---- memory phase of step s
+            if constexpr (COMPUTE) read_all(wsl, xsl);
+            if (!grp_b) {
+                if (s + 1 < steps) dma_x(s + 1, xsl ^ 1);
+            } else {
+                if (s + 2 < steps) {
+                    dma_w(s + 2, wsl == 0 ? 2 : wsl - 1);  // the slot of step s-1
+                    wait_vmcnt<kWInstr>();                  // step s+1 has landed
+                } else {
+                    wait_vmcnt<0>();
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS reads of step s are done
+            barrier();
+            // ---- compute phase of step s
+            if constexpr (COMPUTE) mfma_all();
+            if (!grp_b) wait_vmcnt<0>();  // token rows of step s+1 have landed
+            barrier();
+            wsl = wsl + 1 == WST ? 0 : wsl + 1;
+            xsl ^= 1;
+        }
+#pragma unroll
+        for (int a = 0; a < FW; ++a)
+#pragma unroll
+            for (int b = 0; b < FT; ++b) pin(acc[a][b]);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP,
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     int max_blocks, uint16_t* __restrict__ act) {
-    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW>;
+    // PP: the ping-pong core (256 token rows, 8 waves)
+    using Core = typename std::conditional<PP, PingPongCore<TW, BK, WST, XST>,
+                                           PrefillCore<TW, TT, BK, WST, XST, WW, NW>>::type;
+    static_assert(!PP || (TT == 256 && NW == 8), "the ping-pong core takes 256-row tiles");
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int HW = TW / 2;  // n-values per tile
     constexpr int WN = HW / WW; // n-values per wave
@@ -367,7 +566,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const int npad = *num_padded;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int wa = wave % WW, wb = wave / WW;
+    const int wa = Core::wave_a(wave), wb = Core::wave_b(wave);
     TileWalk<GROUP> walk(N / HW, max_blocks);
     int wt, blk;
     while (walk.next(wt, blk)) {
@@ -386,8 +585,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
                            Core::dma_chunk(row0, lane) * 16;
 #pragma unroll
     for (int q = 0; q < Core::kWInstr; ++q) {
-        const int first = (q * NW + wave) * Core::kRowsPerInstr;  // wave-uniform
-        const int shift = q * NW * Core::kRowsPerInstr + (first >= HW ? N - HW : 0);
+        const int first = Core::dma_row(wave, q, 0);  // wave-uniform
+        const int shift = first - Core::dma_row(wave, 0, 0) + (first >= HW ? N - HW : 0);
         wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * row_bytes));
     }
 #pragma unroll
@@ -426,6 +625,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
             }
         }
     }
+    core.finish(wave);
     }  // tiles
 }
 
@@ -433,13 +633,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
 // GEMM2 (bf16): weight tile wt covers output rows wt*TW..+TW; the epilogue
 // multiplies by the routing weight and scatters token row r to slot p.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP,
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
-    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW>;
+    using Core = typename std::conditional<PP, PingPongCore<TW, BK, WST, XST>,
+                                           PrefillCore<TW, TT, BK, WST, XST, WW, NW>>::type;
+    static_assert(!PP || (TT == 256 && NW == 8), "the ping-pong core takes 256-row tiles");
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int WR = TW / WW;  // output rows per wave
 
@@ -448,7 +651,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const int npad = *num_padded;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int wa = wave % WW, wb = wave / WW;
+    const int wa = Core::wave_a(wave), wb = Core::wave_b(wave);
     TileWalk<GROUP> walk(n_wt * nsplit, max_blocks);
     int wtz, blk;
     while (walk.next(wtz, blk)) {
@@ -468,7 +671,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
 #pragma unroll
     for (int q = 0; q < Core::kWInstr; ++q)
         wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane(
-            (int)(q * NW * Core::kRowsPerInstr * row_bytes));
+            (int)((Core::dma_row(wave, q, 0) - Core::dma_row(wave, 0, 0)) * row_bytes));
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
@@ -504,6 +707,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
             }
         }
     }
+    core.finish(wave);
     }  // tiles
 }
 
@@ -549,8 +753,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
                            Core::dma_chunk(row0, lane) * 16;
 #pragma unroll
     for (int q = 0; q < Core::kWInstr; ++q) {
-        const int first = (q * NW + wave) * Core::kRowsPerInstr;  // wave-uniform
-        const int shift = q * NW * Core::kRowsPerInstr + (first >= HW ? N - HW : 0);
+        const int first = Core::dma_row(wave, q, 0);  // wave-uniform
+        const int shift = first - Core::dma_row(wave, 0, 0) + (first >= HW ? N - HW : 0);
         wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * row_bytes));
     }
 #pragma unroll
@@ -642,7 +846,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
 #pragma unroll
     for (int q = 0; q < Core::kWInstr; ++q)
         wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane(
-            (int)(q * NW * Core::kRowsPerInstr * row_bytes));
+            (int)((Core::dma_row(wave, q, 0) - Core::dma_row(wave, 0, 0)) * row_bytes));
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
@@ -706,9 +910,8 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
             (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
             topk, nslots, K, N, max_blocks, (uint16_t*)act);
     else
-        gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm1WeightSlots,
-                                  tune::kPrefillGemm1TokenSlots, 2, 8, 1, tune::kPrefillGemm1Group>
-            <<<grid, 512, 0, s>>>(
+        gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, tune::kPrefillGemm1Group,
+                                  true><<<grid, 512, 0, s>>>(
             (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
             topk, nslots, K, N, max_blocks, (uint16_t*)act);
 }
@@ -739,9 +942,8 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
     } else if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
         // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, tune::kPrefillGemm2WeightSlots,
-                                  tune::kPrefillGemm2TokenSlots, 2, 8, 1, tune::kPrefillGemm2Group>
-            <<<grid, 512, 0, s>>>(
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, tune::kPrefillGemm2Group,
+                                  true><<<grid, 512, 0, s>>>(
             (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
             num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else if (K % 256 == 0) {

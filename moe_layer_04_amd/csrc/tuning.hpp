@@ -90,10 +90,17 @@ constexpr long kPrefillSplitTargetTiles = 1024;
 // 4 against 990 with 8 and 1042 with 16)
 constexpr int kPrefillGemm1Group = 4;
 constexpr int kPrefillGemm2Group = 4;
-// LDS ring slots (weight, token) of the 64-deep steps: GEMM1 3 + 2; GEMM2
-// 2 + 3 (933-935 us against 946-950 with 3 + 2)
-constexpr int kPrefillGemm1WeightSlots = 3, kPrefillGemm1TokenSlots = 2;
-constexpr int kPrefillGemm2WeightSlots = 2, kPrefillGemm2TokenSlots = 3;
+// The 256-row bf16 tiles of both GEMMs run the ping-pong core (two wave
+// groups a phase apart, 3 weight + 2 token ring slots).  Against the shared
+// core on one box, Mixtral-shaped prefill (alternating runs): GEMM1 1621-1626
+// against 1705-1712 us, GEMM2 849-854 against 947 us, step 2.62 against
+// 2.79 ms; counters: matrix cores busy 68 % (GEMM1) / 67 % (GEMM2) against
+// 62 / 57 %, at a lower clock (1.63 / 1.53 GHz against 1.70 / 1.59), L2 hit
+// rate 65 / 68 % against 58 / 66 %.  With the ping-pong core, tile groups of
+// 2 and 4 weight tiles are equal for GEMM1 (1625 us), 8 slower (1685); GEMM2
+// 4 best (849-854 us against 878 with 2, 890 with 8).
+// (Before the ping-pong core, the shared core's rings measured best at 3 + 2
+// slots for GEMM1 and 2 + 3 for GEMM2: 933-935 us against 946-950 with 3 + 2.)
 // the e4m3 full tiles (same bytes per K-step as the bf16 ones).  GEMM1
 // group, rings (weight + token slots), us on the Mixtral shape with 4096
 // tokens / the DeepSeek shape with 4096 tokens (two runs where given):
