@@ -380,10 +380,10 @@ struct PrefillCore {
 // the barrier that ends B's memory phase of step s, and a step's copies are
 // complete before the barrier that starts A's memory phase of it.
 // ---------------------------------------------------------------------------
-template <int TW, int BK, int WST, int XST>
+template <int TW, int BK, int WST, int XST, bool F8 = false>
 struct PingPongCore {
     static constexpr int TT = 256, NW = 8;
-    static constexpr int kRowBytes = BK * 2;
+    static constexpr int kRowBytes = F8 ? BK : BK * 2;
     static constexpr int kCPR = kRowBytes / 16;
     static constexpr int kRowsPerInstr = 64 / kCPR;
     static constexpr int kWInstr = TW / kRowsPerInstr / 4;  // per wave of group B
@@ -396,7 +396,8 @@ struct PingPongCore {
     static constexpr int WT = 4;                // 64-row token quarters of the tile
     static constexpr int FW = TW / WW / 32;     // 32-row A tiles per wave
     static constexpr int FT = 2;                // 32-column B tiles per wave
-    static constexpr int KS = BK / 16;          // 32x32x16 k-slices per step
+    // MFMA k-slices per step: 32x32x16 bf16 or 32x32x64 e4m3
+    static constexpr int KS = F8 ? BK / 64 : BK / 16;
     static_assert(WST == 3 && XST == 2, "the copy schedule below is written for 3 + 2 slots");
     static_assert(kWInstr * kRowsPerInstr * 4 == TW && kXInstr * kRowsPerInstr * 4 == TT,
                   "tile rows must split evenly over a group's DMA instructions");
@@ -454,18 +455,35 @@ struct PingPongCore {
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(
                     rx, (lds_ptr_t)(base + (q * 4 + gw) * 1024), 16, xoff[q] + kb, 0, 0, 0);
         };
+        // per-lane LDS offsets of the first A and B fragment of each k-slice
+        // (as PrefillCore): bf16 lane half h reads chunk 2*ks + h; e4m3
+        // chunks 4*ks + 2h and 4*ks + 2h + 1, the same chunks for both
+        // operands, so each product pairs matching reduction indices
         const int li = lane & 31, half = lane >> 5;
-        int aoff[KS], boff[KS];
+        constexpr int NC = F8 ? 2 : 1;  // 16-byte reads per fragment
+        int aoff[KS][NC], boff[KS][NC];
         {
             const int ra = arow0 + li, rb = wb * (TT / WT) + li;
 #pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c = 2 * ks + half;
-                aoff[ks] = ra * kRowBytes + ((c ^ swz<kCPR>(ra)) << 4);
-                boff[ks] = rb * kRowBytes + ((c ^ swz<kCPR>(rb)) << 4);
-            }
+            for (int ks = 0; ks < KS; ++ks)
+#pragma unroll
+                for (int h = 0; h < NC; ++h) {
+                    const int c = F8 ? 4 * ks + 2 * half + h : 2 * ks + half;
+                    aoff[ks][h] = ra * kRowBytes + ((c ^ swz<kCPR>(ra)) << 4);
+                    boff[ks][h] = rb * kRowBytes + ((c ^ swz<kCPR>(rb)) << 4);
+                }
         }
-        bf16x8_t fa[KS][FW], fb[KS][FT];
+        typedef typename std::conditional<F8, i32x8_t, bf16x8_t>::type frag_t;
+        auto ld = [&](const char* base, const int (&off)[NC]) {
+            if constexpr (F8) {
+                const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(base + off[0]);
+                const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(base + off[1]);
+                return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                return *reinterpret_cast<const bf16x8_t*>(base + off[0]);
+            }
+        };
+        frag_t fa[KS][FW], fb[KS][FT];
         auto read_all = [&](int wslot, int xslot) {
             const char* wbase = lds + wslot * kWSlot;
             const char* xbase = lds + kXBase + xslot * kXSlot;
@@ -473,12 +491,9 @@ struct PingPongCore {
             for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
                 for (int a = 0; a < FW; ++a)
-                    fa[ks][a] = *reinterpret_cast<const bf16x8_t*>(
-                        wbase + arow_delta<AJUMP>(a) * kRowBytes + aoff[ks]);
+                    fa[ks][a] = ld(wbase + arow_delta<AJUMP>(a) * kRowBytes, aoff[ks]);
 #pragma unroll
-                for (int b = 0; b < FT; ++b)
-                    fb[ks][b] = *reinterpret_cast<const bf16x8_t*>(xbase + b * 32 * kRowBytes +
-                                                                   boff[ks]);
+                for (int b = 0; b < FT; ++b) fb[ks][b] = ld(xbase + b * 32 * kRowBytes, boff[ks]);
             }
         };
         auto mfma_all = [&]() {
@@ -487,7 +502,12 @@ struct PingPongCore {
 #pragma unroll
                 for (int a = 0; a < FW; ++a)
 #pragma unroll
-                    for (int b = 0; b < FT; ++b) acc[a][b] = mfma32_bf16(fa[ks][a], fb[ks][b], acc[a][b]);
+                    for (int b = 0; b < FT; ++b) {
+                        if constexpr (F8)
+                            acc[a][b] = mfma32_fp8(fa[ks][a], fb[ks][b], acc[a][b]);
+                        else
+                            acc[a][b] = mfma32_bf16(fa[ks][a], fb[ks][b], acc[a][b]);
+                    }
         };
         auto barrier = [&]() {
             __builtin_amdgcn_sched_barrier(0);
@@ -722,14 +742,17 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
 // values); GEMM2 multiplies by the output row's (or expert's) W2 scale, the
 // sorted row's activation scale s_a[r] and the routing weight.
 // ---------------------------------------------------------------------------
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP,
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
     const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
     const uint8_t* __restrict__ w1, const float* __restrict__ w1_scale, int rowwise,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     int max_blocks, float* __restrict__ act, uint32_t* __restrict__ amax) {
-    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW, true>;
+    using Core = typename std::conditional<PP, PingPongCore<TW, BK, WST, XST, true>,
+                                           PrefillCore<TW, TT, BK, WST, XST, WW, NW, true>>::type;
+    static_assert(!PP || (TT == 256 && NW == 8), "the ping-pong core takes 256-row tiles");
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int HW = TW / 2;  // n-values per tile
     constexpr int WN = HW / WW; // n-values per wave
@@ -737,7 +760,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
     const int npad = *num_padded;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int wa = wave % WW, wb = wave / WW;
+    const int wa = Core::wave_a(wave), wb = Core::wave_b(wave);
     TileWalk<GROUP> walk(N / HW, max_blocks);
     int wt, blk;
     while (walk.next(wt, blk)) {
@@ -808,17 +831,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
         const uint32_t mb = max(__float_as_uint(m), (uint32_t)__shfl_xor((int)__float_as_uint(m), 32));
         if (valid && lane < 32) atomicMax(amax + r, mb);
     }
+    core.finish(wave);
     }  // tiles
 }
 
-template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP>
+template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP,
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
     const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
     const uint8_t* __restrict__ w2, const float* __restrict__ w2_scale, int rowwise,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
-    using Core = PrefillCore<TW, TT, BK, WST, XST, WW, NW, true>;
+    using Core = typename std::conditional<PP, PingPongCore<TW, BK, WST, XST, true>,
+                                           PrefillCore<TW, TT, BK, WST, XST, WW, NW, true>>::type;
+    static_assert(!PP || (TT == 256 && NW == 8), "the ping-pong core takes 256-row tiles");
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int WR = TW / WW;  // output rows per wave
 
@@ -826,7 +853,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
     const int npad = *num_padded;
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
-    const int wa = wave % WW, wb = wave / WW;
+    const int wa = Core::wave_a(wave), wb = Core::wave_b(wave);
     TileWalk<GROUP> walk(n_wt * nsplit, max_blocks);
     int wtz, blk;
     while (walk.next(wtz, blk)) {
@@ -886,6 +913,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
             }
         }
     }
+    core.finish(wave);
     }  // tiles
 }
 
@@ -974,9 +1002,8 @@ void launch_gemm1_prefill_fp8(const uint8_t* xq, const float* xscale, const void
             xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids, block_expert,
             num_padded, M, topk, nslots, K, N, max_blocks, act, amax);
     else
-        gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm1WeightSlots,
-                                 tune::kPrefillFp8Gemm1TokenSlots, 2, 8, 1,
-                                 tune::kPrefillFp8Gemm1Group><<<grid, 512, 0, s>>>(
+        gemm1_prefill_fp8_kernel<256, kPrefillRows, 128, 3, 2, 2, 8, 1,
+                                 tune::kPrefillFp8Gemm1Group, true><<<grid, 512, 0, s>>>(
             xq, xscale, (const uint8_t*)w1, w1_scale, rowwise, sorted_ids, block_expert,
             num_padded, M, topk, nslots, K, N, max_blocks, act, amax);
 }
@@ -995,9 +1022,8 @@ void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const v
             block_expert, num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else if (K % 256 == 0) {
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        gemm2_prefill_fp8_kernel<256, kPrefillRows, 128, tune::kPrefillFp8Gemm2WeightSlots,
-                                 tune::kPrefillFp8Gemm2TokenSlots, 2, 8, 1,
-                                 tune::kPrefillFp8Gemm2Group>
+        gemm2_prefill_fp8_kernel<256, kPrefillRows, 128, 3, 2, 2, 8, 1,
+                                 tune::kPrefillFp8Gemm2Group, true>
             <<<grid, 512, 0, s>>>(act_q, ascale, (const uint8_t*)w2, w2_scale, rowwise, topk_w,
                                   sorted_ids, block_expert, num_padded, cap, nslots, K, N, nsplit,
                                   max_blocks, ypart);

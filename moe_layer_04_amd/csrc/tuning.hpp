@@ -109,9 +109,11 @@ constexpr int kPrefillGemm2Group = 4;
 // 2, 2+3: 1016 / 1844; 3, 3+2: 1014 / 2267.  GEMM2: 4, 2+3: 520 / 1148;
 // 4, 3+2: 555 / 1112; 2, 3+2: 582 / 1216; 2, 2+3: 542 / 1326; 8, 2+2:
 // 593 / 1440; 8, 2+3: 579 / 1564.
+// The e4m3 256-row tiles run the ping-pong core too (3 + 2 slots): Mixtral
+// shape with e4m3 weights, alternating runs against the shared core (3 + 2
+// for GEMM1, 3 + 2 for GEMM2): GEMM1 971-972 against 986-998 us, GEMM2
+// 526-529 against 552-555 us, step 1.766-1.775 against 1.799-1.809 ms.
 constexpr int kPrefillFp8Gemm1Group = 2, kPrefillFp8Gemm2Group = 4;
-constexpr int kPrefillFp8Gemm1WeightSlots = 3, kPrefillFp8Gemm1TokenSlots = 2;
-constexpr int kPrefillFp8Gemm2WeightSlots = 2, kPrefillFp8Gemm2TokenSlots = 3;
 
 // ---- two-launch decode of one or two tokens (bf16) -----------------------------
 // every workgroup recomputes all router logits, M*E pairs of K-long fp64 dot
