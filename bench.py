@@ -614,6 +614,10 @@ def bench_workload(moe, wlm, wl, args, dev, hip, cpu_seconds):
             "seconds": round(cpu_s, 3)}
         result["parity_vs_oracle"] = {"max_row_rel_err": err, "tokens": n_tok, "tol": tol,
                                       "ok": bool(np.isfinite(got).all() and err <= tol)}
+    # the padded row count of this batch's routing, from the workspace (the
+    # number of token blocks the GEMMs ran over)
+    npad = int(moe.fused_routing(ws, plan, wl.M, wl.E, wl.topk)["num_padded"].item())
+    result["routed_blocks"] = npad // plan.block_m
     del g, w1s, w2s, ws, out
     return result
 

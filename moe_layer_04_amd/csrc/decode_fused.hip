@@ -32,6 +32,9 @@ constexpr int kFusedRot = 7;                 // GEMM1 K-step rotation per wave
 constexpr int kFusedSliceGroup = 8;         // router: row slices loaded together
 constexpr int kFusedExpertGroup = 4;        // router: expert rows of a wave in flight
 constexpr int kFusedMaxBlocks = 4;          // routed experts (16-row blocks) of the layer
+// GEMM2 + combine: waves splitting N (8 when N % 1024 == 0: single-token
+// decode, 1 x 4096 and 4096 x 8192 experts, 78.3-78.6 against 79.9 us per
+// layer call with 4)
 
 typedef __amdgpu_buffer_rsrc_t frsrc_t;
 
@@ -249,28 +252,29 @@ __global__ __launch_bounds__(256) void decode_route_gemm1_bf16_kernel(
 // ---------------------------------------------------------------------------
 // GEMM2 and the combine of one or two tokens in one launch: workgroup g owns
 // output rows r0 = 16*g .. r0+15 of every routed expert (NB 16-row blocks of
-// the sorted rows, block b owned by block_expert[b], -1 if unused); its four
-// waves split the reduction (N) into quarters and stream those rows of W2[e]
-// against the block's activation rows (Swap-AB, as gemm2_decode_bf16_kernel).
+// the sorted rows, block b owned by block_expert[b], -1 if unused); its
+// kG2Waves waves split the reduction (N) into equal ranges and stream those
+// rows of W2[e] against the block's activation rows (Swap-AB, as
+// gemm2_decode_bf16_kernel).
 // The wave partials meet in LDS, and out[t][r] = bf16( sum over the token's
 // slots j in ascending order of w[t,j] * (sum over the waves in order of the
 // partial of its block and column) ): a fixed order, and no partial rows
 // leave the workgroup.
 // ---------------------------------------------------------------------------
-template <int MT, int NB>
-__global__ __launch_bounds__(256) void decode_gemm2_combine_bf16_kernel(
+template <int MT, int NB, int kG2Waves>
+__global__ __launch_bounds__(kG2Waves * 64) void decode_gemm2_combine_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, int K, int N, int topk, int cap,
     uint16_t* __restrict__ out) {
-    __shared__ float red[4][NB][16][17];  // [wave][block][row][column], padded
+    __shared__ float red[kG2Waves][NB][16][17];  // [wave][block][row][column], padded
     __shared__ int spos[kWave];            // sorted row of each slot
     const int lane = lane_id();
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     const int nslots = MT * topk;
     const int r0 = (int)blockIdx.x * 16;
     const int i = lane & 15, kq = lane >> 4;
-    const int nq = N / 4, nbeg = wave * nq;
+    const int nq = N / kG2Waves, nbeg = wave * nq;
 
     int eb[NB];
     bool vb[NB];
@@ -351,7 +355,7 @@ __global__ __launch_bounds__(256) void decode_gemm2_combine_bf16_kernel(
             const int b = r / 16, col = r % 16;
             float s = 0.0f;
 #pragma unroll
-            for (int w = 0; w < 4; ++w) s += red[w][b][row][col];
+            for (int w = 0; w < kG2Waves; ++w) s += red[w][b][row][col];
             y += topk_w[p] * s;
         }
         out[(size_t)t * K + r0 + row] = f32_to_bf16_bits(y);
@@ -389,9 +393,16 @@ void launch_decode_gemm2_combine_bf16(const void* act, const void* w2, const flo
                                       hipStream_t s) {
     const int nb = min(E, M * topk);
 #define MOE_G2C(MT, NB)                                                                      \
-    decode_gemm2_combine_bf16_kernel<MT, NB><<<K / 16, 256, 0, s>>>(                         \
-        (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert, K, N,   \
-        topk, cap, (uint16_t*)out)
+    do {                                                                                     \
+        if (N % 1024 == 0)                                                                   \
+            decode_gemm2_combine_bf16_kernel<MT, NB, 8><<<K / 16, 512, 0, s>>>(              \
+                (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert, \
+                K, N, topk, cap, (uint16_t*)out);                                            \
+        else                                                                                 \
+            decode_gemm2_combine_bf16_kernel<MT, NB, 4><<<K / 16, 256, 0, s>>>(              \
+                (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert, \
+                K, N, topk, cap, (uint16_t*)out);                                            \
+    } while (0)
     if (M == 2) {
         if (nb <= 2) MOE_G2C(2, 2);
         else MOE_G2C(2, 4);
