@@ -195,14 +195,15 @@ def mfma_summary(csv_path, l2_csv=None):
 
 
 def regime_sweep(moe, wlm, wl, dev, ms_list=None):
-    """Both kernel families (the workload's bf16 or e4m3 weights) on batches of
+    """Both kernel families (the workload's bf16, e4m3 or MXFP4 weights) on batches of
     M = 8 .. 1024 tokens (or ms_list) of this workload's shape: mean ms per
     layer call over 10 calls after 3."""
     import torch
     ms_list = ms_list or [8, 16, 32, 48, 64, 96, 128, 192, 256, 384, 512, 768, 1024]
     big = wlm.Workload(wl.name + "_sweep", M=max(ms_list), K=wl.K, N=wl.N, E=wl.E,
-                       topk=wl.topk, fp8=wl.fp8, fp8_rowwise=wl.fp8_rowwise, seed=wl.seed)
-    dtype = (moe.MOE_FP8_E4M3_ROWWISE if wl.fp8_rowwise else
+                       topk=wl.topk, fp8=wl.fp8, fp8_rowwise=wl.fp8_rowwise, mxfp4=wl.mxfp4,
+                       seed=wl.seed)
+    dtype = (moe.MOE_MXFP4_E2M1 if wl.mxfp4 else moe.MOE_FP8_E4M3_ROWWISE if wl.fp8_rowwise else
              moe.MOE_FP8_E4M3 if wl.fp8 else moe.MOE_BF16)
     g = wlm.generate(big, dev)
     for M in ms_list:
@@ -272,7 +273,7 @@ def main():
                          "elements) and e4m3 activations")
     ap.add_argument("--regime-sweep", action="store_true",
                     help="time the decode and full-tile kernel families (the workload's "
-                         "bf16 or e4m3 weights) over batch sizes M = 8 .. 1024 (or "
+                         "bf16, e4m3 or MXFP4 weights) over batch sizes M = 8 .. 1024 (or "
                          "--sweep-tokens) at this workload's K, N, E, top-k; one JSON line "
                          "per M, then exit")
     ap.add_argument("--sweep-tokens", type=int, nargs="+", default=None,

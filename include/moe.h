@@ -80,13 +80,15 @@ typedef enum {
  * summation order whichever is picked. */
 typedef enum {
     MOE_REGIME_AUTO = 0,    /* DECODE while M*topk <= 8*E (bf16: at most 8
-                               token-slots per expert on average) or
-                               M*topk <= 16*E (e4m3), always for MXFP4
-                               weights, else PREFILL: the measured crossovers */
+                               token-slots per expert on average),
+                               M*topk <= 16*E (e4m3) or M*topk <= 24*E
+                               (MXFP4), else PREFILL: the measured crossovers */
     MOE_REGIME_DECODE = 1,  /* Swap-AB: weight rows on the MFMA row dimension;
                                blocks of 16, 32 or 64 sorted rows sized from
                                the expected rows per expert */
-    MOE_REGIME_PREFILL = 2  /* full MFMA tiles of token rows x weight rows */
+    MOE_REGIME_PREFILL = 2  /* full MFMA tiles of token rows x weight rows
+                               (blocks of 128 or 256 sorted rows; 256 for
+                               MXFP4) */
 } moe_regime;
 
 /* Supported envelope: 1 <= E <= 256, 1 <= topk <= min(E,16), K >= 1 and
@@ -242,9 +244,9 @@ moe_status moe_quant_rows_e4m3(const void *x, int M, int K, uint8_t *q, float *s
  * Errors: as moe_topk, plus INVALID_ARG for null w1/w2/out/workspace_bytes,
  * N < 1, a bad dtype, scales given for bf16 or missing for fp8;
  * UNSUPPORTED for K or N not a multiple of 128 or the size limits above
- * (MXFP4 also: K or N not a multiple of 256, K > 16384, or N that cannot be
- * split into GEMM2 reduction ranges of at most 8192 multiples of 256), and
- * for MOE_REGIME_PREFILL with MXFP4 weights;
+ * (MXFP4 also: K or N not a multiple of 256, K > 16384, or, on the decode
+ * kernels, N that cannot be split into GEMM2 reduction ranges of at most 8192
+ * multiples of 256);
  * WORKSPACE if *workspace_bytes is below the required size.
  */
 moe_status moe_fused_forward(const void *x, const void *w_router, const float *router_bias,

@@ -65,19 +65,19 @@ Plan make_plan(int dtype, int M, int K, int N, int E, int topk, int regime) {
     p.fused = regime == MOE_REGIME_AUTO && dtype == MOE_BF16 &&
               moe::decode_fused_fits(M, K, N, E, topk);
     if (regime == MOE_REGIME_AUTO) {
-        // MXFP4 weights have only the decode kernels
-        const long rows = dtype == MOE_BF16 ? moe::tune::kDecodeMaxRowsPerExpert
-                                            : moe::tune::kFp8DecodeMaxRowsPerExpert;
-        regime = (dtype == MOE_MXFP4_E2M1 || slots <= rows * E) ? MOE_REGIME_DECODE
-                                                                : MOE_REGIME_PREFILL;
+        const long rows = dtype == MOE_BF16           ? moe::tune::kDecodeMaxRowsPerExpert
+                          : dtype == MOE_MXFP4_E2M1 ? moe::tune::kMxDecodeMaxRowsPerExpert
+                                                      : moe::tune::kFp8DecodeMaxRowsPerExpert;
+        regime = slots <= rows * E ? MOE_REGIME_DECODE : MOE_REGIME_PREFILL;
     }
     p.regime = regime;
     p.block = (regime == MOE_REGIME_DECODE) ? kDecodeBlock : kPrefillBlock;
     // full tiles: 128-row token blocks when the experts receive few rows
-    // (tuning.hpp); those kernels are built for K % 256 == 0
+    // (tuning.hpp); those kernels are built for K % 256 == 0.  MXFP4 weights
+    // have 256-row tiles only.
     const long small_rows = dtype == MOE_BF16 ? moe::tune::kPrefillSmallTileMaxRows
                                               : moe::tune::kPrefillFp8SmallTileMaxRows;
-    if (regime == MOE_REGIME_PREFILL && K % 256 == 0 &&
+    if (regime == MOE_REGIME_PREFILL && K % 256 == 0 && dtype != MOE_MXFP4_E2M1 &&
         slots <= small_rows * (slots < E ? slots : E))
         p.block = moe::kPrefillSmallRows;
     // larger decode blocks when experts receive more rows (sized in tuning.hpp)
@@ -276,11 +276,11 @@ static moe_status fused_shape_check(int dtype, int M, int K, int N, int E, int t
     if (M < 0 || K < 1 || N < 1 || E < 1 || topk < 1 || topk > E) return MOE_ERR_INVALID_ARG;
     if (E > MOE_MAX_EXPERTS || topk > MOE_MAX_TOPK) return MOE_ERR_UNSUPPORTED;
     if (K % 128 || N % 128) return MOE_ERR_UNSUPPORTED;
-    // MXFP4: 256-deep steps; GEMM1 keeps K/32 scale bytes per row of its
-    // waves in LDS (K <= 16384: 64 KB per workgroup)
+    // MXFP4: 256-deep decode steps and 256-row weight tiles; the decode
+    // GEMM1 keeps K/32 scale bytes per row of its waves in LDS (K <= 16384:
+    // 64 KB per workgroup)
     if (dtype == MOE_MXFP4_E2M1 && (K % 256 || N % 256 || K > moe::tune::kMxMaxK))
         return MOE_ERR_UNSUPPORTED;
-    if (dtype == MOE_MXFP4_E2M1 && regime == MOE_REGIME_PREFILL) return MOE_ERR_UNSUPPORTED;
     const long slots = (long)M * topk;
     // 32-bit buffer offsets: the sorted activation rows GEMM2 reads (bf16, or
     // e4m3 codes), the tokens and one expert's W1 must each stay below 2 GiB
@@ -292,8 +292,9 @@ static moe_status fused_shape_check(int dtype, int M, int K, int N, int E, int t
         return MOE_ERR_UNSUPPORTED;
     const Plan p = make_plan(dtype, M, K, N, E, topk, regime);
     if (p.max_blocks > 65535) return MOE_ERR_UNSUPPORTED;
-    // MXFP4 GEMM2: a split's scale bytes must fit its LDS copy
-    if (dtype == MOE_MXFP4_E2M1 && N / p.nsplit > moe::tune::kMxMaxSplitLen)
+    // MXFP4 decode GEMM2: a split's scale bytes must fit its LDS copy
+    if (dtype == MOE_MXFP4_E2M1 && p.regime == MOE_REGIME_DECODE &&
+        N / p.nsplit > moe::tune::kMxMaxSplitLen)
         return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
@@ -432,8 +433,11 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         uint8_t* actq = (uint8_t*)(ws + p.actq);
         float* as = (float*)(ws + p.as);
         const bool mx = dtype == MOE_MXFP4_E2M1;
-        const bool tiles = p.regime == MOE_REGIME_PREFILL;  // e4m3 only
-        if (tiles)
+        const bool tiles = p.regime == MOE_REGIME_PREFILL;
+        if (tiles && mx)
+            moe::launch_gemm1_prefill_mx(xq, xs, w1, (const uint8_t*)w1_scale, sorted, bexp, npad,
+                                         M, topk, nslots, K, N, p.grid_blocks, act, amax, s);
+        else if (tiles)
             moe::launch_gemm1_prefill_fp8(xq, xs, w1, (const float*)w1_scale, rowwise, sorted, bexp, npad, M,
                                           topk, nslots, K, N, p.grid_blocks, p.block, act, amax,
                                           s);
@@ -448,7 +452,11 @@ static moe_status fused_impl(const void* x, const void* w_router, const float* r
         mark(4);
         moe::launch_act_quant(act, amax, inv, nslots, N, actq, as, s);
         mark(5);
-        if (tiles)
+        if (tiles && mx)
+            moe::launch_gemm2_prefill_mx(actq, as, w2, (const uint8_t*)w2_scale, wts, sorted, bexp,
+                                         npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks, ypart,
+                                         s);
+        else if (tiles)
             moe::launch_gemm2_prefill_fp8(actq, as, w2, (const float*)w2_scale, rowwise, wts, sorted, bexp,
                                           npad, p.cap, nslots, K, N, p.nsplit, p.grid_blocks,
                                           p.block, ypart, s);

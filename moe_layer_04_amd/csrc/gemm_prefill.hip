@@ -565,6 +565,208 @@ struct PingPongCore {
 };
 
 // ---------------------------------------------------------------------------
+// The ping-pong loop for MXFP4 weights (OCP microscaling: e2m1 codes two per
+// byte, even element in the low nibble, one E8M0 scale per 32 elements of a
+// row) against e4m3 token rows, TW x 256 tiles, 8 waves in the two groups
+// and phases of PingPongCore.  A K-step is 128 codes: a weight row is 64
+// bytes (16 KB per slot), its 4 scale bytes go to a scale slot (1 KB), a
+// token row is 128 bytes (32 KB per slot).  The MFMA is the scaled
+// 16x16x128 one with A = e2m1: an FP4 lane of group q holds K 32q ..
+// 32q+31 of the step, exactly one MX block, whose E8M0 byte is the lane's
+// scale operand; the e4m3 operand's lane group q holds K 16q .. 16q+15 and
+// 64+16q .. 64+16q+15 (the layouts the decode MXFP4 kernels use, measured
+// on gfx950).  A wave covers (TW/2) x 64 of the tile as 8 x 4 16x16 tiles.
+// Group B copies the weight rows and their scales (two steps ahead), group
+// A the token rows (one step ahead).
+// ---------------------------------------------------------------------------
+template <int TW>
+struct PingPongMxCore {
+    static constexpr int TT = 256, NW = 8, BK = 128;
+    static constexpr int WST = 3, XST = 2;
+    static constexpr int kWRowBytes = BK / 2;                 // 64
+    static constexpr int kXRowBytes = BK;                     // 128
+    static constexpr int kWCPR = kWRowBytes / 16;             // 4 chunks per weight row
+    static constexpr int kXCPR = kXRowBytes / 16;             // 8 chunks per token row
+    static constexpr int kWRowsPerInstr = 64 / kWCPR;         // 16
+    static constexpr int kXRowsPerInstr = 64 / kXCPR;         // 8
+    static constexpr int kWInstr = TW / kWRowsPerInstr / 4;   // per wave of group B
+    static constexpr int kXInstr = TT / kXRowsPerInstr / 4;   // per wave of group A
+    static constexpr int kSInstr = 1;                         // TW/4 rows of 4 scale bytes
+    static constexpr int kWSlot = TW * kWRowBytes;
+    static constexpr int kSSlot = TW * 4;
+    static constexpr int kXSlot = TT * kXRowBytes;
+    static constexpr int kSBase = WST * kWSlot;
+    static constexpr int kXBase = kSBase + WST * kSSlot;
+    static constexpr int kLdsBytes = kXBase + XST * kXSlot;
+    static constexpr int WW = 2, WT = 4;
+    static constexpr int FW = TW / WW / 16;   // 16-row A tiles per wave (8)
+    static constexpr int FT = 4;              // 16-column B tiles per wave
+    static constexpr int kBInstr = kWInstr + kSInstr;  // a group-B wave's copies per step
+    static_assert(TW == 256, "MXFP4 tiles are 256 weight rows");
+    static_assert(kWInstr * kWRowsPerInstr * 4 == TW && kXInstr * kXRowsPerInstr * 4 == TT,
+                  "tile rows must split evenly over a group's DMA instructions");
+
+    f32x4_t acc[FW][FT];
+
+    // weight row copied by lane `lane` of weight instruction q (group B)
+    __device__ static __forceinline__ int w_dma_row(int wave, int q, int lane) {
+        return (q * 4 + (wave & 3)) * kWRowsPerInstr + lane / kWCPR;
+    }
+    __device__ static __forceinline__ int w_dma_chunk(int row, int lane) {
+        return (lane % kWCPR) ^ swz<kWCPR>(row);
+    }
+    // token row copied by lane `lane` of token instruction q (group A)
+    __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
+        return (q * 4 + (wave & 3)) * kXRowsPerInstr + lane / kXCPR;
+    }
+    __device__ static __forceinline__ int dma_chunk(int row, int lane) {
+        return (lane % kXCPR) ^ swz<kXCPR>(row);
+    }
+    // weight row whose 4 scale bytes lane `lane` of a group-B wave copies
+    __device__ static __forceinline__ int s_dma_row(int wave, int lane) {
+        return (wave & 3) * 64 + lane;
+    }
+    __device__ static __forceinline__ int wave_a(int wave) { return (wave & 3) % WW; }
+    __device__ static __forceinline__ int wave_b(int wave) { return 2 * (wave >> 2) + (wave & 3) / WW; }
+    template <int AJUMP>
+    __device__ static constexpr int arow_delta(int a) {
+        return AJUMP ? (a % (FW / 2)) * 16 + (a / (FW / 2)) * AJUMP : a * 16;
+    }
+    __device__ __forceinline__ void finish(int wave) {
+        if (wave < 4) __builtin_amdgcn_s_barrier();
+    }
+
+    // wvoff + wsoff[q]: weight instruction q's source (row offsets and the
+    // lane's chunk, at k = 0); svoff: the lane's scale row (at k = 0);
+    // xoff[q]: token instruction q's source.  klen in codes.
+    template <bool COMPUTE, int AJUMP>
+    __device__ __forceinline__ void run(char* lds, prsrc_t rw, uint32_t wvoff,
+                                        const uint32_t* wsoff, prsrc_t rs, uint32_t svoff,
+                                        prsrc_t rx, const uint32_t* xoff, int klen, int wave,
+                                        int wb, int arow0) {
+        static_assert(AJUMP % 16 == 0, "fragment rows must share one swizzle");
+        const int lane = lane_id();
+        const bool grp_b = wave >= 4;
+        const int gw = wave & 3;
+#pragma unroll
+        for (int a = 0; a < FW; ++a)
+#pragma unroll
+            for (int b = 0; b < FT; ++b) acc[a][b] = f32x4_t{0, 0, 0, 0};
+
+        typedef __attribute__((address_space(3))) void* lds_ptr_t;
+        auto dma_w = [&](int step, int slot) {
+            char* base = lds + slot * kWSlot;
+#pragma unroll
+            for (int q = 0; q < kWInstr; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rw, (lds_ptr_t)(base + (q * 4 + gw) * 1024), 16,
+                    wvoff + (uint32_t)step * kWRowBytes, wsoff[q], 0, 0);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                rs, (lds_ptr_t)(lds + kSBase + slot * kSSlot + gw * 256), 4,
+                svoff + (uint32_t)step * 4, 0, 0, 0);
+        };
+        auto dma_x = [&](int step, int slot) {
+            char* base = lds + kXBase + slot * kXSlot;
+#pragma unroll
+            for (int q = 0; q < kXInstr; ++q)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(
+                    rx, (lds_ptr_t)(base + (q * 4 + gw) * 1024), 16,
+                    xoff[q] + (uint32_t)step * kXRowBytes, 0, 0, 0);
+        };
+        const int li = lane & 15, q4 = lane >> 4;
+        int aoff, boff[2], soff;
+        {
+            const int ra = arow0 + li, rb = wb * (TT / WT) + li;
+            aoff = ra * kWRowBytes + ((q4 ^ swz<kWCPR>(ra)) << 4);
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                boff[h] = rb * kXRowBytes + (((4 * h + q4) ^ swz<kXCPR>(rb)) << 4);
+            soff = ra * 4;
+        }
+        i32x4_t fa[FW];
+        i32x8_t fb[FT];
+        int sc[FW];
+        auto read_all = [&](int wslot, int xslot) {
+            const char* wbase = lds + wslot * kWSlot;
+            const char* sbase = lds + kSBase + wslot * kSSlot;
+            const char* xbase = lds + kXBase + xslot * kXSlot;
+#pragma unroll
+            for (int a = 0; a < FW; ++a) {
+                fa[a] = *reinterpret_cast<const i32x4_t*>(wbase + arow_delta<AJUMP>(a) * kWRowBytes +
+                                                          aoff);
+                sc[a] = *reinterpret_cast<const int*>(sbase + arow_delta<AJUMP>(a) * 4 + soff);
+            }
+#pragma unroll
+            for (int b = 0; b < FT; ++b) {
+                const i32x4_t lo = *reinterpret_cast<const i32x4_t*>(xbase + b * 16 * kXRowBytes +
+                                                                     boff[0]);
+                const i32x4_t hi = *reinterpret_cast<const i32x4_t*>(xbase + b * 16 * kXRowBytes +
+                                                                     boff[1]);
+                fb[b] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            }
+        };
+        auto mfma_all = [&]() {
+#pragma unroll
+            for (int a = 0; a < FW; ++a) {
+                const int sa = (sc[a] >> (8 * q4)) & 0xff;
+                const i32x8_t a8 = {fa[a][0], fa[a][1], fa[a][2], fa[a][3], 0, 0, 0, 0};
+#pragma unroll
+                for (int b = 0; b < FT; ++b)
+                    acc[a][b] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(
+                        a8, fb[b], acc[a][b], 4, 0, 0, sa, 0, 127);
+            }
+        };
+        auto barrier = [&]() {
+            __builtin_amdgcn_sched_barrier(0);
+            __builtin_amdgcn_s_barrier();
+            __builtin_amdgcn_sched_barrier(0);
+        };
+
+        const int steps = klen / BK;
+        barrier();
+        if (!grp_b) {
+            if (steps > 0) dma_x(0, 0);
+            wait_vmcnt<0>();
+        } else {
+            if (steps > 0) dma_w(0, 0);
+            if (steps > 1) {
+                dma_w(1, 1);
+                wait_vmcnt<kBInstr>();
+            } else {
+                wait_vmcnt<0>();
+            }
+        }
+        barrier();
+        if (grp_b) barrier();
+        int wsl = 0, xsl = 0;
+        for (int s = 0; s < steps; ++s) {
+            if constexpr (COMPUTE) read_all(wsl, xsl);
+            if (!grp_b) {
+                if (s + 1 < steps) dma_x(s + 1, xsl ^ 1);
+            } else {
+                if (s + 2 < steps) {
+                    dma_w(s + 2, wsl == 0 ? 2 : wsl - 1);
+                    wait_vmcnt<kBInstr>();
+                } else {
+                    wait_vmcnt<0>();
+                }
+            }
+            __builtin_amdgcn_s_waitcnt(0xC07F);
+            barrier();
+            if constexpr (COMPUTE) mfma_all();
+            if (!grp_b) wait_vmcnt<0>();
+            barrier();
+            wsl = wsl + 1 == WST ? 0 : wsl + 1;
+            xsl ^= 1;
+        }
+#pragma unroll
+        for (int a = 0; a < FW; ++a)
+#pragma unroll
+            for (int b = 0; b < FT; ++b) pin(acc[a][b]);
+    }
+};
+
+// ---------------------------------------------------------------------------
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
@@ -918,6 +1120,163 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
 }
 
 // ---------------------------------------------------------------------------
+// MXFP4 weights on the full tiles (PingPongMxCore), against the per-token
+// e4m3 activations of the e4m3 path: GEMM1 applies s_x[t] (the E8M0 block
+// scales are inside the MFMA), forms SiLU(gate)*up in fp32, stores it and
+// folds each row's |act| max into amax[r]; GEMM2 multiplies by the sorted
+// row's activation scale s_a[r] and the routing weight.
+// ---------------------------------------------------------------------------
+template <int GROUP>
+__global__ __launch_bounds__(512, 1) void gemm1_prefill_mx_kernel(
+    const uint8_t* __restrict__ xq, const float* __restrict__ xscale,
+    const uint8_t* __restrict__ w1, const uint8_t* __restrict__ w1e8,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
+    int max_blocks, float* __restrict__ act, uint32_t* __restrict__ amax) {
+    using Core = PingPongMxCore<256>;
+    __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
+    constexpr int TT = Core::TT;
+    constexpr int HW = 128;     // n-values per tile (128 gate + 128 up weight rows)
+    constexpr int WN = HW / Core::WW;
+
+    const int npad = *num_padded;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wa = Core::wave_a(wave), wb = Core::wave_b(wave);
+    TileWalk<GROUP> walk(N / HW, max_blocks);
+    int wt, blk;
+    while (walk.next(wt, blk)) {
+    if (blk * TT >= npad) continue;
+    const int e = block_expert[blk];
+
+    const size_t wrow = (size_t)K / 2, srow = (size_t)K / 32, xrow = (size_t)K;
+    const prsrc_t rw = pmake_rsrc(w1 + (size_t)e * 2 * N * wrow, (uint32_t)(2 * (size_t)N * wrow));
+    const prsrc_t rs = pmake_rsrc(w1e8 + (size_t)e * 2 * N * srow, (uint32_t)(2 * (size_t)N * srow));
+    const prsrc_t rx = pmake_rsrc(xq, (uint32_t)((size_t)M * xrow));
+    // tile weight row lr is gate row wt*HW + lr (lr < HW) or up row
+    // N + wt*HW + lr - HW; a weight copy's 16 rows never straddle the two
+    uint32_t wsoff[Core::kWInstr], xoff[Core::kXInstr];
+    const int row0 = Core::w_dma_row(wave, 0, lane);
+    const uint32_t wvoff = (uint32_t)((wt * HW + row0) * wrow) + Core::w_dma_chunk(row0, lane) * 16;
+#pragma unroll
+    for (int q = 0; q < Core::kWInstr; ++q) {
+        const int first = Core::w_dma_row(wave, q, 0);
+        const int shift = first - Core::w_dma_row(wave, 0, 0) + (first >= HW ? N - HW : 0);
+        wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * wrow));
+    }
+    const int sr = Core::s_dma_row(wave, lane);
+    const uint32_t svoff = (uint32_t)((sr < HW ? wt * HW + sr : N + wt * HW + sr - HW) * srow);
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
+        const int p = sorted_ids[blk * TT + row];
+        const int t = p < nslots ? p / topk : 0;
+        xoff[q] = (uint32_t)(t * xrow) + Core::dma_chunk(row, lane) * 16;
+    }
+    Core core;
+    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+        core.template run<true, HW>(lds, rw, wvoff, wsoff, rs, svoff, rx, xoff, K, wave, wb, wa * WN);
+    else
+        core.template run<false, HW>(lds, rw, wvoff, wsoff, rs, svoff, rx, xoff, K, wave, wb, wa * WN);
+
+    const int li = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 16 + li;
+        const int p = sorted_ids[r];
+        const bool valid = p < nslots;
+        const float sx = valid ? xscale[p / topk] : 0.0f;
+        float m = 0.0f;
+#pragma unroll
+        for (int a = 0; a < Core::FW / 2; ++a) {
+            // accumulator element v: gate row n0 + v (and that up row)
+            const int n0 = wt * HW + wa * WN + a * 16 + 4 * q4;
+            f32x4_t o;
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                o[v] = silu(core.acc[a][b][v] * sx) * (core.acc[a + Core::FW / 2][b][v] * sx);
+                m = fmaxf(m, fabsf(o[v]));
+            }
+            if (valid) *reinterpret_cast<f32x4_t*>(act + (size_t)r * N + n0) = o;
+        }
+        // lanes l, l^16, l^32, l^48 hold the same token row
+        const uint32_t mb = col_max_bits(__float_as_uint(m));
+        if (valid && lane < 16) atomicMax(amax + r, mb);
+    }
+    core.finish(wave);
+    }  // tiles
+}
+
+template <int GROUP>
+__global__ __launch_bounds__(512, 1) void gemm2_prefill_mx_kernel(
+    const uint8_t* __restrict__ act_q, const float* __restrict__ ascale,
+    const uint8_t* __restrict__ w2, const uint8_t* __restrict__ w2e8,
+    const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
+    int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
+    using Core = PingPongMxCore<256>;
+    __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
+    constexpr int TT = Core::TT, TW = 256;
+    constexpr int WR = TW / Core::WW;  // output rows per wave
+
+    const int n_wt = K / TW;
+    const int npad = *num_padded;
+    const int lane = lane_id();
+    const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int wa = Core::wave_a(wave), wb = Core::wave_b(wave);
+    TileWalk<GROUP> walk(n_wt * nsplit, max_blocks);
+    int wtz, blk;
+    while (walk.next(wtz, blk)) {
+    if (blk * TT >= npad) continue;
+    const int wt = wtz % n_wt, z = wtz / n_wt;
+    const int nlen = N / nsplit, nbeg = z * nlen;
+    const int e = block_expert[blk];
+
+    const size_t wrow = (size_t)N / 2, srow = (size_t)N / 32, xrow = (size_t)N;
+    const prsrc_t rw = pmake_rsrc(w2 + ((size_t)e * K + (size_t)wt * TW) * wrow,
+                                  (uint32_t)(TW * wrow));
+    const prsrc_t rs = pmake_rsrc(w2e8 + ((size_t)e * K + (size_t)wt * TW) * srow,
+                                  (uint32_t)(TW * srow));
+    const prsrc_t ra = pmake_rsrc(act_q, (uint32_t)((size_t)cap * xrow));
+    uint32_t wsoff[Core::kWInstr], aoff[Core::kXInstr];
+    const int row0 = Core::w_dma_row(wave, 0, lane);
+    const uint32_t wvoff = (uint32_t)(row0 * wrow) + nbeg / 2 + Core::w_dma_chunk(row0, lane) * 16;
+#pragma unroll
+    for (int q = 0; q < Core::kWInstr; ++q)
+        wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane(
+            (int)((Core::w_dma_row(wave, q, 0) - Core::w_dma_row(wave, 0, 0)) * wrow));
+    const uint32_t svoff = (uint32_t)(Core::s_dma_row(wave, lane) * srow) + nbeg / 32;
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) {
+        const int row = Core::dma_row(wave, q, lane);
+        // padding rows (never written) copy the block's first row; their
+        // columns are never stored
+        const int src = sorted_ids[blk * TT + row] < nslots ? blk * TT + row : blk * TT;
+        aoff[q] = (uint32_t)(src * xrow) + nbeg + Core::dma_chunk(row, lane) * 16;
+    }
+    Core core;
+    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+        core.template run<true, 0>(lds, rw, wvoff, wsoff, rs, svoff, ra, aoff, nlen, wave, wb, wa * WR);
+    else
+        core.template run<false, 0>(lds, rw, wvoff, wsoff, rs, svoff, ra, aoff, nlen, wave, wb, wa * WR);
+
+    const int li = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 16 + li;
+        const int p = sorted_ids[r];
+        if (p >= nslots) continue;
+        const float w = topk_w[p] * ascale[r];
+        float* dst = ypart + ((size_t)z * nslots + p) * K + wt * TW + wa * WR + 4 * q4;
+#pragma unroll
+        for (int a = 0; a < Core::FW; ++a)
+            *reinterpret_cast<f32x4_t*>(dst + a * 16) = core.acc[a][b] * w;
+    }
+    core.finish(wave);
+    }  // tiles
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 // One workgroup per tile, rounded up to whole XCD groups of 8.
@@ -1033,6 +1392,30 @@ void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const v
             act_q, ascale, (const uint8_t*)w2, w2_scale, rowwise, topk_w, sorted_ids,
             block_expert, num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     }
+}
+
+// MXFP4 weights on the full tiles (256-row blocks; K, N multiples of 256;
+// GEMM2 splits of multiples of 128 codes)
+void launch_gemm1_prefill_mx(const uint8_t* xq, const float* xscale, const void* w1,
+                             const uint8_t* w1e8, const int32_t* sorted_ids,
+                             const int32_t* block_expert, const int32_t* num_padded, int M,
+                             int topk, int nslots, int K, int N, int max_blocks, float* act,
+                             uint32_t* amax, hipStream_t s) {
+    const int grid = tile_grid((N / 128) * max_blocks);
+    gemm1_prefill_mx_kernel<tune::kPrefillMxGemm1Group><<<grid, 512, 0, s>>>(
+        xq, xscale, (const uint8_t*)w1, w1e8, sorted_ids, block_expert, num_padded, M, topk,
+        nslots, K, N, max_blocks, act, amax);
+}
+
+void launch_gemm2_prefill_mx(const uint8_t* act_q, const float* ascale, const void* w2,
+                             const uint8_t* w2e8, const float* topk_w, const int32_t* sorted_ids,
+                             const int32_t* block_expert, const int32_t* num_padded, int cap,
+                             int nslots, int K, int N, int nsplit, int max_blocks, float* ypart,
+                             hipStream_t s) {
+    const int grid = tile_grid((K / 256) * nsplit * max_blocks);
+    gemm2_prefill_mx_kernel<tune::kPrefillMxGemm2Group><<<grid, 512, 0, s>>>(
+        act_q, ascale, (const uint8_t*)w2, w2e8, topk_w, sorted_ids, block_expert, num_padded,
+        cap, nslots, K, N, nsplit, max_blocks, ypart);
 }
 
 }  // namespace moe

@@ -128,6 +128,20 @@ void launch_gemm2_prefill_fp8(const uint8_t* act_q, const float* ascale, const v
                               const int32_t* num_padded, int cap, int nslots, int K, int N,
                               int nsplit, int max_blocks, int tt, float* ypart, hipStream_t s);
 
+// MXFP4 weights on the full tiles (256-row blocks only; K, N multiples of
+// 256; with nsplit > 1, (N / nsplit) % 128 == 0): the activations as the
+// e4m3 full tiles
+void launch_gemm1_prefill_mx(const uint8_t* xq, const float* xscale, const void* w1,
+                             const uint8_t* w1e8, const int32_t* sorted_ids,
+                             const int32_t* block_expert, const int32_t* num_padded, int M,
+                             int topk, int nslots, int K, int N, int max_blocks, float* act,
+                             uint32_t* amax, hipStream_t s);
+void launch_gemm2_prefill_mx(const uint8_t* act_q, const float* ascale, const void* w2,
+                             const uint8_t* w2e8, const float* topk_w, const int32_t* sorted_ids,
+                             const int32_t* block_expert, const int32_t* num_padded, int cap,
+                             int nslots, int K, int N, int nsplit, int max_blocks, float* ypart,
+                             hipStream_t s);
+
 void launch_combine(const float* ypart, int M, int K, int topk, int nsplit, void* out,
                     hipStream_t s);
 

@@ -19,7 +19,7 @@ namespace tune {
 // blocks (Mixtral shape, 16 rows: 0.586 ms decode against 0.548 tiles).
 constexpr long kDecodeMaxRowsPerExpert = 8;
 // e4m3 weights: the decode kernels up to this many token-slots per expert,
-// the full tiles above (MXFP4 weights have only the decode kernels).  Sweep
+// the full tiles above.  Sweep
 // of both families (bench.py --fp8 --regime-sweep), ms per layer call at
 // 8 / 16 / 32 / 64 rows per expert, decode against tiles:
 //   K, N, E, k = 4096, 14336, 8, 2: 0.300/0.330, 0.332/0.338, 0.422/0.353,
@@ -27,6 +27,14 @@ constexpr long kDecodeMaxRowsPerExpert = 8;
 //   K, N, E, k = 7168, 2048, 256, 8: 2.14/2.42, 2.43/2.54, 3.09/2.82,
 //                                   4.85/3.20 (128 rows: 8.73/4.16)
 constexpr long kFp8DecodeMaxRowsPerExpert = 16;
+// MXFP4 weights: the same rule.  Sweep (bench.py --mxfp4 --regime-sweep),
+// ms per layer call at 8 / 16 / 24 / 32 / 48 / 64 rows per expert, decode
+// against tiles:
+//   K, N, E, k = 4096, 14336, 8, 2: 0.234/0.311, 0.252/0.311, 0.319/0.314,
+//                                   0.338/0.319, 0.387/0.330, 0.575/0.344
+//   K, N, E, k = 7168, 2048, 256, 8: 1.35/2.11, 1.68/2.18, 2.17/2.28,
+//                                   2.38/2.39, 2.85/2.54, 3.89/2.75
+constexpr long kMxDecodeMaxRowsPerExpert = 24;
 
 // ---- decode block rows ------------------------------------------------------
 // 16, 32 or 64 sorted rows per block (1, 2 or 4 token tiles multiplied by
@@ -114,6 +122,8 @@ constexpr int kPrefillGemm2Group = 4;
 // for GEMM1, 3 + 2 for GEMM2): GEMM1 971-972 against 986-998 us, GEMM2
 // 526-529 against 552-555 us, step 1.766-1.775 against 1.799-1.809 ms.
 constexpr int kPrefillFp8Gemm1Group = 2, kPrefillFp8Gemm2Group = 4;
+// MXFP4 weights on the full tiles (256-row blocks, the ping-pong core)
+constexpr int kPrefillMxGemm1Group = 2, kPrefillMxGemm2Group = 4;
 
 // ---- two-launch decode of one or two tokens (bf16) -----------------------------
 // every workgroup recomputes all router logits, M*E pairs of K-long fp64 dot

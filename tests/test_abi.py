@@ -108,13 +108,16 @@ def test_fused_validation(lib):
     INV, UNS, WSP = B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE
     assert fused(lib, dtype=4)[0] == INV
     assert fused(lib, dtype=3)[0] == INV                              # MXFP4 without scales
-    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, regime=2)[0] == UNS
+    # MXFP4 full tiles (size query only)
+    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, regime=2, ws=None)[0] == B.MOE_OK
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=384)[0] == UNS       # MXFP4: multiples of 256
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, K=16640)[0] == UNS     # MXFP4: K <= 16384
     # MXFP4: GEMM2 splits must hold <= 8192 reduction elements; 8448 = 33*256
     # cannot be halved into multiples of 256
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=8448)[0] == UNS
     assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=8192, ws=None)[0] == 0  # size query succeeds
+    # the full tiles copy their scales per step: no such limit there
+    assert fused(lib, dtype=3, s1=FAKE, s2=FAKE, N=8448, regime=2, ws=None)[0] == 0
     assert fused(lib, dtype=2)[0] == INV                              # rowwise fp8 without scales
     assert fused(lib, dtype=2, s1=FAKE, s2=None)[0] == INV
     # e4m3 weights have full-tile kernels too (size query only: no launch here)
@@ -188,7 +191,7 @@ def test_fused_plan(lib):
     p = P()
     assert lib.moe_fused_plan(0, 8, 200, 512, 8, 2, 0, ctypes.byref(p)) == B.MOE_ERR_UNSUPPORTED
     assert lib.moe_fused_plan(5, 8, 256, 512, 8, 2, 0, ctypes.byref(p)) == B.MOE_ERR_INVALID_ARG
-    assert lib.moe_fused_plan(3, 8, 256, 512, 8, 2, 2, ctypes.byref(p)) == B.MOE_ERR_UNSUPPORTED
+    assert lib.moe_fused_plan(3, 8, 256, 384, 8, 2, 2, ctypes.byref(p)) == B.MOE_ERR_UNSUPPORTED
     cases = {  # (dtype, M, K, N, E, k): regime, block
         (0, 64, 256, 512, 8, 2): (2, 128),      # 16 rows per expert: full tiles
         (0, 8, 4096, 14336, 8, 2): (1, 16),
@@ -196,6 +199,14 @@ def test_fused_plan(lib):
         (0, 4096, 4096, 14336, 8, 2): (2, 256),
         (1, 128, 7168, 2048, 256, 8): (1, 16),
         (1, 4096, 7168, 2048, 256, 8): (2, 128),
+        # MXFP4: the decode kernels up to 24 rows per expert, then the full
+        # tiles, always with 256-row blocks
+        (3, 128, 7168, 2048, 256, 8): (1, 16),
+        (3, 8, 4096, 14336, 8, 2): (1, 16),
+        (3, 4096, 7168, 2048, 256, 8): (2, 256),
+        (3, 96, 4096, 14336, 8, 2): (1, 64),       # 24 rows per expert
+        (3, 100, 4096, 14336, 8, 2): (2, 256),
+        (3, 4096, 4096, 14336, 8, 2): (2, 256),
     }
     for (dt, M, K, N, E, k), (regime, block) in cases.items():
         p = moe.fused_plan(dt, M, K, N, E, k)

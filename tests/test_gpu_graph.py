@@ -25,6 +25,7 @@ CASES = [
     ("decode_mxfp4", 8, 512, 512, 8, 2, "mxfp4", 0),
     ("fp8_32_row_blocks", 48, 512, 256, 8, 2, "fp8", 0),
     ("full_tiles_fp8", 96, 512, 512, 6, 2, "fp8", 2),
+    ("full_tiles_mxfp4", 300, 512, 512, 8, 2, "mxfp4", 0),
     # more than 2048 token-slots: the multi-workgroup align in the graph
     ("multi_align_tiles", 1100, 256, 256, 8, 2, "bf16", 0),
     ("multi_align_tiles_fp8", 1100, 256, 256, 8, 2, "fp8", 0),

@@ -270,7 +270,7 @@ SMALL = [
     # MXFP4 weights (e2m1, E8M0 per 32 elements) with e4m3 activations
     ("mxfp4_tiny", 16, 512, 256, 16, 4, "mxfp4", None, 0),
     ("mxfp4_ragged", 7, 768, 512, 32, 8, "mxfp4", None, 0),
-    ("mxfp4_many_rows", 300, 256, 512, 8, 2, "mxfp4", None, 0),
+    ("mxfp4_many_rows", 300, 256, 512, 8, 2, "mxfp4", None, 1),
     # tiny batches through the single-workgroup routing, with router bias;
     # FP8 with K > 1024 quantises the token rows in their own kernel
     ("tiny_route_bias", 8, 768, 512, 8, 2, False, 0.5, 0),
@@ -280,7 +280,7 @@ SMALL = [
     ("router_split_k", 80, 2048, 256, 128, 4, False, 0.5, 0),
     # MXFP4 with 32- and 64-row blocks
     ("mxfp4_two_tiles", 48, 512, 512, 8, 2, "mxfp4", None, 0),
-    ("mxfp4_four_tiles", 160, 256, 512, 8, 2, "mxfp4", 0.5, 0),
+    ("mxfp4_four_tiles", 160, 256, 512, 8, 2, "mxfp4", 0.5, 1),
     # many experts and a wider intermediate dimension
     ("mxfp4_wide_grid", 32, 512, 1024, 64, 4, "mxfp4", None, 0),
     ("single_token", 1, 512, 1024, 16, 2, False, None, 0),
@@ -294,6 +294,16 @@ SMALL = [
     ("fp8_rowwise_prefill", 200, 256, 256, 4, 2, "rowwise", None, 2),
     ("fp8_rowwise_prefill_ragged", 97, 384, 384, 3, 2, "rowwise", 0.5, 2),
     ("fp8_prefill_auto_skewed", 700, 256, 384, 8, 2, True, 0.5, 0),
+    # MXFP4 weights on the full tiles (256-row blocks): forced, ragged token
+    # count and expert count, reduction split in 2 and 4, 256 experts with
+    # a few rows each, top-16, and the automatic choice at many rows
+    ("mxfp4_prefill_tiles", 300, 256, 512, 8, 2, "mxfp4", None, 2),
+    ("mxfp4_prefill_ragged", 333, 512, 768, 5, 3, "mxfp4", None, 2),
+    ("mxfp4_prefill_split2", 150, 256, 256, 4, 2, "mxfp4", None, 2),
+    ("mxfp4_prefill_split4", 260, 512, 512, 4, 2, "mxfp4", 0.5, 2),
+    ("mxfp4_prefill_many_experts", 300, 256, 256, 256, 8, "mxfp4", None, 2),
+    ("mxfp4_topk16_tiles", 40, 256, 256, 32, 16, "mxfp4", None, 2),
+    ("mxfp4_prefill_auto_skewed", 700, 256, 512, 8, 2, "mxfp4", 0.5, 0),
     # full tiles over 256 experts with a few rows each (one mostly-padding
     # block per expert, block owners and sentinels over a long sorted list)
     ("fp8_prefill_many_experts", 300, 256, 256, 256, 8, True, None, 2),
@@ -422,17 +432,36 @@ def test_fp8_decode_vs_tiles(moe):
     assert eab <= 2e-2
 
 
+def test_mxfp4_decode_vs_tiles(moe):
+    """MXFP4 weights on the decode kernels and on the full tiles, identical
+    inputs: both within tolerance of the oracle and close to each other (the
+    block scales act inside the MFMA on both; they differ by fp32 summation
+    order and the e4m3 activation codes that order can move)."""
+    note("mxfp4 decode vs full tiles")
+    wl = wlm.Workload("xcheck_mx", M=96, K=512, N=768, E=6, topk=2, mxfp4=True, seed=13)
+    d, g = gen_small(wl)
+    a = out_f64(run_layer(moe, g, wl, 1))
+    b = out_f64(run_layer(moe, g, wl, 2))
+    ref, _, _ = oracle_layer(d, wl)
+    ea, eb, eab = row_rel_err(a, ref), row_rel_err(b, ref), row_rel_err(a, b)
+    note(f"  decode {ea:.3e} tiles {eb:.3e} between {eab:.3e}")
+    assert ea <= TOL_FP8 and eb <= TOL_FP8
+    assert eab <= 2e-2
+
+
 def test_fused_deterministic(moe):
     """Ten calls on the same inputs are bitwise identical on every path: the
-    decode and full-tile kernels, bf16 and e4m3, the multi-workgroup align
+    decode and full-tile kernels, bf16, e4m3 and MXFP4, the multi-workgroup align
     and the routing GEMM1 with GEMM2 + combine of two tokens (no result
     depends on the order of atomics or on timing)."""
     note("determinism")
     wl = wlm.Workload("det", M=40, K=512, N=512, E=8, topk=2, seed=4)
     big = wlm.Workload("det_big", M=1100, K=256, N=256, E=8, topk=2, seed=5)
     two = wlm.Workload("det_two_tokens", M=2, K=512, N=512, E=8, topk=2, seed=6)
-    for w, regimes in ((wl, (1, 2)), (wl.resized(fp8=True), (1, 2)), (big, (0,)),
-                       (big.resized(fp8=True), (0,)), (two, (0,))):
+    for w, regimes in ((wl, (1, 2)), (wl.resized(fp8=True), (1, 2)),
+                       (wl.resized(mxfp4=True), (1, 2)), (big, (0,)),
+                       (big.resized(fp8=True), (0,)), (big.resized(mxfp4=True), (0,)),
+                       (two, (0,))):
         d, g = gen_small(w)
         for regime in regimes:
             outs = [run_layer(moe, g, w, regime).clone() for _ in range(10)]
@@ -475,11 +504,18 @@ def stratified_tokens(rids, E, B, M, k, n_min=64, max_experts=16):
 
 
 # the DeepSeek-shaped batch also with per-channel e4m3 weight scales and with
-# MXFP4 weights and at 4096 tokens; the prefill batch also with e4m3 weights
-@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + ["dsv3_fp8_rowwise", "dsv3_mxfp4",
-                                                      "mixtral_prefill_fp8", "dsv3_fp8_4096"])
+# MXFP4 weights and at 4096 tokens; the prefill batch also with e4m3 and with
+# MXFP4 weights
+@pytest.mark.parametrize("name", list(wlm.WORKLOADS) + [
+    "dsv3_fp8_rowwise", "dsv3_mxfp4", "mixtral_prefill_fp8", "mixtral_prefill_mxfp4",
+    "dsv3_fp8_4096", "dsv3_mxfp4_4096"])
 def test_fused_full_size_sampled(moe, name):
-    if name == "dsv3_fp8_4096":
+    if name == "dsv3_mxfp4_4096":
+        # MXFP4 full tiles over 256 experts (about 128 rows each, 256-row blocks)
+        wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, M=4096, fp8=False, mxfp4=True)
+    elif name == "mixtral_prefill_mxfp4":
+        wl = wlm.WORKLOADS["mixtral_prefill"].resized(name=name, mxfp4=True)
+    elif name == "dsv3_fp8_4096":
         # 4096 tokens on the DeepSeek shape: 32 768 token-slots over 256
         # experts (about 128 each): e4m3 full tiles with 128-row blocks and
         # the multi-workgroup align
