@@ -34,7 +34,11 @@ constexpr int kFusedExpertGroup = 4;        // router: expert rows of a wave in 
 constexpr int kFusedMaxBlocks = 4;          // routed experts (16-row blocks) of the layer
 // GEMM2 + combine: waves splitting N (8 when N % 1024 == 0: single-token
 // decode, 1 x 4096 and 4096 x 8192 experts, 78.3-78.6 against 79.9 us per
-// layer call with 4)
+// layer call with 4).  Both kernels stream with two fragments (the next
+// step's loads issued before the current step's MFMAs); rotations of 3 or 4
+// fragments with the loads of 2 or 3 steps in flight measured slower on
+// that shape: routing GEMM1 57.4 (3) and 57.5 (4) against 54.5 us, GEMM2
+// 35.3 (3) and 48.9 (4, spilling) against 28.3 us.
 
 typedef __amdgpu_buffer_rsrc_t frsrc_t;
 

@@ -109,6 +109,20 @@ constexpr int kPrefillGemm2Group = 4;
 // 4 best (849-854 us against 878 with 2, 890 with 8).
 // (Before the ping-pong core, the shared core's rings measured best at 3 + 2
 // slots for GEMM1 and 2 + 3 for GEMM2: 933-935 us against 946-950 with 3 + 2.)
+// Tried on the ping-pong core and dropped:
+// * the token rows as the ring copied two steps ahead (2 weight + 3 token
+//   slots): GEMM1 1612-1618 against 1619-1659 us, GEMM2 907 against
+//   851-878, e4m3 GEMM1 1018 against 975;
+// * for an expert's last block with at most 128 (64) valid rows, all 8
+//   waves on those rows with a quarter of the weight rows each: GEMM1
+//   1623-1627 against 1611 us, GEMM2 850-854 against 847-850 (e4m3
+//   993 / 522 against 983 / 526).  Skipping those blocks' tiles outright
+//   (a timing probe) takes GEMM1 from 1640 to 1380 us: they cost about 70 %
+//   of a full tile whatever their MFMA count.
+// * (probes) all experts reading expert 0's weights: GEMM1 1600 against
+//   1690 us on one box, L2 hit rate 71 % against 65 %, clock 1.67 against
+//   1.56 GHz, matrix cores busy 68.6 % in both: fewer bytes from beyond L2
+//   buy clock, not utilisation.
 // the e4m3 full tiles (same bytes per K-step as the bf16 ones).  GEMM1
 // group, rings (weight + token slots), us on the Mixtral shape with 4096
 // tokens / the DeepSeek shape with 4096 tokens (two runs where given):
@@ -122,7 +136,11 @@ constexpr int kPrefillGemm2Group = 4;
 // for GEMM1, 3 + 2 for GEMM2): GEMM1 971-972 against 986-998 us, GEMM2
 // 526-529 against 552-555 us, step 1.766-1.775 against 1.799-1.809 ms.
 constexpr int kPrefillFp8Gemm1Group = 2, kPrefillFp8Gemm2Group = 4;
-// MXFP4 weights on the full tiles (256-row blocks, the ping-pong core)
+// MXFP4 weights on the full tiles (256-row blocks, the ping-pong core).
+// GEMM1 / GEMM2 us, Mixtral shape with 4096 tokens / DeepSeek shape with
+// 4096 tokens, for groups (GEMM1, GEMM2): (1, 4) 949/1608, 522/1160;
+// (2, 4) 944/1594, 521/1151; (4, 4) 928/2309, 522/1150; (2, 2) 944/1593,
+// 529/1169; (2, 8) 945/1610, 538/1474.
 constexpr int kPrefillMxGemm1Group = 2, kPrefillMxGemm2Group = 4;
 
 // ---- two-launch decode of one or two tokens (bf16) -----------------------------
