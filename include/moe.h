@@ -321,6 +321,44 @@ moe_status moe_fused_plan(int dtype, int M, int K, int N, int E, int topk, int r
                           moe_plan *plan);
 
 /*
+ * moe_fused_graph_create / _launch / _destroy -- moe_fused_forward_ex
+ * captured once into a HIP graph, for callers that re-run the layer on fixed
+ * buffers (serving loops): each moe_fused_graph_launch is one graph launch
+ * instead of the layer's six to eight kernel launches.
+ * ("AI混合专家模型性能优化全链路解析" §3.1 captures the expert computation in
+ * a graph to cut launch overhead; this is the HIP form of that step.)
+ *
+ *   arguments    as moe_fused_forward_ex; workspace_bytes is the size of the
+ *                caller's workspace (not a pointer: no size query here)
+ *   stream       create: the stream the one eager call runs on
+ *   graph        out: the handle (NULL on error)
+ *
+ * Create runs the layer once eagerly on `stream` (this loads every kernel of
+ * the sequence and computes `out`), then captures the same launch sequence
+ * on a stream of its own and instantiates the graph.  The graph is bound to
+ * the pointers given: a launch recomputes out from whatever x, the weights
+ * and the scales hold when it runs, using the same workspace; launches that
+ * overlap with each other or with other users of that workspace race.
+ * Launch enqueues the graph on `stream` (asynchronous).  Destroy releases
+ * the graph (NULL is a no-op); the caller keeps every buffer.
+ *
+ * Errors: create -- as moe_fused_forward_ex (checked before any HIP call),
+ * INVALID_ARG for a NULL graph pointer, NULL workspace or M == 0, WORKSPACE
+ * when workspace_bytes is below the required size, HIP when the capture or
+ * instantiation fails; launch -- INVALID_ARG for a NULL handle, HIP when the
+ * launch fails.
+ */
+typedef struct moe_graph_s *moe_graph;
+moe_status moe_fused_graph_create(const void *x, const void *w_router, const float *router_bias,
+                                  const void *w1, const void *w2,
+                                  const void *w1_scale, const void *w2_scale,
+                                  int dtype, int M, int K, int N, int E, int topk, int regime,
+                                  void *out, void *workspace, size_t workspace_bytes,
+                                  void *stream, moe_graph *graph);
+moe_status moe_fused_graph_launch(moe_graph graph, void *stream);
+moe_status moe_fused_graph_destroy(moe_graph graph);
+
+/*
  * moe_fused_forward_noalloc -- moe_fused_forward for callers that cannot
  * allocate device memory (code under HIP graph capture, tight serving loops,
  * harnesses that forbid hipMalloc): no workspace argument, no allocation,

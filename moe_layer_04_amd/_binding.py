@@ -36,7 +36,8 @@ MOE_REGIME_PREFILL = 2
 
 EXPORTS = ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3", "moe_fused_forward",
            "moe_fused_forward_ex", "moe_fused_forward_timed", "moe_fused_plan",
-           "moe_fused_forward_noalloc", "moe_status_string")
+           "moe_fused_forward_noalloc", "moe_fused_graph_create", "moe_fused_graph_launch",
+           "moe_fused_graph_destroy", "moe_status_string")
 
 NOALLOC_SCRATCH_BYTES = 128 << 20   # MOE_NOALLOC_SCRATCH_BYTES
 
@@ -88,9 +89,14 @@ def load_library(build_if_missing: bool = False):
                                                 SZP, P, P]
         lib.moe_fused_plan.argtypes = [I, I, I, I, I, I, I, ctypes.POINTER(Plan)]
         lib.moe_fused_forward_noalloc.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, P, P]
+        lib.moe_fused_graph_create.argtypes = [P, P, P, P, P, P, P, I, I, I, I, I, I, I, P, P,
+                                               ctypes.c_size_t, P, ctypes.POINTER(P)]
+        lib.moe_fused_graph_launch.argtypes = [P, P]
+        lib.moe_fused_graph_destroy.argtypes = [P]
         for name in ("moe_topk", "moe_align", "moe_align_ex", "moe_quant_rows_e4m3",
                      "moe_fused_forward", "moe_fused_forward_ex", "moe_fused_forward_timed",
-                     "moe_fused_plan", "moe_fused_forward_noalloc"):
+                     "moe_fused_plan", "moe_fused_forward_noalloc", "moe_fused_graph_create",
+                     "moe_fused_graph_launch", "moe_fused_graph_destroy"):
             getattr(lib, name).restype = ctypes.c_int
         lib.moe_status_string.argtypes = [I]
         lib.moe_status_string.restype = ctypes.c_char_p
@@ -273,10 +279,30 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
     ``workspace`` (uint8, at least workspace_size bytes) may be passed to
     avoid an allocation per call."""
     lib = load_library()
+    dtype, M, K, N, E = _fused_args(x, w_router, router_bias, w1, w2, w1_scale, w2_scale)
+    dev = x.device
+    if out is None:
+        out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+    _dev(out, "out", torch.bfloat16, (M, K))
+    need = workspace_size(dtype, M, K, N, E, topk, regime)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
+    _dev(workspace, "workspace", torch.uint8)
+    nbytes = ctypes.c_size_t(workspace.numel())
+    _check(lib.moe_fused_forward_ex(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1),
+                                    _ptr(w2), _ptr(w1_scale), _ptr(w2_scale), dtype, M, K, N, E,
+                                    topk, regime, _ptr(out), _ptr(workspace),
+                                    ctypes.byref(nbytes), _stream(dev)),
+           "moe_fused_forward")
+    return out
+
+
+def _fused_args(x, w_router, router_bias, w1, w2, w1_scale, w2_scale):
+    """Checks the layer's tensors; returns (dtype, M, K, N, E)."""
     fp8 = w1.dtype == torch.uint8
     dtype = _weight_dtype(w1, w1_scale)
     M, K = x.shape
-    E, twoN, K1 = w1.shape
+    E, twoN, _ = w1.shape
     N = twoN // 2
     _dev(x, "x", torch.bfloat16)
     _dev(w_router, "w_router", torch.bfloat16, (E, K))
@@ -299,21 +325,7 @@ def moe_fused_forward(x: torch.Tensor, w_router: torch.Tensor,
             _dev(w2_scale, "w2_scale", torch.float32, (E,))
         elif w1_scale is not None or w2_scale is not None:
             raise ValueError("scales are only for e4m3 / MXFP4 weights")
-    dev = x.device
-    if out is None:
-        out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-    _dev(out, "out", torch.bfloat16, (M, K))
-    need = workspace_size(dtype, M, K, N, E, topk, regime)
-    if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-    _dev(workspace, "workspace", torch.uint8)
-    nbytes = ctypes.c_size_t(workspace.numel())
-    _check(lib.moe_fused_forward_ex(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1),
-                                    _ptr(w2), _ptr(w1_scale), _ptr(w2_scale), dtype, M, K, N, E,
-                                    topk, regime, _ptr(out), _ptr(workspace),
-                                    ctypes.byref(nbytes), _stream(dev)),
-           "moe_fused_forward")
-    return out
+    return dtype, M, K, N, E
 
 
 def moe_fused_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor,
@@ -349,40 +361,53 @@ def moe_fused_forward_noalloc(x: torch.Tensor, w_router: torch.Tensor,
 
 
 class FusedForwardGraph:
-    """One moe_fused_forward captured in a HIP graph (torch.cuda.CUDAGraph),
-    for serving loops that re-run the layer on fixed buffers.
+    """One moe_fused_forward captured in a HIP graph by the library
+    (moe_fused_graph_create), for serving loops that re-run the layer on
+    fixed buffers: ``replay()`` is one moe_fused_graph_launch on the current
+    stream.
 
-    The layer's launches only enqueue kernels on the current stream (no
-    allocation, host synchronisation or memset), so the whole launch
-    sequence is captured as it is.  The graph is bound to the tensors given
-    here: ``replay()`` recomputes ``out`` from whatever ``x`` (and the
-    weights) hold at that moment.  ``out`` and the workspace are owned by
-    this object."""
+    The graph is bound to the tensors given here (this object keeps them
+    alive): a replay recomputes ``out`` from whatever ``x`` (and the weights)
+    hold at that moment.  ``out`` and the workspace are owned by this
+    object.  Creating it runs the layer once eagerly on the current stream."""
 
     def __init__(self, x: torch.Tensor, w_router: torch.Tensor,
                  router_bias: Optional[torch.Tensor], w1: torch.Tensor, w2: torch.Tensor,
                  topk: int, *, w1_scale: Optional[torch.Tensor] = None,
                  w2_scale: Optional[torch.Tensor] = None, regime: int = MOE_REGIME_AUTO):
-        dev = x.device
-        M, K = x.shape
-        E, twoN, _ = w1.shape
-        need = workspace_size(_weight_dtype(w1, w1_scale), M, K, twoN // 2, E, topk, regime)
-        self.out = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=dev)
-        args = (x, w_router, router_bias, w1, w2, topk)
-        kw = dict(w1_scale=w1_scale, w2_scale=w2_scale, regime=regime, out=self.out,
-                  workspace=self.workspace)
-        # one eager call on a side stream before capture (library and kernel
-        # loading happen outside the graph)
-        side = torch.cuda.Stream(device=dev)
-        side.wait_stream(torch.cuda.current_stream(dev))
-        with torch.cuda.stream(side):
-            moe_fused_forward(*args, **kw)
-        torch.cuda.current_stream(dev).wait_stream(side)
-        self.graph = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(self.graph):
-            moe_fused_forward(*args, **kw)
+        lib = load_library()
+        self._handle = None
+        dtype, M, K, N, E = _fused_args(x, w_router, router_bias, w1, w2, w1_scale, w2_scale)
+        self.device = x.device
+        need = workspace_size(dtype, M, K, N, E, topk, regime)
+        self.out = torch.empty((M, K), dtype=torch.bfloat16, device=self.device)
+        self.workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=self.device)
+        self._inputs = (x, w_router, router_bias, w1, w2, w1_scale, w2_scale)
+        handle = ctypes.c_void_p()
+        _check(lib.moe_fused_graph_create(_ptr(x), _ptr(w_router), _ptr(router_bias), _ptr(w1),
+                                          _ptr(w2), _ptr(w1_scale), _ptr(w2_scale), dtype, M, K,
+                                          N, E, topk, regime, _ptr(self.out),
+                                          _ptr(self.workspace), self.workspace.numel(),
+                                          _stream(self.device), ctypes.byref(handle)),
+               "moe_fused_graph_create")
+        self._handle = handle
 
     def replay(self) -> torch.Tensor:
-        self.graph.replay()
+        _check(load_library().moe_fused_graph_launch(self._handle, _stream(self.device)),
+               "moe_fused_graph_launch")
         return self.out
+
+    def close(self) -> None:
+        """Releases the graph (after the work already enqueued has run)."""
+        if self._handle is not None:
+            torch.cuda.synchronize(self.device)
+            _check(load_library().moe_fused_graph_destroy(self._handle),
+                   "moe_fused_graph_destroy")
+            self._handle = None
+
+    def __del__(self):
+        if getattr(self, "_handle", None) is not None and _lib is not None:
+            try:
+                self.close()
+            except Exception:
+                pass

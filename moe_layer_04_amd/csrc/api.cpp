@@ -14,6 +14,7 @@
 #include <cmath>
 #include <hip/hip_runtime.h>
 #include <mutex>
+#include <new>
 #include <stdint.h>
 #include <string.h>
 
@@ -523,6 +524,91 @@ MOE_API moe_status moe_fused_forward(const void* x, const void* w_router,
     return moe_fused_forward_ex(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K,
                                 N, E, topk, MOE_REGIME_AUTO, out, workspace, workspace_bytes,
                                 stream);
+}
+
+// ---------------------------------------------------------------------------
+// The fused forward captured once into a HIP graph, for callers that replay
+// the layer on fixed buffers (serving loops): one graph launch per call
+// instead of the six to eight kernel launches.  The capture runs on a
+// library-created stream; the layer issues no allocation, host
+// synchronisation or memset, so its launch sequence is captured whole.
+// ---------------------------------------------------------------------------
+struct moe_graph_s {
+    hipGraphExec_t exec = nullptr;
+};
+
+MOE_API moe_status moe_fused_graph_create(const void* x, const void* w_router,
+                                          const float* router_bias, const void* w1,
+                                          const void* w2, const void* w1_scale,
+                                          const void* w2_scale, int dtype, int M, int K, int N,
+                                          int E, int topk, int regime, void* out,
+                                          void* workspace, size_t workspace_bytes, void* stream,
+                                          moe_graph* graph) {
+    if (!graph) return MOE_ERR_INVALID_ARG;
+    *graph = nullptr;
+    // every argument check of the eager call, before any HIP call
+    {
+        size_t need = 0;
+        const moe_status st = fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale,
+                                         dtype, M, K, N, E, topk, regime, out, nullptr, &need,
+                                         stream, nullptr, false);
+        if (st != MOE_OK) return st;
+        if (M == 0) return MOE_ERR_INVALID_ARG;  // nothing to capture
+        if (!workspace) return MOE_ERR_INVALID_ARG;
+        if (workspace_bytes < need) return MOE_ERR_WORKSPACE;
+    }
+    // one eager call on the caller's stream: validates the pointers and loads
+    // every kernel the sequence uses before capture
+    size_t have = workspace_bytes;
+    {
+        const moe_status st = fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale,
+                                         dtype, M, K, N, E, topk, regime, out, workspace, &have,
+                                         stream, nullptr, false);
+        if (st != MOE_OK) return st;
+    }
+    hipStream_t cs = nullptr;
+    if (hipStreamCreateWithFlags(&cs, hipStreamNonBlocking) != hipSuccess) return MOE_ERR_HIP;
+    hipGraph_t g = nullptr;
+    moe_status st = MOE_OK;
+    if (hipStreamBeginCapture(cs, hipStreamCaptureModeThreadLocal) != hipSuccess) {
+        st = MOE_ERR_HIP;
+    } else {
+        st = fused_impl(x, w_router, router_bias, w1, w2, w1_scale, w2_scale, dtype, M, K, N, E,
+                        topk, regime, out, workspace, &have, cs, nullptr, false);
+        // the capture always ends, whatever the layer returned
+        if (hipStreamEndCapture(cs, &g) != hipSuccess && st == MOE_OK) st = MOE_ERR_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    if (st == MOE_OK && (!g || hipGraphInstantiate(&exec, g, nullptr, nullptr, 0) != hipSuccess))
+        st = MOE_ERR_HIP;
+    if (g) (void)hipGraphDestroy(g);
+    (void)hipStreamDestroy(cs);
+    (void)hipGetLastError();
+    if (st != MOE_OK) {
+        if (exec) (void)hipGraphExecDestroy(exec);
+        return st;
+    }
+    moe_graph h = new (std::nothrow) moe_graph_s;
+    if (!h) {
+        (void)hipGraphExecDestroy(exec);
+        return MOE_ERR_HIP;
+    }
+    h->exec = exec;
+    *graph = h;
+    return MOE_OK;
+}
+
+MOE_API moe_status moe_fused_graph_launch(moe_graph graph, void* stream) {
+    if (!graph || !graph->exec) return MOE_ERR_INVALID_ARG;
+    (void)hipGetLastError();
+    return hipGraphLaunch(graph->exec, (hipStream_t)stream) == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+MOE_API moe_status moe_fused_graph_destroy(moe_graph graph) {
+    if (!graph) return MOE_OK;
+    const hipError_t e = graph->exec ? hipGraphExecDestroy(graph->exec) : hipSuccess;
+    delete graph;
+    return e == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 // ---------------------------------------------------------------------------

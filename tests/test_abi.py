@@ -256,3 +256,33 @@ def test_noalloc_validation(lib):
     # the decode batches fit
     for dt, M, K, N, E, k in ((0, 8, 4096, 14336, 8, 2), (0, 1, 4096, 8192, 16, 2)):
         assert moe.fused_plan(dt, M, K, N, E, k).workspace_bytes <= B.NOALLOC_SCRATCH_BYTES
+
+
+def test_graph_validation(lib):
+    """moe_fused_graph_create rejects bad arguments before any HIP call;
+    launching a NULL handle is an argument error and destroying it a no-op."""
+    create = lib.moe_fused_graph_create
+    INV, UNS, WSP = B.MOE_ERR_INVALID_ARG, B.MOE_ERR_UNSUPPORTED, B.MOE_ERR_WORKSPACE
+
+    def call(x=FAKE, w1=FAKE, s1=None, s2=None, dtype=0, M=8, K=256, N=512, E=8, k=2,
+             regime=0, out=FAKE, ws=FAKE, nbytes=1 << 40, handle=True):
+        h = ctypes.c_void_p(0x1234)
+        rc = create(x, FAKE, None, w1, FAKE, s1, s2, dtype, M, K, N, E, k, regime, out, ws,
+                    nbytes, None, ctypes.byref(h) if handle else None)
+        # on every error the handle comes back NULL (or was never written)
+        assert rc == B.MOE_OK or not handle or h.value is None
+        return rc
+
+    assert call(handle=False) == INV
+    assert call(M=-1) == INV
+    assert call(K=200) == UNS
+    assert call(dtype=1) == INV                       # e4m3 without scales
+    assert call(regime=3) == INV
+    assert call(M=0) == INV                           # nothing to capture
+    assert call(ws=None) == INV
+    need = moe.workspace_size(0, 8, 256, 512, 8, 2)
+    assert call(nbytes=need - 1) == WSP
+    assert call(x=None) == INV                        # the eager call's pointer checks
+    assert call(out=MISALIGNED) == INV
+    assert lib.moe_fused_graph_launch(None, None) == INV
+    assert lib.moe_fused_graph_destroy(None) == B.MOE_OK

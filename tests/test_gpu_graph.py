@@ -1,4 +1,5 @@
-"""The fused layer captured in a HIP graph (FusedForwardGraph).
+"""The fused layer captured in a HIP graph by the library
+(moe_fused_graph_create, through FusedForwardGraph).
 
 A captured launch sequence must give, on every replay, exactly what an eager
 call on the same inputs gives (the kernels are deterministic), and stay
