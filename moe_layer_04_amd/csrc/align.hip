@@ -39,15 +39,51 @@ __global__ __launch_bounds__(kAlignThreads) void topk_align_kernel(
     int32_t* __restrict__ expert_offsets, int32_t* __restrict__ num_padded,
     uint32_t* __restrict__ zero_buf, int zero_words, int32_t* __restrict__ inv) {
     __shared__ int32_t sid[kRouteSmallMaxSlots];
+    __shared__ float swt[kRouteSmallMaxSlots];
+    __shared__ float slog[kRouteSmallMaxTokens * MOE_KERNEL_MAX_EXPERTS];
     __shared__ AlignShared sh;
     const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
+    const int tid = (int)threadIdx.x;
+    // The batch's logits go to LDS in one pass, and each token's picks stay
+    // in LDS until all are done: a wave takes several tokens in turn, and
+    // with global loads and stores per token every token would wait for the
+    // previous one's stores (one counter tracks both) and for its own load.
+    {
+        constexpr int kPer = kRouteSmallMaxTokens * MOE_KERNEL_MAX_EXPERTS / kAlignThreads;
+        const int n = M * E;
+        float v[kPer];
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + j * kAlignThreads;
+            v[j] = i < n ? logits[i] : 0.0f;
+        }
+#pragma unroll
+        for (int j = 0; j < kPer; ++j) {
+            const int i = tid + j * kAlignThreads;
+            if (i < n) slog[i] = v[j];
+        }
+    }
     if (xq)
         for (int t = wave; t < M; t += kAlignWaves)
             quant_row_wave(x + (size_t)t * K, K, xq + (size_t)t * K, xscale + t);
-    for (int t = wave; t < M; t += kAlignWaves)
-        topk_wave(logits + (size_t)t * E, E, topk, topk_ids + (size_t)t * topk,
-                  topk_weights + (size_t)t * topk, sid + t * topk);
     __syncthreads();
+    if (E <= 16) {
+        // four tokens per wave at once, one per 16-lane row
+        for (int t0 = 4 * wave; t0 < M; t0 += 4 * kAlignWaves) {
+            const int t = t0 + (lane_id() >> 4);
+            const bool valid = t < M;
+            const int tt = valid ? t : 0;
+            topk_row16(slog + tt * E, valid, E, topk, sid + tt * topk, swt + tt * topk);
+        }
+    } else {
+        for (int t = wave; t < M; t += kAlignWaves)
+            topk_wave(slog + t * E, E, topk, sid + t * topk, swt + t * topk, nullptr);
+    }
+    __syncthreads();
+    for (int i = tid; i < M * topk; i += kAlignThreads) {
+        topk_ids[i] = sid[i];
+        topk_weights[i] = swt[i];
+    }
     align_body(sh, sid, M * topk, E, B, cap, sorted_ids, block_expert, expert_offsets,
                num_padded, zero_buf, zero_words, inv);
 }

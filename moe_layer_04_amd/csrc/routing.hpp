@@ -88,6 +88,55 @@ __device__ __forceinline__ void topk_wave(const float* row, int E, int topk,
     }
 }
 
+// The same selection and weights for E <= 16 experts with one token per
+// 16-lane row of the wave (four tokens at once): lane r of a row holds
+// expert r of its token, and the row max takes only the four in-row
+// exchange steps of the wave max.  Rows whose `valid` is false take no part
+// in any write.  ids, weights and arithmetic are those of topk_wave.
+// Wave-uniform call.
+__device__ __forceinline__ void topk_row16(const float* row, bool valid, int E, int topk,
+                                           int32_t* __restrict__ ids_out,
+                                           float* __restrict__ w_out) {
+    const int lane = lane_id();
+    const int r = lane & 15;
+    float lv = 0.0f;
+    uint64_t key = 0;
+    if (valid && r < E) {
+        lv = row[r];
+        key = ((uint64_t)ordered_bits(lv) << 32) | (uint32_t)(~(uint32_t)r);
+    }
+    float sel_l[MOE_KERNEL_MAX_TOPK];
+    int sel_e[MOE_KERNEL_MAX_TOPK];
+#pragma unroll
+    for (int j = 0; j < MOE_KERNEL_MAX_TOPK; ++j) {
+        if (j >= topk) break;
+        uint64_t best = key;
+        best = max_u64(best, xchg_u64<0>(best));
+        best = max_u64(best, xchg_u64<1>(best));
+        best = max_u64(best, xchg_u64<2>(best));
+        best = max_u64(best, xchg_u64<3>(best));
+        const int e = (int)(~(uint32_t)best) & 15;
+        sel_e[j] = e;
+        float l = 0.0f;
+        if (r == e) { key = 0; l = lv; }
+        sel_l[j] = __shfl(l, (lane & ~15) | e);
+    }
+    if (valid && r < topk) {
+        const float l0 = sel_l[0];
+        float den = 0.0f, mine = 0.0f;
+        int mye = 0;
+#pragma unroll
+        for (int j = 0; j < MOE_KERNEL_MAX_TOPK; ++j) {
+            if (j >= topk) break;
+            const float w = expf(sel_l[j] - l0);
+            den += w;
+            if (j == r) { mine = w; mye = sel_e[j]; }
+        }
+        ids_out[r] = mye;
+        w_out[r] = mine / den;
+    }
+}
+
 // ---------------------------------------------------------------------------
 // one router logit, one e4m3 row
 // ---------------------------------------------------------------------------
