@@ -505,12 +505,18 @@ def stratified_tokens(rids, E, B, M, k, n_min=64, max_experts=16):
 
 # the DeepSeek-shaped batch also with per-channel e4m3 weight scales and with
 # MXFP4 weights and at 4096 tokens; the prefill batch also with e4m3 and with
-# MXFP4 weights
+# MXFP4 weights; the Mixtral decode batch with e4m3 and MXFP4 weights and the
+# single token with MXFP4 weights
 @pytest.mark.parametrize("name", list(wlm.WORKLOADS) + [
     "dsv3_fp8_rowwise", "dsv3_mxfp4", "mixtral_prefill_fp8", "mixtral_prefill_mxfp4",
-    "dsv3_fp8_4096", "dsv3_mxfp4_4096"])
+    "dsv3_fp8_4096", "dsv3_mxfp4_4096", "mixtral_decode_fp8", "mixtral_decode_mxfp4",
+    "single_token_decode_mxfp4"])
 def test_fused_full_size_sampled(moe, name):
-    if name == "dsv3_mxfp4_4096":
+    if name in ("mixtral_decode_fp8", "mixtral_decode_mxfp4", "single_token_decode_mxfp4"):
+        # the decode shapes with e4m3 and MXFP4 weights (every token checked)
+        base, fmt = name.rsplit("_", 1)
+        wl = wlm.WORKLOADS[base].resized(name=name, fp8=fmt == "fp8", mxfp4=fmt == "mxfp4")
+    elif name == "dsv3_mxfp4_4096":
         # MXFP4 full tiles over 256 experts (about 128 rows each, 256-row blocks)
         wl = wlm.WORKLOADS["dsv3_fp8"].resized(name=name, M=4096, fp8=False, mxfp4=True)
     elif name == "mixtral_prefill_mxfp4":
