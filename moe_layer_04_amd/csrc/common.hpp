@@ -25,12 +25,16 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
 }
 
-// fp32 -> bf16 bits, round to nearest even (NaN kept quiet).
+// fp32 -> bf16 bits, round to nearest even, by the gfx950 conversion
+// instruction (v_cvt_pk_bf16_f32; NaN stays a quiet NaN).
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return (uint16_t)(u >> 16);
+    return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+// two values in one conversion instruction: lo in bits 0-15, hi in 16-31
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{lo, hi}, bf16x2_t));
 }
 
 // fp32 -> OCP E4M3FN code: nearest value, ties to the even mantissa, after
@@ -169,6 +173,10 @@ __device__ __forceinline__ void pin(T& v) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
-__device__ __forceinline__ float silu(float z) { return z / (1.0f + __expf(-z)); }
+// z / (1 + e^-z) with the hardware reciprocal (1 ulp) in place of the IEEE
+// division sequence; e^-z = inf gives z * 0 = -0, as the division would.
+__device__ __forceinline__ float silu(float z) {
+    return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z));
+}
 
 }  // namespace moe

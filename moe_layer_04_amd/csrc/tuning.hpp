@@ -98,6 +98,16 @@ constexpr long kPrefillSplitTargetTiles = 1024;
 // 4 against 990 with 8 and 1042 with 16)
 constexpr int kPrefillGemm1Group = 4;
 constexpr int kPrefillGemm2Group = 4;
+// bf16 256 x 256 tiles: the four-wave core (true) or the ping-pong core.
+// Mixtral-shaped prefill, alternating runs on one box: GEMM1 1574-1579 us
+// with the four-wave core against 1568 us with the ping-pong core, GEMM2
+// 872-873 against 852-853 us.  Counters of the four-wave core: 128 KB of
+// LDS reads per K-step instead of 192 KB lift the clock (1.73-1.79 against
+// 1.74 GHz at equal time), the matrix cores busy 64-65 % against 67 %;
+// timing probes of it: without its copies GEMM1 takes 1411 us, without its
+// fragment reads 1630 us, without its barrier and copy waits unchanged, with
+// neither reads nor copies 1370 us at 68 % busy.
+constexpr bool kPrefillBf16QuadCore = false;
 // The 256-row bf16 tiles of both GEMMs run the ping-pong core (two wave
 // groups a phase apart, 3 weight + 2 token ring slots).  Against the shared
 // core on one box, Mixtral-shaped prefill (alternating runs): GEMM1 1621-1626
