@@ -106,7 +106,12 @@ constexpr int kPrefillGemm2Group = 4;
 // 1.74 GHz at equal time), the matrix cores busy 64-65 % against 67 %;
 // timing probes of it: without its copies GEMM1 takes 1411 us, without its
 // fragment reads 1630 us, without its barrier and copy waits unchanged, with
-// neither reads nor copies 1370 us at 68 % busy.
+// neither reads nor copies 1370 us at 68 % busy.  A persistent form (one
+// workgroup per CU walking its XCD's tiles, the next tile's first copies
+// issued during the current tile's last steps, so that a tile starts
+// without waiting for memory) measured slower: GEMM1 1721-1723 us against
+// 1562-1568 us for the ping-pong core on one box (GEMM2 898-900 against
+// 862-865).
 constexpr bool kPrefillBf16QuadCore = false;
 // The 256-row bf16 tiles of both GEMMs run the ping-pong core (two wave
 // groups a phase apart, 3 weight + 2 token ring slots).  Against the shared
