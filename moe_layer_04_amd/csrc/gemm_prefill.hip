@@ -565,203 +565,6 @@ struct PingPongCore {
 };
 
 // ---------------------------------------------------------------------------
-// The four-wave loop for 256 x 256 bf16 tiles: one wave per SIMD, the waves
-// 2 x 2 over the tile, each a 128 x 128 block (4 x 4 MFMA tiles, 256
-// accumulator registers, which only a single wave per SIMD can hold).  Per
-// K-step the workgroup reads 128 KB of fragments from LDS, against 192 KB
-// for eight waves of 128 x 64 (each weight row is read by two waves instead
-// of four).  With one wave per SIMD no other wave covers a wave's waits, so
-// every k-slice issues its 16 MFMAs one at a time, each followed by one side
-// instruction: the 8 fragment reads of the next k-slice, then the step's
-// copies (the token rows of step s+1 in the first k-slice, the weight rows
-// of step s+2 in the second).  Rings and leads are the ping-pong core's (3
-// weight slots, 2 token slots); the waves meet once per step, before the
-// last k-slice, having waited for their own copies of step s+1: that barrier
-// publishes step s+1 and proves that step s-1's slots, which the next
-// copies overwrite, are no longer read.
-// ---------------------------------------------------------------------------
-template <int BK>
-struct QuadCore {
-    static constexpr int TW = 256, TT = 256, NW = 4, WW = 2, WT = 2;
-    static constexpr int WST = 3, XST = 2;
-    static constexpr int kRowBytes = BK * 2;
-    static constexpr int kCPR = kRowBytes / 16;
-    static constexpr int kRowsPerInstr = 64 / kCPR;
-    static constexpr int kWInstr = TW / kRowsPerInstr / NW;  // per wave and step
-    static constexpr int kXInstr = TT / kRowsPerInstr / NW;
-    static constexpr int kWSlot = TW * kRowBytes;
-    static constexpr int kXSlot = TT * kRowBytes;
-    static constexpr int kXBase = WST * kWSlot;
-    static constexpr int kLdsBytes = WST * kWSlot + XST * kXSlot;
-    static constexpr int FW = TW / WW / 32;  // 32-row A tiles per wave
-    static constexpr int FT = TT / WT / 32;  // 32-column B tiles per wave
-    static constexpr int KS = BK / 16;       // 32x32x16 k-slices per step
-    static constexpr int kReads = FW + FT;   // fragment reads per k-slice
-    static_assert(KS >= 3 && KS % 2 == 0, "copies in k-slices 0 and 1, the barrier in the last");
-    static_assert(FW == 4 && FT == 4 && kWInstr == 8 && kXInstr == 8,
-                  "the side-instruction schedule below: 8 reads and 4 or 8 copies per k-slice");
-    static_assert(kWInstr * kRowsPerInstr * NW == TW && kXInstr * kRowsPerInstr * NW == TT,
-                  "tile rows must split evenly over the waves' DMA instructions");
-
-    f32x16_t acc[FW][FT];
-
-    __device__ static __forceinline__ int dma_row(int wave, int q, int lane) {
-        return (q * NW + wave) * kRowsPerInstr + lane / kCPR;
-    }
-    __device__ static __forceinline__ int dma_chunk(int row, int lane) {
-        return (lane % kCPR) ^ swz<kCPR>(row);
-    }
-    __device__ static __forceinline__ int wave_a(int wave) { return wave % WW; }
-    __device__ static __forceinline__ int wave_b(int wave) { return wave / WW; }
-    template <int AJUMP>
-    __device__ static constexpr int arow_delta(int a) {
-        return AJUMP ? (a % (FW / 2)) * 32 + (a / (FW / 2)) * AJUMP : a * 32;
-    }
-    __device__ __forceinline__ void finish(int) {}
-
-    template <bool COMPUTE, int AJUMP>
-    __device__ __forceinline__ void run(char* lds, prsrc_t rw, uint32_t wvoff,
-                                        const uint32_t* wsoff, prsrc_t rx, const uint32_t* xoff,
-                                        int klen, int wave, int wb, int arow0) {
-        static_assert(AJUMP % 16 == 0, "fragment rows must share one swizzle");
-        const int lane = lane_id();
-#pragma unroll
-        for (int a = 0; a < FW; ++a)
-#pragma unroll
-            for (int b = 0; b < FT; ++b)
-#pragma unroll
-                for (int v = 0; v < 16; ++v) acc[a][b][v] = 0.0f;
-
-        typedef __attribute__((address_space(3))) void* lds_ptr_t;
-        // the step's K offset goes into the scalar offset, so a copy needs no
-        // vector instruction beside it
-        auto dma_w = [&](int step, int slot, int q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rw, (lds_ptr_t)(lds + slot * kWSlot + (q * NW + wave) * 1024), 16, wvoff,
-                wsoff[q] + (uint32_t)step * kRowBytes, 0, 0);
-        };
-        auto dma_x = [&](int step, int slot, int q) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(
-                rx, (lds_ptr_t)(lds + kXBase + slot * kXSlot + (q * NW + wave) * 1024), 16,
-                xoff[q], (uint32_t)step * kRowBytes, 0, 0);
-        };
-        // per-lane LDS offsets of the first A and B fragment of each k-slice:
-        // lane half h reads chunk 2*ks + h of its row (as PrefillCore)
-        const int li = lane & 31, half = lane >> 5;
-        int aoff[KS], boff[KS];
-        {
-            const int ra = arow0 + li, rb = wb * (TT / WT) + li;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const int c = 2 * ks + half;
-                aoff[ks] = ra * kRowBytes + ((c ^ swz<kCPR>(ra)) << 4);
-                boff[ks] = rb * kRowBytes + ((c ^ swz<kCPR>(rb)) << 4);
-            }
-        }
-        struct Frags { bf16x8_t v[kReads]; };  // A fragments, then B fragments
-        // fragment read r in the order the MFMAs consume them: A0, B0 .. B3,
-        // A1 .. A3
-        auto frag_of = [](int r) { return r == 0 ? 0 : r <= FT ? FW + r - 1 : r - FT; };
-        auto read1 = [&](Frags& f, int wslot, int xslot, int ks, int j) {
-            if (j < FW)
-                f.v[j] = *reinterpret_cast<const bf16x8_t*>(
-                    lds + wslot * kWSlot + arow_delta<AJUMP>(j) * kRowBytes + aoff[ks]);
-            else
-                f.v[j] = *reinterpret_cast<const bf16x8_t*>(
-                    lds + kXBase + xslot * kXSlot + (j - FW) * 32 * kRowBytes + boff[ks]);
-        };
-
-        const int steps = klen / BK;
-        // the previous tile's last LDS reads are done before refilling
-        __builtin_amdgcn_s_barrier();
-        // prologue: both operands of step 0, the weight rows of step 1;
-        // step 0 complete at the first barrier
-        if (steps > 0) {
-#pragma unroll
-            for (int q = 0; q < kWInstr; ++q) dma_w(0, 0, q);
-#pragma unroll
-            for (int q = 0; q < kXInstr; ++q) dma_x(0, 0, q);
-        }
-        if (steps > 1) {
-#pragma unroll
-            for (int q = 0; q < kWInstr; ++q) dma_w(1, 1, q);
-            wait_vmcnt<kWInstr>();
-        } else {
-            wait_vmcnt<0>();
-        }
-        __builtin_amdgcn_s_barrier();
-        Frags f[2];
-        if constexpr (COMPUTE) {
-#pragma unroll
-            for (int r = 0; r < kReads; ++r) read1(f[0], 0, 0, 0, frag_of(r));
-        }
-        int wsl = 0, xsl = 0;  // slots of step s
-        // One K-step.  After MFMA i of k-slice ks comes one side instruction:
-        // in k-slices 0 .. KS-2 at even i the fragment read i/2 of k-slice
-        // ks+1; in k-slice 0 at odd i the token copies of step s+1, in
-        // k-slices 1 and 2 at i = 1, 5, 9, 13 the weight copies of step s+2
-        // (both into step s-1's slots); the last k-slice starts with the
-        // barrier that publishes step s+1 and reads step s+1's first
-        // fragments at even i.  DX / DW: steps s+1 / s+2 exist (compile-time,
-        // so the sequence has no branches).
-        auto body = [&](auto dx_c, auto dw_c, int s) {
-            constexpr bool DX = decltype(dx_c)::value, DW = decltype(dw_c)::value;
-            const int pw = wsl == 0 ? WST - 1 : wsl - 1;  // step s-1's weight slot
-            const int nw = wsl + 1 == WST ? 0 : wsl + 1;  // step s+1's slots
-            const int nx = xsl ^ 1;
-#pragma unroll
-            for (int ks = 0; ks < KS; ++ks) {
-                const Frags& cur = f[ks & 1];
-                Frags& nxt = f[(ks + 1) & 1];
-                const bool last = ks + 1 == KS;
-                if (last && DX) {
-                    // this wave's copies of step s+1 have landed (the weight
-                    // rows of step s+2 may still fly) and its reads of step
-                    // s are done; then the workgroup's
-                    if (DW) wait_vmcnt<kWInstr>();
-                    else wait_vmcnt<0>();
-                    __builtin_amdgcn_s_waitcnt(0xC07F);
-                    __builtin_amdgcn_s_barrier();
-                }
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int i = 0; i < FW * FT; ++i) {
-                    if constexpr (COMPUTE)
-                        acc[i / FT][i % FT] =
-                            mfma32_bf16(cur.v[i / FT], cur.v[FW + i % FT], acc[i / FT][i % FT]);
-                    if (!last) {
-                        if (i % 2 == 0) {
-                            if constexpr (COMPUTE) read1(nxt, wsl, xsl, ks + 1, frag_of(i / 2));
-                        } else if (ks == 0) {
-                            if (DX) dma_x(s + 1, nx, i / 2);
-                        } else if (i % 4 == 1) {
-                            if (DW) dma_w(s + 2, pw, (ks - 1) * 4 + i / 4);
-                        }
-                    } else if (DX) {
-                        if (i % 2 == 0) {
-                            if constexpr (COMPUTE) read1(nxt, nw, nx, 0, frag_of(i / 2));
-                        }
-                    }
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            }
-            wsl = nw;
-            xsl = nx;
-        };
-        int s = 0;
-        for (; s + 2 < steps; ++s) body(std::true_type{}, std::true_type{}, s);
-        if (s + 1 < steps) body(std::true_type{}, std::false_type{}, s++);
-        if (s < steps) body(std::false_type{}, std::false_type{}, s);
-        // pinned where the MFMAs leave them, in the accumulator registers
-        // (a VGPR pin would copy all 256 of them out at once)
-#pragma unroll
-        for (int a = 0; a < FW; ++a)
-#pragma unroll
-            for (int b = 0; b < FT; ++b) asm volatile("" : "+a"(acc[a][b]));
-    }
-};
-
-// ---------------------------------------------------------------------------
 // The ping-pong loop for MXFP4 weights (OCP microscaling: e2m1 codes two per
 // byte, even element in the low nibble, one E8M0 scale per 32 elements of a
 // row) against e4m3 token rows, TW x 256 tiles, 8 waves in the two groups
@@ -963,37 +766,21 @@ struct PingPongMxCore {
     }
 };
 
-// The bf16 kernels' main loops: the shared core (any tile, NW waves), the
-// ping-pong core (256 token rows, 8 waves) or the four-wave core (256 x 256,
-// 4 waves); the template arguments must match the chosen core's shape.
-constexpr int kCoreShared = 0, kCorePingPong = 1, kCoreQuad = 2;
-template <int CORE, int TW, int TT, int BK, int WST, int XST, int WW, int NW>
-struct Bf16CoreSel {
-    static_assert(CORE != kCorePingPong || (TT == 256 && NW == 8 && WST == 3 && XST == 2),
-                  "the ping-pong core takes 256-row tiles and 8 waves");
-    static_assert(CORE != kCoreQuad ||
-                      (TW == 256 && TT == 256 && NW == 4 && WW == 2 && WST == 3 && XST == 2),
-                  "the four-wave core takes 256 x 256 tiles and 4 waves");
-    using type = typename std::conditional<
-        CORE == kCorePingPong, PingPongCore<TW, BK, WST, XST>,
-        typename std::conditional<CORE == kCoreQuad, QuadCore<BK>,
-                                  PrefillCore<TW, TT, BK, WST, XST, WW, NW>>::type>::type;
-};
-template <int CORE, int TW, int TT, int BK, int WST, int XST, int WW, int NW>
-using Bf16Core = typename Bf16CoreSel<CORE, TW, TT, BK, WST, XST, WW, NW>::type;
-
 // ---------------------------------------------------------------------------
 // GEMM1 + SiLU*up (bf16).  Weight tile wt covers n in [wt*TW/2, (wt+1)*TW/2):
 // LDS weight rows [0,TW/2) are those gate rows, [TW/2,TW) the up rows.
 // ---------------------------------------------------------------------------
 template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP,
-          int CORE = kCoreShared>
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w1,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, int M, int topk, int nslots, int K, int N,
     int max_blocks, uint16_t* __restrict__ act) {
-    using Core = Bf16Core<CORE, TW, TT, BK, WST, XST, WW, NW>;
+    // PP: the ping-pong core (256 token rows, 8 waves)
+    using Core = typename std::conditional<PP, PingPongCore<TW, BK, WST, XST>,
+                                           PrefillCore<TW, TT, BK, WST, XST, WW, NW>>::type;
+    static_assert(!PP || (TT == 256 && NW == 8), "the ping-pong core takes 256-row tiles");
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int HW = TW / 2;  // n-values per tile
     constexpr int WN = HW / WW; // n-values per wave
@@ -1059,8 +846,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
                 *reinterpret_cast<uint2*>(dst + 8 * vg) =
                     make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
             }
-            // with 256 accumulators, one fragment pair in registers at a time
-            if constexpr (CORE == kCoreQuad) __builtin_amdgcn_sched_barrier(0);
         }
     }
     core.finish(wave);
@@ -1072,13 +857,15 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
 // multiplies by the routing weight and scatters token row r to slot p.
 // ---------------------------------------------------------------------------
 template <int TW, int TT, int BK, int WST, int XST, int WW, int NW, int OCC, int GROUP,
-          int CORE = kCoreShared>
+          bool PP = false>
 __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const float* __restrict__ topk_w, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded, int cap,
     int nslots, int K, int N, int nsplit, int max_blocks, float* __restrict__ ypart) {
-    using Core = Bf16Core<CORE, TW, TT, BK, WST, XST, WW, NW>;
+    using Core = typename std::conditional<PP, PingPongCore<TW, BK, WST, XST>,
+                                           PrefillCore<TW, TT, BK, WST, XST, WW, NW>>::type;
+    static_assert(!PP || (TT == 256 && NW == 8), "the ping-pong core takes 256-row tiles");
     __shared__ __attribute__((aligned(1024))) char lds[Core::kLdsBytes];
     constexpr int WR = TW / WW;  // output rows per wave
 
@@ -1141,7 +928,6 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
                 for (int v = 0; v < 4; ++v) o[v] = core.acc[a][b][vg * 4 + v] * w;
                 *reinterpret_cast<f32x4_t*>(dst + 8 * vg) = o;
             }
-            if constexpr (CORE == kCoreQuad) __builtin_amdgcn_sched_barrier(0);
         }
     }
     core.finish(wave);
@@ -1511,14 +1297,9 @@ void launch_gemm1_prefill_bf16(const void* x, const void* w1, const int32_t* sor
                                   tune::kPrefillGemm1Group><<<grid, 512, 0, s>>>(
             (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
             topk, nslots, K, N, max_blocks, (uint16_t*)act);
-    else if (tune::kPrefillBf16QuadCore)
-        gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 4, 1, tune::kPrefillGemm1Group,
-                                  kCoreQuad><<<grid, 256, 0, s>>>(
-            (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
-            topk, nslots, K, N, max_blocks, (uint16_t*)act);
     else
         gemm1_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, tune::kPrefillGemm1Group,
-                                  kCorePingPong><<<grid, 512, 0, s>>>(
+                                  true><<<grid, 512, 0, s>>>(
             (const uint16_t*)x, (const uint16_t*)w1, sorted_ids, block_expert, num_padded, M,
             topk, nslots, K, N, max_blocks, (uint16_t*)act);
 }
@@ -1549,17 +1330,10 @@ void launch_gemm2_prefill_bf16(const void* act, const void* w2, const float* top
     } else if (K % 256 == 0 && (N / nsplit) % 64 == 0) {
         // 64-deep K-steps: each row copy is a whole 128-byte line
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
-        if (tune::kPrefillBf16QuadCore)
-            gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 4, 1,
-                                      tune::kPrefillGemm2Group, kCoreQuad><<<grid, 256, 0, s>>>(
-                (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
-                num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
-        else
-            gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1,
-                                      tune::kPrefillGemm2Group, kCorePingPong>
-                <<<grid, 512, 0, s>>>((const uint16_t*)act, (const uint16_t*)w2, topk_w,
-                                      sorted_ids, block_expert, num_padded, cap, nslots, K, N,
-                                      nsplit, max_blocks, ypart);
+        gemm2_prefill_bf16_kernel<256, kPrefillRows, 64, 3, 2, 2, 8, 1, tune::kPrefillGemm2Group,
+                                  true><<<grid, 512, 0, s>>>(
+            (const uint16_t*)act, (const uint16_t*)w2, topk_w, sorted_ids, block_expert,
+            num_padded, cap, nslots, K, N, nsplit, max_blocks, ypart);
     } else if (K % 256 == 0) {
         const int grid = tile_grid((K / 256) * nsplit * max_blocks);
         gemm2_prefill_bf16_kernel<256, kPrefillRows, 32, 3, 3, 4, 8, 1, 8><<<grid, 512, 0, s>>>(

@@ -98,21 +98,25 @@ constexpr long kPrefillSplitTargetTiles = 1024;
 // 4 against 990 with 8 and 1042 with 16)
 constexpr int kPrefillGemm1Group = 4;
 constexpr int kPrefillGemm2Group = 4;
-// bf16 256 x 256 tiles: the four-wave core (true) or the ping-pong core.
-// Mixtral-shaped prefill, alternating runs on one box: GEMM1 1574-1579 us
-// with the four-wave core against 1568 us with the ping-pong core, GEMM2
-// 872-873 against 852-853 us.  Counters of the four-wave core: 128 KB of
-// LDS reads per K-step instead of 192 KB lift the clock (1.73-1.79 against
-// 1.74 GHz at equal time), the matrix cores busy 64-65 % against 67 %;
-// timing probes of it: without its copies GEMM1 takes 1411 us, without its
-// fragment reads 1630 us, without its barrier and copy waits unchanged, with
-// neither reads nor copies 1370 us at 68 % busy.  A persistent form (one
-// workgroup per CU walking its XCD's tiles, the next tile's first copies
-// issued during the current tile's last steps, so that a tile starts
-// without waiting for memory) measured slower: GEMM1 1721-1723 us against
-// 1562-1568 us for the ping-pong core on one box (GEMM2 898-900 against
-// 862-865).
-constexpr bool kPrefillBf16QuadCore = false;
+// Measured and dropped for the bf16 256 x 256 tiles: a four-wave core (one
+// wave per SIMD, 128 x 128 wave tiles, 256 accumulators, every MFMA followed
+// by one fragment read or copy), parity-green.  Mixtral-shaped prefill,
+// alternating runs on one box: GEMM1 1574-1579 us against 1568 us with the
+// ping-pong core, GEMM2 872-873 against 852-853 us.  Its 128 KB of LDS reads
+// per K-step (192 KB for eight 128 x 64 waves) lift the clock (1.79 against
+// 1.74 GHz) but leave the matrix cores busy 64-65 % against 67 %; timing
+// probes of it: without its copies GEMM1 takes 1411 us, without its
+// fragment reads 1630 us, without its barrier and copy waits unchanged,
+// with neither reads nor copies 1370 us (68 % busy; 82 % busy when each
+// tile's loop runs four times as long, so about a fifth of that probe's
+// time is per-tile start and epilogue).  Forms that carry the copy ring
+// from one tile into the next, so that a tile after the first starts
+// without waiting for memory, were slower still: persistent workgroups
+// (1721 against 1562-1568 us; a static walk of equal shares leaves the CUs
+// unbalanced, since an expert's last block costs less), four weight tiles
+// of one token block per workgroup (1706-1712 against 1555-1573 us: 32
+// token blocks resident per XCD instead of 8), two token blocks of one
+// weight tile (1611-1623 against 1544-1551 us).
 // The 256-row bf16 tiles of both GEMMs run the ping-pong core (two wave
 // groups a phase apart, 3 weight + 2 token ring slots).  Against the shared
 // core on one box, Mixtral-shaped prefill (alternating runs): GEMM1 1621-1626
