@@ -173,6 +173,14 @@ __device__ __forceinline__ void pin(T& v) {
 
 __device__ __forceinline__ int lane_id() { return (int)__lane_id(); }
 
+// Token of sorted slot p (p = t*topk + j, non-negative).  The divisor is
+// clamped to 1 so that the compiler may compute the quotient for every lane
+// (a division by a value that might be zero stays behind a lane-divergent
+// branch, which also serialises the loads feeding it).
+__device__ __forceinline__ int slot_token(int p, int topk) {
+    return (int)((uint32_t)p / (uint32_t)max(topk, 1));
+}
+
 // z / (1 + e^-z) with the hardware reciprocal (1 ulp) in place of the IEEE
 // division sequence; e^-z = inf gives z * 0 = -0, as the division would.
 __device__ __forceinline__ float silu(float z) {

@@ -204,7 +204,7 @@ __global__ __launch_bounds__(256) void decode_route_gemm1_bf16_kernel(
     const frsrc_t rx = fmake_rsrc(x, (uint32_t)((size_t)M * row1));
     const uint32_t wo = (uint32_t)(i * row1) + kq * 16;
     const int slot_i = i < cnt ? blk_slot[i] : -1;
-    const uint32_t xo = slot_i >= 0 ? (uint32_t)((size_t)(slot_i / topk) * row1) + kq * 16
+    const uint32_t xo = slot_i >= 0 ? (uint32_t)((size_t)slot_token(slot_i, topk) * row1) + kq * 16
                                     : kFusedOob;
 
     struct Frag { i32x4_t g[4], u[4], b[4]; };

@@ -112,11 +112,13 @@ __global__ __launch_bounds__(256) void gemm1_decode_bf16_kernel(
     const uint32_t wo = (uint32_t)(i * row_bytes) + kq * 16;
     bool vj[NT];
     uint32_t xo[NT];
+    int pj[NT];  // the rows' slots, loaded together
+#pragma unroll
+    for (int j = 0; j < NT; ++j) pj[j] = sorted_ids[blk * BR + 16 * j + i];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = sorted_ids[blk * BR + 16 * j + i];
-        vj[j] = p < nslots;
-        xo[j] = vj[j] ? (uint32_t)((size_t)(p / topk) * row_bytes) + kq * 16 : kOob;
+        vj[j] = pj[j] < nslots;
+        xo[j] = vj[j] ? (uint32_t)((size_t)slot_token(pj[j], topk) * row_bytes) + kq * 16 : kOob;
     }
 
     struct Frag { i32x4_t g[4], u[4], b[NT][4]; };
@@ -300,11 +302,13 @@ __global__ __launch_bounds__(256) void gemm1_decode_fp8_kernel(
     int tj[NT];
     bool vj[NT];
     uint32_t xo[NT];
+    int pj[NT];  // the rows' slots, loaded together
+#pragma unroll
+    for (int j = 0; j < NT; ++j) pj[j] = sorted_ids[blk * BR + 16 * j + i];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = sorted_ids[blk * BR + 16 * j + i];
-        vj[j] = p < nslots;
-        tj[j] = vj[j] ? p / topk : 0;
+        vj[j] = pj[j] < nslots;
+        tj[j] = vj[j] ? slot_token(pj[j], topk) : 0;
         xo[j] = vj[j] ? (uint32_t)((size_t)tj[j] * row_bytes) + kq * 32 : kOob;
     }
 
@@ -572,11 +576,13 @@ __global__ __launch_bounds__(256) void gemm1_decode_mxfp4_kernel(
     const int i = lane & 15, kq = lane >> 4;
     int tj[NT];
     bool vj[NT];
+    int pj[NT];  // the rows' slots, loaded together
+#pragma unroll
+    for (int j = 0; j < NT; ++j) pj[j] = sorted_ids[blk * BR + 16 * j + i];
 #pragma unroll
     for (int j = 0; j < NT; ++j) {
-        const int p = sorted_ids[blk * BR + 16 * j + i];
-        vj[j] = p < nslots;
-        tj[j] = vj[j] ? p / topk : 0;
+        vj[j] = pj[j] < nslots;
+        tj[j] = vj[j] ? slot_token(pj[j], topk) : 0;
     }
 
     const size_t row_bytes = (size_t)K / 2;   // packed e2m1

@@ -811,11 +811,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
         const int shift = first - Core::dma_row(wave, 0, 0) + (first >= HW ? N - HW : 0);
         wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * row_bytes));
     }
+    // all of the wave's row loads first, in flight together
+    int pv[Core::kXInstr];
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) pv[q] = sorted_ids[blk * TT + Core::dma_row(wave, q, lane)];
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
-        const int p = sorted_ids[blk * TT + row];
-        const int t = p < nslots ? p / topk : 0;
+        const int t = pv[q] < nslots ? slot_token(pv[q], topk) : 0;
         xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
     // A tiles of this wave: its gate frags (LDS rows wa*WN + 32a), then the
@@ -983,11 +986,14 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
         const int shift = first - Core::dma_row(wave, 0, 0) + (first >= HW ? N - HW : 0);
         wsoff[q] = (uint32_t)__builtin_amdgcn_readfirstlane((int)(shift * row_bytes));
     }
+    // all of the wave's row loads first, in flight together
+    int pv[Core::kXInstr];
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) pv[q] = sorted_ids[blk * TT + Core::dma_row(wave, q, lane)];
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
-        const int p = sorted_ids[blk * TT + row];
-        const int t = p < nslots ? p / topk : 0;
+        const int t = pv[q] < nslots ? slot_token(pv[q], topk) : 0;
         xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
     Core core;
@@ -1003,7 +1009,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
         const int p = sorted_ids[r];
         const bool valid = p < nslots;
-        const float sx = valid ? xscale[p / topk] : 0.0f;
+        const float sx = valid ? xscale[slot_token(p, topk)] : 0.0f;
         float m = 0.0f;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
@@ -1167,11 +1173,14 @@ __global__ __launch_bounds__(512, 1) void gemm1_prefill_mx_kernel(
     }
     const int sr = Core::s_dma_row(wave, lane);
     const uint32_t svoff = (uint32_t)((sr < HW ? wt * HW + sr : N + wt * HW + sr - HW) * srow);
+    // all of the wave's row loads first, in flight together
+    int pv[Core::kXInstr];
+#pragma unroll
+    for (int q = 0; q < Core::kXInstr; ++q) pv[q] = sorted_ids[blk * TT + Core::dma_row(wave, q, lane)];
 #pragma unroll
     for (int q = 0; q < Core::kXInstr; ++q) {
         const int row = Core::dma_row(wave, q, lane);
-        const int p = sorted_ids[blk * TT + row];
-        const int t = p < nslots ? p / topk : 0;
+        const int t = pv[q] < nslots ? slot_token(pv[q], topk) : 0;
         xoff[q] = (uint32_t)(t * xrow) + Core::dma_chunk(row, lane) * 16;
     }
     Core core;
@@ -1186,7 +1195,7 @@ __global__ __launch_bounds__(512, 1) void gemm1_prefill_mx_kernel(
         const int r = blk * TT + wb * (TT / Core::WT) + b * 16 + li;
         const int p = sorted_ids[r];
         const bool valid = p < nslots;
-        const float sx = valid ? xscale[p / topk] : 0.0f;
+        const float sx = valid ? xscale[slot_token(p, topk)] : 0.0f;
         float m = 0.0f;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
