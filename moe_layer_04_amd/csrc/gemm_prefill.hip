@@ -823,6 +823,12 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     }
     // A tiles of this wave: its gate frags (LDS rows wa*WN + 32a), then the
     // matching up frags HW rows further
+    // the epilogue's rows, looked up before the main loop: their loads
+    // overlap the first copies instead of trailing the last MFMAs
+    bool row_ok[Core::FT];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_ok[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + (lane & 31)] < nslots;
     Core core;
     // a wave whose token rows are all padding (the tail of an expert's last
     // block) skips its MFMAs
@@ -835,7 +841,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
-        if (sorted_ids[r] >= nslots) continue;
+        if (!row_ok[b]) continue;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
             uint16_t* dst = act + (size_t)r * N + wt * HW + wa * WN + a * 32 + 4 * (lane >> 5);
@@ -914,12 +920,21 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
         core.template run<false, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
 
     const int li = lane & 31;
+    // the epilogue's rows: all slots, then all routing weights, loaded
+    // together (kept out of the main loop, whose registers are full)
+    int row_p[Core::FT];
+    float row_w[Core::FT];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_p[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + li];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) row_w[b] = row_p[b] < nslots ? topk_w[row_p[b]] : 0.0f;
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
-        const int p = sorted_ids[r];
+        const int p = row_p[b];
         if (p >= nslots) continue;
-        const float w = topk_w[p];
+        const float w = row_w[b];
 #pragma unroll
         for (int a = 0; a < Core::FW; ++a) {
             float* dst = ypart + ((size_t)z * nslots + p) * K + wt * TW + wa * WR + a * 32 +
@@ -996,6 +1011,16 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
         const int t = pv[q] < nslots ? slot_token(pv[q], topk) : 0;
         xoff[q] = (uint32_t)(t * row_bytes) + Core::dma_chunk(row, lane) * 16;
     }
+    // the epilogue's rows, looked up before the main loop: their loads
+    // overlap the first copies instead of trailing the last MFMAs
+    int row_p[Core::FT];
+    float row_sx[Core::FT];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_p[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + (lane & 31)];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_sx[b] = row_p[b] < nslots ? xscale[slot_token(row_p[b], topk)] : 0.0f;
     Core core;
     if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
         core.template run<true, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
@@ -1007,9 +1032,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
-        const int p = sorted_ids[r];
-        const bool valid = p < nslots;
-        const float sx = valid ? xscale[slot_token(p, topk)] : 0.0f;
+        const bool valid = row_p[b] < nslots;
+        const float sx = row_sx[b];
         float m = 0.0f;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
@@ -1097,13 +1121,26 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
         core.template run<false, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
 
     const int li = lane & 31;
+    // the epilogue's rows: all slots, then all routing weights and row
+    // scales, loaded together (kept out of the main loop, whose registers
+    // are full)
+    int row_p[Core::FT];
+    float row_w[Core::FT];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_p[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + li];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
+        row_w[b] = row_p[b] < nslots ? topk_w[row_p[b]] * ascale[r] : 0.0f;
+    }
     const float ws = rowwise ? 0.0f : w2_scale[e];
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
-        const int p = sorted_ids[r];
+        const int p = row_p[b];
         if (p >= nslots) continue;
-        const float w = topk_w[p] * ascale[r];
+        const float w = row_w[b];
 #pragma unroll
         for (int a = 0; a < Core::FW; ++a) {
             const int c0 = wt * TW + wa * WR + a * 32 + 4 * (lane >> 5);
@@ -1183,6 +1220,16 @@ __global__ __launch_bounds__(512, 1) void gemm1_prefill_mx_kernel(
         const int t = pv[q] < nslots ? slot_token(pv[q], topk) : 0;
         xoff[q] = (uint32_t)(t * xrow) + Core::dma_chunk(row, lane) * 16;
     }
+    // the epilogue's rows, looked up before the main loop: their loads
+    // overlap the first copies instead of trailing the last MFMAs
+    int row_p[Core::FT];
+    float row_sx[Core::FT];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_p[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 16 + (lane & 15)];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_sx[b] = row_p[b] < nslots ? xscale[slot_token(row_p[b], topk)] : 0.0f;
     Core core;
     if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
         core.template run<true, HW>(lds, rw, wvoff, wsoff, rs, svoff, rx, xoff, K, wave, wb, wa * WN);
@@ -1193,9 +1240,8 @@ __global__ __launch_bounds__(512, 1) void gemm1_prefill_mx_kernel(
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 16 + li;
-        const int p = sorted_ids[r];
-        const bool valid = p < nslots;
-        const float sx = valid ? xscale[slot_token(p, topk)] : 0.0f;
+        const bool valid = row_p[b] < nslots;
+        const float sx = row_sx[b];
         float m = 0.0f;
 #pragma unroll
         for (int a = 0; a < Core::FW / 2; ++a) {
@@ -1264,6 +1310,18 @@ __global__ __launch_bounds__(512, 1) void gemm2_prefill_mx_kernel(
         const int src = sorted_ids[blk * TT + row] < nslots ? blk * TT + row : blk * TT;
         aoff[q] = (uint32_t)(src * xrow) + nbeg + Core::dma_chunk(row, lane) * 16;
     }
+    // the epilogue's rows, looked up before the main loop: their loads
+    // overlap the first copies instead of trailing the last MFMAs
+    int row_p[Core::FT];
+    float row_w[Core::FT];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b)
+        row_p[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 16 + (lane & 15)];
+#pragma unroll
+    for (int b = 0; b < Core::FT; ++b) {
+        const int r = blk * TT + wb * (TT / Core::WT) + b * 16 + (lane & 15);
+        row_w[b] = row_p[b] < nslots ? topk_w[row_p[b]] * ascale[r] : 0.0f;
+    }
     Core core;
     if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
         core.template run<true, 0>(lds, rw, wvoff, wsoff, rs, svoff, ra, aoff, nlen, wave, wb, wa * WR);
@@ -1274,9 +1332,9 @@ __global__ __launch_bounds__(512, 1) void gemm2_prefill_mx_kernel(
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 16 + li;
-        const int p = sorted_ids[r];
+        const int p = row_p[b];
         if (p >= nslots) continue;
-        const float w = topk_w[p] * ascale[r];
+        const float w = row_w[b];
         float* dst = ypart + ((size_t)z * nslots + p) * K + wt * TW + wa * WR + 4 * q4;
 #pragma unroll
         for (int a = 0; a < Core::FW; ++a)
