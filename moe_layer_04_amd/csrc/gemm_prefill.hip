@@ -127,6 +127,97 @@ __device__ __forceinline__ void wait_vmcnt() {
     __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+// The wave's LDS accesses issued so far are complete (lgkmcnt(0)), and the
+// compiler moves no memory access across this point.  A wave's LDS
+// instructions execute in order, so after it the wave's lanes read what its
+// other lanes wrote before it.
+__device__ __forceinline__ void lds_wave_fence() {
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+// v, computed where it is used: an epilogue address derived from it is not
+// hoisted to the kernel's start, where it would hold a register through the
+// main loop (the ping-pong loops use all 256)
+__device__ __forceinline__ int late_uniform(int v) {
+    __asm__ volatile("" : "+s"(v));
+    return v;
+}
+
+// Epilogue staging of fp32 results through a ping-pong wave's own LDS area
+// (kStagedRowsBytes: 64 token rows x 64 columns plus the rows' 64 slots).
+// Stored straight from the 32x32 accumulator layout, a store instruction
+// writes 16 or 32 bytes to each of 32 rows; staged, it writes four rows'
+// whole 256-byte segments.  stage_put places the values of output columns
+// 32a + 8vg + 4*(lane/32) + 0..3 (a = 0, 1: a 64-column pass) of token row
+// 32b + lane%32; stage_slots records the rows' slots; stage_flush sends the
+// 64 staged rows to their destination rows, row j to dst + j*ld (contiguous
+// rows) or with SCATTER to dst + slot[j]*ld, skipping padding rows (slot[j]
+// >= nslots).
+constexpr int kStagedRowBytes = 64 * 4 + 16;  // the pad spreads a column's rows over the banks
+constexpr int kStagedRowsBytes = 64 * kStagedRowBytes + 64 * 4;
+
+// the lane's index, computed where it is used: per-lane epilogue addresses
+// are not hoisted to the kernel's start, where they would hold registers
+// through the main loop
+__device__ __forceinline__ int late_lane() {
+    int v;
+    __asm__ volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(v));
+    return v;
+}
+
+// lane: late_lane() of the epilogue
+__device__ __forceinline__ void stage_put(char* st, int lane, int b, int a, int vg, f32x4_t v) {
+    *reinterpret_cast<f32x4_t*>(st + (b * 32 + (lane & 31)) * kStagedRowBytes +
+                                (a * 32 + 8 * vg + 4 * (lane >> 5)) * 4) = v;
+}
+
+// slot of token row 32b + lane%32: row_p[b] (both lane halves write the same value)
+template <int FT>
+__device__ __forceinline__ void stage_slots(char* st, int lane, const int (&row_p)[FT]) {
+    int* slot = reinterpret_cast<int*>(st + 64 * kStagedRowBytes);
+#pragma unroll
+    for (int b = 0; b < FT; ++b) slot[b * 32 + (lane & 31)] = row_p[b];
+}
+
+template <bool SCATTER>
+__device__ __forceinline__ void stage_flush(const char* st, int lane, float* dst, size_t ld,
+                                            int nslots) {
+    const int rr = lane >> 4, c = lane & 15;
+    const int* slot = reinterpret_cast<const int*>(st + 64 * kStagedRowBytes);
+    lds_wave_fence();  // the wave's stage_put writes are done
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+        const int row = 4 * i + rr;
+        const f32x4_t v = *reinterpret_cast<const f32x4_t*>(st + row * kStagedRowBytes + c * 16);
+        const int p = slot[row];
+        if (p < nslots)
+            *reinterpret_cast<f32x4_t*>(dst + (size_t)(SCATTER ? p : row) * ld + c * 4) = v;
+    }
+    lds_wave_fence();  // its reads are done before the area is written again
+}
+
+// A wave's 64 token rows x WR results scattered to the rows of their slots
+// (row_p[j / 32] of lane j % 32 for token row j) in 64-column passes;
+// val(a, b, vg) gives accumulator (a, b)'s values 4vg..4vg+3.
+template <int WR, int FT, typename Val>
+__device__ __forceinline__ void store_rows_staged(char* st, const Val& val, const int (&row_p)[FT],
+                                                  int nslots, float* dst, int ld) {
+    static_assert(FT == 2 && WR % 64 == 0, "64 token rows, 64-column passes");
+    const int lane = late_lane();
+    lds_wave_fence();
+    stage_slots(st, lane, row_p);
+#pragma unroll
+    for (int pass = 0; pass < WR / 64; ++pass) {
+#pragma unroll
+        for (int b = 0; b < FT; ++b)
+#pragma unroll
+            for (int a = 0; a < 2; ++a)
+#pragma unroll
+                for (int vg = 0; vg < 4; ++vg) stage_put(st, lane, b, a, vg, val(2 * pass + a, b, vg));
+        stage_flush<true>(st, lane, dst + pass * 64, (size_t)ld, nslots);
+    }
+}
+
 // The shared main loop.  The weight rows and the token rows of each K-step
 // stream through two LDS rings, of WST and XST slots: the weight copy of a
 // step is issued WST-1 steps ahead, the token copy XST-1 steps ahead (when
@@ -418,7 +509,11 @@ struct PingPongCore {
         return AJUMP ? (a % (FW / 2)) * 32 + (a / (FW / 2)) * AJUMP : a * 32;
     }
     // group A's last barrier, matching group B's last compute phase; taken
-    // after the tile's epilogue so that A's stores overlap B's last MFMAs
+    // after the tile's epilogue so that A's stores overlap B's last MFMAs,
+    // and B's epilogue, which may stage through the same LDS, follows A's
+    // (dropping this pairing, so that the two epilogues overlap, measured
+    // no faster for the bf16 tiles and 9-18 % slower for the e4m3 and MXFP4
+    // GEMM1s)
     __device__ __forceinline__ void finish(int wave) {
         if (wave < 4) __builtin_amdgcn_s_barrier();
     }
@@ -832,12 +927,66 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
     Core core;
     // a wave whose token rows are all padding (the tail of an expert's last
     // block) skips its MFMAs
-    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+    const bool wave_valid = sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots;
+    if (wave_valid)
         core.template run<true, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
     else
         core.template run<false, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
 
     const int li = lane & 31;
+    if constexpr (PP) {
+        // The wave's 64 token rows x WN values go out through its own LDS
+        // area (the rings are idle once the group's last step is done), so
+        // that each store instruction writes whole 128-byte row segments
+        // (from the accumulator layout an instruction would write 16 bytes
+        // of each of 32 rows); the rows' validity is staged beside them.
+        if (wave_valid) {
+            constexpr int kSt = WN * 2 + 16;  // staged row bytes; the pad spreads the banks
+            constexpr int kArea = 64 * kSt + 64 * 4;
+            static_assert(4 * kArea <= Core::kLdsBytes, "the staging fits the rings");
+            char* st = lds + (wave & 3) * kArea;
+            int* ok = reinterpret_cast<int*>(st + 64 * kSt);
+            const int ln = late_lane(), lj = ln & 31;
+            // the rows' slots, loaded here (through the main loop they would
+            // hold registers) and needed only after the SiLU products
+            int pe[Core::FT];
+#pragma unroll
+            for (int b = 0; b < Core::FT; ++b)
+                pe[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + lj];
+            lds_wave_fence();
+#pragma unroll
+            for (int b = 0; b < Core::FT; ++b) {
+#pragma unroll
+                for (int a = 0; a < Core::FW / 2; ++a)
+#pragma unroll
+                    for (int vg = 0; vg < 4; ++vg) {
+                        float h[4];
+#pragma unroll
+                        for (int v = 0; v < 4; ++v)
+                            h[v] = silu(core.acc[a][b][vg * 4 + v]) *
+                                   core.acc[a + Core::FW / 2][b][vg * 4 + v];
+                        *reinterpret_cast<uint2*>(st + (b * 32 + lj) * kSt +
+                                                  (a * 32 + 8 * vg + 4 * (ln >> 5)) * 2) =
+                            make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                    }
+            }
+#pragma unroll
+            for (int b = 0; b < Core::FT; ++b)
+                ok[b * 32 + lj] = pe[b] < nslots;  // both lane halves write the same value
+            lds_wave_fence();
+            constexpr int kCpr = WN * 2 / 16;  // 16-byte chunks per row
+            constexpr int kRpi = 64 / kCpr;    // rows per instruction
+            const int rr = ln / kCpr, c = ln % kCpr;
+            uint16_t* dst = act + (size_t)(blk * TT + wb * (TT / Core::WT) + rr) * N + wt * HW +
+                            wa * WN + c * 8;
+#pragma unroll
+            for (int i = 0; i < 64 / kRpi; ++i) {
+                const uint4 v = *reinterpret_cast<const uint4*>(st + (i * kRpi + rr) * kSt + c * 16);
+                if (ok[i * kRpi + rr]) *reinterpret_cast<uint4*>(dst + (size_t)i * kRpi * N) = v;
+            }
+            lds_wave_fence();
+        }
+    } else {
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
@@ -856,6 +1005,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_bf16_kernel(
                     make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
             }
         }
+    }
     }
     core.finish(wave);
     }  // tiles
@@ -914,7 +1064,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
     }
     Core core;
     // A tiles of this wave: LDS rows wa*WR + 32a
-    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+    const bool wave_valid = sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots;
+    if (wave_valid)
         core.template run<true, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
     else
         core.template run<false, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
@@ -929,9 +1080,23 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
         row_p[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + li];
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) row_w[b] = row_p[b] < nslots ? topk_w[row_p[b]] : 0.0f;
+    if constexpr (PP) {
+        // the wave's 64 token rows x WR partial sums go out through its own
+        // LDS area (the rings are idle once the group's last step is done)
+        static_assert(4 * kStagedRowsBytes <= Core::kLdsBytes, "the staging fits the rings");
+        if (wave_valid)
+            store_rows_staged<WR>(
+                lds + late_uniform(wave & 3) * kStagedRowsBytes,
+                [&](int a, int b, int vg) {
+                    f32x4_t o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[v] = core.acc[a][b][vg * 4 + v] * row_w[b];
+                    return o;
+                },
+                row_p, nslots, ypart + (size_t)z * nslots * K + wt * TW + wa * WR, K);
+    } else {
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
-        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
         const int p = row_p[b];
         if (p >= nslots) continue;
         const float w = row_w[b];
@@ -947,6 +1112,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_bf16_kernel(
                 *reinterpret_cast<f32x4_t*>(dst + 8 * vg) = o;
             }
         }
+    }
     }
     core.finish(wave);
     }  // tiles
@@ -1022,13 +1188,67 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
     for (int b = 0; b < Core::FT; ++b)
         row_sx[b] = row_p[b] < nslots ? xscale[slot_token(row_p[b], topk)] : 0.0f;
     Core core;
-    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+    const bool wave_valid = sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots;
+    if (wave_valid)
         core.template run<true, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
     else
         core.template run<false, HW>(lds, rw, wvoff, wsoff, rx, xoff, K, wave, wb, wa * WN);
 
     const int li = lane & 31;
     const float ws = rowwise ? 0.0f : w1_scale[e];
+    if constexpr (PP) {
+        // the wave's 64 token rows x WN activations go out through its own
+        // LDS area, whole 256-byte row segments per store instruction
+        static_assert(WN == 64 && 4 * kStagedRowsBytes <= Core::kLdsBytes, "one staged pass");
+        if (wave_valid) {
+            char* st = lds + late_uniform(wave & 3) * kStagedRowsBytes;
+            const int ln = late_lane();
+            // the rows' slots, loaded again here rather than held through the
+            // main loop (only their activation scales are)
+            int pe[Core::FT];
+#pragma unroll
+            for (int b = 0; b < Core::FT; ++b)
+                pe[b] = sorted_ids[blk * TT + wb * (TT / Core::WT) + b * 32 + (ln & 31)];
+            lds_wave_fence();
+#pragma unroll
+            for (int b = 0; b < Core::FT; ++b) {
+                const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + (ln & 31);
+                const float sx = row_sx[b];
+                float m = 0.0f;
+#pragma unroll
+                for (int a = 0; a < Core::FW / 2; ++a) {
+                    const int n0 = wt * HW + wa * WN + a * 32 + 4 * (ln >> 5);
+#pragma unroll
+                    for (int vg = 0; vg < 4; ++vg) {
+                        f32x4_t sg, su;
+                        if (rowwise) {
+                            const float* sr = w1_scale + (size_t)e * 2 * N + n0 + 8 * vg;
+                            sg = *reinterpret_cast<const f32x4_t*>(sr);
+                            su = *reinterpret_cast<const f32x4_t*>(sr + N);
+                        } else {
+                            sg = su = f32x4_t{ws, ws, ws, ws};
+                        }
+                        f32x4_t o;
+#pragma unroll
+                        for (int v = 0; v < 4; ++v) {
+                            o[v] = silu(core.acc[a][b][vg * 4 + v] * (sx * sg[v])) *
+                                   (core.acc[a + Core::FW / 2][b][vg * 4 + v] * (sx * su[v]));
+                            m = fmaxf(m, fabsf(o[v]));
+                        }
+                        stage_put(st, ln, b, a, vg, o);
+                    }
+                }
+                // lanes l and l ^ 32 hold the same token row
+                const uint32_t mb =
+                    max(__float_as_uint(m), (uint32_t)__shfl_xor((int)__float_as_uint(m), 32));
+                if (pe[b] < nslots && ln < 32) atomicMax(amax + r, mb);
+            }
+            stage_slots(st, ln, pe);
+            stage_flush<false>(st, ln,
+                               act + (size_t)(blk * TT + wb * (TT / Core::WT)) * N + wt * HW + wa * WN,
+                               (size_t)N, nslots);
+        }
+    } else {
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
         const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
@@ -1063,6 +1283,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm1_prefill_fp8_kernel(
         // lanes l and l ^ 32 hold the same token row
         const uint32_t mb = max(__float_as_uint(m), (uint32_t)__shfl_xor((int)__float_as_uint(m), 32));
         if (valid && lane < 32) atomicMax(amax + r, mb);
+    }
     }
     core.finish(wave);
     }  // tiles
@@ -1115,7 +1336,8 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
         aoff[q] = (uint32_t)(src * row_bytes) + nbeg + Core::dma_chunk(row, lane) * 16;
     }
     Core core;
-    if (sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots)
+    const bool wave_valid = sorted_ids[blk * TT + wb * (TT / Core::WT)] < nslots;
+    if (wave_valid)
         core.template run<true, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
     else
         core.template run<false, 0>(lds, rw, wvoff, wsoff, ra, aoff, nlen, wave, wb, wa * WR);
@@ -1135,9 +1357,29 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
         row_w[b] = row_p[b] < nslots ? topk_w[row_p[b]] * ascale[r] : 0.0f;
     }
     const float ws = rowwise ? 0.0f : w2_scale[e];
+    if constexpr (PP) {
+        // the wave's 64 token rows x WR partial sums go out through its own
+        // LDS area (the rings are idle once the group's last step is done)
+        static_assert(4 * kStagedRowsBytes <= Core::kLdsBytes, "the staging fits the rings");
+        if (wave_valid)
+            store_rows_staged<WR>(
+                lds + late_uniform(wave & 3) * kStagedRowsBytes,
+                [&](int a, int b, int vg) {
+                    const int c0 = wt * TW + wa * WR + a * 32 + 4 * (lane >> 5);
+                    f32x4_t sc;
+                    if (rowwise)
+                        sc = *reinterpret_cast<const f32x4_t*>(w2_scale + (size_t)e * K + c0 + 8 * vg);
+                    else
+                        sc = f32x4_t{ws, ws, ws, ws};
+                    f32x4_t o;
+#pragma unroll
+                    for (int v = 0; v < 4; ++v) o[v] = core.acc[a][b][vg * 4 + v] * (sc[v] * row_w[b]);
+                    return o;
+                },
+                row_p, nslots, ypart + (size_t)z * nslots * K + wt * TW + wa * WR, K);
+    } else {
 #pragma unroll
     for (int b = 0; b < Core::FT; ++b) {
-        const int r = blk * TT + wb * (TT / Core::WT) + b * 32 + li;
         const int p = row_p[b];
         if (p >= nslots) continue;
         const float w = row_w[b];
@@ -1158,6 +1400,7 @@ __global__ __launch_bounds__(NW * 64, OCC) void gemm2_prefill_fp8_kernel(
                 *reinterpret_cast<f32x4_t*>(dst + 8 * vg) = o;
             }
         }
+    }
     }
     core.finish(wave);
     }  // tiles
