@@ -293,6 +293,9 @@ SMALL = [
     ("fp8_prefill_split4", 260, 512, 512, 4, 2, True, None, 2),
     ("fp8_rowwise_prefill", 200, 256, 256, 4, 2, "rowwise", None, 2),
     ("fp8_rowwise_prefill_ragged", 97, 384, 384, 3, 2, "rowwise", 0.5, 2),
+    # per-channel scales on the 256-row (ping-pong) tiles: 160-250 rows per
+    # expert, so every expert's last block is part padding
+    ("fp8_rowwise_prefill_256", 333, 256, 512, 3, 2, "rowwise", 0.5, 2),
     ("fp8_prefill_auto_skewed", 700, 256, 384, 8, 2, True, 0.5, 0),
     # MXFP4 weights on the full tiles (256-row blocks): forced, ragged token
     # count and expert count, reduction split in 2 and 4, 256 experts with
